@@ -1,0 +1,176 @@
+"""Python wrapper of the DSA oracle (oracle/dsa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, ``__graft_entry__.smoke()`` and the
+cpu_baseline leg of bench.py may import this package.  The product library
+(dsa_lightning_indexer_02_amd) never imports it, and this package never
+imports the product library.
+
+Every function takes host numpy arrays in the input formats of the method
+(FP8 E4M3 codes as uint8, bf16 as uint16 bit patterns) and returns numpy
+arrays.  ``pos`` is the absolute position of each query row; row t sees keys
+0 .. min(S, pos[t] + 1) - 1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+def load(path: Optional[str] = None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        from . import build as _b
+        _b.build(out=p)
+    lib = ctypes.CDLL(p)
+    lib.oracle_e4m3_table.argtypes = [_p]
+    lib.oracle_e4m3_table.restype = None
+    lib.oracle_bf16_round.argtypes = [_p, _p, _i64]
+    lib.oracle_bf16_round.restype = None
+    lib.oracle_gather_rows.argtypes = [_p, _i64, _p, _i32, _i64, _p]
+    lib.oracle_gather_rows.restype = ctypes.c_int
+    lib.oracle_indexer.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _i64, _i32, _i32, _p, _i64, _i32]
+    lib.oracle_indexer.restype = ctypes.c_int
+    lib.oracle_topk.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _p, _i32]
+    lib.oracle_topk.restype = ctypes.c_int
+    lib.oracle_sparse_mla.argtypes = [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _i64,
+                                      ctypes.c_float, _p, _p, _p, _i32]
+    lib.oracle_sparse_mla.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def e4m3_table(lib=None) -> np.ndarray:
+    lib = lib or load()
+    out = np.empty(256, dtype=np.float32)
+    lib.oracle_e4m3_table(_ptr(out))
+    return out
+
+
+def bf16_round(x: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.oracle_bf16_round(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def gather_rows(pool: np.ndarray, block_table: np.ndarray, n: int, lib=None) -> np.ndarray:
+    """Logical rows 0..n-1 of a paged pool [NB, bs, ...] via one sequence's block table."""
+    lib = lib or load()
+    pool = np.ascontiguousarray(pool)
+    bs = pool.shape[1]
+    row_shape = pool.shape[2:]
+    row_bytes = int(np.prod(row_shape, dtype=np.int64)) * pool.itemsize
+    out = np.empty((n,) + row_shape, dtype=pool.dtype)
+    tbl = _c(block_table, np.int32)
+    rc = lib.oracle_gather_rows(_ptr(pool), row_bytes, _ptr(tbl), bs, n, _ptr(out))
+    if rc:
+        raise ValueError("oracle_gather_rows: negative block id inside the sequence")
+    return out
+
+
+def indexer(q8, qs, w, pos, k8, ks, nthreads: int = 0, lib=None) -> np.ndarray:
+    """Index scores [T, S] float32; entries past each row's visible range are NaN."""
+    lib = lib or load()
+    q8 = _c(q8, np.uint8)
+    T, H_I, D_I = q8.shape
+    k8 = _c(k8, np.uint8)
+    S = k8.shape[0]
+    qs, w, ks = _c(qs, np.float32), _c(w, np.float32), _c(ks, np.float32)
+    pos = _c(pos, np.int64)
+    out = np.full((T, S), np.nan, dtype=np.float32)
+    rc = lib.oracle_indexer(_ptr(q8), _ptr(qs), _ptr(w), _ptr(pos), T, _ptr(k8), _ptr(ks), S,
+                            H_I, D_I, _ptr(out), S, nthreads)
+    if rc:
+        raise RuntimeError("oracle_indexer failed (%d)" % rc)
+    return out
+
+
+def topk(logits, pos, k: int, nthreads: int = 0, lib=None) -> np.ndarray:
+    """Top-k index lists [T, k] int32 (score descending, index ascending; -1 padded)."""
+    lib = lib or load()
+    logits = _c(logits, np.float32)
+    T, S = logits.shape
+    pos = _c(pos, np.int64)
+    out = np.empty((T, k), dtype=np.int32)
+    rc = lib.oracle_topk(_ptr(logits), S, _ptr(pos), T, S, k, _ptr(out), nthreads)
+    if rc:
+        raise RuntimeError("oracle_topk failed (%d)" % rc)
+    return out
+
+
+def sparse_mla(q, idx, pos, kv, D_v: int, sm_scale: float, nthreads: int = 0, lib=None):
+    """(out fp32 [T,H,D_v], out bf16 bits [T,H,D_v], lse fp32 [T,H])."""
+    lib = lib or load()
+    q = _c(q, np.uint16)
+    T, H, D_qk = q.shape
+    idx = _c(idx, np.int32)
+    k = idx.shape[1]
+    kv = _c(kv, np.uint16)
+    S = kv.shape[0]
+    pos = _c(pos, np.int64)
+    out = np.empty((T, H, D_v), dtype=np.float32)
+    outb = np.empty((T, H, D_v), dtype=np.uint16)
+    lse = np.empty((T, H), dtype=np.float32)
+    rc = lib.oracle_sparse_mla(_ptr(q), _ptr(idx), _ptr(pos), T, H, D_qk, D_v, k, _ptr(kv), S,
+                               ctypes.c_float(sm_scale), _ptr(out), _ptr(outb), _ptr(lse), nthreads)
+    if rc:
+        raise RuntimeError("oracle_sparse_mla failed (%d)" % rc)
+    return out, outb, lse
+
+
+def prefill(inp, nthreads: int = 0, lib=None):
+    """Whole path for prefill inputs (dsa_inputs.PrefillInputs): logits, indices, out, out_bf16, lse."""
+    wl = inp.wl
+    pos = inp.pos
+    logits = indexer(inp.q8, inp.qs, inp.w, pos, inp.k8, inp.ks, nthreads, lib)
+    idx = topk(logits, pos, wl.topk, nthreads, lib)
+    out, outb, lse = sparse_mla(inp.q, idx, pos, inp.kv, wl.D_v, wl.sm_scale, nthreads, lib)
+    return logits, idx, out, outb, lse
+
+
+def decode(inp, nthreads: int = 0, lib=None, seqs=None):
+    """Whole path for paged decode inputs (dsa_inputs.DecodeInputs), per sequence.
+
+    Returns per-sequence lists (logits row of length n_b, indices [k], out [H, D_v] fp32,
+    out bf16, lse [H]).  Keys and KV rows are read through each sequence's block table.
+    """
+    wl = inp.wl
+    res = []
+    seqs = range(len(inp.seq_lens)) if seqs is None else seqs
+    for b in seqs:
+        n = int(inp.seq_lens[b])
+        tbl = inp.block_table[b]
+        k8 = gather_rows(inp.k8_pool, tbl, n, lib)
+        ks = gather_rows(inp.ks_pool[..., None], tbl, n, lib)[:, 0]
+        kv = gather_rows(inp.kv_pool, tbl, n, lib)
+        pos = np.array([n - 1], dtype=np.int64)
+        lg = indexer(inp.q8[b:b + 1], inp.qs[b:b + 1], inp.w[b:b + 1], pos, k8, ks, nthreads, lib)
+        ix = topk(lg, pos, wl.topk, nthreads, lib)
+        o, ob, l = sparse_mla(inp.q[b:b + 1], ix, pos, kv, wl.D_v, wl.sm_scale, nthreads, lib)
+        res.append((lg[0], ix[0], o[0], ob[0], l[0]))
+    return res

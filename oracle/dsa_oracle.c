@@ -1,0 +1,318 @@
+/*
+ * DSA oracle: plain, slow, obviously correct CPU implementation of the
+ * DeepSeek Sparse Attention hot path.  TEST INFRASTRUCTURE ONLY: it is built
+ * and called by tests/, by __graft_entry__.smoke() and by the cpu_baseline leg
+ * of bench.py, never by the product library.  It shares no code, header,
+ * table or constant with the GPU path.
+ *
+ * Sources (web pages; section named for each function):
+ *  - DeepSeek-V3.2-Exp summary page, section "Method": the index score
+ *    I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j] . k_I[s]) against all prior tokens,
+ *    H_I heads, FP8; top-k = 2048; MLA in MQA mode, the latent KV row shared by
+ *    all query heads of a token.
+ *  - AMD "MI355X GPUs Power DeepSeek-V3.2-Exp" article, section "DeepSeek
+ *    Sparse Attention (DSA)": the indexer scores all preceding tokens; the top
+ *    2048 key-value pairs per query go to the main attention.
+ *  - gist listing of the indexer kernel: FP8 E4M3 cast along the last dim.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - the query's own position is visible: n_t = min(S, pos_t + 1);
+ *  - rows with n_t < k select every visible key and pad with -1;
+ *  - equal scores: the lower key index wins; -0.0 equals +0.0;
+ *  - MLA: K = all D_qk columns of the latent row, V = its first D_v columns;
+ *    softmax scale is a parameter; LSE is natural-log, fp32;
+ *  - index entries outside [0, n_t) are skipped, duplicates count with
+ *    multiplicity; a row with no valid entry gives out = 0, lse = -inf.
+ *
+ * Arithmetic: fp32 with a fixed ascending summation order (no fused
+ * multiply-add; built with -ffp-contract=off).  Each query row is computed by
+ * one thread, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- value formats --------------------------------------------------- */
+
+/* OCP FP8 E4M3 ("fn"): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN; there are
+ * no infinities.  Largest finite value 1.75 * 2^8 = 448. */
+static float e4m3_value(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 7;
+    float v;
+    if (e == 0xF && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexpf((float)m, -9);
+    else
+        v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return sign ? -v : v;
+}
+
+static float g_e4m3[256];
+static int g_e4m3_ready = 0;
+
+static void e4m3_init(void)
+{
+    if (g_e4m3_ready)
+        return;
+    for (int c = 0; c < 256; ++c)
+        g_e4m3[c] = e4m3_value((uint8_t)c);
+    g_e4m3_ready = 1;
+}
+
+/* bf16 is the upper half of an IEEE binary32 word. */
+static float bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint16_t bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x40); /* quiet NaN */
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb; /* round to nearest, ties to even */
+    return (uint16_t)(u >> 16);
+}
+
+static void set_threads(int32_t nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+static int64_t visible_keys(int64_t pos, int64_t S)
+{
+    int64_t n = pos + 1;
+    return n < S ? n : S;
+}
+
+/* ---- exported helpers ------------------------------------------------- */
+
+void oracle_e4m3_table(float *out256)
+{
+    e4m3_init();
+    memcpy(out256, g_e4m3, sizeof g_e4m3);
+}
+
+void oracle_bf16_round(const float *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = bf16_round(x[i]);
+}
+
+/* Copy logical rows 0..n-1 of a paged pool into a contiguous array: logical
+ * row r lives at physical row block_table[r / block_size] * block_size +
+ * r % block_size.  Returns 0, or 1 if a table entry is negative. */
+int oracle_gather_rows(const void *pool, int64_t row_bytes, const int32_t *block_table,
+                       int32_t block_size, int64_t n, void *out)
+{
+    const uint8_t *src = (const uint8_t *)pool;
+    uint8_t *dst = (uint8_t *)out;
+    for (int64_t r = 0; r < n; ++r) {
+        int32_t blk = block_table[r / block_size];
+        if (blk < 0)
+            return 1;
+        int64_t phys = (int64_t)blk * block_size + r % block_size;
+        memcpy(dst + r * row_bytes, src + phys * row_bytes, (size_t)row_bytes);
+    }
+    return 0;
+}
+
+/* ---- step 1: lightning indexer ---------------------------------------
+ * DeepSeek-V3.2-Exp summary, "Method": for query row t (absolute position
+ * pos[t]) and every visible key s < n_t,
+ *     I[t,s] = sum_j w[t,j] * max(0, q_I[t,j] . k_I[s]),
+ * with the FP8 inputs dequantized first: q_I[t,j,i] = qs[t,j] * dec(q8[t,j,i]),
+ * k_I[s,i] = ks[s] * dec(k8[s,i]).  Entries s >= n_t are not written. */
+int oracle_indexer(const uint8_t *q8, const float *qs, const float *w, const int64_t *pos,
+                   int64_t T, const uint8_t *k8, const float *ks, int64_t S, int32_t H_I,
+                   int32_t D_I, float *logits, int64_t ld, int32_t nthreads)
+{
+    if (T < 0 || S < 0 || H_I <= 0 || D_I <= 0 || ld < S)
+        return 1;
+    e4m3_init();
+    float *kdec = (float *)malloc(sizeof(float) * (size_t)(S > 0 ? S : 1) * (size_t)D_I);
+    if (!kdec)
+        return 3;
+    for (int64_t s = 0; s < S; ++s)
+        for (int32_t i = 0; i < D_I; ++i)
+            kdec[s * D_I + i] = ks[s] * g_e4m3[k8[s * D_I + i]];
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        float *qdec = (float *)malloc(sizeof(float) * (size_t)H_I * (size_t)D_I);
+        if (!qdec) {
+            bad = 3;
+            continue;
+        }
+        for (int32_t j = 0; j < H_I; ++j)
+            for (int32_t i = 0; i < D_I; ++i)
+                qdec[j * D_I + i] = qs[t * H_I + j] * g_e4m3[q8[(t * H_I + j) * D_I + i]];
+        int64_t n = visible_keys(pos[t], S);
+        for (int64_t s = 0; s < n; ++s) {
+            float I = 0.0f;
+            for (int32_t j = 0; j < H_I; ++j) {
+                float d = 0.0f;
+                for (int32_t i = 0; i < D_I; ++i)
+                    d += qdec[j * D_I + i] * kdec[s * D_I + i];
+                float r = d > 0.0f ? d : 0.0f;
+                I += w[t * H_I + j] * r;
+            }
+            logits[t * ld + s] = I;
+        }
+        free(qdec);
+    }
+    free(kdec);
+    return bad;
+}
+
+/* ---- step 2: top-k selection -----------------------------------------
+ * AMD article, "Fine-Grained Token Selection" and the summary's "Method":
+ * keep the k highest-scoring visible keys.  Candidates s < n_t are sorted by
+ * (score descending, index ascending); the first min(k, n_t) are returned,
+ * the rest of the row is -1.  Non-finite scores are rejected (return 2). */
+typedef struct {
+    float v;
+    int32_t i;
+} scored_t;
+
+static int by_score_then_index(const void *a, const void *b)
+{
+    const scored_t *x = (const scored_t *)a, *y = (const scored_t *)b;
+    if (x->v > y->v)
+        return -1;
+    if (x->v < y->v)
+        return 1;
+    return (x->i > y->i) - (x->i < y->i);
+}
+
+int oracle_topk(const float *logits, int64_t ld, const int64_t *pos, int64_t T, int64_t S,
+                int32_t k, int32_t *idx, int32_t nthreads)
+{
+    if (T < 0 || S < 0 || k <= 0 || ld < S)
+        return 1;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = visible_keys(pos[t], S);
+        scored_t *c = (scored_t *)malloc(sizeof(scored_t) * (size_t)(n > 0 ? n : 1));
+        if (!c) {
+            bad = 3;
+            continue;
+        }
+        for (int64_t s = 0; s < n; ++s) {
+            float v = logits[t * ld + s];
+            if (!isfinite(v))
+                bad = 2;
+            c[s].v = v == 0.0f ? 0.0f : v; /* -0.0 -> +0.0 */
+            c[s].i = (int32_t)s;
+        }
+        qsort(c, (size_t)n, sizeof(scored_t), by_score_then_index);
+        int64_t m = n < k ? n : k;
+        for (int64_t r = 0; r < k; ++r)
+            idx[t * k + r] = r < m ? c[r].i : -1;
+        free(c);
+    }
+    return bad;
+}
+
+/* ---- step 3: sparse MLA forward, MQA mode ----------------------------
+ * Summary page, "Method": the main attention reads only the selected latent
+ * KV rows, one row shared by all H query heads.  For query row t, head h and
+ * the valid entries i of the index list (0 <= idx < n_t):
+ *     z_i = sm_scale * (q[t,h,:] . kv[idx_i, :D_qk])
+ *     m = max z, e_i = exp(z_i - m), l = sum e_i
+ *     out[t,h,d] = (sum_i e_i * kv[idx_i, d]) / l   for d < D_v
+ *     lse[t,h] = m + log(l)
+ * out_bf16 (optional) is out rounded to bf16. */
+int oracle_sparse_mla(const uint16_t *q, const int32_t *idx, const int64_t *pos, int64_t T,
+                      int32_t H, int32_t D_qk, int32_t D_v, int32_t k, const uint16_t *kv,
+                      int64_t S, float sm_scale, float *out, uint16_t *out_bf16, float *lse,
+                      int32_t nthreads)
+{
+    if (T < 0 || S < 0 || H <= 0 || D_qk <= 0 || D_v <= 0 || D_v > D_qk || k <= 0)
+        return 1;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = visible_keys(pos[t], S);
+        const int32_t *row = idx + t * k;
+        float *z = (float *)malloc(sizeof(float) * (size_t)k);
+        float *acc = (float *)malloc(sizeof(float) * (size_t)D_v);
+        if (!z || !acc) {
+            bad = 3;
+            free(z);
+            free(acc);
+            continue;
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            const uint16_t *qh = q + (t * H + h) * (int64_t)D_qk;
+            float m = -INFINITY;
+            for (int32_t i = 0; i < k; ++i) {
+                int32_t s = row[i];
+                if (s < 0 || s >= n)
+                    continue;
+                const uint16_t *kr = kv + (int64_t)s * D_qk;
+                float dot = 0.0f;
+                for (int32_t d = 0; d < D_qk; ++d)
+                    dot += bf16_value(qh[d]) * bf16_value(kr[d]);
+                z[i] = sm_scale * dot;
+                if (z[i] > m)
+                    m = z[i];
+            }
+            float *o = out + (t * H + h) * (int64_t)D_v;
+            if (m == -INFINITY) { /* no valid entry */
+                for (int32_t d = 0; d < D_v; ++d)
+                    o[d] = 0.0f;
+                if (out_bf16)
+                    for (int32_t d = 0; d < D_v; ++d)
+                        out_bf16[(t * H + h) * (int64_t)D_v + d] = 0;
+                lse[t * H + h] = -INFINITY;
+                continue;
+            }
+            float l = 0.0f;
+            for (int32_t d = 0; d < D_v; ++d)
+                acc[d] = 0.0f;
+            for (int32_t i = 0; i < k; ++i) {
+                int32_t s = row[i];
+                if (s < 0 || s >= n)
+                    continue;
+                float e = expf(z[i] - m);
+                l += e;
+                const uint16_t *vr = kv + (int64_t)s * D_qk;
+                for (int32_t d = 0; d < D_v; ++d)
+                    acc[d] += e * bf16_value(vr[d]);
+            }
+            for (int32_t d = 0; d < D_v; ++d)
+                o[d] = acc[d] / l;
+            if (out_bf16)
+                for (int32_t d = 0; d < D_v; ++d)
+                    out_bf16[(t * H + h) * (int64_t)D_v + d] = bf16_round(o[d]);
+            lse[t * H + h] = m + logf(l);
+        }
+        free(z);
+        free(acc);
+    }
+    return bad;
+}

@@ -1,0 +1,280 @@
+"""Checks that pin the oracle to things other than itself.
+
+Each check takes an oracle library handle (so the same check can be run
+against deliberately broken copies of the oracle) and raises AssertionError
+when the oracle disagrees with the pages' definitions, a library routine, a
+closed form, an error bound or an invariant.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from dsa_inputs import get, prefill_inputs
+from dsa_inputs.generate import block_rng, quantize_fp8_rows, to_bf16_bits
+
+import brute
+
+U = 2.0 ** -24   # unit roundoff of fp32
+
+
+def indexer_bound(D_I: int, H_I: int) -> float:
+    """First-order forward error bound of the fp32 oracle relative to the magnitude scale A:
+    dequantization (2 roundings), products and D_I-term dot (gamma_{D_I}), weighting and
+    H_I-term sum (gamma_{H_I + 1})."""
+    return 1.01 * (D_I + H_I + 4) * U
+
+
+# ---------------------------------------------------------------- formats
+def check_e4m3_table(lib):
+    t = oracle.e4m3_table(lib)
+    ref = brute.e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float32)
+    assert np.array_equal(t, ref, equal_nan=True), "E4M3 table differs from torch.float8_e4m3fn"
+    # closed forms from the format definition
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and not np.isinf(t).any()
+
+
+def check_bf16_round(lib):
+    g = block_rng(123, 99, 0)
+    x = np.concatenate([g.standard_normal(20000).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0, 3.0e38, -3.0e38, 1e-40, np.inf, -np.inf], np.float32)])
+    mine = oracle.bf16_round(x, lib)
+    ref = to_bf16_bits(x)
+    assert np.array_equal(mine, ref), "bf16 rounding differs from torch"
+
+
+# ---------------------------------------------------------------- indexer
+def check_indexer_tiny(lib):
+    wl = get("tiny")
+    inp = prefill_inputs(wl)
+    o = oracle.indexer(inp.q8, inp.qs, inp.w, inp.pos, inp.k8, inp.ks, lib=lib)
+    b, A = brute.indexer(inp.q8, inp.qs, inp.w, inp.pos, inp.k8, inp.ks)
+    m = ~np.isnan(b)
+    assert np.array_equal(m, ~np.isnan(o)), "causal region of the oracle is wrong"
+    err = np.abs(o[m] - b[m])
+    assert np.all(err <= indexer_bound(wl.D_I, wl.H_I) * A[m] + 1e-30), \
+        "indexer exceeds fp32 error bound (max %.3e of A)" % np.max(err / np.maximum(A[m], 1e-30))
+
+
+def check_indexer_full_heads(lib, rows=(0, 1, 777, 2047, 2048, 4095)):
+    wl = get("prefill_4k")
+    inp = prefill_inputs(wl, rows=rows, with_q=False)
+    o = oracle.indexer(inp.q8, inp.qs, inp.w, inp.pos, inp.k8, inp.ks, lib=lib)
+    b, A = brute.indexer(inp.q8, inp.qs, inp.w, inp.pos, inp.k8, inp.ks)
+    m = ~np.isnan(b)
+    assert np.array_equal(m, ~np.isnan(o))
+    assert np.all(np.abs(o[m] - b[m]) <= indexer_bound(wl.D_I, wl.H_I) * A[m])
+
+
+def check_indexer_relu_matmul(lib):
+    """H_I = 1, w = 1, unit scales: I = ReLU(Q K^T) (library matmul in fp64)."""
+    g = block_rng(7, 1, 0)
+    T, S, D = 40, 40, 64
+    q8 = g.integers(0, 256, size=(T, 1, D)).astype(np.uint8)
+    k8 = g.integers(0, 256, size=(S, D)).astype(np.uint8)
+    q8[(q8 & 0x7F) == 0x7F] = 0x10    # no NaN codes
+    k8[(k8 & 0x7F) == 0x7F] = 0x20
+    ones_q = np.ones((T, 1), np.float32)
+    o = oracle.indexer(q8, ones_q, ones_q, np.arange(T), k8, np.ones(S, np.float32), lib=lib)
+    Q = torch.from_numpy(brute.e4m3_decode(q8[:, 0, :]))
+    K = torch.from_numpy(brute.e4m3_decode(k8))
+    ref = torch.relu(torch.matmul(Q, K.T)).numpy()
+    tri = np.tril(np.ones((T, S), bool))
+    # integer-valued products x 2^-18 summed exactly in fp64; fp32 may round the sum
+    A = torch.matmul(Q.abs(), K.abs().T).numpy()
+    assert np.all(np.abs(o[tri] - ref[tri]) <= (D + 2) * U * A[tri])
+    assert np.all(np.isnan(o[~tri]))
+
+
+def check_indexer_scale_invariants(lib):
+    wl = get("tiny")
+    inp = prefill_inputs(wl)
+    o = oracle.indexer(inp.q8, inp.qs, inp.w, inp.pos, inp.k8, inp.ks, lib=lib)
+    o2 = oracle.indexer(inp.q8, inp.qs, 2.0 * inp.w, inp.pos, inp.k8, inp.ks, lib=lib)
+    m = ~np.isnan(o)
+    assert np.array_equal(o2[m], 2.0 * o[m]), "doubling w must double every score exactly"
+    # a negative weight is used literally (no clamping of w)
+    wneg = inp.w.copy()
+    wneg[:, 0] = -wneg[:, 0]
+    o3 = oracle.indexer(inp.q8, inp.qs, wneg, inp.pos, inp.k8, inp.ks, lib=lib)
+    b3, A3 = brute.indexer(inp.q8, inp.qs, wneg, inp.pos, inp.k8, inp.ks)
+    assert np.all(np.abs(o3[m] - b3[m]) <= indexer_bound(wl.D_I, wl.H_I) * A3[m] + 1e-30)
+    assert (o3[m] < 0).any()
+
+
+# ---------------------------------------------------------------- top-k
+def _rows_check(o, scores, pos, k):
+    S = scores.shape[1]
+    for t in range(scores.shape[0]):
+        n = int(min(S, pos[t] + 1))
+        ref = brute.topk_lexsort(scores[t], n, k)
+        assert np.array_equal(o[t].astype(np.int64), ref), "top-k row %d differs from lexsort" % t
+
+
+def check_topk_lexsort(lib):
+    g = block_rng(11, 2, 0)
+    T, S, k = 64, 300, 37
+    scores = g.standard_normal((T, S)).astype(np.float32)
+    pos = g.integers(0, S + 20, size=T)
+    o = oracle.topk(scores, pos, k, lib=lib)
+    _rows_check(o, scores, pos, k)
+
+
+def check_topk_ties(lib):
+    """Integer scores from {0..7}: massive ties, the lower index must win."""
+    g = block_rng(12, 2, 0)
+    T, S, k = 48, 257, 64
+    scores = g.integers(0, 8, size=(T, S)).astype(np.float32)
+    scores[:, 5] = -0.0      # -0.0 ties with +0.0
+    pos = np.arange(T) * 5 + 10
+    o = oracle.topk(scores, pos, k, lib=lib)
+    _rows_check(o, scores, pos, k)
+
+
+def check_topk_special_cases(lib):
+    g = block_rng(13, 2, 0)
+    T, S = 20, 50
+    scores = g.standard_normal((T, S)).astype(np.float32)
+    pos = np.arange(T)
+    # k >= n_t: every visible key, then -1
+    o = oracle.topk(scores, pos, 64, lib=lib)
+    for t in range(T):
+        n = t + 1
+        assert sorted(o[t, :n].tolist()) == list(range(n))
+        assert np.all(o[t, n:] == -1)
+    # k = 1: first argmax
+    pos2 = np.full(T, S - 1)
+    o1 = oracle.topk(scores, pos2, 1, lib=lib)
+    assert np.array_equal(o1[:, 0], np.argmax(scores, axis=1))
+    # causal: nothing past the query's own position
+    o3 = oracle.topk(scores, pos, 5, lib=lib)
+    assert np.all(o3 <= pos[:, None])
+    # -0.0 and +0.0 are equal: the lower index wins
+    z = np.zeros((1, 4), np.float32)
+    z[0, 0] = -0.0
+    z[0, 1] = 0.0
+    z[0, 2:] = -1.0
+    assert oracle.topk(z, np.array([3]), 1, lib=lib)[0, 0] == 0
+
+
+# ---------------------------------------------------------------- sparse MLA
+def _mla_inputs(T, S, H, D_qk, seed):
+    g = block_rng(seed, 3, 0)
+    q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
+    return q, kv
+
+
+def check_mla_dense_equivalence(lib):
+    """k >= n_t with every visible key listed: equals dense causal attention (torch SDPA, fp64)."""
+    T = S = 64
+    H, D_qk, D_v = 8, 80, 64
+    sm = 1.0 / np.sqrt(80.0)
+    q, kv = _mla_inputs(T, S, H, D_qk, 21)
+    k = 64
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        idx[t, :t + 1] = np.arange(t + 1)[::-1]    # any order
+    out, _, lse = oracle.sparse_mla(q, idx, np.arange(T), kv, D_v, sm, lib=lib)
+    Q = torch.from_numpy(brute.bf16_decode(q)).permute(1, 0, 2)             # [H,T,D]
+    KV = torch.from_numpy(brute.bf16_decode(kv))
+    K = KV[None].expand(H, S, D_qk)
+    V = KV[None, :, :D_v].expand(H, S, D_v)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=sm)
+    ref = ref.permute(1, 0, 2).numpy()
+    rel = np.abs(out - ref).max(axis=2) / np.abs(ref).max(axis=2)
+    assert rel.max() < 2e-5, "oracle MLA differs from dense causal attention (%.2e)" % rel.max()
+    z = sm * np.einsum("htd,sd->hts", Q.numpy(), KV.numpy())
+    z = np.where(np.tril(np.ones((T, S), bool))[None], z, -np.inf)
+    lse_ref = torch.logsumexp(torch.from_numpy(z), dim=-1).numpy().T
+    assert np.abs(lse - lse_ref).max() < 2e-5
+
+
+def check_mla_brute(lib):
+    """Random index lists with duplicates and invalid entries vs the fp64 brute force."""
+    T, S, H, D_qk, D_v = 16, 200, 8, 80, 64
+    q, kv = _mla_inputs(T, S, H, D_qk, 22)
+    g = block_rng(22, 4, 0)
+    k = 32
+    pos = g.integers(40, S, size=T)
+    idx = g.integers(-3, S, size=(T, k)).astype(np.int32)
+    idx[:, 3] = idx[:, 2]                            # duplicates
+    out, _, lse = oracle.sparse_mla(q, idx, pos, kv, D_v, 0.125, lib=lib)
+    ref, lse_ref = brute.sparse_mla(q, idx, pos, kv, D_v, 0.125)
+    rel = np.abs(out - ref).max(axis=2) / np.abs(ref).max(axis=2)
+    assert rel.max() < 2e-5 and np.abs(lse - lse_ref).max() < 2e-5
+
+
+def check_mla_special_cases(lib):
+    T, S, H, D_qk, D_v = 8, 64, 8, 80, 64
+    q, kv = _mla_inputs(T, S, H, D_qk, 23)
+    kvf = brute.bf16_decode(kv)
+    pos = np.full(T, S - 1)
+    # k = 1: output is the selected V row exactly, lse = the one logit
+    idx1 = (np.arange(T) * 7 % S).astype(np.int32)[:, None]
+    out, outb, lse = oracle.sparse_mla(q, idx1, pos, kv, D_v, 0.1, lib=lib)
+    for t in range(T):
+        assert np.array_equal(out[t], np.broadcast_to(kvf[idx1[t, 0], :D_v], (H, D_v)).astype(np.float32))
+        assert np.array_equal(outb[t], np.broadcast_to(kv[idx1[t, 0], :D_v], (H, D_v)))
+    z = 0.1 * np.einsum("thd,td->th", brute.bf16_decode(q), kvf[idx1[:, 0]])
+    assert np.abs(lse - z).max() < 1e-5
+    # q = 0: uniform weights, output is the mean of the selected V rows, lse = log(count)
+    q0 = np.zeros_like(q)
+    idx = np.stack([np.arange(10) * 3 + t for t in range(T)]).astype(np.int32)
+    out0, _, lse0 = oracle.sparse_mla(q0, idx, pos, kv, D_v, 0.3, lib=lib)
+    for t in range(T):
+        mean = kvf[idx[t], :D_v].mean(axis=0)
+        assert np.abs(out0[t] - mean[None]).max() <= 16 * U * np.abs(kvf[idx[t], :D_v]).max() * 10
+    assert np.abs(lse0 - np.log(10.0)).max() < 1e-6
+    # invalid entries are skipped exactly; an all-invalid row gives 0 and -inf
+    idx2 = np.concatenate([idx, np.full((T, 3), -1, np.int32), np.full((T, 2), S + 5, np.int32)], axis=1)
+    outa, _, lsea = oracle.sparse_mla(q, idx, pos, kv, D_v, 0.3, lib=lib)
+    outb2, _, lseb = oracle.sparse_mla(q, idx2, pos, kv, D_v, 0.3, lib=lib)
+    assert np.array_equal(outa, outb2) and np.array_equal(lsea, lseb)
+    # keys beyond the query position are invalid too
+    posn = np.full(T, 5)
+    outc, _, lsec = oracle.sparse_mla(q, idx, posn, kv, D_v, 0.3, lib=lib)
+    keep = np.where((idx >= 0) & (idx <= 5), idx, -1).astype(np.int32)
+    outd, _, lsed = oracle.sparse_mla(q, keep, pos, kv, D_v, 0.3, lib=lib)
+    assert np.array_equal(outc, outd) and np.array_equal(lsec, lsed)
+    none = np.full((T, 4), -1, np.int32)
+    oute, _, lsee = oracle.sparse_mla(q, none, pos, kv, D_v, 0.3, lib=lib)
+    assert np.all(oute == 0) and np.all(np.isneginf(lsee))
+    # index order does not change the result beyond fp32 rounding
+    perm = idx[:, ::-1].copy()
+    outp, _, lsep = oracle.sparse_mla(q, perm, pos, kv, D_v, 0.3, lib=lib)
+    assert np.abs(outp - outa).max() < 1e-5 and np.abs(lsep - lsea).max() < 1e-5
+
+
+# ---------------------------------------------------------------- end to end
+def check_dense_when_k_covers(lib, rows=(0, 1, 5, 1000, 2047)):
+    """spec invariant: when k >= n_t, sparse attention equals dense causal MLA."""
+    wl = get("prefill_4k")
+    inp = prefill_inputs(wl, rows=rows)
+    logits, idx, out, _, lse = oracle.prefill(inp, lib=lib)
+    Q = brute.bf16_decode(inp.q)
+    KV = brute.bf16_decode(inp.kv)
+    for r, t in enumerate(rows):
+        n = t + 1
+        assert sorted(idx[r][:n].tolist()) == list(range(n)) and np.all(idx[r][n:] == -1)
+        z = wl.sm_scale * (Q[r] @ KV[:n].T)
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        ref = (e @ KV[:n, :wl.D_v]) / e.sum(axis=1, keepdims=True)
+        rel = np.abs(out[r] - ref).max(axis=1) / np.abs(ref).max(axis=1)
+        assert rel.max() < 1e-4
+
+
+def check_causal_end_to_end(lib):
+    wl = get("tiny")
+    inp = prefill_inputs(wl)
+    logits, idx, out, _, lse = oracle.prefill(inp, lib=lib)
+    pos = inp.pos
+    assert np.all(idx <= pos[:, None])
+    for t in range(wl.T):
+        n = t + 1
+        v = idx[t][idx[t] >= 0]
+        assert len(v) == min(n, wl.topk) and len(set(v.tolist())) == len(v)

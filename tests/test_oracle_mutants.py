@@ -1,0 +1,61 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that a pin catches each.
+
+Every mutant is the oracle source with one textual edit, compiled with gcc
+into a temporary library; the real oracle source is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+
+import pins
+
+MUTANTS = [
+    # (name, original text, replacement, checks expected to fail)
+    ("relu_dropped", "float r = d > 0.0f ? d : 0.0f;", "float r = d;",
+     [pins.check_indexer_tiny]),
+    ("diagonal_excluded", "int64_t n = pos + 1;", "int64_t n = pos;",
+     [pins.check_indexer_tiny]),
+    ("key_dim_reversed", "d += qdec[j * D_I + i] * kdec[s * D_I + i];",
+     "d += qdec[j * D_I + i] * kdec[s * D_I + (D_I - 1 - i)];", [pins.check_indexer_tiny]),
+    ("key_scale_dropped", "kdec[s * D_I + i] = ks[s] * g_e4m3[k8[s * D_I + i]];",
+     "kdec[s * D_I + i] = g_e4m3[k8[s * D_I + i]];", [pins.check_indexer_tiny]),
+    ("head_weight_index", "I += w[t * H_I + j] * r;", "I += w[t * H_I + (H_I - 1 - j)] * r;",
+     [pins.check_indexer_tiny]),
+    ("e4m3_bias", "ldexpf(1.0f + (float)m / 8.0f, e - 7)", "ldexpf(1.0f + (float)m / 8.0f, e - 8)",
+     [pins.check_e4m3_table]),
+    ("e4m3_subnormal", "ldexpf((float)m, -9)", "ldexpf((float)m, -10)", [pins.check_e4m3_table]),
+    ("tie_to_higher_index", "return (x->i > y->i) - (x->i < y->i);",
+     "return (x->i < y->i) - (x->i > y->i);", [pins.check_topk_ties]),
+    ("ascending_scores", "if (x->v > y->v)\n        return -1;", "if (x->v < y->v)\n        return -1;",
+     [pins.check_topk_lexsort]),
+    ("topk_no_causal", "int64_t n = visible_keys(pos[t], S);\n        scored_t",
+     "int64_t n = S;\n        scored_t", [pins.check_topk_special_cases]),
+    ("mla_scale_dropped", "z[i] = sm_scale * dot;", "z[i] = dot;", [pins.check_mla_brute]),
+    ("mla_value_columns", "acc[d] += e * bf16_value(vr[d]);",
+     "acc[d] += e * bf16_value(vr[d + (D_qk - D_v)]);", [pins.check_mla_brute]),
+    ("mla_lse_no_max", "lse[t * H + h] = m + logf(l);", "lse[t * H + h] = logf(l);",
+     [pins.check_mla_dense_equivalence]),
+    ("mla_future_keys", "int64_t n = visible_keys(pos[t], S);\n        const int32_t *row",
+     "int64_t n = S;\n        const int32_t *row", [pins.check_mla_brute]),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(obuild.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,orig,repl,checks", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pin_catches_mutant(name, orig, repl, checks, source, tmp_path):
+    assert source.count(orig) == 1, "mutation anchor for %s must occur exactly once" % name
+    src = tmp_path / ("mutant_%s.c" % name)
+    src.write_text(source.replace(orig, repl))
+    lib_path = obuild.build(str(src), str(tmp_path / ("libmutant_%s.so" % name)))
+    lib = oracle.load(lib_path)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check(lib)
