@@ -1,0 +1,11 @@
+"""DeepSeek Sparse Attention hot path on AMD Instinct MI355X (gfx950).
+
+Lightning-indexer scoring -> per-query top-k -> MQA-mode sparse MLA, as hand-written HIP
+kernels behind the C ABI of include/dsa.h (libdsa.so).  This package is the thin Python
+binding: torch provides device memory and streams, the library does every step.
+"""
+from ._lib import DSAError, EXPORTS, LIB_PATH, load  # noqa: F401
+from .api import (  # noqa: F401
+    PagedKV, decode_workspace_size, dsa_decode_paged, dsa_indexer_logits, dsa_prefill_paged,
+    dsa_sparse_mla_fwd, dsa_topk, ld_for, make_dims, prefill_workspace_size,
+)

@@ -1,0 +1,183 @@
+"""Python entry points with the same names as the C ABI, over torch device tensors.
+
+Each function checks shapes and dtypes, allocates any output the caller did not pass (torch
+as the device allocator), and calls the library on the current HIP stream.  Nothing here
+computes any part of the method.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from ._lib import Dims, PagedCache, check, load
+
+_BYTES = {1: (torch.uint8, torch.int8, torch.float8_e4m3fn),
+          2: (torch.bfloat16, torch.int16, torch.uint16),
+          4: (torch.float32, torch.int32)}
+
+
+def _dev(t: torch.Tensor, name: str, ndim: int, itemsize: int) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %s" % (name, ndim, tuple(t.shape)))
+    if t.element_size() != itemsize:
+        raise ValueError("%s must have %d-byte elements, got %s" % (name, itemsize, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _opt(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def ld_for(S: int) -> int:
+    return (S + 3) // 4 * 4
+
+
+# ------------------------------------------------------------------------------------------------
+def dsa_indexer_logits(q8, q_scale, w, k8, k_scale, q_start: int = 0, logits=None) -> torch.Tensor:
+    """Index scores into ``logits`` [T, ld >= S] float32 (entries past each row's causal range untouched)."""
+    lib = load()
+    T, H_I, D_I = q8.shape
+    S = k8.shape[0]
+    if logits is None:
+        logits = torch.empty((T, ld_for(S)), dtype=torch.float32, device=q8.device)
+    status = lib.dsa_indexer_logits(
+        _dev(q8, "q8", 3, 1), _dev(q_scale, "q_scale", 2, 4), _dev(w, "w", 2, 4), _dev(k8, "k8", 2, 1),
+        _dev(k_scale, "k_scale", 1, 4), T, S, H_I, D_I, q_start, _dev(logits, "logits", 2, 4),
+        logits.shape[1], _stream(q8))
+    check("dsa_indexer_logits", status)
+    return logits
+
+
+def dsa_topk(logits, k: int, S: int, q_start: int = 0, indices=None, workspace=None) -> torch.Tensor:
+    """Top-k key indices [T, k] int32 of each logits row's visible part (-1 padded)."""
+    lib = load()
+    T = logits.shape[0]
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    need = lib.dsa_topk_workspace_size(T, S, k)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = lib.dsa_topk(_dev(logits, "logits", 2, 4), logits.shape[1], T, S, q_start, k,
+                          _dev(indices, "indices", 2, 4), _opt(workspace), ws_bytes, _stream(logits))
+    check("dsa_topk", status)
+    return indices
+
+
+def dsa_sparse_mla_fwd(q, kv, indices, sm_scale: float, D_v: int, q_start: int = 0, out=None,
+                       out_f32=None, lse=None, want_f32: bool = False, want_lse: bool = True):
+    """(out bf16 [T,H,D_v], out_f32 or None, lse or None) of MQA-mode sparse MLA."""
+    lib = load()
+    T, H, D_qk = q.shape
+    S = kv.shape[0]
+    k = indices.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, D_v), dtype=torch.bfloat16, device=dev)
+    if out_f32 is None and want_f32:
+        out_f32 = torch.empty((T, H, D_v), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    status = lib.dsa_sparse_mla_fwd(
+        _dev(q, "q", 3, 2), _dev(kv, "kv", 2, 2), _dev(indices, "indices", 2, 4), T, S, H, D_qk, D_v, k,
+        q_start, ctypes.c_float(sm_scale), _dev(out, "out", 3, 2), _opt(out_f32), _opt(lse), None, 0,
+        _stream(q))
+    check("dsa_sparse_mla_fwd", status)
+    return out, out_f32, lse
+
+
+# ------------------------------------------------------------------------------------------------
+@dataclass
+class PagedKV:
+    """Paged cache tensors: pools [NB, bs, ...], block_table [B, max_blocks] i32, seq_lens [B] i32."""
+    k8: torch.Tensor
+    k_scale: torch.Tensor
+    kv: torch.Tensor
+    block_table: torch.Tensor
+    seq_lens: Optional[torch.Tensor] = None
+
+    def struct(self) -> PagedCache:
+        NB, bs, _ = self.k8.shape
+        _dev(self.k8, "k8 pool", 3, 1)
+        _dev(self.k_scale, "k_scale pool", 2, 4)
+        _dev(self.kv, "kv pool", 3, 2)
+        _dev(self.block_table, "block_table", 2, 4)
+        if self.seq_lens is not None:
+            _dev(self.seq_lens, "seq_lens", 1, 4)
+        return PagedCache(self.k8.data_ptr(), self.k_scale.data_ptr(), self.kv.data_ptr(), NB, bs,
+                          self.block_table.data_ptr(), self.block_table.shape[1], _opt(self.seq_lens))
+
+
+def make_dims(H_I, D_I, H, D_qk, D_v, topk, sm_scale) -> Dims:
+    return Dims(H_I, D_I, H, D_qk, D_v, topk, sm_scale)
+
+
+def prefill_workspace_size(dims: Dims, T: int, S: int) -> int:
+    return load().dsa_prefill_workspace_size(ctypes.byref(dims), T, S)
+
+
+def decode_workspace_size(dims: Dims, B: int, max_seq_len: int) -> int:
+    return load().dsa_decode_workspace_size(ctypes.byref(dims), B, max_seq_len)
+
+
+def _workspace(nbytes: int, device, given=None):
+    if given is not None and given.numel() * given.element_size() >= nbytes:
+        return given
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def dsa_prefill_paged(cache: PagedKV, seq: int, dims: Dims, q_start: int, q8, q_scale, w, q, out=None,
+                      want_f32: bool = False, want_lse: bool = True, want_indices: bool = False,
+                      workspace=None):
+    """Fused indexer -> top-k -> sparse MLA for T queries of sequence ``seq`` at q_start .. q_start+T-1."""
+    lib = load()
+    T = q8.shape[0]
+    dev = q8.device
+    if out is None:
+        out = torch.empty((T, dims.H, dims.D_v), dtype=torch.bfloat16, device=dev)
+    out_f32 = torch.empty((T, dims.H, dims.D_v), dtype=torch.float32, device=dev) if want_f32 else None
+    lse = torch.empty((T, dims.H), dtype=torch.float32, device=dev) if want_lse else None
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device=dev) if want_indices else None
+    ws = _workspace(prefill_workspace_size(dims, T, q_start + T), dev, workspace)
+    c = cache.struct()
+    status = lib.dsa_prefill_paged(
+        ctypes.byref(c), seq, ctypes.byref(dims), T, q_start, _dev(q8, "q8", 3, 1),
+        _dev(q_scale, "q_scale", 2, 4), _dev(w, "w", 2, 4), _dev(q, "q", 3, 2), _dev(out, "out", 3, 2),
+        _opt(out_f32), _opt(lse), _opt(idx), ws.data_ptr(), ws.numel(), _stream(q8))
+    check("dsa_prefill_paged", status)
+    return out, out_f32, lse, idx
+
+
+def dsa_decode_paged(cache: PagedKV, max_seq_len: int, dims: Dims, q8, q_scale, w, q, out=None,
+                     want_f32: bool = False, want_lse: bool = True, want_indices: bool = False,
+                     workspace=None):
+    """Fused decode: one query per sequence at position seq_lens[b] - 1."""
+    lib = load()
+    B = q8.shape[0]
+    dev = q8.device
+    if out is None:
+        out = torch.empty((B, dims.H, dims.D_v), dtype=torch.bfloat16, device=dev)
+    out_f32 = torch.empty((B, dims.H, dims.D_v), dtype=torch.float32, device=dev) if want_f32 else None
+    lse = torch.empty((B, dims.H), dtype=torch.float32, device=dev) if want_lse else None
+    idx = torch.empty((B, dims.topk), dtype=torch.int32, device=dev) if want_indices else None
+    ws = _workspace(decode_workspace_size(dims, B, max_seq_len), dev, workspace)
+    c = cache.struct()
+    status = lib.dsa_decode_paged(
+        ctypes.byref(c), B, max_seq_len, ctypes.byref(dims), _dev(q8, "q8", 3, 1),
+        _dev(q_scale, "q_scale", 2, 4), _dev(w, "w", 2, 4), _dev(q, "q", 3, 2), _dev(out, "out", 3, 2),
+        _opt(out_f32), _opt(lse), _opt(idx), ws.data_ptr(), ws.numel(), _stream(q8))
+    check("dsa_decode_paged", status)
+    return out, out_f32, lse, idx

@@ -1,0 +1,385 @@
+// C ABI of the DSA hot path: host-side argument validation, workspace carving and the launch
+// sequence.  Every check happens before the first launch, so a failing call enqueues nothing.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status_t fail(dsa_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+dsa_status_t ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+dsa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, status, ...)        \
+  do {                                    \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr && aligned16(p), DSA_ERR_INVALID_ARGUMENT, \
+                               "%s must be a non-null 16-byte aligned pointer", #p)
+#define OPTIONAL_PTR(p) REQUIRE((p) == nullptr || aligned16(p), DSA_ERR_INVALID_ARGUMENT, \
+                                "%s must be 16-byte aligned when given", #p)
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ld_for(int64_t S) { return (S + 3) / 4 * 4; }
+
+int block_shift_of(int32_t bs) {
+  int s = 0;
+  while ((1 << s) < bs) ++s;
+  return s;
+}
+
+dsa_status_t check_indexer_dims(int32_t H_I, int32_t D_I) {
+  REQUIRE(H_I >= 1 && H_I <= 64, DSA_ERR_UNSUPPORTED, "H_I=%d not in [1, 64]", H_I);
+  REQUIRE(D_I == 32 || D_I == 64 || D_I == 96 || D_I == 128, DSA_ERR_UNSUPPORTED,
+          "D_I=%d not in {32, 64, 96, 128}", D_I);
+  return DSA_OK;
+}
+
+dsa_status_t check_mla_dims(int32_t H, int32_t D_qk, int32_t D_v, int32_t k) {
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 1", k);
+  REQUIRE(dsa::mla_supported(D_qk, D_v, H, k), DSA_ERR_UNSUPPORTED,
+          "sparse MLA shape H=%d D_qk=%d D_v=%d k=%d not supported", H, D_qk, D_v, k);
+  return DSA_OK;
+}
+
+dsa_status_t check_topk(int64_t S, int32_t k) {
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 1", k);
+  REQUIRE(dsa::topk_supported(S, k), DSA_ERR_UNSUPPORTED, "top-k with k=%d over rows of %lld not supported",
+          k, (long long)S);
+  return DSA_OK;
+}
+
+int32_t decode_splits(int32_t B, int32_t k) {
+  int32_t want = (512 + B - 1) / B;
+  int32_t cap = std::max(1, k / 64);
+  return std::max(1, std::min(want, cap));
+}
+
+struct PrefillLayout {
+  size_t logits, indices, topk, total;
+  int64_t ld;
+};
+PrefillLayout prefill_layout(const dsa_dims_t* d, int64_t T, int64_t S) {
+  PrefillLayout L{};
+  L.ld = ld_for(S);
+  L.logits = 0;
+  L.indices = round_up((size_t)T * L.ld * sizeof(float), kAlign);
+  L.topk = L.indices + round_up((size_t)T * d->topk * sizeof(int32_t), kAlign);
+  L.total = L.topk + round_up(dsa::topk_workspace_bytes(T, S, d->topk), kAlign);
+  return L;
+}
+
+struct DecodeLayout {
+  size_t logits, indices, topk, part_out, part_lse, total;
+  int64_t ld;
+  int32_t nsplit;
+};
+DecodeLayout decode_layout(const dsa_dims_t* d, int32_t B, int64_t max_len) {
+  DecodeLayout L{};
+  L.ld = ld_for(max_len);
+  L.nsplit = decode_splits(B, d->topk);
+  L.logits = 0;
+  L.indices = round_up((size_t)B * L.ld * sizeof(float), kAlign);
+  L.topk = L.indices + round_up((size_t)B * d->topk * sizeof(int32_t), kAlign);
+  L.part_out = L.topk + round_up(dsa::topk_workspace_bytes(B, max_len, d->topk), kAlign);
+  L.part_lse = L.part_out + round_up((size_t)B * L.nsplit * d->H * d->D_v * sizeof(float), kAlign);
+  L.total = L.part_lse + round_up((size_t)B * L.nsplit * d->H * sizeof(float), kAlign);
+  return L;
+}
+
+dsa_status_t check_dims(const dsa_dims_t* d) {
+  REQUIRE(d != nullptr, DSA_ERR_INVALID_ARGUMENT, "dims must not be NULL");
+  dsa_status_t s = check_indexer_dims(d->H_I, d->D_I);
+  if (s != DSA_OK) return s;
+  s = check_mla_dims(d->H, d->D_qk, d->D_v, d->topk);
+  if (s != DSA_OK) return s;
+  REQUIRE(d->topk <= 2048, DSA_ERR_UNSUPPORTED, "topk=%d above 2048", d->topk);
+  REQUIRE(d->sm_scale > 0.f, DSA_ERR_INVALID_ARGUMENT, "sm_scale must be positive");
+  return DSA_OK;
+}
+
+dsa_status_t check_cache(const dsa_paged_cache_t* c, int64_t rows_needed_per_seq, int32_t seqs) {
+  REQUIRE(c != nullptr, DSA_ERR_INVALID_ARGUMENT, "cache must not be NULL");
+  REQUIRE_PTR(c->k8);
+  REQUIRE_PTR(c->k_scale);
+  REQUIRE_PTR(c->kv);
+  REQUIRE_PTR(c->block_table);
+  REQUIRE(c->block_size >= 1 && c->block_size <= (1 << 20) && (c->block_size & (c->block_size - 1)) == 0,
+          DSA_ERR_INVALID_ARGUMENT, "block_size=%d must be a power of two", c->block_size);
+  REQUIRE(c->num_blocks >= 1, DSA_ERR_INVALID_ARGUMENT, "num_blocks must be >= 1");
+  REQUIRE(c->num_blocks * (int64_t)c->block_size <= INT32_MAX, DSA_ERR_UNSUPPORTED,
+          "pool of %lld rows exceeds 2^31", (long long)(c->num_blocks * c->block_size));
+  const int64_t blocks_needed = (rows_needed_per_seq + c->block_size - 1) / c->block_size;
+  REQUIRE(c->max_blocks_per_seq >= blocks_needed, DSA_ERR_INVALID_ARGUMENT,
+          "max_blocks_per_seq=%lld < %lld blocks needed", (long long)c->max_blocks_per_seq,
+          (long long)blocks_needed);
+  (void)seqs;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status_t s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARGUMENT: return "DSA_ERR_INVALID_ARGUMENT";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "DSA_ERR_WORKSPACE_TOO_SMALL";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "unknown dsa_status_t";
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+dsa_status_t dsa_indexer_logits(const uint8_t* q8, const float* q_scale, const float* w, const uint8_t* k8,
+                                const float* k_scale, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
+                                int64_t q_start, float* logits, int64_t ld_logits, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  dsa_status_t s = check_indexer_dims(H_I, D_I);
+  if (s != DSA_OK) return s;
+  if (T == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1 when T > 0");
+  REQUIRE(ld_logits >= S && ld_logits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_logits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_logits, (long long)S);
+  REQUIRE_PTR(q8);
+  REQUIRE_PTR(q_scale);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(k8);
+  REQUIRE_PTR(k_scale);
+  REQUIRE_PTR(logits);
+  return hip_status(dsa::launch_indexer_prefill(q8, q_scale, w, k8, k_scale, nullptr, 0, T, S, H_I, D_I,
+                                                q_start, logits, ld_logits, stream),
+                    "indexer launch");
+}
+
+size_t dsa_topk_workspace_size(int64_t T, int64_t S, int32_t k) {
+  if (T <= 0 || S <= 0 || k <= 0) return 0;
+  return dsa::topk_workspace_bytes(T, S, k);
+}
+
+dsa_status_t dsa_topk(const float* logits, int64_t ld_logits, int64_t T, int64_t S, int64_t q_start, int32_t k,
+                      int32_t* indices, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  dsa_status_t s = check_topk(S, k);
+  if (s != DSA_OK) return s;
+  if (T == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1 when T > 0");
+  REQUIRE(k <= 2048 || S <= 32768, DSA_ERR_UNSUPPORTED, "k=%d above 2048 needs S <= 32768", k);
+  REQUIRE(ld_logits >= S && ld_logits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_logits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_logits, (long long)S);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(indices);
+  const size_t need = dsa::topk_workspace_bytes(T, S, k);
+  REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "top-k workspace %zu < %zu bytes",
+          workspace_bytes, need);
+  if (need) REQUIRE_PTR(workspace);
+  return hip_status(dsa::launch_topk(logits, ld_logits, T, S, q_start, nullptr, k, indices, workspace, stream),
+                    "top-k launch");
+}
+
+size_t dsa_sparse_mla_workspace_size(int64_t, int32_t, int32_t, int32_t) { return 0; }
+
+dsa_status_t dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int64_t T,
+                                int64_t S, int32_t H, int32_t D_qk, int32_t D_v, int32_t k, int64_t q_start,
+                                float sm_scale, uint16_t* out, float* out_f32, float* lse, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  dsa_status_t s = check_mla_dims(H, D_qk, D_v, k);
+  if (s != DSA_OK) return s;
+  REQUIRE(sm_scale > 0.f, DSA_ERR_INVALID_ARGUMENT, "sm_scale must be positive");
+  if (T == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1 when T > 0");
+  REQUIRE(S <= INT32_MAX, DSA_ERR_UNSUPPORTED, "S above 2^31");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kv);
+  REQUIRE_PTR(indices);
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(out_f32);
+  OPTIONAL_PTR(lse);
+  dsa::MlaArgs a{};
+  a.q = q;
+  a.kv = kv;
+  a.idx = indices;
+  a.R = T;
+  a.S = S;
+  a.q_start = q_start;
+  a.H = H;
+  a.D_qk = D_qk;
+  a.D_v = D_v;
+  a.k = k;
+  a.sm_scale = sm_scale;
+  a.nsplit = 1;
+  a.out = out;
+  a.out_f32 = out_f32;
+  a.lse = lse;
+  return hip_status(dsa::launch_sparse_mla(a, stream), "sparse MLA launch");
+}
+
+size_t dsa_prefill_workspace_size(const dsa_dims_t* d, int64_t T, int64_t S) {
+  if (!d || T <= 0 || S <= 0 || d->topk <= 0) return 0;
+  return prefill_layout(d, T, S).total;
+}
+
+dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t* c, int32_t seq, const dsa_dims_t* d, int64_t T,
+                               int64_t q_start, const uint8_t* q8, const float* q_scale, const float* w,
+                               const uint16_t* q, uint16_t* out, float* out_f32, float* lse,
+                               int32_t* indices_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  dsa_status_t s = check_dims(d);
+  if (s != DSA_OK) return s;
+  REQUIRE(T >= 0 && q_start >= 0 && seq >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, q_start or seq");
+  if (T == 0) return ok();
+  const int64_t S = q_start + T;
+  s = check_cache(c, S, seq + 1);
+  if (s != DSA_OK) return s;
+  REQUIRE(S <= (int64_t)c->num_blocks * c->block_size, DSA_ERR_INVALID_ARGUMENT,
+          "context of %lld keys exceeds the pool", (long long)S);
+  REQUIRE_PTR(q8);
+  REQUIRE_PTR(q_scale);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(out_f32);
+  OPTIONAL_PTR(lse);
+  OPTIONAL_PTR(indices_out);
+  const PrefillLayout L = prefill_layout(d, T, S);
+  REQUIRE(workspace_bytes >= L.total, DSA_ERR_WORKSPACE_TOO_SMALL, "prefill workspace %zu < %zu bytes",
+          workspace_bytes, L.total);
+  REQUIRE(workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % kAlign) == 0,
+          DSA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 256-byte aligned");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = indices_out ? indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
+  const int32_t* table = c->block_table + (int64_t)seq * c->max_blocks_per_seq;
+  const int shift = block_shift_of(c->block_size);
+
+  hipError_t e = dsa::launch_indexer_prefill(q8, q_scale, w, c->k8, c->k_scale, table, shift, T, S, d->H_I,
+                                             d->D_I, q_start, logits, L.ld, stream);
+  if (e != hipSuccess) return hip_status(e, "indexer launch");
+  e = dsa::launch_topk(logits, L.ld, T, S, q_start, nullptr, d->topk, idx, ws + L.topk, stream);
+  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  dsa::MlaArgs a{};
+  a.q = q;
+  a.kv = c->kv;
+  a.idx = idx;
+  a.table = table;
+  a.max_blocks = c->max_blocks_per_seq;
+  a.block_shift = shift;
+  a.per_row_table = 0;
+  a.R = T;
+  a.S = S;
+  a.q_start = q_start;
+  a.H = d->H;
+  a.D_qk = d->D_qk;
+  a.D_v = d->D_v;
+  a.k = d->topk;
+  a.sm_scale = d->sm_scale;
+  a.nsplit = 1;
+  a.out = out;
+  a.out_f32 = out_f32;
+  a.lse = lse;
+  return hip_status(dsa::launch_sparse_mla(a, stream), "sparse MLA launch");
+}
+
+size_t dsa_decode_workspace_size(const dsa_dims_t* d, int32_t B, int64_t max_seq_len) {
+  if (!d || B <= 0 || max_seq_len <= 0 || d->topk <= 0 || d->H <= 0 || d->D_v <= 0) return 0;
+  return decode_layout(d, B, max_seq_len).total;
+}
+
+dsa_status_t dsa_decode_paged(const dsa_paged_cache_t* c, int32_t B, int64_t max_seq_len, const dsa_dims_t* d,
+                              const uint8_t* q8, const float* q_scale, const float* w, const uint16_t* q,
+                              uint16_t* out, float* out_f32, float* lse, int32_t* indices_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  dsa_status_t s = check_dims(d);
+  if (s != DSA_OK) return s;
+  REQUIRE(B >= 0 && max_seq_len >= 0, DSA_ERR_INVALID_ARGUMENT, "negative B or max_seq_len");
+  if (B == 0) return ok();
+  REQUIRE(max_seq_len >= 1, DSA_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 1");
+  s = check_cache(c, max_seq_len, B);
+  if (s != DSA_OK) return s;
+  REQUIRE_PTR(c->seq_lens);
+  s = check_topk(max_seq_len, d->topk);
+  if (s != DSA_OK) return s;
+  REQUIRE_PTR(q8);
+  REQUIRE_PTR(q_scale);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(out_f32);
+  OPTIONAL_PTR(lse);
+  OPTIONAL_PTR(indices_out);
+  const DecodeLayout L = decode_layout(d, B, max_seq_len);
+  REQUIRE(workspace_bytes >= L.total, DSA_ERR_WORKSPACE_TOO_SMALL, "decode workspace %zu < %zu bytes",
+          workspace_bytes, L.total);
+  REQUIRE(workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % kAlign) == 0,
+          DSA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 256-byte aligned");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = indices_out ? indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
+  const int shift = block_shift_of(c->block_size);
+
+  hipError_t e = dsa::launch_indexer_decode(q8, q_scale, w, c->k8, c->k_scale, c->block_table,
+                                            c->max_blocks_per_seq, shift, c->seq_lens, B, max_seq_len, d->H_I,
+                                            d->D_I, logits, L.ld, stream);
+  if (e != hipSuccess) return hip_status(e, "decode indexer launch");
+  e = dsa::launch_topk(logits, L.ld, B, max_seq_len, 0, c->seq_lens, d->topk, idx, ws + L.topk, stream);
+  if (e != hipSuccess) return hip_status(e, "top-k launch");
+  dsa::MlaArgs a{};
+  a.q = q;
+  a.kv = c->kv;
+  a.idx = idx;
+  a.table = c->block_table;
+  a.max_blocks = c->max_blocks_per_seq;
+  a.block_shift = shift;
+  a.per_row_table = 1;
+  a.seq_lens = c->seq_lens;
+  a.R = B;
+  a.S = max_seq_len;
+  a.q_start = 0;
+  a.H = d->H;
+  a.D_qk = d->D_qk;
+  a.D_v = d->D_v;
+  a.k = d->topk;
+  a.sm_scale = d->sm_scale;
+  a.nsplit = L.nsplit;
+  a.out = out;
+  a.out_f32 = out_f32;
+  a.lse = lse;
+  a.part_out = reinterpret_cast<float*>(ws + L.part_out);
+  a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  return hip_status(dsa::launch_sparse_mla(a, stream), "sparse MLA launch");
+}
+
+}  // extern "C"

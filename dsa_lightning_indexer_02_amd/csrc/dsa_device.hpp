@@ -1,0 +1,80 @@
+// Device-side building blocks shared by the DSA kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA operand layouts used throughout (16x16 tiles; lane l, group g = l / 16):
+//  - A (M x K) and B (K x N) operands: lane l supplies row (A) / column (B) l % 16 and
+//    a contiguous run of the contraction index starting at (run length) * g.  Only the
+//    agreement between the A and B runs matters for a full-K dot product.
+//  - C / D (16 x 16 fp32): lane l holds rows 4 g + r (r = 0..3) of column l % 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+// FP8 (OCP E4M3) 16x16x128 MFMA, fp32 accumulate, no block scales.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const s16x8& a, const s16x8& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_f16_16x16x32(const s16x8& a, const s16x8& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Order-preserving map of an fp32 score to uint32 (larger score -> larger key); -0.0 maps
+// like +0.0 so that the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Physical row of logical position s in one sequence's paged storage.  A null table is
+// the identity (contiguous storage).
+struct RowMap {
+  const int32_t* table;
+  int32_t block_shift;  // log2(block size)
+  __device__ __forceinline__ int64_t operator()(int64_t s) const {
+    if (!table) return s;
+    int64_t blk = table[s >> block_shift];
+    return (blk << block_shift) | (s & ((1 << block_shift) - 1));
+  }
+};
+
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+}  // namespace dsa

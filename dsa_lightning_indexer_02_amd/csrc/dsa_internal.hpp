@@ -1,0 +1,58 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "dsa_device.hpp"
+
+namespace dsa {
+
+// ---- lightning indexer
+size_t indexer_prefill_smem(int32_t H_I);
+hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
+                                  const float* ks, const int32_t* table, int32_t block_shift, int64_t T,
+                                  int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, float* logits,
+                                  int64_t ld, hipStream_t stream);
+hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
+                                 const float* ks, const int32_t* table, int64_t max_blocks,
+                                 int32_t block_shift, const int32_t* seq_lens, int32_t B, int64_t max_len,
+                                 int32_t H_I, int32_t D_I, float* logits, int64_t ld, hipStream_t stream);
+
+// ---- top-k
+int32_t topk_chunks(int64_t S);
+size_t topk_workspace_bytes(int64_t T, int64_t S, int32_t k);
+bool topk_supported(int64_t S, int32_t k);
+hipError_t launch_topk(const float* logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
+                       const int32_t* seq_lens, int32_t k, int32_t* indices, void* workspace,
+                       hipStream_t stream);
+
+// ---- sparse MLA
+struct MlaArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* idx;
+  const int32_t* table;
+  int64_t max_blocks;
+  int32_t block_shift;
+  int32_t per_row_table;   // decode: row r uses table + r * max_blocks
+  const int32_t* seq_lens; // decode: visible keys per row; null for prefill
+  int64_t R;               // query rows
+  int64_t S;
+  int64_t q_start;
+  int32_t H, D_qk, D_v, k;
+  float sm_scale;
+  int32_t nsplit;
+  uint16_t* out;
+  float* out_f32;
+  float* lse;
+  float* part_out;
+  float* part_lse;
+};
+bool mla_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k);
+hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,330 @@
+// Per-query top-k selection (AMD MI355X DeepSeek-V3.2-Exp article, section "Fine-Grained Token
+// Selection"; DeepSeek-V3.2-Exp summary page, section "Method": top-k = 2048): for query row t,
+// the k highest scores among its n_t visible keys; equal scores go to the lower key index.
+//
+// A workgroup of 512 threads holds up to 32768 scores of one row in registers as
+// order-preserving uint32 keys and runs an exact radix select over them: the first digit
+// window starts at the highest bit where the row's minimum and maximum keys differ, each
+// pass builds an LDS histogram of an 11-bit digit among the keys that still match the
+// threshold's known prefix, and at most three passes pin the k-th largest key exactly.
+// Emission is an ordered compaction (wave ballots and prefix counts), so the output is
+// deterministic: every key above the threshold in index order, then the lowest-index ties.
+//
+// Rows longer than 32768 are cut into chunks; each chunk emits its own top-k candidates
+// (key, index) and a merge pass runs the same select over the concatenated candidates.  This
+// is exact: an element in the row's top-k is in its chunk's top-k under the same order.
+#include "dsa_internal.hpp"
+
+namespace dsa {
+
+constexpr int TK_THREADS = 512;
+constexpr int TK_WAVES = TK_THREADS / WAVE;
+constexpr int TK_BINS = 2048;
+constexpr int TK_DIGIT = 11;
+constexpr int TK_CHUNK_EPT = 64;  // 512 * 64 = 32768 scores per workgroup
+constexpr int64_t TK_CHUNK = (int64_t)TK_THREADS * TK_CHUNK_EPT;
+constexpr int TK_MERGE_EPT = 16;  // 8192 candidates per merge
+
+struct TopkShared {
+  uint32_t hist[TK_BINS];
+  uint32_t wsum[TK_WAVES][2];
+  uint32_t red[TK_WAVES][2];
+  uint32_t sel_bin, sel_above;
+  uint32_t kmax, kmin;
+};
+
+// Position of element e of this thread inside the workgroup's range.
+template <int EPT>
+__device__ __forceinline__ int elem_pos(int wave, int lane, int e) {
+  return wave * (WAVE * EPT) + (e >> 2) * (4 * WAVE) + 4 * lane + (e & 3);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+// inclusive prefix sum over the wave
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t u = (uint32_t)__shfl_up((int)v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Exact threshold search.  keys: this thread's EPT keys (0 = no element).  Returns tau (the
+// k-th largest key) and k_rem (how many elements equal to tau are selected).  Requires at
+// least k valid elements.
+template <int EPT>
+__device__ void radix_threshold(const uint32_t (&key)[EPT], uint32_t k, TopkShared& sh,
+                                uint32_t& tau, uint32_t& k_rem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t mx = 0, mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (key[e]) {
+      mx = max(mx, key[e]);
+      mn = min(mn, key[e]);
+    }
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if (lane == 0) {
+    sh.red[wave][0] = mx;
+    sh.red[wave][1] = mn;
+  }
+  __syncthreads();
+  mx = 0;
+  mn = 0xFFFFFFFFu;
+  for (int i = 0; i < TK_WAVES; ++i) {
+    mx = max(mx, sh.red[i][0]);
+    mn = min(mn, sh.red[i][1]);
+  }
+  __syncthreads();
+  if (mx == mn) {  // every valid element is equal
+    tau = mx;
+    k_rem = k;
+    return;
+  }
+  const int hb = 31 - __clz(mx ^ mn);
+  int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
+  int bits = hb - shift + 1;
+  uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));  // bits above the window
+  uint32_t need = k;
+  while (true) {
+    for (int i = tid; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
+    __syncthreads();
+    const int hi_shift = shift + bits;
+    const uint32_t dmask = (1u << bits) - 1u;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t kk = key[e];
+      const bool match = kk != 0 && (hi_shift >= 32 ? true : ((kk >> hi_shift) == prefix));
+      if (match) atomicAdd(&sh.hist[(kk >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // suffix counts: thread t owns the 4 bins 4*(511 - t) .. +3 (highest bins first)
+    const int b0 = 4 * (TK_THREADS - 1 - tid);
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = sh.hist[b0 + i];
+    const uint32_t own = h[0] + h[1] + h[2] + h[3];
+    const uint32_t incl = wave_incl_scan(own, lane);
+    if (lane == 63) sh.wsum[wave][0] = incl;
+    __syncthreads();
+    uint32_t above = incl - own;
+    for (int i = 0; i < wave; ++i) above += sh.wsum[i][0];
+    if (above < need && need <= above + own) {
+      uint32_t a = above;
+      for (int i = 3; i >= 0; --i) {
+        if (need <= a + h[i]) {
+          sh.sel_bin = (uint32_t)(b0 + i);
+          sh.sel_above = a;
+          break;
+        }
+        a += h[i];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sh.sel_bin;
+    need -= sh.sel_above;
+    __syncthreads();
+    prefix = (hi_shift >= 32 ? 0u : (prefix << bits)) | bin;
+    if (shift == 0) break;
+    bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
+    shift -= bits;
+  }
+  tau = prefix;
+  k_rem = need;
+}
+
+// Ordered emission of the selected elements: all keys > tau in position order, then the
+// first k_rem keys == tau.  emit(pos, e, slot) is called once per selected element.
+template <int EPT, typename Emit>
+__device__ void emit_selected(const uint32_t (&key)[EPT], uint32_t tau, uint32_t k, uint32_t k_rem,
+                              TopkShared& sh, Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t cg = 0, ce = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    cg += key[e] > tau;
+    ce += key[e] == tau;
+  }
+  // wave totals
+  uint32_t tg = cg, te = ce;
+  for (int o = 32; o > 0; o >>= 1) {
+    tg += (uint32_t)__shfl_xor((int)tg, o);
+    te += (uint32_t)__shfl_xor((int)te, o);
+  }
+  if (lane == 0) {
+    sh.wsum[wave][0] = tg;
+    sh.wsum[wave][1] = te;
+  }
+  __syncthreads();
+  uint32_t gbase = 0, ebase = 0;
+  for (int i = 0; i < wave; ++i) {
+    gbase += sh.wsum[i][0];
+    ebase += sh.wsum[i][1];
+  }
+  const uint32_t n_gt = k - k_rem;
+#pragma unroll
+  for (int q = 0; q < EPT / 4; ++q) {
+    uint32_t sg = 0, se = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sg += key[4 * q + c] > tau;
+      se += key[4 * q + c] == tau;
+    }
+    const uint32_t packed = sg | (se << 16);
+    const uint32_t incl = wave_incl_scan(packed, lane);
+    const uint32_t excl = incl - packed;
+    uint32_t og = gbase + (excl & 0xFFFFu), oe = ebase + (excl >> 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * q + c;
+      const uint32_t kk = key[e];
+      if (kk > tau) {
+        emit(elem_pos<EPT>(wave, lane, e), e, og);
+        ++og;
+      } else if (kk == tau) {
+        if (oe < k_rem) emit(elem_pos<EPT>(wave, lane, e), e, n_gt + oe);
+        ++oe;
+      }
+    }
+    const uint32_t tot = (uint32_t)__shfl((int)incl, 63);
+    gbase += tot & 0xFFFFu;
+    ebase += tot >> 16;
+  }
+}
+
+// Load this thread's elements of scores[0 .. n) (n <= 512 * EPT) as keys.
+template <int EPT>
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t n, uint32_t (&key)[EPT]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < EPT / 4; ++q) {
+    const int p = elem_pos<EPT>(wave, lane, 4 * q);
+    if (p + 3 < n) {
+      const v4f v = *reinterpret_cast<const v4f*>(row + p);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[4 * q + c] = score_key(v[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) key[4 * q + c] = (p + c < n) ? score_key(row[p + c]) : 0u;
+    }
+  }
+}
+
+// One chunk of one row.  Rows with a single chunk write the final index list; otherwise the
+// chunk's candidates go to cand_key / cand_idx [rows][G][k] (key 0 = empty slot).
+// mode 0: prefill rows (n_t = min(S, q_start + t + 1)); mode 1: decode rows (n = seq_lens[t]).
+__global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
+    const float* __restrict__ logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
+    const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices,
+    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, int32_t G) {
+  __shared__ TopkShared sh;
+  const int64_t t = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const int64_t n = seq_lens ? min((int64_t)max(seq_lens[t], 0), S) : min(S, q_start + t + 1);
+  const int64_t c0 = (int64_t)chunk * TK_CHUNK;
+  if (c0 >= n && chunk > 0) return;
+  const int64_t cn = min(n - c0, TK_CHUNK);  // elements of this chunk
+  const bool single = n <= TK_CHUNK;
+  const int tid = threadIdx.x;
+  int32_t* out_idx = indices + t * k;
+  uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
+  int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
+
+  if (cn <= k) {  // everything in the chunk is selected
+    for (int64_t i = tid; i < k; i += TK_THREADS) {
+      if (single) {
+        out_idx[i] = i < cn ? (int32_t)(c0 + i) : -1;
+      } else {
+        ck[i] = i < cn ? score_key(logits[t * ld + c0 + i]) : 0u;
+        ci[i] = i < cn ? (int32_t)(c0 + i) : -1;
+      }
+    }
+    return;
+  }
+  uint32_t key[TK_CHUNK_EPT];
+  load_keys<TK_CHUNK_EPT>(logits + t * ld + c0, cn, key);
+  uint32_t tau, k_rem;
+  radix_threshold<TK_CHUNK_EPT>(key, (uint32_t)k, sh, tau, k_rem);
+  if (single) {
+    emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                                [&](int pos, int, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
+  } else {
+    emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh, [&](int pos, int e, uint32_t slot) {
+      ck[slot] = key[e];
+      ci[slot] = (int32_t)(c0 + pos);
+    });
+  }
+}
+
+// Merge the chunk candidates of rows with more than one chunk.
+__global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
+    int64_t T, int64_t S, int64_t q_start, const int32_t* __restrict__ seq_lens, int32_t k,
+    int32_t* __restrict__ indices, const uint32_t* __restrict__ cand_key,
+    const int32_t* __restrict__ cand_idx, int32_t G) {
+  __shared__ TopkShared sh;
+  const int64_t t = blockIdx.x;
+  const int64_t n = seq_lens ? min((int64_t)max(seq_lens[t], 0), S) : min(S, q_start + t + 1);
+  if (n <= TK_CHUNK) return;  // finished by the chunk kernel
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = (int)((n + TK_CHUNK - 1) / TK_CHUNK);
+  const int64_t total = (int64_t)nch * k;  // <= 512 * TK_MERGE_EPT (checked on the host)
+  const uint32_t* ck = cand_key + t * G * (int64_t)k;
+  const int32_t* ci = cand_idx + t * G * (int64_t)k;
+  uint32_t key[TK_MERGE_EPT];
+  int32_t idx[TK_MERGE_EPT];
+#pragma unroll
+  for (int e = 0; e < TK_MERGE_EPT; ++e) {
+    const int p = elem_pos<TK_MERGE_EPT>(wave, lane, e);
+    key[e] = p < total ? ck[p] : 0u;
+    idx[e] = p < total ? ci[p] : -1;
+  }
+  uint32_t tau, k_rem;
+  radix_threshold<TK_MERGE_EPT>(key, (uint32_t)k, sh, tau, k_rem);
+  int32_t* out_idx = indices + t * k;
+  emit_selected<TK_MERGE_EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                              [&](int, int e, uint32_t slot) { out_idx[slot] = idx[e]; });
+}
+
+int32_t topk_chunks(int64_t S) { return (int32_t)((S + TK_CHUNK - 1) / TK_CHUNK); }
+
+size_t topk_workspace_bytes(int64_t T, int64_t S, int32_t k) {
+  const int32_t G = topk_chunks(S);
+  if (G <= 1) return 0;
+  return (size_t)T * G * k * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
+bool topk_supported(int64_t S, int32_t k) {
+  const int32_t G = topk_chunks(S);
+  return k >= 1 && k <= TK_CHUNK && (G <= 1 || (int64_t)G * k <= (int64_t)TK_THREADS * TK_MERGE_EPT);
+}
+
+hipError_t launch_topk(const float* logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
+                       const int32_t* seq_lens, int32_t k, int32_t* indices, void* workspace,
+                       hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int32_t G = topk_chunks(S);
+  uint32_t* ck = nullptr;
+  int32_t* ci = nullptr;
+  if (G > 1) {
+    ck = reinterpret_cast<uint32_t*>(workspace);
+    ci = reinterpret_cast<int32_t*>(ck + (size_t)T * G * k);
+  }
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)G, (unsigned)T), dim3(TK_THREADS), 0, stream,
+                     logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || G <= 1) return e;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, T, S, q_start,
+                     seq_lens, k, indices, ck, ci, G);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,161 @@
+/*
+ * dsa.h - C ABI of the DeepSeek Sparse Attention (DSA) hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method (DeepSeek-V3.2-Exp summary page, section "Method"; AMD "MI355X GPUs Power
+ * DeepSeek-V3.2-Exp" article, sections "Lightning Indexer" and "Fine-Grained Token Selection"):
+ *   1. a lightning indexer scores every causally visible key s of query token t,
+ *        I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j] . k_I[s]),  H_I heads, FP8 inputs;
+ *   2. the top-k (k = 2048 in the model) keys per query are selected;
+ *   3. MLA attention in MQA mode (one latent KV row shared by all query heads of a token)
+ *      runs over only the selected rows.
+ *
+ * Conventions shared by every call
+ *  - Pointers are device memory owned by the caller (hipMalloc / framework tensors), unless a
+ *    parameter says otherwise.  The library allocates no device memory, keeps no pointer after a
+ *    call returns and never synchronises: work is enqueued on `stream`; the caller keeps every
+ *    buffer alive until that work completes.
+ *  - Tensors are dense row-major.  FP8 means OCP E4M3 ("e4m3fn": bias 7, max 448, no infinity)
+ *    passed as uint8 codes; bf16 is passed as uint16 bit patterns; scales are fp32, one per row
+ *    of the last dimension, positive.
+ *  - Causality: query row t sits at absolute position q_start + t and sees keys
+ *    0 .. n_t - 1 with n_t = min(S, q_start + t + 1) (its own position included).
+ *  - Base pointers must be 16-byte aligned.  Argument errors are detected on the host before
+ *    anything is enqueued (no partial work) and return DSA_ERR_INVALID_ARGUMENT, or
+ *    DSA_ERR_UNSUPPORTED for shapes outside the compiled set, or DSA_ERR_WORKSPACE_TOO_SMALL.
+ *    Launch failures return DSA_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  dsa_last_error() gives a thread-local message for the last failing call.
+ *  - T == 0 (or B == 0) is a valid no-op.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_HIP = 4
+} dsa_status_t;
+
+const char *dsa_status_string(dsa_status_t s);
+/* Message of the last failing call on this host thread ("" if none). */
+const char *dsa_last_error(void);
+int dsa_abi_version(void);
+
+/*
+ * Lightning-indexer scores (summary page, "Method"; AMD article, "Lightning Indexer"):
+ *   logits[t][s] = sum_j w[t][j] * max(0, (q_scale[t][j] dec(q8[t][j][:])) . (k_scale[s] dec(k8[s][:])))
+ * for s < n_t.  Entries s >= n_t of each logits row are not written.
+ *   q8 [T][H_I][D_I] u8, q_scale [T][H_I] f32, w [T][H_I] f32 (used as given, any sign),
+ *   k8 [S][D_I] u8, k_scale [S] f32, logits [T][ld_logits] f32 with ld_logits >= S and a
+ *   multiple of 4.  Supported: 1 <= H_I <= 64, D_I in {32, 64, 96, 128}.
+ */
+dsa_status_t dsa_indexer_logits(const uint8_t *q8, const float *q_scale, const float *w,
+                                const uint8_t *k8, const float *k_scale, int64_t T, int64_t S,
+                                int32_t H_I, int32_t D_I, int64_t q_start, float *logits,
+                                int64_t ld_logits, hipStream_t stream);
+
+/*
+ * Per-query top-k (AMD article, "Fine-Grained Token Selection"): indices[t][0 .. m) with
+ * m = min(k, n_t) are the key indices of the m largest logits[t][0 .. n_t) (finite scores;
+ * -0.0 equals +0.0; equal scores go to the lower index), every index above the k-th score
+ * first in ascending order, then the selected ties in ascending order (rows with n_t <= k list
+ * 0 .. n_t - 1); indices[t][m .. k) = -1.
+ * The order is deterministic.  Rows longer than 32768 need a workspace of
+ * dsa_topk_workspace_size() bytes (0 otherwise).  Supported: 1 <= k <= 2048 (larger k up to
+ * 32768 when S <= 32768).
+ */
+size_t dsa_topk_workspace_size(int64_t T, int64_t S, int32_t k);
+dsa_status_t dsa_topk(const float *logits, int64_t ld_logits, int64_t T, int64_t S, int64_t q_start,
+                      int32_t k, int32_t *indices, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * Sparse MLA forward, MQA mode (summary page, "Method"): for query row t, head h and the valid
+ * entries i of indices[t] (0 <= idx < n_t; anything else, including -1, is skipped; duplicates
+ * count with multiplicity):
+ *   z_i = sm_scale * q[t][h][:] . kv[idx_i][:],   out[t][h][:] = sum_i softmax(z)_i kv[idx_i][:D_v],
+ *   lse[t][h] = log sum_i exp(z_i)   (natural log; -inf and out = 0 for a row with no valid entry).
+ *   q [T][H][D_qk] bf16, kv [S][D_qk] bf16 (K = all D_qk columns, V = the first D_v),
+ *   indices [T][k] i32, out [T][H][D_v] bf16, out_f32 [T][H][D_v] f32 (optional, NULL to skip),
+ *   lse [T][H] f32 (optional).  Probabilities are rounded to fp16 for the P.V product and V is
+ *   converted bf16 -> fp16, exact for |v| in [2^-14, 65504] (precondition |v| <= 65504).
+ *   Supported: (D_qk, D_v) in {(576, 512), (80, 64)}, 1 <= H <= 128, 1 <= k <= 8192.
+ *   The workspace is unused (size 0) and may be NULL.
+ */
+size_t dsa_sparse_mla_workspace_size(int64_t T, int32_t H, int32_t D_v, int32_t k);
+dsa_status_t dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *indices,
+                                int64_t T, int64_t S, int32_t H, int32_t D_qk, int32_t D_v, int32_t k,
+                                int64_t q_start, float sm_scale, uint16_t *out, float *out_f32,
+                                float *lse, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Paged cache (summary page, section "Key claims": the released indexer-logit kernels include paged
+ * versions).  Logical key s
+ * of sequence b lives in block block_table[b][s / block_size], slot s % block_size, of the pools
+ *   k8 [num_blocks][block_size][D_I] u8, k_scale [num_blocks][block_size] f32,
+ *   kv [num_blocks][block_size][D_qk] bf16.
+ * block_table [B][max_blocks_per_seq] i32; seq_lens [B] i32 (device; includes new tokens).
+ * block_size must be a power of two (64 in the model deployment).
+ */
+typedef struct {
+  const uint8_t *k8;
+  const float *k_scale;
+  const uint16_t *kv;
+  int64_t num_blocks;
+  int32_t block_size;
+  const int32_t *block_table;
+  int64_t max_blocks_per_seq;
+  const int32_t *seq_lens;
+} dsa_paged_cache_t;
+
+typedef struct {
+  int32_t H_I, D_I, H, D_qk, D_v, topk;
+  float sm_scale;
+} dsa_dims_t;
+
+/*
+ * Fused prefill of sequence `seq`: T queries at positions q_start .. q_start + T - 1 over the
+ * S = q_start + T keys already in the paged cache: indexer -> top-k -> sparse MLA, the same
+ * kernels as the three standalone calls.  q8/q_scale/w/q as in the standalone calls,
+ * out [T][H][D_v] bf16, out_f32 (optional), lse [T][H] (optional), indices_out [T][topk]
+ * (optional; written when non-NULL).  Workspace: dsa_prefill_workspace_size() bytes, 256-byte
+ * aligned.
+ */
+size_t dsa_prefill_workspace_size(const dsa_dims_t *d, int64_t T, int64_t S);
+dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t *c, int32_t seq, const dsa_dims_t *d, int64_t T,
+                               int64_t q_start, const uint8_t *q8, const float *q_scale, const float *w,
+                               const uint16_t *q, uint16_t *out, float *out_f32, float *lse,
+                               int32_t *indices_out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Fused decode: one new query per sequence b at position seq_lens[b] - 1 over its seq_lens[b]
+ * keys (max_seq_len >= every seq_lens[b], used for grid and workspace sizing).
+ * q8 [B][H_I][D_I], q_scale [B][H_I], w [B][H_I], q [B][H][D_qk], out [B][H][D_v],
+ * out_f32 / lse / indices_out optional as above.  Sparse MLA is split over index chunks and the
+ * partial results are re-reduced in fp32.
+ */
+size_t dsa_decode_workspace_size(const dsa_dims_t *d, int32_t B, int64_t max_seq_len);
+dsa_status_t dsa_decode_paged(const dsa_paged_cache_t *c, int32_t B, int64_t max_seq_len,
+                              const dsa_dims_t *d, const uint8_t *q8, const float *q_scale,
+                              const float *w, const uint16_t *q, uint16_t *out, float *out_f32,
+                              float *lse, int32_t *indices_out, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,117 @@
+"""The C ABI library: loads without a GPU, exports every declared symbol, rejects bad arguments
+on the host before any launch (these calls never reach a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dsa_lightning_indexer_02_amd as dsa
+from dsa_lightning_indexer_02_amd._lib import Dims, PagedCache
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return dsa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_match_header(lib):
+    decl = declared_functions()
+    assert decl == sorted(dsa.EXPORTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r" T (dsa_\w+)", nm))
+    missing = [f for f in decl if f not in exported]
+    assert not missing, missing
+    for f in decl:
+        assert hasattr(lib, f)
+
+
+def test_version_and_strings(lib):
+    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def _err(lib):
+    return lib.dsa_last_error().decode()
+
+
+def test_indexer_argument_errors(lib):
+    f = lib.dsa_indexer_logits
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 65, 128, 0, FAKE, 8, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 64, 100, 0, FAKE, 8, None) == UNSUPPORTED
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 4, 8, 64, 128, 0, FAKE, 8, None) == INVALID
+    assert "q8" in _err(lib)
+    assert f(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 64, 128, 0, FAKE, 8, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 64, 128, 0, FAKE, 6, None) == INVALID   # ld < S
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 10, 64, 128, 0, FAKE, 10, None) == INVALID  # ld % 4
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 64, 128, 0, FAKE, 8, None) == INVALID
+    assert f(None, None, None, None, None, 0, 8, 64, 128, 0, None, 8, None) == OK         # T = 0
+
+
+def test_topk_argument_errors(lib):
+    f = lib.dsa_topk
+    assert f(FAKE, 8, 4, 8, 0, 0, FAKE, None, 0, None) == INVALID                     # k = 0
+    need = lib.dsa_topk_workspace_size(4, 100000, 2048)
+    assert need > 0 and lib.dsa_topk_workspace_size(4, 32768, 2048) == 0
+    assert f(FAKE, 100000, 4, 100000, 0, 2048, FAKE, FAKE, need - 1, None) == WS_SMALL
+    assert f(FAKE, 100000, 4, 100000, 0, 4096, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+    assert f(FAKE, 8, 4, 8, 0, 64, None, None, 0, None) == INVALID
+    assert f(None, 8, 0, 8, 0, 64, None, None, 0, None) == OK
+
+
+def test_mla_argument_errors(lib):
+    f = lib.dsa_sparse_mla_fwd
+    sm = ctypes.c_float(0.1)
+    assert f(FAKE, FAKE, FAKE, 4, 8, 128, 512, 512, 64, 0, sm, FAKE, None, None, None, 0, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 4, 8, 129, 576, 512, 64, 0, sm, FAKE, None, None, None, 0, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 4, 8, 128, 576, 512, 0, 0, sm, FAKE, None, None, None, 0, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 4, 8, 128, 576, 512, 64, 0, ctypes.c_float(0.0), FAKE, None, None, None, 0,
+             None) == INVALID
+    assert f(FAKE, FAKE, None, 4, 8, 128, 576, 512, 64, 0, sm, FAKE, None, None, None, 0, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 4, 8, 128, 576, 512, 64, 0, sm, FAKE, FAKE + 8, None, None, 0, None) == INVALID
+
+
+def test_fused_argument_errors(lib):
+    d = Dims(64, 128, 128, 576, 512, 2048, 0.07)
+    c = PagedCache(FAKE, FAKE, FAKE, 100, 64, FAKE, 100, FAKE)
+    need = lib.dsa_prefill_workspace_size(ctypes.byref(d), 4096, 4096)
+    assert need >= 4096 * 4096 * 4
+    f = lib.dsa_prefill_paged
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE]
+    assert f(ctypes.byref(c), 0, ctypes.byref(d), 4096, 0, *args, need - 1, None) == WS_SMALL
+    assert f(ctypes.byref(c), 0, ctypes.byref(d), 4096, 0, *args[:-1], FAKE + 16, need, None) == INVALID
+    bad_bs = PagedCache(FAKE, FAKE, FAKE, 100, 48, FAKE, 100, FAKE)
+    assert f(ctypes.byref(bad_bs), 0, ctypes.byref(d), 4096, 0, *args, need, None) == INVALID
+    small_tbl = PagedCache(FAKE, FAKE, FAKE, 100, 64, FAKE, 10, FAKE)
+    assert f(ctypes.byref(small_tbl), 0, ctypes.byref(d), 4096, 0, *args, need, None) == INVALID
+    d_bad = Dims(64, 128, 128, 576, 512, 4096, 0.07)
+    assert f(ctypes.byref(c), 0, ctypes.byref(d_bad), 4096, 0, *args, need, None) == UNSUPPORTED
+    assert f(ctypes.byref(c), 0, ctypes.byref(d), 0, 0, *args, 0, None) == OK
+    g = lib.dsa_decode_paged
+    need_d = lib.dsa_decode_workspace_size(ctypes.byref(d), 64, 131072)
+    assert need_d > 64 * 131072 * 4
+    no_lens = PagedCache(FAKE, FAKE, FAKE, 100000, 64, FAKE, 2048, None)
+    assert g(ctypes.byref(no_lens), 64, 131072, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+             None, FAKE, need_d, None) == INVALID
+    c2 = PagedCache(FAKE, FAKE, FAKE, 100000, 64, FAKE, 2048, FAKE)
+    assert g(ctypes.byref(c2), 64, 131072, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+             FAKE, need_d - 1, None) == WS_SMALL
+    assert g(ctypes.byref(c2), 0, 131072, ctypes.byref(d), None, None, None, None, None, None, None, None,
+             None, 0, None) == OK

@@ -1,0 +1,127 @@
+"""Edge cases of the top-k and sparse-MLA kernels through the C ABI vs the oracle (needs an MI355X)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from dsa_inputs.generate import block_rng, to_bf16_bits
+from gpu_helpers import bf16_vals, dget, dput
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dsa_lightning_indexer_02_amd as dsa
+    dsa.load()
+    return torch.device("cuda:0")
+
+
+def _topk_case(dev, scores: np.ndarray, q_start: int, k: int, name: str):
+    import dsa_lightning_indexer_02_amd as dsa
+    print("case", name, scores.shape, "k", k, flush=True)
+    T, S = scores.shape
+    ld = dsa.ld_for(S)
+    host = np.zeros((T, ld), np.float32)
+    host[:, :S] = scores
+    g = dget(dsa.dsa_topk(dput(host, dev), k, S, q_start=q_start))
+    pos = q_start + np.arange(T)
+    o = oracle.topk(scores, pos, k)
+    parity.check_topk_exact(g, o, name)
+    # ordering contract: keys above the k-th score first (ascending), then the ties (ascending)
+    for t in range(T):
+        v = g[t][g[t] >= 0]
+        if min(S, pos[t] + 1) <= k:      # every visible key: ascending index order
+            assert np.array_equal(v, np.arange(len(v)))
+            continue
+        sc = scores[t][v]
+        tau = sc.min()
+        gt = v[sc > tau]
+        eq = v[sc == tau]
+        assert np.array_equal(v, np.concatenate([np.sort(gt), np.sort(eq)]))
+
+
+def test_topk_random_rows(dev):
+    g = block_rng(31, 0, 0)
+    _topk_case(dev, g.standard_normal((300, 5000)).astype(np.float32), 4000, 2048, "normal")
+
+
+def test_topk_massive_ties(dev):
+    g = block_rng(32, 0, 0)
+    s = g.integers(0, 8, size=(64, 6000)).astype(np.float32)
+    s[:, ::7] = -0.0
+    _topk_case(dev, s, 5900, 2048, "ties")
+    _topk_case(dev, np.zeros((8, 3000), np.float32), 2990, 2048, "all-equal")
+    _topk_case(dev, s[:, :200], 0, 64, "short rows n_t < k")
+
+
+def test_topk_k1_and_negative(dev):
+    g = block_rng(33, 0, 0)
+    s = -np.abs(g.standard_normal((40, 999))).astype(np.float32)
+    _topk_case(dev, s, 998, 1, "k=1")
+    _topk_case(dev, s, 500, 300, "negative scores")
+
+
+def test_topk_long_rows_split(dev):
+    """Rows longer than one workgroup's chunk (split + merge path), including ties across chunks."""
+    g = block_rng(34, 0, 0)
+    S = 131072
+    s = g.standard_normal((6, S)).astype(np.float32)
+    s[1] = np.round(s[1] * 2)          # heavy ties straddling chunk borders
+    s[2, 100000:] += 5.0               # all winners in the last chunks
+    s[3] = 1.0                         # all equal
+    _topk_case(dev, s, S - 6, 2048, "long rows")
+    _topk_case(dev, s[:, :70001], 70000 - 5, 2048, "rows of 70001")
+
+
+def test_topk_heavy_tail(dev):
+    g = block_rng(35, 0, 0)
+    s = (g.standard_normal((16, 40000)) ** 3).astype(np.float32)
+    s[:, g.choice(40000, 400, replace=False)] *= 64.0
+    _topk_case(dev, s, 39990, 2048, "heavy tail")
+
+
+# ------------------------------------------------------------------------------------- MLA
+def _mla_case(dev, T, S, H, D_qk, D_v, k, idx, q_start, sm, name, seed=40):
+    import dsa_lightning_indexer_02_amd as dsa
+    print("case", name, flush=True)
+    g = block_rng(seed, 0, 0)
+    q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
+    out, f32, lse = dsa.dsa_sparse_mla_fwd(dput(q, dev).view(torch.bfloat16), dput(kv, dev).view(torch.bfloat16),
+                                           dput(idx.astype(np.int32), dev), sm, D_v, q_start=q_start, want_f32=True)
+    o, _, ol = oracle.sparse_mla(q, idx.astype(np.int32), q_start + np.arange(T), kv, D_v, sm)
+    parity.check_mla(bf16_vals(out), dget(f32), dget(lse), o, ol, name)
+    return dget(f32), dget(lse)
+
+
+def test_mla_invalid_duplicate_entries(dev):
+    g = block_rng(41, 0, 0)
+    T, S, k = 24, 3000, 2048
+    idx = g.integers(-5, S + 50, size=(T, k))
+    idx[:, 10:20] = idx[:, 0:10]          # duplicates
+    idx[5] = -1                           # nothing valid in row 5
+    idx[6, 1:] = -1                       # a single entry
+    _mla_case(dev, T, S, 128, 576, 512, k, idx, 2000, 1 / np.sqrt(192), "invalid/duplicate")
+
+
+def test_mla_small_dims_and_heads(dev):
+    g = block_rng(42, 0, 0)
+    T, S, k = 40, 256, 64
+    idx = np.stack([g.permutation(S)[:k] for _ in range(T)])
+    _mla_case(dev, T, S, 8, 80, 64, k, idx, 200, 1 / np.sqrt(80), "tiny dims")
+    _mla_case(dev, T, S, 100, 576, 512, k, idx, 200, 0.07, "H=100 (partial head tile)")
+
+
+def test_mla_k1_and_large_logits(dev):
+    g = block_rng(43, 0, 0)
+    T, S = 16, 500
+    idx1 = g.integers(0, S, size=(T, 1))
+    f32, lse = _mla_case(dev, T, S, 128, 576, 512, 1, idx1, S, 1 / np.sqrt(192), "k=1")
+    idx = np.stack([g.permutation(S)[:256] for _ in range(T)])
+    _mla_case(dev, T, S, 128, 576, 512, 256, idx, S, 2.0, "sharp softmax (rescale path)")
