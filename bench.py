@@ -1,0 +1,244 @@
+"""Throughput of the DSA hot path (lightning indexer -> top-2048 -> sparse MLA) on one MI355X.
+
+One step = one pass of the whole path over the L = 32768 causal prefill batch (the headline
+workload): dsa_indexer_logits, dsa_topk and dsa_sparse_mla_fwd back to back on one stream, with
+HIP events between the stages so every kernel's duration comes from the timed steps themselves.
+The fused entry point (dsa_prefill_paged, the same kernels behind one call) is timed beside it.
+Inputs are generated on the host from the seeded recipe, copied to HBM before timing, and stay
+resident; nothing is generated, quantized or copied inside the timed region.
+
+Prints one JSON line.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # dense bf16 / fp16 MFMA, MI355X published
+PEAK_FP8 = 5.0e15       # dense fp8 MFMA
+PEAK_HBM = 8.0e12       # HBM3E bytes/s
+PMC_FILE = os.path.join(ROOT, "profiles", "sparse_mla_prefill_32k_pmc.json")
+MLA_SOURCE = os.path.join(ROOT, "dsa_lightning_indexer_02_amd", "csrc", "sparse_mla.hip")
+
+
+def work_model(wl):
+    """Algorithmic work of one pass (masked pairs and skipped dense work excluded)."""
+    t = np.arange(wl.T, dtype=np.int64)
+    n = np.minimum(wl.S, wl.q_start + t + 1)
+    sel = np.minimum(n, wl.topk)
+    return {
+        "indexer_flop": float(2 * wl.H_I * wl.D_I * n.sum()),
+        "topk_bytes": float(4 * n.sum() + 4 * wl.T * wl.topk),
+        "mla_flop": float(2 * wl.H * (wl.D_qk + wl.D_v) * sel.sum()),
+        "visible_pairs": int(n.sum()),
+        "selected_rows": int(sel.sum()),
+    }
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per sparse-MLA launch from the committed rocprofv3 counter runs, if they were taken
+    on the current kernel source; None otherwise."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    with open(PMC_FILE) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != source_hash(MLA_SOURCE):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_rows: int, threads: int):
+    """The oracle (as it stands) on a uniform sample of query rows, scaled to the whole workload by the
+    exact per-stage work model."""
+    import oracle
+    from dsa_inputs import prefill_inputs
+    rows = np.unique(np.linspace(0, wl.T - 1, n_rows).round().astype(np.int64))
+    inp = prefill_inputs(wl, rows=rows)
+    pos = inp.pos
+    n = np.minimum(wl.S, pos + 1)
+    t0 = time.perf_counter()
+    lg = oracle.indexer(inp.q8, inp.qs, inp.w, pos, inp.k8, inp.ks, nthreads=threads)
+    t1 = time.perf_counter()
+    ix = oracle.topk(lg, pos, wl.topk, nthreads=threads)
+    t2 = time.perf_counter()
+    oracle.sparse_mla(inp.q, ix, pos, inp.kv, wl.D_v, wl.sm_scale, nthreads=threads)
+    t3 = time.perf_counter()
+    tn = np.arange(wl.T, dtype=np.int64)
+    n_all = np.minimum(wl.S, wl.q_start + tn + 1)
+    est = ((t1 - t0) * n_all.sum() / n.sum() + (t2 - t1) * n_all.sum() / n.sum()
+           + (t3 - t2) * np.minimum(n_all, wl.topk).sum() / np.minimum(n, wl.topk).sum())
+    return {
+        "value": wl.T / est, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+        "sample": "%d query rows evenly spaced over the %d-token prefill (full indexer, top-k and MLA per row), "
+                  "%.1f s measured, scaled per stage by visible / selected key counts" % (len(rows), wl.T, t3 - t0),
+        "sample_seconds": t3 - t0,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_32k")
+    ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-fused", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, copy 1 GiB device-to-device (counter scale reference)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import get, prefill_inputs
+
+    wl = get(args.workload)
+    if wl.kind != "prefill":
+        sys.exit("bench.py times prefill workloads")
+    dev = torch.device("cuda:0")
+    dsa.load()
+
+    def put(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    print("generating %s inputs" % wl.name, file=sys.stderr, flush=True)
+    inp = prefill_inputs(wl)
+    q8, qs, w, k8, ks = put(inp.q8), put(inp.qs), put(inp.w), put(inp.k8), put(inp.ks)
+    q = put(inp.q).view(torch.bfloat16)
+    kv = put(inp.kv).view(torch.bfloat16)
+    del inp
+    S, T = wl.S, wl.T
+    ld = dsa.ld_for(S)
+    logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, wl.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+    tk_ws = torch.empty(max(1, dsa.load().dsa_topk_workspace_size(T, S, wl.topk)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dsa.dsa_indexer_logits(q8, qs, w, k8, ks, wl.q_start, logits)
+        if ev:
+            ev[1].record(stream)
+        dsa.dsa_topk(logits, wl.topk, S, wl.q_start, idx, tk_ws)
+        if ev:
+            ev[2].record(stream)
+        dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v, wl.q_start, out=out, lse=lse)
+        if ev:
+            ev[3].record(stream)
+
+    print("warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print("timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]).mean(axis=0)
+
+    fused_ms = None
+    if not args.skip_fused:
+        nb = (S + 63) // 64
+        pad = nb * 64 - S
+        cache = dsa.PagedKV(
+            torch.cat([k8, torch.zeros((pad, wl.D_I), dtype=k8.dtype, device=dev)]).view(nb, 64, wl.D_I),
+            torch.cat([ks, torch.zeros((pad,), dtype=ks.dtype, device=dev)]).view(nb, 64),
+            torch.cat([kv, torch.zeros((pad, wl.D_qk), dtype=kv.dtype, device=dev)]).view(nb, 64, wl.D_qk),
+            torch.arange(nb, dtype=torch.int32, device=dev)[None])
+        dims = dsa.make_dims(wl.H_I, wl.D_I, wl.H, wl.D_qk, wl.D_v, wl.topk, wl.sm_scale)
+        ws = torch.empty(dsa.prefill_workspace_size(dims, T, wl.q_start + T), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            dsa.dsa_prefill_paged(cache, 0, dims, wl.q_start, q8, qs, w, q, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for _ in range(args.steps):
+            dsa.dsa_prefill_paged(cache, 0, dims, wl.q_start, q8, qs, w, q, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        fused_ms = (time.perf_counter() - f0) * 1e3 / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    wm = work_model(wl)
+    mla_s = stage_ms[2] / 1e3
+    roof = {
+        "kernel": "sparse_mla_kernel<576,512>",
+        "bound": "mfma",
+        "achieved": wm["mla_flop"] / mla_s / 1e12,
+        "peak": PEAK_BF16 / 1e12,
+        "unit": "TFLOP/s",
+        "frac": wm["mla_flop"] / mla_s / PEAK_BF16,
+        "traffic": traffic_from_profile(),
+        "avg_launch_ms": float(stage_ms[2]),
+        "algorithmic_flop_per_launch": wm["mla_flop"],
+    }
+    stages = {
+        "indexer": {"ms": float(stage_ms[0]), "bound": "mfma", "achieved_tflops": wm["indexer_flop"] / stage_ms[0] / 1e9,
+                    "frac": wm["indexer_flop"] / (stage_ms[0] / 1e3) / PEAK_FP8},
+        "topk": {"ms": float(stage_ms[1]), "bound": "hbm", "achieved_gbs": wm["topk_bytes"] / stage_ms[1] / 1e6,
+                 "frac": wm["topk_bytes"] / (stage_ms[1] / 1e3) / PEAK_HBM},
+        "sparse_mla": {"ms": float(stage_ms[2]), "bound": "mfma", "achieved_tflops": roof["achieved"],
+                       "frac": roof["frac"]},
+    }
+    cpu = None
+    if not args.skip_cpu_baseline:
+        print("cpu baseline (oracle)", file=sys.stderr, flush=True)
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cpu = cpu_baseline(wl, args.cpu_rows, threads)
+
+    res = {
+        "metric": "query tokens/s (indexer+top-2048+sparse MLA) at L=32K",
+        "value": T / (ms_step / 1e3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 indexer, bf16/fp16 attention",
+        "data": "synthetic (seeded PCG64 recipe, FP8 per-row absmax codes, bf16 N(0,1))",
+        "config": {"workload": wl.name, "T": T, "S": S, "q_start": wl.q_start, "H_I": wl.H_I, "D_I": wl.D_I,
+                   "topk": wl.topk, "H": wl.H, "D_qk": wl.D_qk, "D_v": wl.D_v, "parallelism": "single GPU"},
+        "roofline": roof,
+        "stages": stages,
+        "fused_ms_per_step": fused_ms,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

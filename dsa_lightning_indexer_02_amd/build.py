@@ -28,7 +28,7 @@ def sources():
 # LLVM's default heuristic every MFMA of the function takes the accumulation-register form and
 # the score tiles no longer fit beside them, so the VGPR form is requested and the compiler moves
 # the long-lived accumulators to accumulation registers itself.
-PER_SOURCE = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+PER_SOURCE = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"]}
 
 
 def _compile(src: str, extra=()) -> str:

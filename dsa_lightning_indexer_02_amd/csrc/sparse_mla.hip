@@ -23,30 +23,56 @@ constexpr int MLA_WAVES = 4;
 constexpr int MLA_THREADS = MLA_WAVES * WAVE;
 constexpr int MLA_KB = 32;             // selected rows per block
 constexpr int MLA_HEADS_PER_WAVE = 32;
-constexpr float MLA_TAU = 8.0f;        // lazy-rescale threshold, log2 units
+constexpr int MLA_STAGES = 3;          // gathered-row buffers in flight
+constexpr int MLA_MAX_K = 2048;        // index entries per workgroup (LDS row list)
+constexpr float MLA_HEADROOM = 15.0f;  // log2 headroom of fp16 probabilities above the reference
 
 template <int DQK, int DV>
 struct MlaCfg {
   static constexpr int DQK_PAD = (DQK + 31) / 32 * 32;
   static constexpr int NKS = DQK_PAD / 32;          // k-steps of the QK^T product
   static constexpr int NDT = DV / 16;               // 16-wide value tiles
-  static constexpr int K_STRIDE = DQK_PAD * 2 + 16; // bytes per gathered bf16 row
+  static constexpr int RC = DQK_PAD / 8;            // 16-byte chunks per gathered row
+  static constexpr int SWZ = RC % 8 == 0 ? 8 : (RC % 4 == 0 ? 4 : 1);  // XOR swizzle span (chunks)
+  static constexpr int SLOTS = MLA_KB * RC;         // 16-byte slots per stage
+  static constexpr int K_BYTES = SLOTS * 16;
+  static constexpr int DMA_INSTR = SLOTS / WAVE;    // wave-wide 1 KiB transfers per block
+  static constexpr bool DMA_UNIFORM = DMA_INSTR % MLA_WAVES == 0;
+  static constexpr int DMA_PER_WAVE = DMA_INSTR / MLA_WAVES;
   static constexpr int VT_STRIDE = MLA_KB * 2 + 8;  // bytes per fp16 value column
-  static constexpr int K_BYTES = MLA_KB * K_STRIDE;
   static constexpr int VT_BYTES = DV * VT_STRIDE;
-  static constexpr int NCH = DV / 8;                // 16-byte chunks of the value part
-  static constexpr int MAIN_ITEMS = NCH * (MLA_KB / 4);
-  static constexpr int MAIN_PER_THREAD = (MAIN_ITEMS + MLA_THREADS - 1) / MLA_THREADS;
-  static constexpr int NR = (DQK - DV) / 8;         // 16-byte chunks of the rope part
-  static constexpr int ROPE_ITEMS = NR * MLA_KB;
-  static constexpr int ROPE_PER_THREAD = (ROPE_ITEMS + MLA_THREADS - 1) / MLA_THREADS;
+  static constexpr int CONV_ITEMS = (DV / 8) * (MLA_KB / 4);  // (16-byte column chunk, 4-key group)
+  static constexpr int CONV_PER_THREAD = (CONV_ITEMS + MLA_THREADS - 1) / MLA_THREADS;
   static_assert(DQK % 8 == 0 && DV % 16 == 0 && DV <= DQK, "unsupported MLA dims");
+  static_assert(SLOTS % WAVE == 0, "gather slots must fill whole waves");
+  // 16-byte slot of chunk c of gathered row r: rows are contiguous, chunks XOR-swizzled within
+  // aligned groups of SWZ so that 8 consecutive rows at one chunk hit 8 distinct bank groups.
+  static __device__ __forceinline__ int slot(int r, int c) { return r * RC + (c ^ (r & (SWZ - 1))); }
 };
 
 template <int DQK, int DV>
 size_t mla_smem_bytes(int32_t keys_per_wg) {
   using C = MlaCfg<DQK, DV>;
-  return (size_t)C::K_BYTES + C::VT_BYTES + (size_t)keys_per_wg * sizeof(int32_t);
+  (void)keys_per_wg;
+  return (size_t)MLA_STAGES * C::K_BYTES + C::VT_BYTES + (size_t)(MLA_MAX_K + 4) * sizeof(int32_t);
+}
+
+// One wave-wide global -> LDS transfer: lane l's 16 bytes at gaddr land at lds_base + 16 l.
+// Issued as inline assembly so that the compiler does not serialise later LDS reads behind it;
+// completion is awaited explicitly (vmcnt) before the barrier that publishes the data.
+__device__ __forceinline__ void dma_16B(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gaddr) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 template <int DQK, int DV>
@@ -59,11 +85,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     float* __restrict__ part_lse) {
   using C = MlaCfg<DQK, DV>;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* Kl = smem;                                           // [32][K_STRIDE] bf16
-  uint8_t* Vt = smem + C::K_BYTES;                              // [DV][VT_STRIDE] fp16
-  int32_t* phys = reinterpret_cast<int32_t*>(smem + C::K_BYTES + C::VT_BYTES);
+  uint8_t* Kbuf = smem;                                                  // [STAGES][SLOTS] x 16 B
+  uint8_t* Vt = smem + MLA_STAGES * C::K_BYTES;                          // [DV][VT_STRIDE] fp16
+  int32_t* phys = reinterpret_cast<int32_t*>(Vt + C::VT_BYTES);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int j16 = lane & 15, g = lane >> 4;
   const int64_t r = blockIdx.y;
   const int sp = blockIdx.x;
@@ -92,14 +119,15 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     const int32_t li = idx[r * k + i0 + i];
     phys[i] = (li >= 0 && li < n) ? (int32_t)map(li) : -1;
   }
-  // skipped entries are gathered from a row that certainly holds finite data (the sequence's
-  // first key) and masked out of the softmax, so no load needs a branch
+  // Skipped entries are gathered from a row that certainly holds finite data (the sequence's
+  // first key) and masked out of the softmax.
   const int32_t safe_row = (int32_t)map(0);
-  // zero the K padding columns once; they are never overwritten
+  // zero the padding chunks of every stage once; the gather never writes them
   if (C::DQK_PAD > DQK) {
-    for (int p = tid; p < MLA_KB * (C::DQK_PAD - DQK) / 8; p += MLA_THREADS) {
-      const int row = p / ((C::DQK_PAD - DQK) / 8), c = p % ((C::DQK_PAD - DQK) / 8);
-      *reinterpret_cast<v4i*>(Kl + row * C::K_STRIDE + (DQK + 8 * c) * 2) = (v4i){0, 0, 0, 0};
+    for (int p = tid; p < MLA_STAGES * MLA_KB * C::RC; p += MLA_THREADS) {
+      const int st = p / (MLA_KB * C::RC), rr = (p / C::RC) % MLA_KB, c = p % C::RC;
+      if (c * 8 >= DQK)
+        *reinterpret_cast<v4i*>(Kbuf + st * C::K_BYTES + C::slot(rr, c) * 16) = (v4i){0, 0, 0, 0};
     }
   }
 
@@ -115,157 +143,158 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       const bool ok = h < H && col < DQK;
       s16x8 v = *reinterpret_cast<const s16x8*>(q + (r * H + (ok ? h : 0)) * (int64_t)DQK + (ok ? col : 0));
       if (!ok) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      asm volatile("" : "+v"(v));  // keep the queries resident: no re-load from memory per block
       Qf[ht][ks] = v;
     }
   }
   __syncthreads();
 
+  const uint32_t kbuf_lds = lds_addr(Kbuf);
+  auto gather = [&](int blk) {
+    const uint32_t base = kbuf_lds + (uint32_t)((blk % MLA_STAGES) * C::K_BYTES);
+    for (int i = wave; i < C::DMA_INSTR; i += MLA_WAVES) {
+      const int s = i * WAVE + lane;
+      const int rr = s / C::RC;
+      const int c = (s % C::RC) ^ (rr & (C::SWZ - 1));
+      const int e = blk * MLA_KB + rr;
+      const int32_t pr = e < cnt ? phys[e] : -1;
+      const uint16_t* src = kv + (int64_t)(pr >= 0 ? pr : safe_row) * DQK + c * 8;
+      if (C::DQK_PAD == DQK || c * 8 < DQK) dma_16B(src, base + (uint32_t)(i * WAVE * 16));
+    }
+  };
+
   v4f O[C::NDT][2];
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) O[dt][0] = O[dt][1] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float mref[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-
-  v4i mreg[C::MAIN_PER_THREAD][4];
-  v4i rreg[C::ROPE_PER_THREAD];
-  auto stage_load = [&](int blk) {
-#pragma unroll
-    for (int it = 0; it < C::MAIN_PER_THREAD; ++it) {
-      const int p = tid + it * MLA_THREADS;
-      const int c8 = p % C::NCH, kg = p / C::NCH;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int e = blk * MLA_KB + kg * 4 + kk;
-        const int32_t pr = (p < C::MAIN_ITEMS && e < cnt) ? phys[e] : -1;
-        mreg[it][kk] = *reinterpret_cast<const v4i*>(kv + (int64_t)(pr >= 0 ? pr : safe_row) * DQK + c8 * 8);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < C::ROPE_PER_THREAD; ++it) {
-      const int p = tid + it * MLA_THREADS;
-      const int row = p / (C::NR > 0 ? C::NR : 1), c = p % (C::NR > 0 ? C::NR : 1);
-      const int e = blk * MLA_KB + row;
-      const int32_t pr = (p < C::ROPE_ITEMS && e < cnt) ? phys[e] : -1;
-      rreg[it] = *reinterpret_cast<const v4i*>(kv + (int64_t)(pr >= 0 ? pr : safe_row) * DQK + DV + c * 8);
-    }
-  };
-  auto stage_store = [&]() {
-#pragma unroll
-    for (int it = 0; it < C::MAIN_PER_THREAD; ++it) {
-      const int p = tid + it * MLA_THREADS;
-      if (p < C::MAIN_ITEMS) {
-        const int c8 = p % C::NCH, kg = p / C::NCH;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          *reinterpret_cast<v4i*>(Kl + (kg * 4 + kk) * C::K_STRIDE + c8 * 16) = mreg[it][kk];
-        // transpose 4 keys x 8 columns into fp16 V^T
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          s16x4 col;
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const uint32_t word = (uint32_t)mreg[it][kk][i >> 1];
-            const uint16_t b = (i & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
-            const _Float16 hv = (_Float16)bf16_to_f32(b);
-            col[kk] = __builtin_bit_cast(short, hv);
-          }
-          *reinterpret_cast<s16x4*>(Vt + (c8 * 8 + i) * C::VT_STRIDE + kg * 8) = col;
-        }
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < C::ROPE_PER_THREAD; ++it) {
-      const int p = tid + it * MLA_THREADS;
-      if (p < C::ROPE_ITEMS) {
-        const int row = p / (C::NR > 0 ? C::NR : 1), c = p % (C::NR > 0 ? C::NR : 1);
-        *reinterpret_cast<v4i*>(Kl + row * C::K_STRIDE + (DV + c * 8) * 2) = rreg[it];
-      }
-    }
-  };
-
+  // Softmax reference: fixed at the first block holding a valid entry (per head).  Later blocks
+  // may exceed it by up to 2^15 in probability, which fp16 still holds, so the accumulators are
+  // never rescaled.  If any head goes further, the workgroup runs the token again with the now
+  // known exact maximum as the reference (probabilities <= 1); the accumulators are only ever
+  // zeroed, accumulated by MFMA and read once at the end.
+  float mref[2], mtrue[2] = {-INFINITY, -INFINITY};
+  float lsum[2];
   const int nblk = (cnt + MLA_KB - 1) / MLA_KB;
-  if (nblk > 0) stage_load(0);
-  for (int blk = 0; blk < nblk; ++blk) {
-    __syncthreads();
-    stage_store();
-    __syncthreads();
-    if (blk + 1 < nblk) stage_load(blk + 1);
-    if (!active) continue;
+  int32_t* overflow_flag = phys + MLA_MAX_K;  // one int after the row list
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) O[dt][0] = O[dt][1] = (v4f){0.f, 0.f, 0.f, 0.f};
+    lsum[0] = lsum[1] = 0.f;
+    mref[0] = pass ? mtrue[0] : -INFINITY;
+    mref[1] = pass ? mtrue[1] : -INFINITY;
+    bool overflow = false;
 
-    // ---- S^T[key][head] for 2 key tiles x 2 head tiles
-    v4f s[2][2];
+    if (nblk > 0) gather(0);
+    if (nblk > 1) gather(1);
+    for (int blk = 0; blk < nblk; ++blk) {
+      const uint8_t* Kst = Kbuf + (blk % MLA_STAGES) * C::K_BYTES;
+      // this wave's transfers of block blk are done once at most those of blk + 1 are pending
+      if (C::DMA_UNIFORM && blk + 1 < nblk)
+        wait_vmcnt<C::DMA_PER_WAVE>();
+      else
+        wait_vmcnt<0>();
+      __syncthreads();
+      if (blk + 2 < nblk) gather(blk + 2);
+
+      // ---- fp16 V^T of this block (read from the gathered rows)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) s[c][0] = s[c][1] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int it = 0; it < C::CONV_PER_THREAD; ++it) {
+        const int p = tid + it * MLA_THREADS;
+        if (C::CONV_ITEMS % MLA_THREADS == 0 || p < C::CONV_ITEMS) {
+          const int kg = p % (MLA_KB / 4), c8 = p / (MLA_KB / 4);
+          v4i rows[4];
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
+          for (int kk = 0; kk < 4; ++kk) rows[kk] = *reinterpret_cast<const v4i*>(Kst + C::slot(kg * 4 + kk, c8) * 16);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const s16x8 A = *reinterpret_cast<const s16x8*>(Kl + (c * 16 + j16) * C::K_STRIDE + (ks * 32 + g * 8) * 2);
-        s[c][0] = mfma_bf16_16x16x32(A, Qf[0][ks], s[c][0]);
-        s[c][1] = mfma_bf16_16x16x32(A, Qf[1][ks], s[c][1]);
-      }
-    }
-    // ---- mask, scale, block maximum per head
-    float x[2][2][4];
-    float mb[2] = {-INFINITY, -INFINITY};
+          for (int i = 0; i < 8; ++i) {
+            s16x4 col;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int e = blk * MLA_KB + c * 16 + 4 * g + rr;
-        const bool valid = e < cnt && phys[e] >= 0;
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
-          const float v = valid ? s[c][ht][rr] * scale_log2 : -INFINITY;
-          x[c][ht][rr] = v;
-          mb[ht] = fmaxf(mb[ht], v);
+            for (int kk = 0; kk < 4; ++kk) {
+              const uint32_t word = (uint32_t)rows[kk][i >> 1];
+              const uint16_t bb = (i & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+              col[kk] = __builtin_bit_cast(short, (_Float16)bf16_to_f32(bb));
+            }
+            *reinterpret_cast<s16x4*>(Vt + (c8 * 8 + i) * C::VT_STRIDE + kg * 8) = col;
+          }
         }
       }
+
+      // ---- S^T[key][head] for 2 key tiles x 2 head tiles
+      v4f sc[2][2];
+      if (active) {
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      mb[ht] = fmaxf(mb[ht], __shfl_xor(mb[ht], 16));
-      mb[ht] = fmaxf(mb[ht], __shfl_xor(mb[ht], 32));
-    }
-    const bool need0 = mb[0] > mref[0] + MLA_TAU, need1 = mb[1] > mref[1] + MLA_TAU;
-    if (__any(need0 || need1)) {
-      float f[2];
-      f[0] = need0 ? exp2f(mref[0] - mb[0]) : 1.0f;
-      f[1] = need1 ? exp2f(mref[1] - mb[1]) : 1.0f;
-      if (need0) mref[0] = mb[0];
-      if (need1) mref[1] = mb[1];
+        for (int c = 0; c < 2; ++c) sc[c][0] = sc[c][1] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
+        for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) O[dt][ht] *= f[ht];
-      lsum[0] *= f[0];
-      lsum[1] *= f[1];
-    }
-    // ---- probabilities (fp16) packed as the B operand of out^T = V^T P^T
-    s16x8 Bp[2];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
+          for (int c = 0; c < 2; ++c) {
+            const s16x8 A = *reinterpret_cast<const s16x8*>(Kst + C::slot(c * 16 + j16, ks * 4 + g) * 16);
+            sc[c][0] = mfma_bf16_16x16x32(A, Qf[0][ks], sc[c][0]);
+            sc[c][1] = mfma_bf16_16x16x32(A, Qf[1][ks], sc[c][1]);
+          }
+        }
+      }
+      __syncthreads();  // V^T complete
+      if (!active) continue;
+
+      // ---- mask, scale, block maximum per head
+      float mb[2] = {-INFINITY, -INFINITY};
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float xv = x[c][ht][rr];
-          const float p = xv == -INFINITY ? 0.0f : exp2f(xv - mref[ht]);
-          const _Float16 ph = (_Float16)p;
-          lsum[ht] += (float)ph;
-          Bp[ht][c * 4 + rr] = __builtin_bit_cast(short, ph);
-        }
-    }
-    // ---- out^T[d][head] += V^T[d][key] P^T[key][head]
+          const int e = blk * MLA_KB + c * 16 + 4 * g + rr;
+          const bool valid = e < cnt && phys[e] >= 0;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-      const uint8_t* vrow = Vt + (dt * 16 + j16) * C::VT_STRIDE;
-      const s16x4 lo = *reinterpret_cast<const s16x4*>(vrow + g * 8);
-      const s16x4 hi = *reinterpret_cast<const s16x4*>(vrow + 32 + g * 8);
-      const s16x8 A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      O[dt][0] = mfma_f16_16x16x32(A, Bp[0], O[dt][0]);
-      O[dt][1] = mfma_f16_16x16x32(A, Bp[1], O[dt][1]);
+          for (int ht = 0; ht < 2; ++ht) {
+            const float v = valid ? sc[c][ht][rr] * scale_log2 : -INFINITY;
+            sc[c][ht][rr] = v;
+            mb[ht] = fmaxf(mb[ht], v);
+          }
+        }
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        mb[ht] = fmaxf(mb[ht], __shfl_xor(mb[ht], 16));
+        mb[ht] = fmaxf(mb[ht], __shfl_xor(mb[ht], 32));
+        mtrue[ht] = fmaxf(mtrue[ht], mb[ht]);
+        if (mref[ht] == -INFINITY) mref[ht] = mb[ht];
+        overflow |= mb[ht] > mref[ht] + MLA_HEADROOM;
+      }
+      // ---- probabilities (fp16) packed as the B operand of out^T = V^T P^T
+      s16x8 Bp[2];
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float xv = sc[c][ht][rr];
+            // (an overflowing pass is discarded; the clamp only keeps it finite)
+            const float p = xv == -INFINITY ? 0.0f : fminf(exp2f(xv - mref[ht]), 65504.0f);
+            const _Float16 ph = (_Float16)p;
+            lsum[ht] += (float)ph;
+            Bp[ht][c * 4 + rr] = __builtin_bit_cast(short, ph);
+          }
+      }
+      // ---- out^T[d][head] += V^T[d][key] P^T[key][head]
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const uint8_t* vrow = Vt + (dt * 16 + j16) * C::VT_STRIDE;
+        const s16x4 lo = *reinterpret_cast<const s16x4*>(vrow + g * 8);
+        const s16x4 hi = *reinterpret_cast<const s16x4*>(vrow + 32 + g * 8);
+        const s16x8 A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        O[dt][0] = mfma_f16_16x16x32(A, Bp[0], O[dt][0]);
+        O[dt][1] = mfma_f16_16x16x32(A, Bp[1], O[dt][1]);
+      }
+    }
+    // does any wave need the exact-maximum pass?
+    if (pass == 0) {
+      if (tid == 0) *overflow_flag = 0;
+      __syncthreads();
+      if (active && __any(overflow)) *overflow_flag = 1;
+      __syncthreads();
+      if (*overflow_flag == 0) break;
+      __syncthreads();
     }
   }
+  wait_vmcnt<0>();
   if (!active) return;
 
   // ---- normalise and store
@@ -360,7 +389,7 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
 
 bool mla_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k) {
   const bool dims = (D_qk == 576 && D_v == 512) || (D_qk == 80 && D_v == 64);
-  return dims && H >= 1 && H <= MLA_WAVES * MLA_HEADS_PER_WAVE && k >= 1 && k <= 8192;
+  return dims && H >= 1 && H <= MLA_WAVES * MLA_HEADS_PER_WAVE && k >= 1 && k <= MLA_MAX_K;
 }
 
 size_t mla_smem_for(int32_t D_qk, int32_t D_v, int32_t keys_per_wg) {

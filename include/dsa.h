@@ -90,7 +90,7 @@ dsa_status_t dsa_topk(const float *logits, int64_t ld_logits, int64_t T, int64_t
  *   indices [T][k] i32, out [T][H][D_v] bf16, out_f32 [T][H][D_v] f32 (optional, NULL to skip),
  *   lse [T][H] f32 (optional).  Probabilities are rounded to fp16 for the P.V product and V is
  *   converted bf16 -> fp16, exact for |v| in [2^-14, 65504] (precondition |v| <= 65504).
- *   Supported: (D_qk, D_v) in {(576, 512), (80, 64)}, 1 <= H <= 128, 1 <= k <= 8192.
+ *   Supported: (D_qk, D_v) in {(576, 512), (80, 64)}, 1 <= H <= 128, 1 <= k <= 2048.
  *   The workspace is unused (size 0) and may be NULL.
  */
 size_t dsa_sparse_mla_workspace_size(int64_t T, int32_t H, int32_t D_v, int32_t k);
