@@ -54,7 +54,7 @@ template <int DQK, int DV>
 size_t mla_smem_bytes(int32_t keys_per_wg) {
   using C = MlaCfg<DQK, DV>;
   (void)keys_per_wg;
-  return (size_t)MLA_STAGES * C::K_BYTES + C::VT_BYTES + (size_t)(MLA_MAX_K + 4) * sizeof(int32_t);
+  return (size_t)MLA_STAGES * C::K_BYTES + C::VT_BYTES + (size_t)(MLA_MAX_K + 4 + MLA_MAX_K / MLA_KB) * sizeof(int32_t);
 }
 
 // One wave-wide global -> LDS transfer: lane l's 16 bytes at gaddr land at lds_base + 16 l.
@@ -119,6 +119,21 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     const int32_t li = idx[r * k + i0 + i];
     phys[i] = (li >= 0 && li < n) ? (int32_t)map(li) : -1;
   }
+  // validity bit mask of every 32-entry block (bit i: entry 32 b + i is gathered and attended)
+  uint32_t* vmask_lds = reinterpret_cast<uint32_t*>(phys + MLA_MAX_K + 4);
+  for (int base = wave * WAVE; base < (cnt + 63) / 64 * 64; base += MLA_WAVES * WAVE) {
+    const int i = base + lane;
+    bool v = false;
+    if (i < cnt) {
+      const int32_t li = idx[r * k + i0 + i];
+      v = li >= 0 && li < n;
+    }
+    const uint64_t bits = __ballot(v);
+    if (lane == 0) {
+      vmask_lds[base / 32] = (uint32_t)bits;
+      if (base + 32 < cnt) vmask_lds[base / 32 + 1] = (uint32_t)(bits >> 32);
+    }
+  }
   // Skipped entries are gathered from a row that certainly holds finite data (the sequence's
   // first key) and masked out of the softmax.
   const int32_t safe_row = (int32_t)map(0);
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   // never rescaled.  If any head goes further, the workgroup runs the token again with the now
   // known exact maximum as the reference (probabilities <= 1); the accumulators are only ever
   // zeroed, accumulated by MFMA and read once at the end.
-  float mref[2], mtrue[2] = {-INFINITY, -INFINITY};
+  float mref[2], mlane[2] = {-INFINITY, -INFINITY};  // mlane: this lane's running maximum
   float lsum[2];
   const int nblk = (cnt + MLA_KB - 1) / MLA_KB;
   int32_t* overflow_flag = phys + MLA_MAX_K;  // one int after the row list
@@ -177,8 +192,18 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) O[dt][0] = O[dt][1] = (v4f){0.f, 0.f, 0.f, 0.f};
     lsum[0] = lsum[1] = 0.f;
-    mref[0] = pass ? mtrue[0] : -INFINITY;
-    mref[1] = pass ? mtrue[1] : -INFINITY;
+    if (pass) {  // exact row maximum of pass 0, reduced over the lanes holding each head
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        float m = mlane[ht];
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        mref[ht] = m;
+      }
+    } else {
+      mref[0] = mref[1] = INFINITY;  // unset: every probability is exp2(-inf) = 0 until a valid entry
+    }
+    bool have_ref = pass != 0;  // wave-uniform: every head of a wave gets its reference together
     bool overflow = false;
 
     if (nblk > 0) gather(0);
@@ -216,72 +241,102 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         }
       }
 
-      // ---- S^T[key][head] for 2 key tiles x 2 head tiles
+      // ---- S^T[key][head] for 2 key tiles x 2 head tiles; the K fragments of step ks + 1 are
+      // requested before the MFMAs of step ks so that LDS latency hides behind them
       v4f sc[2][2];
       if (active) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) sc[c][0] = sc[c][1] = (v4f){0.f, 0.f, 0.f, 0.f};
+        s16x8 Acur[2], Anext[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          Acur[c] = *reinterpret_cast<const s16x8*>(Kst + C::slot(c * 16 + j16, g) * 16);
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
+          if (ks + 1 < C::NKS) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              Anext[c] = *reinterpret_cast<const s16x8*>(Kst + C::slot(c * 16 + j16, (ks + 1) * 4 + g) * 16);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+          }
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const s16x8 A = *reinterpret_cast<const s16x8*>(Kst + C::slot(c * 16 + j16, ks * 4 + g) * 16);
-            sc[c][0] = mfma_bf16_16x16x32(A, Qf[0][ks], sc[c][0]);
-            sc[c][1] = mfma_bf16_16x16x32(A, Qf[1][ks], sc[c][1]);
+            sc[c][0] = mfma_bf16_16x16x32(Acur[c], Qf[0][ks], sc[c][0]);
+            sc[c][1] = mfma_bf16_16x16x32(Acur[c], Qf[1][ks], sc[c][1]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // 4 MFMA
+          if (ks + 1 < C::NKS) {
+            Acur[0] = Anext[0];
+            Acur[1] = Anext[1];
           }
         }
       }
       __syncthreads();  // V^T complete
       if (!active) continue;
 
-      // ---- mask, scale, block maximum per head
-      float mb[2] = {-INFINITY, -INFINITY};
+      // ---- scaled logits (log2 units), masked entries at -inf
+      const uint32_t vm = vmask_lds[blk];
+      const uint32_t vbits = ((vm >> (4 * g)) & 0xFu) | (((vm >> (16 + 4 * g)) & 0xFu) << 4);  // bit 4c + rr
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int e = blk * MLA_KB + c * 16 + 4 * g + rr;
-          const bool valid = e < cnt && phys[e] >= 0;
+          const bool valid = (vbits >> (c * 4 + rr)) & 1u;
 #pragma unroll
           for (int ht = 0; ht < 2; ++ht) {
             const float v = valid ? sc[c][ht][rr] * scale_log2 : -INFINITY;
             sc[c][ht][rr] = v;
-            mb[ht] = fmaxf(mb[ht], v);
+            mlane[ht] = fmaxf(mlane[ht], v);
           }
         }
+      if (!have_ref && vm != 0u) {  // wave-uniform: the block mask is shared by all lanes
+        // first block with a valid entry: its maximum becomes the reference
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        mb[ht] = fmaxf(mb[ht], __shfl_xor(mb[ht], 16));
-        mb[ht] = fmaxf(mb[ht], __shfl_xor(mb[ht], 32));
-        mtrue[ht] = fmaxf(mtrue[ht], mb[ht]);
-        if (mref[ht] == -INFINITY) mref[ht] = mb[ht];
-        overflow |= mb[ht] > mref[ht] + MLA_HEADROOM;
+        for (int ht = 0; ht < 2; ++ht) {
+          float m = mlane[ht];
+          m = fmaxf(m, __shfl_xor(m, 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          mref[ht] = m;
+        }
+        have_ref = true;
       }
       // ---- probabilities (fp16) packed as the B operand of out^T = V^T P^T
       s16x8 Bp[2];
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
+        overflow |= mlane[ht] > mref[ht] + MLA_HEADROOM;
+        float pr[8];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const float xv = sc[c][ht][rr];
-            // (an overflowing pass is discarded; the clamp only keeps it finite)
-            const float p = xv == -INFINITY ? 0.0f : fminf(exp2f(xv - mref[ht]), 65504.0f);
-            const _Float16 ph = (_Float16)p;
-            lsum[ht] += (float)ph;
-            Bp[ht][c * 4 + rr] = __builtin_bit_cast(short, ph);
+            const float p = __builtin_amdgcn_exp2f(sc[c][ht][rr] - mref[ht]);  // exp2(-inf) = 0
+            pr[c * 4 + rr] = p;
+            lsum[ht] += p;
           }
-      }
-      // ---- out^T[d][head] += V^T[d][key] P^T[key][head]
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
+        for (int i = 0; i < 8; ++i) Bp[ht][i] = __builtin_bit_cast(short, (_Float16)pr[i]);
+      }
+      // ---- out^T[d][head] += V^T[d][key] P^T[key][head], value fragments requested one tile ahead
+      auto vfrag = [&](int dt) {
         const uint8_t* vrow = Vt + (dt * 16 + j16) * C::VT_STRIDE;
         const s16x4 lo = *reinterpret_cast<const s16x4*>(vrow + g * 8);
         const s16x4 hi = *reinterpret_cast<const s16x4*>(vrow + 32 + g * 8);
-        const s16x8 A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        O[dt][0] = mfma_f16_16x16x32(A, Bp[0], O[dt][0]);
-        O[dt][1] = mfma_f16_16x16x32(A, Bp[1], O[dt][1]);
+        return (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      constexpr int VLA = 2;  // value fragments in flight
+      s16x8 Vf[VLA];
+#pragma unroll
+      for (int i = 0; i < VLA - 1; ++i) Vf[i] = vfrag(i);
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        if (dt + VLA - 1 < C::NDT) {
+          Vf[(dt + VLA - 1) % VLA] = vfrag(dt + VLA - 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read (one ds_read2)
+        }
+        O[dt][0] = mfma_f16_16x16x32(Vf[dt % VLA], Bp[0], O[dt][0]);
+        O[dt][1] = mfma_f16_16x16x32(Vf[dt % VLA], Bp[1], O[dt][1]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);    // 2 MFMA
       }
     }
     // does any wave need the exact-maximum pass?
