@@ -4,9 +4,9 @@ This module holds no arithmetic of the method itself.  It draws random
 numbers and encodes them into the input formats the method consumes:
 
 * FP8 E4M3 (OCP "fn" variant: max 448, no infinities) codes with one fp32
-  scale per row of the last dimension ("cast along last dim to FP8 E4M3" in
-  the lightning-indexer gist listing; FP8 indexer per the DeepSeek-V3.2-Exp
-  summary page, section "Method").  The encoding is torch's own
+  scale per row of the last dimension (the indexer listing on the createthis
+  gist page quantizes its inputs along the last dimension; the indexer runs in
+  FP8 per the DeepSeek-V3.2-Exp summary page, section "Method").  The encoding is torch's own
   ``float8_e4m3fn`` cast (round to nearest even) after clamping to +-448.
 * bf16 bit patterns (round to nearest even, torch's cast).
 

@@ -7,13 +7,14 @@
  *
  * Sources (web pages; section named for each function):
  *  - DeepSeek-V3.2-Exp summary page, section "Method": the index score
- *    I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j] . k_I[s]) against all prior tokens,
- *    H_I heads, FP8; top-k = 2048; MLA in MQA mode, the latent KV row shared by
- *    all query heads of a token.
+ *    I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j] . k_I[s]) over every earlier key,
+ *    H_I heads, FP8; top-k = 2048; MLA in MQA mode, one latent KV row serving
+ *    every query head of its token.
  *  - AMD "MI355X GPUs Power DeepSeek-V3.2-Exp" article, section "DeepSeek
- *    Sparse Attention (DSA)": the indexer scores all preceding tokens; the top
- *    2048 key-value pairs per query go to the main attention.
- *  - gist listing of the indexer kernel: FP8 E4M3 cast along the last dim.
+ *    Sparse Attention (DSA)": the indexer scores the keys before the query;
+ *    2048 keys per query are kept for the main attention.
+ *  - createthis gist page, indexer listing: FP8 E4M3 inputs quantized along the
+ *    last dimension.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - the query's own position is visible: n_t = min(S, pos_t + 1);

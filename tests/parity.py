@@ -1,4 +1,4 @@
-"""Comparison rules between the HIP path and the oracle (tolerances from the spec bar).
+"""Comparison rules between the HIP path and the oracle (the project's parity tolerances).
 
 Indexer: (i) |g - o| <= 1e-3 * A everywhere in the causal range, A = sum_j |w| qs ks sum_i |dec q8 * dec k8|
          (the magnitude scale of the sum, A >= |o|); (ii) |g - o| / |o| <= 1e-3 where the relative error is

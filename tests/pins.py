@@ -251,7 +251,7 @@ def check_mla_special_cases(lib):
 
 # ---------------------------------------------------------------- end to end
 def check_dense_when_k_covers(lib, rows=(0, 1, 5, 1000, 2047)):
-    """spec invariant: when k >= n_t, sparse attention equals dense causal MLA."""
+    """Invariant: when k >= n_t, sparse attention equals dense causal MLA."""
     wl = get("prefill_4k")
     inp = prefill_inputs(wl, rows=rows)
     logits, idx, out, _, lse = oracle.prefill(inp, lib=lib)
