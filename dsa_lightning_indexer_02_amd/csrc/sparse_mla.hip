@@ -19,10 +19,11 @@
 
 namespace dsa {
 
-constexpr int MLA_WAVES = 4;
+constexpr int MLA_WAVES = 8;
 constexpr int MLA_THREADS = MLA_WAVES * WAVE;
 constexpr int MLA_KB = 32;             // selected rows per block
-constexpr int MLA_HEADS_PER_WAVE = 32;
+constexpr int MLA_HEADS_PER_WAVE = 16;
+constexpr int MLA_HT = MLA_HEADS_PER_WAVE / 16;  // 16-head MFMA tiles per wave
 constexpr int MLA_STAGES = 3;          // gathered-row buffers in flight
 constexpr int MLA_MAX_K = 2048;        // index entries per workgroup (LDS row list)
 constexpr float MLA_HEADROOM = 15.0f;  // log2 headroom of fp16 probabilities above the reference
@@ -37,8 +38,7 @@ struct MlaCfg {
   static constexpr int SLOTS = MLA_KB * RC;         // 16-byte slots per stage
   static constexpr int K_BYTES = SLOTS * 16;
   static constexpr int DMA_INSTR = SLOTS / WAVE;    // wave-wide 1 KiB transfers per block
-  static constexpr bool DMA_UNIFORM = DMA_INSTR % MLA_WAVES == 0;
-  static constexpr int DMA_PER_WAVE = DMA_INSTR / MLA_WAVES;
+  static constexpr int DMA_MAX_PER_WAVE = (DMA_INSTR + MLA_WAVES - 1) / MLA_WAVES;
   static constexpr int VT_STRIDE = MLA_KB * 2 + 8;  // bytes per fp16 value column
   static constexpr int VT_BYTES = DV * VT_STRIDE;
   static constexpr int CONV_ITEMS = (DV / 8) * (MLA_KB / 4);  // (16-byte column chunk, 4-key group)
@@ -73,6 +73,22 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most n of this wave's vector-memory operations are pending (n wave-uniform, small).
+__device__ __forceinline__ void wait_vmcnt_pending(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    default: wait_vmcnt<9>(); break;
+  }
 }
 
 template <int DQK, int DV>
@@ -148,9 +164,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 
   // queries of this wave's 32 heads, as B operands of S^T = K Q^T
   const bool active = wave * MLA_HEADS_PER_WAVE < H;
-  s16x8 Qf[2][C::NKS];
+  s16x8 Qf[MLA_HT][C::NKS];
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
+  for (int ht = 0; ht < MLA_HT; ++ht) {
     const int h = wave * MLA_HEADS_PER_WAVE + ht * 16 + j16;
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
@@ -165,6 +181,20 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   __syncthreads();
 
   const uint32_t kbuf_lds = lds_addr(Kbuf);
+  const int my_dma = (C::DMA_INSTR - wave + MLA_WAVES - 1) / MLA_WAVES;  // this wave's transfers per block
+  // Byte offset in a stage of the K fragment (step ks, key tile c) this lane reads: chunk 4 ks + g
+  // of row 16 c + j16.  The swizzle XORs the low log2(SWZ) chunk bits with the row, so the offset is
+  // one of two per-lane bases (by the parity of ks when SWZ is 8) plus a compile-time constant, and
+  // no per-step address has to stay live.
+  static_assert(C::SWZ == 8 || C::SWZ == 4 || C::SWZ == 1, "swizzle span");
+  const int xr = j16 & (C::SWZ - 1);
+  const int abase0 = (j16 * C::RC + (g ^ xr)) * 16;            // even ks (and every ks when SWZ <= 4)
+  const int abase1 = (j16 * C::RC + ((4 + g) ^ xr)) * 16;      // odd ks when SWZ == 8
+  auto afrag_off = [&](int ks, int c) -> int {
+    if (C::SWZ == 8)
+      return ((ks & 1) ? abase1 : abase0) + (ks >> 1) * 128 + c * 16 * C::RC * 16;
+    return abase0 + ks * 64 + c * 16 * C::RC * 16;
+  };
   auto gather = [&](int blk) {
     const uint32_t base = kbuf_lds + (uint32_t)((blk % MLA_STAGES) * C::K_BYTES);
     for (int i = wave; i < C::DMA_INSTR; i += MLA_WAVES) {
@@ -178,30 +208,35 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     }
   };
 
-  v4f O[C::NDT][2];
+  v4f O[C::NDT][MLA_HT];
   // Softmax reference: fixed at the first block holding a valid entry (per head).  Later blocks
   // may exceed it by up to 2^15 in probability, which fp16 still holds, so the accumulators are
   // never rescaled.  If any head goes further, the workgroup runs the token again with the now
   // known exact maximum as the reference (probabilities <= 1); the accumulators are only ever
   // zeroed, accumulated by MFMA and read once at the end.
-  float mref[2], mlane[2] = {-INFINITY, -INFINITY};  // mlane: this lane's running maximum
-  float lsum[2];
+  float mref[MLA_HT], mlane[MLA_HT], lsum[MLA_HT];  // mlane: this lane's running maximum
+#pragma unroll
+  for (int ht = 0; ht < MLA_HT; ++ht) mlane[ht] = -INFINITY;
   const int nblk = (cnt + MLA_KB - 1) / MLA_KB;
   int32_t* overflow_flag = phys + MLA_MAX_K;  // one int after the row list
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) O[dt][0] = O[dt][1] = (v4f){0.f, 0.f, 0.f, 0.f};
-    lsum[0] = lsum[1] = 0.f;
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < MLA_HT; ++ht) O[dt][ht] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ht = 0; ht < MLA_HT; ++ht) lsum[ht] = 0.f;
     if (pass) {  // exact row maximum of pass 0, reduced over the lanes holding each head
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
+      for (int ht = 0; ht < MLA_HT; ++ht) {
         float m = mlane[ht];
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         mref[ht] = m;
       }
     } else {
-      mref[0] = mref[1] = INFINITY;  // unset: every probability is exp2(-inf) = 0 until a valid entry
+#pragma unroll
+      for (int ht = 0; ht < MLA_HT; ++ht) mref[ht] = INFINITY;  // unset: probabilities are 0 until a valid entry
     }
     bool have_ref = pass != 0;  // wave-uniform: every head of a wave gets its reference together
     bool overflow = false;
@@ -211,8 +246,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     for (int blk = 0; blk < nblk; ++blk) {
       const uint8_t* Kst = Kbuf + (blk % MLA_STAGES) * C::K_BYTES;
       // this wave's transfers of block blk are done once at most those of blk + 1 are pending
-      if (C::DMA_UNIFORM && blk + 1 < nblk)
-        wait_vmcnt<C::DMA_PER_WAVE>();
+      if (blk + 1 < nblk)
+        wait_vmcnt_pending(my_dma);
       else
         wait_vmcnt<0>();
       __syncthreads();
@@ -243,28 +278,27 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 
       // ---- S^T[key][head] for 2 key tiles x 2 head tiles; the K fragments of step ks + 1 are
       // requested before the MFMAs of step ks so that LDS latency hides behind them
-      v4f sc[2][2];
+      v4f sc[2][MLA_HT];
       if (active) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) sc[c][0] = sc[c][1] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int ht = 0; ht < MLA_HT; ++ht) sc[c][ht] = (v4f){0.f, 0.f, 0.f, 0.f};
         s16x8 Acur[2], Anext[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          Acur[c] = *reinterpret_cast<const s16x8*>(Kst + C::slot(c * 16 + j16, g) * 16);
+        for (int c = 0; c < 2; ++c) Acur[c] = *reinterpret_cast<const s16x8*>(Kst + afrag_off(0, c));
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           if (ks + 1 < C::NKS) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-              Anext[c] = *reinterpret_cast<const s16x8*>(Kst + C::slot(c * 16 + j16, (ks + 1) * 4 + g) * 16);
+            for (int c = 0; c < 2; ++c) Anext[c] = *reinterpret_cast<const s16x8*>(Kst + afrag_off(ks + 1, c));
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
           }
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            sc[c][0] = mfma_bf16_16x16x32(Acur[c], Qf[0][ks], sc[c][0]);
-            sc[c][1] = mfma_bf16_16x16x32(Acur[c], Qf[1][ks], sc[c][1]);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // 4 MFMA
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ht = 0; ht < MLA_HT; ++ht) sc[c][ht] = mfma_bf16_16x16x32(Acur[c], Qf[ht][ks], sc[c][ht]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * MLA_HT, 0);  // the step's MFMAs
           if (ks + 1 < C::NKS) {
             Acur[0] = Anext[0];
             Acur[1] = Anext[1];
@@ -283,7 +317,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         for (int rr = 0; rr < 4; ++rr) {
           const bool valid = (vbits >> (c * 4 + rr)) & 1u;
 #pragma unroll
-          for (int ht = 0; ht < 2; ++ht) {
+          for (int ht = 0; ht < MLA_HT; ++ht) {
             const float v = valid ? sc[c][ht][rr] * scale_log2 : -INFINITY;
             sc[c][ht][rr] = v;
             mlane[ht] = fmaxf(mlane[ht], v);
@@ -292,7 +326,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       if (!have_ref && vm != 0u) {  // wave-uniform: the block mask is shared by all lanes
         // first block with a valid entry: its maximum becomes the reference
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) {
+        for (int ht = 0; ht < MLA_HT; ++ht) {
           float m = mlane[ht];
           m = fmaxf(m, __shfl_xor(m, 16));
           m = fmaxf(m, __shfl_xor(m, 32));
@@ -301,9 +335,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         have_ref = true;
       }
       // ---- probabilities (fp16) packed as the B operand of out^T = V^T P^T
-      s16x8 Bp[2];
+      s16x8 Bp[MLA_HT];
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
+      for (int ht = 0; ht < MLA_HT; ++ht) {
         overflow |= mlane[ht] > mref[ht] + MLA_HEADROOM;
         float pr[8];
 #pragma unroll
@@ -334,9 +368,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
           Vf[(dt + VLA - 1) % VLA] = vfrag(dt + VLA - 1);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read (one ds_read2)
         }
-        O[dt][0] = mfma_f16_16x16x32(Vf[dt % VLA], Bp[0], O[dt][0]);
-        O[dt][1] = mfma_f16_16x16x32(Vf[dt % VLA], Bp[1], O[dt][1]);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);    // 2 MFMA
+#pragma unroll
+        for (int ht = 0; ht < MLA_HT; ++ht) O[dt][ht] = mfma_f16_16x16x32(Vf[dt % VLA], Bp[ht], O[dt][ht]);
+        __builtin_amdgcn_sched_group_barrier(0x008, MLA_HT, 1);  // the tile's MFMAs
       }
     }
     // does any wave need the exact-maximum pass?
@@ -354,7 +388,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 
   // ---- normalise and store
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
+  for (int ht = 0; ht < MLA_HT; ++ht) {
     const float l = wave_sum_xor16_32(lsum[ht]);
     const int h = wave * MLA_HEADS_PER_WAVE + ht * 16 + j16;
     if (h >= H) continue;
