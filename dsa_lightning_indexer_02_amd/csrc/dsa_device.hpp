@@ -5,6 +5,9 @@
 //    a contiguous run of the contraction index starting at (run length) * g.  Only the
 //    agreement between the A and B runs matters for a full-K dot product.
 //  - C / D (16 x 16 fp32): lane l holds rows 4 g + r (r = 0..3) of column l % 16.
+// 32x32x16 tiles (lane l, half h = l / 32): A / B lane l supplies row / column l % 32 and
+// contraction indices 8 h + j (j = 0..7); C / D lane l holds element r (r = 0..15) at row
+// 8 (r / 4) + 4 h + r % 4 of column l % 32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +19,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -36,6 +40,16 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(const s16x8& a, const s16x8& b
 
 __device__ __forceinline__ v4f mfma_f16_16x16x32(const s16x8& a, const s16x8& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const s16x8& a, const s16x8& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_f16_32x32x16(const s16x8& a, const s16x8& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 

@@ -6,15 +6,21 @@
 //   z_i = sm_scale * q[t,h,:] . kv[idx_i, :D_qk],  p = softmax(z),
 //   out[t,h,:] = sum_i p_i kv[idx_i, :D_v],        lse[t,h] = log sum_i exp(z_i).
 //
-// One workgroup (4 waves) per query row (or per row and index split in decode).  Each wave owns
-// 32 heads: their queries stay in registers, their fp32 output accumulators in the accumulation
-// registers.  Blocks of 32 selected rows are gathered from HBM/L2 into LDS twice: row-major bf16
-// for S^T = K Q^T (bf16 MFMA) and transposed fp16 for out^T = V^T P^T (fp16 MFMA).  The S^T
-// accumulator layout of one 16x16 tile is exactly the B-operand layout the P^T V^T product
-// needs, so probabilities never leave registers.  P is rounded to fp16 (11-bit significand)
-// instead of bf16; V is converted bf16 -> fp16 once per row in LDS, exact for |v| in
-// [2^-14, 65504].  Softmax is online with a lazy rescale: the running reference maximum only
-// moves when a block's maximum exceeds it by more than 2^8 in probability.
+// One workgroup (8 waves) per query row (or per row and index split in decode).  Heads form
+// groups of 32, one 32x32 MFMA tile each; every group is served by a pair of waves that split
+// the contraction: wave half f holds the queries of columns [f D_qk/2, (f+1) D_qk/2) and the
+// fp32 output accumulators of value columns [f D_v/2, (f+1) D_v/2).  Per block of 32 selected
+// rows (gathered HBM/L2 -> LDS by DMA, bf16, row-major):
+//   1. each wave forms its partial S^T = K_f Q_f^T (bf16 32x32x16 MFMA) and posts it in LDS;
+//   2. each wave adds its partner's partial (addition commutes, so both hold the same S^T),
+//      and computes the probabilities of its 16 entries per lane in fp16;
+//   3. out^T = V^T P^T (fp16 32x32x16 MFMA): the S^T accumulator layout is the B-operand layout
+//      of P^T, so probabilities never leave registers.  V^T is built once per block by all waves
+//      (transposing LDS reads of the gathered rows, bf16 -> fp16 in registers, exact for |v| in
+//      [2^-14, 65504]) into an fp16 buffer whose key order matches that B-operand layout.
+// P is rounded to fp16 (11-bit significand) rather than bf16.  The softmax reference maximum is
+// fixed at the first block holding a valid entry; a second pass with the exact row maximum runs
+// only if a later block exceeds it by more than 2^15 (the fp16 headroom).
 #include "dsa_internal.hpp"
 
 namespace dsa {
@@ -22,31 +28,31 @@ namespace dsa {
 constexpr int MLA_WAVES = 8;
 constexpr int MLA_THREADS = MLA_WAVES * WAVE;
 constexpr int MLA_KB = 32;             // selected rows per block
-constexpr int MLA_HEADS_PER_WAVE = 16;
-constexpr int MLA_HT = MLA_HEADS_PER_WAVE / 16;  // 16-head MFMA tiles per wave
-constexpr int MLA_STAGES = 3;          // gathered-row buffers in flight
+constexpr int MLA_GROUP_HEADS = 32;    // heads per group (one 32x32 tile), served by a wave pair
+constexpr int MLA_GROUPS = MLA_WAVES / 2;
+constexpr int MLA_STAGES = 2;          // gathered-row buffers in flight
 constexpr int MLA_MAX_K = 2048;        // index entries per workgroup (LDS row list)
 constexpr float MLA_HEADROOM = 15.0f;  // log2 headroom of fp16 probabilities above the reference
 
 template <int DQK, int DV>
 struct MlaCfg {
-  static constexpr int DQK_PAD = (DQK + 31) / 32 * 32;
-  static constexpr int NKS = DQK_PAD / 32;          // k-steps of the QK^T product
-  static constexpr int NDT = DV / 16;               // 16-wide value tiles
-  static constexpr int RC = DQK_PAD / 8;            // 16-byte chunks per gathered row
+  static constexpr int DH = ((DQK + 1) / 2 + 15) / 16 * 16;  // q.k columns per wave of a pair
+  static constexpr int DQK_PAD = 2 * DH;
+  static constexpr int NKS = DH / 16;                        // 32x32x16 steps of the partial S^T
+  static constexpr int DVH = DV / 2;                         // value columns per wave of a pair
+  static constexpr int NDT = DVH / 32;                       // 32-wide value tiles per wave
+  static constexpr int RC = DQK_PAD / 8;                     // 16-byte chunks per gathered row
   static constexpr int SWZ = RC % 8 == 0 ? 8 : (RC % 4 == 0 ? 4 : 1);  // XOR swizzle span (chunks)
-  static constexpr int SLOTS = MLA_KB * RC;         // 16-byte slots per stage
+  static constexpr int SLOTS = MLA_KB * RC;                  // 16-byte slots per stage
   static constexpr int K_BYTES = SLOTS * 16;
-  static constexpr int DMA_INSTR = SLOTS / WAVE;    // wave-wide 1 KiB transfers per block
-  static constexpr int DMA_MAX_PER_WAVE = (DMA_INSTR + MLA_WAVES - 1) / MLA_WAVES;
-  static constexpr int VT_STRIDE = MLA_KB * 2 + 8;  // bytes per fp16 value column
+  static constexpr int DMA_INSTR = SLOTS / WAVE;             // wave-wide 1 KiB transfers per block
+  static constexpr int SX_BYTES = MLA_WAVES * WAVE * 16 * 4; // partial S^T of every wave (fp32)
+  static constexpr int VT_STRIDE = 2 * MLA_KB + 16;          // bytes per fp16 V^T row (one value column)
   static constexpr int VT_BYTES = DV * VT_STRIDE;
-  static constexpr int CONV_ITEMS = (DV / 8) * (MLA_KB / 4);  // (16-byte column chunk, 4-key group)
-  static constexpr int CONV_PER_THREAD = (CONV_ITEMS + MLA_THREADS - 1) / MLA_THREADS;
-  static_assert(DQK % 8 == 0 && DV % 16 == 0 && DV <= DQK, "unsupported MLA dims");
+  static_assert(DQK % 8 == 0 && DV % 64 == 0 && DV <= DQK && DV <= 64 * MLA_WAVES, "unsupported MLA dims");
   static_assert(SLOTS % WAVE == 0, "gather slots must fill whole waves");
   // 16-byte slot of chunk c of gathered row r: rows are contiguous, chunks XOR-swizzled within
-  // aligned groups of SWZ so that 8 consecutive rows at one chunk hit 8 distinct bank groups.
+  // aligned groups of SWZ.
   static __device__ __forceinline__ int slot(int r, int c) { return r * RC + (c ^ (r & (SWZ - 1))); }
 };
 
@@ -54,7 +60,8 @@ template <int DQK, int DV>
 size_t mla_smem_bytes(int32_t keys_per_wg) {
   using C = MlaCfg<DQK, DV>;
   (void)keys_per_wg;
-  return (size_t)MLA_STAGES * C::K_BYTES + C::VT_BYTES + (size_t)(MLA_MAX_K + 4 + MLA_MAX_K / MLA_KB) * sizeof(int32_t);
+  return (size_t)MLA_STAGES * C::K_BYTES + C::SX_BYTES + C::VT_BYTES +
+         (size_t)(MLA_MAX_K + 4 + MLA_MAX_K / MLA_KB) * sizeof(int32_t);
 }
 
 // One wave-wide global -> LDS transfer: lane l's 16 bytes at gaddr land at lds_base + 16 l.
@@ -91,6 +98,24 @@ __device__ __forceinline__ void wait_vmcnt_pending(int n) {
   }
 }
 
+// Transposing LDS read (gfx950): within each group of 16 lanes, lane i receives element i % 4 of
+// the 4 x 16-bit words addressed by lanes 4 j + i / 4 of its group, j = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+// Four bf16 values (two packed words each) -> fp16, as one half of an MFMA operand.
+__device__ __forceinline__ void bf16x4_to_f16(const s16x4 raw, s16x8& dst, int half) {
+  const v2i w = __builtin_bit_cast(v2i, raw);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float lo = __uint_as_float((uint32_t)w[e] << 16);
+    const float hi = __uint_as_float((uint32_t)w[e] & 0xFFFF0000u);
+    dst[4 * half + 2 * e] = __builtin_bit_cast(short, (_Float16)lo);
+    dst[4 * half + 2 * e + 1] = __builtin_bit_cast(short, (_Float16)hi);
+  }
+}
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
@@ -102,12 +127,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   using C = MlaCfg<DQK, DV>;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* Kbuf = smem;                                                  // [STAGES][SLOTS] x 16 B
-  uint8_t* Vt = smem + MLA_STAGES * C::K_BYTES;                          // [DV][VT_STRIDE] fp16
+  float* Sx = reinterpret_cast<float*>(smem + MLA_STAGES * C::K_BYTES);  // [WAVES][4][64] x v4f
+  uint8_t* Vt = smem + MLA_STAGES * C::K_BYTES + C::SX_BYTES;            // [DV][VT_STRIDE] fp16
   int32_t* phys = reinterpret_cast<int32_t*>(Vt + C::VT_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int j16 = lane & 15, g = lane >> 4;
+  const int hg = wave >> 1, hf = wave & 1;                    // head group, contraction half
+  const int l32 = lane & 31, lh = lane >> 5;
   const int64_t r = blockIdx.y;
   const int sp = blockIdx.x;
   const int64_t n = seq_lens ? min((int64_t)max(seq_lens[r], 0), S) : min(S, q_start + r + 1);
@@ -162,39 +189,51 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     }
   }
 
-  // queries of this wave's 32 heads, as B operands of S^T = K Q^T
-  const bool active = wave * MLA_HEADS_PER_WAVE < H;
-  s16x8 Qf[MLA_HT][C::NKS];
+  // queries of this wave's head group and contraction half, as B operands of S^T = K Q^T
+  const bool active = hg * MLA_GROUP_HEADS < H;
+  const int head = hg * MLA_GROUP_HEADS + l32;
+  s16x8 Qf[C::NKS];
 #pragma unroll
-  for (int ht = 0; ht < MLA_HT; ++ht) {
-    const int h = wave * MLA_HEADS_PER_WAVE + ht * 16 + j16;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      const int col = ks * 32 + g * 8;
-      const bool ok = h < H && col < DQK;
-      s16x8 v = *reinterpret_cast<const s16x8*>(q + (r * H + (ok ? h : 0)) * (int64_t)DQK + (ok ? col : 0));
-      if (!ok) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-      asm volatile("" : "+v"(v));  // keep the queries resident: no re-load from memory per block
-      Qf[ht][ks] = v;
-    }
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    const int col = hf * C::DH + ks * 16 + lh * 8;
+    const bool ok = head < H && col < DQK;
+    s16x8 v = *reinterpret_cast<const s16x8*>(q + (r * H + (ok ? head : 0)) * (int64_t)DQK + (ok ? col : 0));
+    if (!ok) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    asm volatile("" : "+v"(v));  // keep the queries resident: no re-load from memory per block
+    Qf[ks] = v;
   }
   __syncthreads();
 
   const uint32_t kbuf_lds = lds_addr(Kbuf);
   const int my_dma = (C::DMA_INSTR - wave + MLA_WAVES - 1) / MLA_WAVES;  // this wave's transfers per block
-  // Byte offset in a stage of the K fragment (step ks, key tile c) this lane reads: chunk 4 ks + g
-  // of row 16 c + j16.  The swizzle XORs the low log2(SWZ) chunk bits with the row, so the offset is
-  // one of two per-lane bases (by the parity of ks when SWZ is 8) plus a compile-time constant, and
-  // no per-step address has to stay live.
   static_assert(C::SWZ == 8 || C::SWZ == 4 || C::SWZ == 1, "swizzle span");
-  const int xr = j16 & (C::SWZ - 1);
-  const int abase0 = (j16 * C::RC + (g ^ xr)) * 16;            // even ks (and every ks when SWZ <= 4)
-  const int abase1 = (j16 * C::RC + ((4 + g) ^ xr)) * 16;      // odd ks when SWZ == 8
-  auto afrag_off = [&](int ks, int c) -> int {
-    if (C::SWZ == 8)
-      return ((ks & 1) ? abase1 : abase0) + (ks >> 1) * 128 + c * 16 * C::RC * 16;
-    return abase0 + ks * 64 + c * 16 * C::RC * 16;
-  };
+  // K fragment of step ks (A operand): row l32, chunk cb + 2 ks.  XOR-ing the row into the low
+  // log2(SWZ) chunk bits leaves steps that are SWZ chunks apart a constant distance apart, so the
+  // offset is one of KP per-lane bases plus a compile-time constant.
+  constexpr int KP = C::SWZ >= 2 ? C::SWZ / 2 : 1;
+  const int kx = l32 & (C::SWZ - 1);
+  const int kcb = hf * (C::DH / 8) + lh;
+  int kbase[KP];
+#pragma unroll
+  for (int u = 0; u < KP; ++u) kbase[u] = (l32 * C::RC + ((kcb + 2 * u) ^ kx)) * 16;
+  auto kfrag_off = [&](int ks) { return kbase[ks % KP] + (ks / KP) * (2 * KP * 16); };
+  // V^T construction: wave w converts value columns [64 w, 64 w + 64); its 16-lane group G
+  // columns 64 w + 16 G + 0..15.  Transposing read j gives lane i of the group column
+  // 64 w + 16 G + i at keys 4 j' + 0..3 when lane a of the group addresses row 4 j' + a / 4,
+  // columns 64 w + 16 G + 4 (a % 4) .. + 3.  Keys are stored per column in the order
+  // [16 m + 4 lh + 0..3, 16 m + 8 + 4 lh + 0..3] at 16-byte unit 2 m + lh, which is the order of
+  // the probabilities a lane holds in elements 8 m .. 8 m + 7 of the S^T accumulator.
+  const bool converts = wave * 64 < DV;
+  const int tg = (lane >> 4) & 3, ti = lane & 15;
+  const int trow = (lane & 15) >> 2;                                   // + 4 j'
+  const int tch = (wave * 64 + 16 * tg) / 8 + ((lane & 3) >> 1);      // chunk of the addressed columns
+  // row 4 jq + trow: its swizzle bits are trow | 4 (jq & 1) when SWZ is 8, trow when SWZ is 4
+  constexpr int TQ = C::SWZ >= 8 ? 2 : 1;
+  int tb[TQ];
+#pragma unroll
+  for (int e = 0; e < TQ; ++e) tb[e] = (trow * C::RC + (tch ^ ((trow | 4 * e) & (C::SWZ - 1)))) * 16 + 8 * (lane & 1);
+  auto tr_off = [&](int jq) { return tb[jq % TQ] + 4 * jq * C::RC * 16; };  // key quad jq: rows 4 jq + 0..3
+  uint8_t* vt_dst = Vt + (wave * 64 + 16 * tg + ti) * C::VT_STRIDE;
   auto gather = [&](int blk) {
     const uint32_t base = kbuf_lds + (uint32_t)((blk % MLA_STAGES) * C::K_BYTES);
     for (int i = wave; i < C::DMA_INSTR; i += MLA_WAVES) {
@@ -208,37 +247,19 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     }
   };
 
-  v4f O[C::NDT][MLA_HT];
-  // Softmax reference: fixed at the first block holding a valid entry (per head).  Later blocks
-  // may exceed it by up to 2^15 in probability, which fp16 still holds, so the accumulators are
-  // never rescaled.  If any head goes further, the workgroup runs the token again with the now
-  // known exact maximum as the reference (probabilities <= 1); the accumulators are only ever
-  // zeroed, accumulated by MFMA and read once at the end.
-  float mref[MLA_HT], mlane[MLA_HT], lsum[MLA_HT];  // mlane: this lane's running maximum
-#pragma unroll
-  for (int ht = 0; ht < MLA_HT; ++ht) mlane[ht] = -INFINITY;
+  v16f O[C::NDT];
+  float mref, mlane = -INFINITY, lsum;  // mlane: this lane's running maximum (its head, its keys)
   const int nblk = (cnt + MLA_KB - 1) / MLA_KB;
   int32_t* overflow_flag = phys + MLA_MAX_K;  // one int after the row list
+  const v4f* Sx_mine = reinterpret_cast<const v4f*>(Sx) + wave * 4 * WAVE + lane;
+  const v4f* Sx_peer = reinterpret_cast<const v4f*>(Sx) + (wave ^ 1) * 4 * WAVE + lane;
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int ht = 0; ht < MLA_HT; ++ht) O[dt][ht] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ht = 0; ht < MLA_HT; ++ht) lsum[ht] = 0.f;
-    if (pass) {  // exact row maximum of pass 0, reduced over the lanes holding each head
-#pragma unroll
-      for (int ht = 0; ht < MLA_HT; ++ht) {
-        float m = mlane[ht];
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        mref[ht] = m;
-      }
-    } else {
-#pragma unroll
-      for (int ht = 0; ht < MLA_HT; ++ht) mref[ht] = INFINITY;  // unset: probabilities are 0 until a valid entry
-    }
-    bool have_ref = pass != 0;  // wave-uniform: every head of a wave gets its reference together
+    for (int dt = 0; dt < C::NDT; ++dt) O[dt] = (v16f){};
+    lsum = 0.f;
+    // pass 1: the exact row maximum of pass 0; pass 0: unset, probabilities are 0 until a valid entry
+    mref = pass ? fmaxf(mlane, __shfl_xor(mlane, 32)) : INFINITY;
+    bool have_ref = pass != 0;  // wave-uniform: all heads of a wave get their reference together
     bool overflow = false;
 
     if (nblk > 0) gather(0);
@@ -250,127 +271,93 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         wait_vmcnt_pending(my_dma);
       else
         wait_vmcnt<0>();
-      __syncthreads();
-      if (blk + 2 < nblk) gather(blk + 2);
+      __syncthreads();  // stage blk complete; every wave is done with block blk - 1
 
-      // ---- fp16 V^T of this block (read from the gathered rows)
+      // ---- fp16 V^T of this block
+      if (converts) {
 #pragma unroll
-      for (int it = 0; it < C::CONV_PER_THREAD; ++it) {
-        const int p = tid + it * MLA_THREADS;
-        if (C::CONV_ITEMS % MLA_THREADS == 0 || p < C::CONV_ITEMS) {
-          const int kg = p % (MLA_KB / 4), c8 = p / (MLA_KB / 4);
-          v4i rows[4];
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) rows[kk] = *reinterpret_cast<const v4i*>(Kst + C::slot(kg * 4 + kk, c8) * 16);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            s16x4 col;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              const uint32_t word = (uint32_t)rows[kk][i >> 1];
-              const uint16_t bb = (i & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
-              col[kk] = __builtin_bit_cast(short, (_Float16)bf16_to_f32(bb));
-            }
-            *reinterpret_cast<s16x4*>(Vt + (c8 * 8 + i) * C::VT_STRIDE + kg * 8) = col;
-          }
+        for (int u = 0; u < 4; ++u) {  // unit u = 2 m + lh: key quads 4 m + lh and 4 m + 2 + lh
+          const int m = u >> 1, hh = u & 1;
+          s16x8 vv;
+          bf16x4_to_f16(lds_read_tr16(Kst + tr_off(4 * m + hh)), vv, 0);
+          bf16x4_to_f16(lds_read_tr16(Kst + tr_off(4 * m + 2 + hh)), vv, 1);
+          *reinterpret_cast<s16x8*>(vt_dst + 16 * u) = vv;
         }
       }
 
-      // ---- S^T[key][head] for 2 key tiles x 2 head tiles; the K fragments of step ks + 1 are
-      // requested before the MFMAs of step ks so that LDS latency hides behind them
-      v4f sc[2][MLA_HT];
+      // ---- partial S^T[key][head] over this wave's contraction half; the K fragment of step
+      // ks + 1 is requested before the MFMA of step ks
+      v16f sc = {};
       if (active) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int ht = 0; ht < MLA_HT; ++ht) sc[c][ht] = (v4f){0.f, 0.f, 0.f, 0.f};
-        s16x8 Acur[2], Anext[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) Acur[c] = *reinterpret_cast<const s16x8*>(Kst + afrag_off(0, c));
+        s16x8 Acur = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(0));
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
+          s16x8 Anext;
           if (ks + 1 < C::NKS) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) Anext[c] = *reinterpret_cast<const s16x8*>(Kst + afrag_off(ks + 1, c));
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+            Anext = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(ks + 1));
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
           }
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int ht = 0; ht < MLA_HT; ++ht) sc[c][ht] = mfma_bf16_16x16x32(Acur[c], Qf[ht][ks], sc[c][ht]);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * MLA_HT, 0);  // the step's MFMAs
-          if (ks + 1 < C::NKS) {
-            Acur[0] = Anext[0];
-            Acur[1] = Anext[1];
-          }
+          sc = mfma_bf16_32x32x16(Acur, Qf[ks], sc);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+          if (ks + 1 < C::NKS) Acur = Anext;
         }
+        v4f* dst = reinterpret_cast<v4f*>(Sx) + wave * 4 * WAVE + lane;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          dst[qd * WAVE] = (v4f){sc[4 * qd], sc[4 * qd + 1], sc[4 * qd + 2], sc[4 * qd + 3]};
       }
-      __syncthreads();  // V^T complete
+      __syncthreads();  // partial scores of both halves posted; V^T complete; stage blk no longer read
+      if (blk + 2 < nblk) gather(blk + 2);
       if (!active) continue;
 
-      // ---- scaled logits (log2 units), masked entries at -inf
+      // ---- full scores (own + partner partial) in log2 units, masked entries at -inf
       const uint32_t vm = vmask_lds[blk];
-      const uint32_t vbits = ((vm >> (4 * g)) & 0xFu) | (((vm >> (16 + 4 * g)) & 0xFu) << 4);  // bit 4c + rr
+      const uint32_t vt = vm >> (4 * lh);
+      const uint32_t vbits = (vt & 0xFu) | ((vt >> 4) & 0xF0u) | ((vt >> 8) & 0xF00u) | ((vt >> 12) & 0xF000u);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int qd = 0; qd < 4; ++qd) {
+        const v4f pv = Sx_peer[qd * WAVE];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const bool valid = (vbits >> (c * 4 + rr)) & 1u;
-#pragma unroll
-          for (int ht = 0; ht < MLA_HT; ++ht) {
-            const float v = valid ? sc[c][ht][rr] * scale_log2 : -INFINITY;
-            sc[c][ht][rr] = v;
-            mlane[ht] = fmaxf(mlane[ht], v);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 4 * qd + e;
+          const bool valid = (vbits >> rr) & 1u;
+          const float v = valid ? (sc[rr] + pv[e]) * scale_log2 : -INFINITY;
+          sc[rr] = v;
+          mlane = fmaxf(mlane, v);
         }
+      }
+      (void)Sx_mine;
       if (!have_ref && vm != 0u) {  // wave-uniform: the block mask is shared by all lanes
         // first block with a valid entry: its maximum becomes the reference
-#pragma unroll
-        for (int ht = 0; ht < MLA_HT; ++ht) {
-          float m = mlane[ht];
-          m = fmaxf(m, __shfl_xor(m, 16));
-          m = fmaxf(m, __shfl_xor(m, 32));
-          mref[ht] = m;
-        }
+        mref = fmaxf(mlane, __shfl_xor(mlane, 32));
         have_ref = true;
       }
-      // ---- probabilities (fp16) packed as the B operand of out^T = V^T P^T
-      s16x8 Bp[MLA_HT];
+      overflow |= mlane > mref + MLA_HEADROOM;
+      // ---- probabilities (fp16) packed as the B operands of out^T = V^T P^T (keys 0-15, 16-31)
+      s16x8 Bp[2];
 #pragma unroll
-      for (int ht = 0; ht < MLA_HT; ++ht) {
-        overflow |= mlane[ht] > mref[ht] + MLA_HEADROOM;
-        float pr[8];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const float p = __builtin_amdgcn_exp2f(sc[c][ht][rr] - mref[ht]);  // exp2(-inf) = 0
-            pr[c * 4 + rr] = p;
-            lsum[ht] += p;
-          }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) Bp[ht][i] = __builtin_bit_cast(short, (_Float16)pr[i]);
+      for (int rr = 0; rr < 16; ++rr) {
+        const float p = __builtin_amdgcn_exp2f(sc[rr] - mref);  // exp2(-inf) = 0
+        lsum += p;
+        Bp[rr >> 3][rr & 7] = __builtin_bit_cast(short, (_Float16)p);
       }
-      // ---- out^T[d][head] += V^T[d][key] P^T[key][head], value fragments requested one tile ahead
-      auto vfrag = [&](int dt) {
-        const uint8_t* vrow = Vt + (dt * 16 + j16) * C::VT_STRIDE;
-        const s16x4 lo = *reinterpret_cast<const s16x4*>(vrow + g * 8);
-        const s16x4 hi = *reinterpret_cast<const s16x4*>(vrow + 32 + g * 8);
-        return (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      // ---- out^T[d][head] += V^T[d][key] P^T[key][head]; consecutive MFMAs use different tiles,
+      // fragments are requested one step ahead
+      constexpr int NSTEP = C::NDT * 2;
+      const uint8_t* vsrc = Vt + (hf * C::DVH + l32) * C::VT_STRIDE + 16 * lh;
+      auto vfrag = [&](int st) {  // step st: key half m = st / NDT, value tile dt = st % NDT
+        return *reinterpret_cast<const s16x8*>(vsrc + (st % C::NDT) * 32 * C::VT_STRIDE + 32 * (st / C::NDT));
       };
-      constexpr int VLA = 2;  // value fragments in flight
-      s16x8 Vf[VLA];
+      s16x8 Vf[2];
+      Vf[0] = vfrag(0);
 #pragma unroll
-      for (int i = 0; i < VLA - 1; ++i) Vf[i] = vfrag(i);
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        if (dt + VLA - 1 < C::NDT) {
-          Vf[(dt + VLA - 1) % VLA] = vfrag(dt + VLA - 1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read (one ds_read2)
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + 1 < NSTEP) {
+          Vf[(st + 1) & 1] = vfrag(st + 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
         }
-#pragma unroll
-        for (int ht = 0; ht < MLA_HT; ++ht) O[dt][ht] = mfma_f16_16x16x32(Vf[dt % VLA], Bp[ht], O[dt][ht]);
-        __builtin_amdgcn_sched_group_barrier(0x008, MLA_HT, 1);  // the tile's MFMAs
+        O[st % C::NDT] = mfma_f16_32x32x16(Vf[st & 1], Bp[st / C::NDT], O[st % C::NDT]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);    // MFMA
       }
     }
     // does any wave need the exact-maximum pass?
@@ -384,36 +371,39 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     }
   }
   wait_vmcnt<0>();
-  if (!active) return;
+  if (!active || head >= H) return;
 
-  // ---- normalise and store
+  // ---- normalise and store: element rr of tile dt is value column f DV/2 + 32 dt + 8 (rr / 4)
+  // + 4 lh + rr % 4 of head `head`
+  const float l = lsum + __shfl_xor(lsum, 32);
+  const float inv = l > 0.f ? 1.0f / l : 0.0f;
+  const float lse_v = l > 0.f ? (mref + log2f(l)) * 0.69314718055994531f : -INFINITY;
+  if (nsplit == 1) {
+    uint16_t* orow = out + (r * H + head) * (int64_t)DV;
 #pragma unroll
-  for (int ht = 0; ht < MLA_HT; ++ht) {
-    const float l = wave_sum_xor16_32(lsum[ht]);
-    const int h = wave * MLA_HEADS_PER_WAVE + ht * 16 + j16;
-    if (h >= H) continue;
-    const float inv = l > 0.f ? 1.0f / l : 0.0f;
-    const float lse_v = l > 0.f ? (mref[ht] + log2f(l)) * 0.69314718055994531f : -INFINITY;
-    if (nsplit == 1) {
-      uint16_t* orow = out + (r * H + h) * (int64_t)DV;
+    for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const int d = dt * 16 + 4 * g;
-        v4f o = O[dt][ht] * inv;
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d = hf * C::DVH + dt * 32 + 8 * qd + 4 * lh;
+        const v4f o = (v4f){O[dt][4 * qd], O[dt][4 * qd + 1], O[dt][4 * qd + 2], O[dt][4 * qd + 3]} * inv;
         s16x4 ob;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) ob[rr] = (short)f32_to_bf16(o[rr]);
+        for (int e = 0; e < 4; ++e) ob[e] = (short)f32_to_bf16(o[e]);
         *reinterpret_cast<s16x4*>(orow + d) = ob;
-        if (out_f32) *reinterpret_cast<v4f*>(out_f32 + (r * H + h) * (int64_t)DV + d) = o;
+        if (out_f32) *reinterpret_cast<v4f*>(out_f32 + (r * H + head) * (int64_t)DV + d) = o;
       }
-      if (g == 0 && lse) lse[r * H + h] = lse_v;
-    } else {
-      float* prow = part_out + ((r * nsplit + sp) * (int64_t)H + h) * DV;
+    if (hf == 0 && lh == 0 && lse) lse[r * H + head] = lse_v;
+  } else {
+    float* prow = part_out + ((r * nsplit + sp) * (int64_t)H + head) * DV;
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
-        *reinterpret_cast<v4f*>(prow + dt * 16 + 4 * g) = O[dt][ht] * inv;
-      if (g == 0) part_lse[(r * nsplit + sp) * (int64_t)H + h] = lse_v;
-    }
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d = hf * C::DVH + dt * 32 + 8 * qd + 4 * lh;
+        *reinterpret_cast<v4f*>(prow + d) =
+            (v4f){O[dt][4 * qd], O[dt][4 * qd + 1], O[dt][4 * qd + 2], O[dt][4 * qd + 3]} * inv;
+      }
+    if (hf == 0 && lh == 0) part_lse[(r * nsplit + sp) * (int64_t)H + head] = lse_v;
   }
 }
 
@@ -478,7 +468,7 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
 
 bool mla_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k) {
   const bool dims = (D_qk == 576 && D_v == 512) || (D_qk == 80 && D_v == 64);
-  return dims && H >= 1 && H <= MLA_WAVES * MLA_HEADS_PER_WAVE && k >= 1 && k <= MLA_MAX_K;
+  return dims && H >= 1 && H <= MLA_GROUPS * MLA_GROUP_HEADS && k >= 1 && k <= MLA_MAX_K;
 }
 
 size_t mla_smem_for(int32_t D_qk, int32_t D_v, int32_t keys_per_wg) {
