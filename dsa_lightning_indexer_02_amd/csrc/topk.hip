@@ -7,8 +7,10 @@
 // window starts at the highest bit where the row's minimum and maximum keys differ, each
 // pass builds an LDS histogram of an 11-bit digit among the keys that still match the
 // threshold's known prefix, and at most three passes pin the k-th largest key exactly.
-// Emission is an ordered compaction (wave ballots and prefix counts), so the output is
-// deterministic: every key above the threshold in index order, then the lowest-index ties.
+// Emission is an ordered compaction: per group of 256 positions, wave ballots give every
+// selected element its rank (mbcnt), the slots are staged in LDS and the index list leaves in
+// coalesced 16-byte stores.  The output is deterministic: every key above the threshold in index
+// order, then the lowest-index ties.
 //
 // Rows longer than 32768 are cut into chunks; each chunk emits its own top-k candidates
 // (key, index) and a merge pass runs the same select over the concatenated candidates.  This
@@ -24,9 +26,11 @@ constexpr int TK_DIGIT = 11;
 constexpr int TK_CHUNK_EPT = 64;  // 512 * 64 = 32768 scores per workgroup
 constexpr int64_t TK_CHUNK = (int64_t)TK_THREADS * TK_CHUNK_EPT;
 constexpr int TK_MERGE_EPT = 16;  // 8192 candidates per merge
+constexpr int TK_STAGE = 2048;    // index lists up to this length are staged in LDS
 
 struct TopkShared {
   uint32_t hist[TK_BINS];
+  int32_t stage[TK_STAGE];
   uint32_t wsum[TK_WAVES][2];
   uint32_t red[TK_WAVES][2];
   uint32_t sel_bin, sel_above;
@@ -142,20 +146,30 @@ __device__ void radix_threshold(const uint32_t (&key)[EPT], uint32_t k, TopkShar
   k_rem = need;
 }
 
+// Number of set bits of a wave mask held by lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m, uint32_t acc) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, acc));
+}
+
 // Ordered emission of the selected elements: all keys > tau in position order, then the
-// first k_rem keys == tau.  emit(pos, e, slot) is called once per selected element.
+// first k_rem keys == tau.  emit(pos, slot) is called once per selected element.  The selection
+// is first reduced to two bit masks per thread (bit e: element e), so the emission loop does not
+// index the key array.  Within a group of 4 WAVE positions (4 lane + c), the rank of an element
+// is the number of selected elements of lower lanes (ballots, mbcnt) plus this lane's selected
+// elements of lower c.
 template <int EPT, typename Emit>
 __device__ void emit_selected(const uint32_t (&key)[EPT], uint32_t tau, uint32_t k, uint32_t k_rem,
                               TopkShared& sh, Emit emit) {
+  static_assert(EPT <= 64 && EPT % 4 == 0, "one 64-bit mask per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t cg = 0, ce = 0;
+  uint64_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    cg += key[e] > tau;
-    ce += key[e] == tau;
+    gtm |= (uint64_t)(key[e] > tau) << e;
+    eqm |= (uint64_t)(key[e] == tau) << e;
   }
   // wave totals
-  uint32_t tg = cg, te = ce;
+  uint32_t tg = (uint32_t)__builtin_popcountll(gtm), te = (uint32_t)__builtin_popcountll(eqm);
   for (int o = 32; o > 0; o >>= 1) {
     tg += (uint32_t)__shfl_xor((int)tg, o);
     te += (uint32_t)__shfl_xor((int)te, o);
@@ -165,39 +179,58 @@ __device__ void emit_selected(const uint32_t (&key)[EPT], uint32_t tau, uint32_t
     sh.wsum[wave][1] = te;
   }
   __syncthreads();
-  uint32_t gbase = 0, ebase = 0;
+  uint32_t gbase = 0, ebase = 0;  // wave-uniform
   for (int i = 0; i < wave; ++i) {
     gbase += sh.wsum[i][0];
     ebase += sh.wsum[i][1];
   }
   const uint32_t n_gt = k - k_rem;
-#pragma unroll
+#pragma unroll 2
   for (int q = 0; q < EPT / 4; ++q) {
-    uint32_t sg = 0, se = 0;
+    const uint32_t ng = (uint32_t)(gtm >> (4 * q)) & 0xFu, ne = (uint32_t)(eqm >> (4 * q)) & 0xFu;
+    const int pos0 = elem_pos<EPT>(wave, lane, 4 * q);
+    uint64_t m[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      sg += key[4 * q + c] > tau;
-      se += key[4 * q + c] == tau;
-    }
-    const uint32_t packed = sg | (se << 16);
-    const uint32_t incl = wave_incl_scan(packed, lane);
-    const uint32_t excl = incl - packed;
-    uint32_t og = gbase + (excl & 0xFFFFu), oe = ebase + (excl >> 16);
+    for (int c = 0; c < 4; ++c) m[c] = __ballot((ng >> c) & 1u);
+    if (m[0] | m[1] | m[2] | m[3]) {
+      uint32_t r = gbase;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = 4 * q + c;
-      const uint32_t kk = key[e];
-      if (kk > tau) {
-        emit(elem_pos<EPT>(wave, lane, e), e, og);
-        ++og;
-      } else if (kk == tau) {
-        if (oe < k_rem) emit(elem_pos<EPT>(wave, lane, e), e, n_gt + oe);
-        ++oe;
-      }
+      for (int c = 0; c < 4; ++c) r = lanes_below(m[c], r);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((ng >> c) & 1u) emit(pos0 + c, r++);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gbase += (uint32_t)__builtin_popcountll(m[c]);
     }
-    const uint32_t tot = (uint32_t)__shfl((int)incl, 63);
-    gbase += tot & 0xFFFFu;
-    ebase += tot >> 16;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) m[c] = __ballot((ne >> c) & 1u);
+    if (m[0] | m[1] | m[2] | m[3]) {  // ties: rare
+      uint32_t r = ebase;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r = lanes_below(m[c], r);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((ne >> c) & 1u) {
+          if (r < k_rem) emit(pos0 + c, n_gt + r);
+          ++r;
+        }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ebase += (uint32_t)__builtin_popcountll(m[c]);
+    }
+  }
+}
+
+// Copy the staged index list (k <= TK_STAGE entries) to dst with 16-byte stores where aligned.
+__device__ __forceinline__ void store_staged(const TopkShared& sh, int32_t* __restrict__ dst, int32_t k) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (((uintptr_t)dst & 15) == 0) {
+    const int k4 = k & ~3;
+    for (int i = 4 * tid; i < k4; i += 4 * TK_THREADS)
+      *reinterpret_cast<v4i*>(dst + i) = *reinterpret_cast<const v4i*>(sh.stage + i);
+    for (int i = k4 + tid; i < k; i += TK_THREADS) dst[i] = sh.stage[i];
+  } else {
+    for (int i = tid; i < k; i += TK_THREADS) dst[i] = sh.stage[i];
   }
 }
 
@@ -219,9 +252,11 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t
   }
 }
 
-// One chunk of one row.  Rows with a single chunk write the final index list; otherwise the
-// chunk's candidates go to cand_key / cand_idx [rows][G][k] (key 0 = empty slot).
+// One chunk of one row.  SINGLE (every row fits one chunk): the final index list; otherwise
+// the chunk's candidates go to cand_key / cand_idx [rows][G][k] (key 0 = empty slot) and rows of
+// one chunk still write their final list.
 // mode 0: prefill rows (n_t = min(S, q_start + t + 1)); mode 1: decode rows (n = seq_lens[t]).
+template <bool SINGLE>
 __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     const float* __restrict__ logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
     const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices,
@@ -233,19 +268,17 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   const int64_t c0 = (int64_t)chunk * TK_CHUNK;
   if (c0 >= n && chunk > 0) return;
   const int64_t cn = min(n - c0, TK_CHUNK);  // elements of this chunk
-  const bool single = n <= TK_CHUNK;
+  const bool single = SINGLE || n <= TK_CHUNK;
   const int tid = threadIdx.x;
   int32_t* out_idx = indices + t * k;
-  uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
-  int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
 
   if (cn <= k) {  // everything in the chunk is selected
     for (int64_t i = tid; i < k; i += TK_THREADS) {
       if (single) {
         out_idx[i] = i < cn ? (int32_t)(c0 + i) : -1;
       } else {
-        ck[i] = i < cn ? score_key(logits[t * ld + c0 + i]) : 0u;
-        ci[i] = i < cn ? (int32_t)(c0 + i) : -1;
+        cand_key[(t * G + chunk) * (int64_t)k + i] = i < cn ? score_key(logits[t * ld + c0 + i]) : 0u;
+        cand_idx[(t * G + chunk) * (int64_t)k + i] = i < cn ? (int32_t)(c0 + i) : -1;
       }
     }
     return;
@@ -255,11 +288,20 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   uint32_t tau, k_rem;
   radix_threshold<TK_CHUNK_EPT>(key, (uint32_t)k, sh, tau, k_rem);
   if (single) {
-    emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh,
-                                [&](int pos, int, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
+    if (k <= TK_STAGE) {
+      emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                                  [&](int pos, uint32_t slot) { sh.stage[slot] = (int32_t)(c0 + pos); });
+      store_staged(sh, out_idx, k);
+    } else {
+      emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                                  [&](int pos, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
+    }
   } else {
-    emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh, [&](int pos, int e, uint32_t slot) {
-      ck[slot] = key[e];
+    uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
+    int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
+    const float* row = logits + t * ld + c0;
+    emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh, [&](int pos, uint32_t slot) {
+      ck[slot] = score_key(row[pos]);  // re-read (L2): keeps the key array out of the loop
       ci[slot] = (int32_t)(c0 + pos);
     });
   }
@@ -280,18 +322,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   const uint32_t* ck = cand_key + t * G * (int64_t)k;
   const int32_t* ci = cand_idx + t * G * (int64_t)k;
   uint32_t key[TK_MERGE_EPT];
-  int32_t idx[TK_MERGE_EPT];
 #pragma unroll
   for (int e = 0; e < TK_MERGE_EPT; ++e) {
     const int p = elem_pos<TK_MERGE_EPT>(wave, lane, e);
     key[e] = p < total ? ck[p] : 0u;
-    idx[e] = p < total ? ci[p] : -1;
   }
   uint32_t tau, k_rem;
   radix_threshold<TK_MERGE_EPT>(key, (uint32_t)k, sh, tau, k_rem);
   int32_t* out_idx = indices + t * k;
-  emit_selected<TK_MERGE_EPT>(key, tau, (uint32_t)k, k_rem, sh,
-                              [&](int, int e, uint32_t slot) { out_idx[slot] = idx[e]; });
+  if (k <= TK_STAGE) {
+    emit_selected<TK_MERGE_EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                                [&](int pos, uint32_t slot) { sh.stage[slot] = ci[pos]; });
+    store_staged(sh, out_idx, k);
+  } else {
+    emit_selected<TK_MERGE_EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                                [&](int pos, uint32_t slot) { out_idx[slot] = ci[pos]; });
+  }
 }
 
 int32_t topk_chunks(int64_t S) { return (int32_t)((S + TK_CHUNK - 1) / TK_CHUNK); }
@@ -318,8 +364,12 @@ hipError_t launch_topk(const float* logits, int64_t ld, int64_t T, int64_t S, in
     ck = reinterpret_cast<uint32_t*>(workspace);
     ci = reinterpret_cast<int32_t*>(ck + (size_t)T * G * k);
   }
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)G, (unsigned)T), dim3(TK_THREADS), 0, stream,
-                     logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
+  if (G <= 1)
+    hipLaunchKernelGGL(topk_chunk_kernel<true>, dim3(1, (unsigned)T), dim3(TK_THREADS), 0, stream, logits, ld,
+                       T, S, q_start, seq_lens, k, indices, ck, ci, G);
+  else
+    hipLaunchKernelGGL(topk_chunk_kernel<false>, dim3((unsigned)G, (unsigned)T), dim3(TK_THREADS), 0, stream,
+                       logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || G <= 1) return e;
   hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, T, S, q_start,
