@@ -24,10 +24,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-# Per-source flags.  The sparse-MLA kernel keeps 256 fp32 output accumulators per lane; with
-# LLVM's default heuristic every MFMA of the function takes the accumulation-register form and
-# the score tiles no longer fit beside them, so the VGPR form is requested and the compiler moves
-# the long-lived accumulators to accumulation registers itself.
+# Per-source flags.  The sparse-MLA kernel issues its gather DMA as inline assembly, and keeps
+# its MFMA accumulators in the architectural VGPRs (the score tiles are read by VALU code right
+# after each product, which the accumulation-register form would turn into copies).
 PER_SOURCE = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"]}
 
 

@@ -289,17 +289,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       // ks + 1 is requested before the MFMA of step ks
       v16f sc = {};
       if (active) {
-        s16x8 Acur = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(0));
+        constexpr int LA = 3;  // K fragments in flight (order pinned by scheduling barriers)
+        s16x8 Af[LA];
+#pragma unroll
+        for (int i = 0; i < LA - 1; ++i) Af[i] = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(i));
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          s16x8 Anext;
-          if (ks + 1 < C::NKS) {
-            Anext = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(ks + 1));
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-          }
-          sc = mfma_bf16_32x32x16(Acur, Qf[ks], sc);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-          if (ks + 1 < C::NKS) Acur = Anext;
+          if (ks + LA - 1 < C::NKS) Af[(ks + LA - 1) % LA] = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(ks + LA - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          sc = mfma_bf16_32x32x16(Af[ks % LA], Qf[ks], sc);
+          __builtin_amdgcn_sched_barrier(0);
         }
         v4f* dst = reinterpret_cast<v4f*>(Sx) + wave * 4 * WAVE + lane;
 #pragma unroll
@@ -348,16 +347,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       auto vfrag = [&](int st) {  // step st: key half m = st / NDT, value tile dt = st % NDT
         return *reinterpret_cast<const s16x8*>(vsrc + (st % C::NDT) * 32 * C::VT_STRIDE + 32 * (st / C::NDT));
       };
-      s16x8 Vf[2];
-      Vf[0] = vfrag(0);
+      constexpr int LV = 3;  // V^T fragments in flight (order pinned by scheduling barriers)
+      s16x8 Vf[LV];
+#pragma unroll
+      for (int i = 0; i < LV - 1; ++i) Vf[i] = vfrag(i);
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st) {
-        if (st + 1 < NSTEP) {
-          Vf[(st + 1) & 1] = vfrag(st + 1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
-        }
-        O[st % C::NDT] = mfma_f16_32x32x16(Vf[st & 1], Bp[st / C::NDT], O[st % C::NDT]);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);    // MFMA
+        if (st + LV - 1 < NSTEP) Vf[(st + LV - 1) % LV] = vfrag(st + LV - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        O[st % C::NDT] = mfma_f16_32x32x16(Vf[st % LV], Bp[st / C::NDT], O[st % C::NDT]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // does any wave need the exact-maximum pass?
