@@ -95,7 +95,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_32k")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-fused", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
