@@ -234,18 +234,53 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   for (int e = 0; e < TQ; ++e) tb[e] = (trow * C::RC + (tch ^ ((trow | 4 * e) & (C::SWZ - 1)))) * 16 + 8 * (lane & 1);
   auto tr_off = [&](int jq) { return tb[jq % TQ] + 4 * jq * C::RC * 16; };  // key quad jq: rows 4 jq + 0..3
   uint8_t* vt_dst = Vt + (wave * 64 + 16 * tg + ti) * C::VT_STRIDE;
-  auto gather = [&](int blk) {
+  // Gather of block blk.  Transfer i covers slots [64 i, 64 i + 64).  When a row holds at least
+  // 64 slots that is at most two gathered rows, (64 i) / RC and (64 i + 63) / RC: gather_rows then
+  // reads the physical rows of all this wave's transfers with one LDS read (lane 2 j / 2 j + 1:
+  // first / last row of its j-th transfer), early enough for the value to be there when
+  // gather_issue takes them by readlane.  Narrower rows look their row up per lane.
+  constexpr int DMA_PW = (C::DMA_INSTR + MLA_WAVES - 1) / MLA_WAVES;  // transfers per wave (max)
+  static_assert(2 * DMA_PW <= WAVE, "one lane pair per transfer");
+  auto gather_rows = [&](int blk) {
+    const int j = lane >> 1, i = wave + j * MLA_WAVES;
+    const int rr = (i * WAVE + (lane & 1) * (WAVE - 1)) / C::RC;
+    const int e = blk * MLA_KB + rr;
+    int32_t pr = -1;
+    if (j < DMA_PW && i < C::DMA_INSTR && e < cnt) pr = phys[e];
+    return pr >= 0 ? pr : safe_row;
+  };
+  auto gather_issue = [&](int blk, int32_t prow) {
     const uint32_t base = kbuf_lds + (uint32_t)((blk % MLA_STAGES) * C::K_BYTES);
-    for (int i = wave; i < C::DMA_INSTR; i += MLA_WAVES) {
-      const int s = i * WAVE + lane;
-      const int rr = s / C::RC;
-      const int c = (s % C::RC) ^ (rr & (C::SWZ - 1));
-      const int e = blk * MLA_KB + rr;
-      const int32_t pr = e < cnt ? phys[e] : -1;
-      const uint16_t* src = kv + (int64_t)(pr >= 0 ? pr : safe_row) * DQK + c * 8;
-      if (C::DQK_PAD == DQK || c * 8 < DQK) dma_16B(src, base + (uint32_t)(i * WAVE * 16));
+    if constexpr (C::RC < WAVE) {
+      (void)prow;
+      for (int i = wave; i < C::DMA_INSTR; i += MLA_WAVES) {
+        const int s = i * WAVE + lane;
+        const int rr = s / C::RC;
+        const int c = (s % C::RC) ^ (rr & (C::SWZ - 1));
+        const int e = blk * MLA_KB + rr;
+        const int32_t pr = e < cnt ? phys[e] : -1;
+        const uint16_t* src = kv + (int64_t)(pr >= 0 ? pr : safe_row) * DQK + c * 8;
+        if (C::DQK_PAD == DQK || c * 8 < DQK) dma_16B(src, base + (uint32_t)(i * WAVE * 16));
+      }
+      return;
+    }
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute the per-lane slot math here rather than keep it live
+#pragma unroll
+    for (int j = 0; j < DMA_PW; ++j) {
+      const int i = wave + j * MLA_WAVES;
+      if (i < C::DMA_INSTR) {  // wave-uniform
+        const int s = i * WAVE + ln;
+        const int rr = s / C::RC;
+        const int c = (s % C::RC) ^ (rr & (C::SWZ - 1));
+        const int first = (i * WAVE) / C::RC;
+        const int32_t pa = __builtin_amdgcn_readlane(prow, 2 * j), pb = __builtin_amdgcn_readlane(prow, 2 * j + 1);
+        const uint16_t* src = kv + (int64_t)(rr == first ? pa : pb) * DQK + c * 8;
+        if (C::DQK_PAD == DQK || c * 8 < DQK) dma_16B(src, base + (uint32_t)(i * WAVE * 16));
+      }
     }
   };
+  auto gather = [&](int blk) { gather_issue(blk, gather_rows(blk)); };
 
   v16f O[C::NDT];
   float mref, mlane = -INFINITY, lsum;  // mlane: this lane's running maximum (its head, its keys)
@@ -285,6 +320,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         }
       }
 
+      // row indices of the next gather, read now so that they are in registers after the barrier
+      const int32_t next_rows = gather_rows(blk + 2);
       // ---- partial S^T[key][head] over this wave's contraction half; the K fragment of step
       // ks + 1 is requested before the MFMA of step ks
       v16f sc = {};
@@ -306,7 +343,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
           dst[qd * WAVE] = (v4f){sc[4 * qd], sc[4 * qd + 1], sc[4 * qd + 2], sc[4 * qd + 3]};
       }
       __syncthreads();  // partial scores of both halves posted; V^T complete; stage blk no longer read
-      if (blk + 2 < nblk) gather(blk + 2);
+      if (blk + 2 < nblk) gather_issue(blk + 2, next_rows);
       if (!active) continue;
 
       // ---- full scores (own + partner partial) in log2 units, masked entries at -inf
