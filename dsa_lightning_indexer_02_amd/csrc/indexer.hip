@@ -14,15 +14,17 @@ namespace dsa {
 // ---------------------------------------------------------------------------------------
 // Prefill: a workgroup owns 16 consecutive query rows (the MFMA M dimension) and a range of
 // keys.  The 16 rows' FP8 queries for every head sit in LDS ([head][row][128 B + pad]); the
-// eight waves take disjoint 16-key tiles, keep NK tiles of keys in registers (MFMA B operand)
+// twelve waves take disjoint 16-key tiles, keep NK tiles of keys in registers (MFMA B operand)
 // and loop over the heads, so the head reduction happens inside each lane's accumulators
 // without any cross-lane traffic.
 // ---------------------------------------------------------------------------------------
 constexpr int IDX_ROWS = 16;
 constexpr int IDX_QROW_BYTES = 144;  // 128 B of codes + 16 B pad (bank spread)
-constexpr int IDX_PREFILL_WAVES = 8;
+constexpr int IDX_PREFILL_WAVES = 12;  // three waves per SIMD: VALU of one beside MFMAs of another
 
-template <int NK>
+// HI > 0: the head count is a compile-time constant and the head loop is fully unrolled;
+// HI == 0: any head count (plain loop).
+template <int NK, int HI>
 __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, RowMap keymap, int64_t T,
@@ -62,9 +64,8 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
 
   const bool klane_has_bytes = (g * 32) < D_I;
   const int64_t pass_keys = (int64_t)IDX_PREFILL_WAVES * NK * 16;
-  for (int64_t base = c0 + (int64_t)wave * NK * 16; base < c1; base += pass_keys) {
-    v8i B[NK];
-    float ksv[NK];
+  // key tiles of one pass (MFMA B operands) and their scales
+  auto load_keys = [&](int64_t base, v8i (&B)[NK], float (&ksv)[NK]) {
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
       const int64_t s = min(base + kt * 16 + j16, S - 1);
@@ -74,20 +75,69 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
       B[kt] = b;
       ksv[kt] = ks[row];
     }
+  };
+  for (int64_t base = c0 + (int64_t)wave * NK * 16; base < c1; base += pass_keys) {
+    v8i B[NK];
+    float ksv[NK];
+    load_keys(base, B, ksv);
     v4f acc[NK];
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) acc[kt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    for (int head = 0; head < H_I; ++head) {
-      const v8i A = *reinterpret_cast<const v8i*>(qtile + (head * IDX_ROWS + j16) * IDX_QROW_BYTES + g * 32);
-      const v4f wv = *reinterpret_cast<const v4f*>(wq + head * IDX_ROWS + 4 * g);
+    auto relu_acc = [&](const v4f& wv, const v4f (&c)[NK]) {
 #pragma unroll
-      for (int kt = 0; kt < NK; ++kt) {
-        const v4f c = mfma_fp8_16x16x128(A, B[kt], (v4f){0.f, 0.f, 0.f, 0.f});
-        acc[kt][0] = fmaf(wv[0], fmaxf(c[0], 0.f), acc[kt][0]);
-        acc[kt][1] = fmaf(wv[1], fmaxf(c[1], 0.f), acc[kt][1]);
-        acc[kt][2] = fmaf(wv[2], fmaxf(c[2], 0.f), acc[kt][2]);
-        acc[kt][3] = fmaf(wv[3], fmaxf(c[3], 0.f), acc[kt][3]);
+      for (int kt = 0; kt < NK; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[kt][r] = fmaf(wv[r], __builtin_amdgcn_fmed3f(c[kt][r], 0.f, 3.402823466e38f), acc[kt][r]);
+    };
+    auto load_a = [&](int head) {
+      return *reinterpret_cast<const v8i*>(qtile + (head * IDX_ROWS + j16) * IDX_QROW_BYTES + g * 32);
+    };
+    auto load_w = [&](int head) { return *reinterpret_cast<const v4f*>(wq + head * IDX_ROWS + 4 * g); };
+    if constexpr (HI > 0) {
+      // Software pipeline over the heads, two per iteration with static slots (last iteration
+      // peeled, so the body has no conditions): the MFMAs of head h + 1 are issued before the
+      // ReLU and weighted accumulation of head h, so the matrix core and the VALU work side by
+      // side; the order is pinned with scheduling barriers.  ReLU is one med3(c, 0, FLT_MAX)
+      // (the products are finite).
+      static_assert(HI % 2 == 0 && HI >= 2, "even head count");
+      v4f c0[NK], c1[NK];
+      v8i A0 = load_a(0), A1;
+      v4f w0 = load_w(0), w1;
+      auto mma = [&](const v8i& A, v4f (&c)[NK]) {
+#pragma unroll
+        for (int kt = 0; kt < NK; ++kt) c[kt] = mfma_fp8_16x16x128(A, B[kt], (v4f){0.f, 0.f, 0.f, 0.f});
+      };
+      mma(A0, c0);
+      for (int head = 0; head < HI - 2; head += 2) {
+        A1 = load_a(head + 1);
+        w1 = load_w(head + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(A1, c1);          // head + 1
+        relu_acc(w0, c0);     // head
+        __builtin_amdgcn_sched_barrier(0);
+        A0 = load_a(head + 2);
+        w0 = load_w(head + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(A0, c0);          // head + 2
+        relu_acc(w1, c1);     // head + 1
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      A1 = load_a(HI - 1);
+      w1 = load_w(HI - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(A1, c1);
+      relu_acc(w0, c0);
+      relu_acc(w1, c1);
+    } else {
+      for (int head = 0; head < H_I; ++head) {
+        const v8i A = load_a(head);
+        const v4f wv = load_w(head);
+        v4f c[NK];
+#pragma unroll
+        for (int kt = 0; kt < NK; ++kt) c[kt] = mfma_fp8_16x16x128(A, B[kt], (v4f){0.f, 0.f, 0.f, 0.f});
+        relu_acc(wv, c);
       }
     }
     // lane (j16, g) holds rows t0 + 4g + r for key base + 16 kt + j16
@@ -185,7 +235,7 @@ hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const floa
                                   int32_t block_shift, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
                                   int64_t q_start, float* logits, int64_t ld, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  constexpr int NK = 8;
+  constexpr int NK = 4;
   const int64_t tiles = (T + IDX_ROWS - 1) / IDX_ROWS;
   const int64_t n_last = std::min<int64_t>(S, q_start + T);
   // split keys only when the tiles alone cannot fill the chip
@@ -199,16 +249,15 @@ hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const floa
   const int64_t chunks = (n_last + key_chunk - 1) / key_chunk;
   dim3 grid((unsigned)chunks, (unsigned)tiles);
   const size_t smem = indexer_prefill_smem(H_I);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)indexer_prefill_kernel<NK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  auto kernel = H_I == 64 ? indexer_prefill_kernel<NK, 64> : indexer_prefill_kernel<NK, 0>;
+  static bool attr_set[2] = {false, false};
+  if (!attr_set[H_I == 64]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[H_I == 64] = true;
   }
-  hipLaunchKernelGGL(indexer_prefill_kernel<NK>, grid, dim3(IDX_PREFILL_WAVES * WAVE), smem, stream,
-                     q8, qs, w, k8, ks, RowMap{table, block_shift}, T, S, H_I, D_I, q_start, logits,
-                     ld, key_chunk);
+  hipLaunchKernelGGL(kernel, grid, dim3(IDX_PREFILL_WAVES * WAVE), smem, stream, q8, qs, w, k8, ks,
+                     RowMap{table, block_shift}, T, S, H_I, D_I, q_start, logits, ld, key_chunk);
   return hipGetLastError();
 }
 
