@@ -1,13 +1,16 @@
 """Throughput of the DSA hot path (lightning indexer -> top-2048 -> sparse MLA) on one MI355X.
 
-One step = one pass of the whole path over the L = 32768 causal prefill batch (the headline
-workload): dsa_indexer_logits, dsa_topk and dsa_sparse_mla_fwd back to back on one stream, with
-HIP events between the stages so every kernel's duration comes from the timed steps themselves.
-The fused entry point (dsa_prefill_paged, the same kernels behind one call) is timed beside it.
-Inputs are generated on the host from the seeded recipe, copied to HBM before timing, and stay
-resident; nothing is generated, quantized or copied inside the timed region.
+Default: one step = one pass of the whole path over the L = 32768 causal prefill batch (the
+headline workload): dsa_indexer_logits, dsa_topk and dsa_sparse_mla_fwd back to back on one
+stream, with HIP events between the stages so every kernel's duration comes from the timed steps
+themselves.  The fused entry point (dsa_prefill_paged, the same kernels behind one call) is timed
+beside it.  Inputs are generated on the host from the seeded recipe, copied to HBM before timing,
+and stay resident; nothing is generated, quantized or copied inside the timed region.  Prints
+one JSON line.
 
-Prints one JSON line.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
+``--workload`` selects another configuration (tiny, prefill_4k, chunked_131k, decode_64; decode
+times the fused paged decode call against its HBM roofline), and ``--all-configs`` prints one
+line per configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -28,17 +31,25 @@ PEAK_FP8 = 5.0e15       # dense fp8 MFMA
 PEAK_HBM = 8.0e12       # HBM3E bytes/s
 PMC_FILE = os.path.join(ROOT, "profiles", "sparse_mla_prefill_32k_pmc.json")
 MLA_SOURCE = os.path.join(ROOT, "dsa_lightning_indexer_02_amd", "csrc", "sparse_mla.hip")
+HEADLINE = "prefill_32k"
+METRIC = "query tokens/s (indexer+top-2048+sparse MLA) at L=32K"
 
 
-def work_model(wl):
-    """Algorithmic work of one pass (masked pairs and skipped dense work excluded)."""
-    t = np.arange(wl.T, dtype=np.int64)
-    n = np.minimum(wl.S, wl.q_start + t + 1)
+def work_model(wl, n=None):
+    """Algorithmic work of one pass (masked pairs and skipped dense work excluded).  ``n``: the
+    visible key count of every query row (default: the prefill causal counts)."""
+    if n is None:
+        t = np.arange(wl.T, dtype=np.int64)
+        n = np.minimum(wl.S, wl.q_start + t + 1)
+    n = np.asarray(n, dtype=np.int64)
     sel = np.minimum(n, wl.topk)
+    T = len(n)
     return {
         "indexer_flop": float(2 * wl.H_I * wl.D_I * n.sum()),
-        "topk_bytes": float(4 * n.sum() + 4 * wl.T * wl.topk),
+        "indexer_bytes": float(n.sum() * (wl.D_I + 4) + T * wl.H_I * (wl.D_I + 8) + 4 * n.sum()),
+        "topk_bytes": float(4 * n.sum() + 4 * T * wl.topk),
         "mla_flop": float(2 * wl.H * (wl.D_qk + wl.D_v) * sel.sum()),
+        "mla_bytes": float(sel.sum() * wl.D_qk * 2 + T * wl.H * (wl.D_qk + wl.D_v) * 2 + T * wl.topk * 4),
         "visible_pairs": int(n.sum()),
         "selected_rows": int(sel.sum()),
     }
@@ -50,8 +61,8 @@ def source_hash(path: str) -> str:
 
 
 def traffic_from_profile():
-    """HBM bytes per sparse-MLA launch from the committed rocprofv3 counter runs, if they were taken
-    on the current kernel source; None otherwise."""
+    """HBM bytes per sparse-MLA launch at L = 32K from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; None otherwise."""
     if not os.path.exists(PMC_FILE):
         return None
     with open(PMC_FILE) as f:
@@ -61,12 +72,18 @@ def traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
+def percentiles(ms):
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"p10": float(np.percentile(ms, 10)), "p50": float(np.percentile(ms, 50)),
+            "p90": float(np.percentile(ms, 90))}
+
+
 def cpu_baseline(wl, n_rows: int, threads: int):
     """The oracle (as it stands) on a uniform sample of query rows, scaled to the whole workload by the
     exact per-stage work model."""
     import oracle
     from dsa_inputs import prefill_inputs
-    rows = np.unique(np.linspace(0, wl.T - 1, n_rows).round().astype(np.int64))
+    rows = np.unique(np.linspace(0, wl.T - 1, min(n_rows, wl.T)).round().astype(np.int64))
     inp = prefill_inputs(wl, rows=rows)
     pos = inp.pos
     n = np.minimum(wl.S, pos + 1)
@@ -81,50 +98,31 @@ def cpu_baseline(wl, n_rows: int, threads: int):
     n_all = np.minimum(wl.S, wl.q_start + tn + 1)
     est = ((t1 - t0) * n_all.sum() / n.sum() + (t2 - t1) * n_all.sum() / n.sum()
            + (t3 - t2) * np.minimum(n_all, wl.topk).sum() / np.minimum(n, wl.topk).sum())
+    sample = ("all %d query rows" % wl.T if len(rows) == wl.T else
+              "%d query rows evenly spaced over the %d-token batch (full indexer, top-k and MLA per row), "
+              "scaled per stage by visible / selected key counts" % (len(rows), wl.T))
     return {
         "value": wl.T / est, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
-        "sample": "%d query rows evenly spaced over the %d-token prefill (full indexer, top-k and MLA per row), "
-                  "%.1f s measured, scaled per stage by visible / selected key counts" % (len(rows), wl.T, t3 - t0),
-        "sample_seconds": t3 - t0,
+        "sample": sample + "; %.1f s measured" % (t3 - t0), "sample_seconds": t3 - t0,
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill_32k")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
-    ap.add_argument("--skip-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-fused", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after timing, copy 1 GiB device-to-device (counter scale reference)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
+def put(a, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
+
+def run_prefill(wl, args, dev):
     import torch
     import dsa_lightning_indexer_02_amd as dsa
-    from dsa_inputs import get, prefill_inputs
-
-    wl = get(args.workload)
-    if wl.kind != "prefill":
-        sys.exit("bench.py times prefill workloads")
-    dev = torch.device("cuda:0")
-    dsa.load()
-
-    def put(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+    from dsa_inputs import prefill_inputs
 
     print("generating %s inputs" % wl.name, file=sys.stderr, flush=True)
     inp = prefill_inputs(wl)
-    q8, qs, w, k8, ks = put(inp.q8), put(inp.qs), put(inp.w), put(inp.k8), put(inp.ks)
-    q = put(inp.q).view(torch.bfloat16)
-    kv = put(inp.kv).view(torch.bfloat16)
+    q8, qs, w, k8, ks = (put(x, dev) for x in (inp.q8, inp.qs, inp.w, inp.k8, inp.ks))
+    q = put(inp.q, dev).view(torch.bfloat16)
+    kv = put(inp.kv, dev).view(torch.bfloat16)
     del inp
     S, T = wl.S, wl.T
     ld = dsa.ld_for(S)
@@ -161,7 +159,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]).mean(axis=0)
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    stage_ms = per.mean(axis=0)
 
     fused_ms = None
     if not args.skip_fused:
@@ -191,53 +190,161 @@ def main():
         del src, dst
 
     wm = work_model(wl)
-    mla_s = stage_ms[2] / 1e3
-    roof = {
-        "kernel": "sparse_mla_kernel<576,512>",
-        "bound": "mfma",
-        "achieved": wm["mla_flop"] / mla_s / 1e12,
-        "peak": PEAK_BF16 / 1e12,
-        "unit": "TFLOP/s",
-        "frac": wm["mla_flop"] / mla_s / PEAK_BF16,
-        "traffic": traffic_from_profile(),
-        "avg_launch_ms": float(stage_ms[2]),
-        "algorithmic_flop_per_launch": wm["mla_flop"],
-    }
     stages = {
         "indexer": {"ms": float(stage_ms[0]), "bound": "mfma", "achieved_tflops": wm["indexer_flop"] / stage_ms[0] / 1e9,
                     "frac": wm["indexer_flop"] / (stage_ms[0] / 1e3) / PEAK_FP8},
         "topk": {"ms": float(stage_ms[1]), "bound": "hbm", "achieved_gbs": wm["topk_bytes"] / stage_ms[1] / 1e6,
                  "frac": wm["topk_bytes"] / (stage_ms[1] / 1e3) / PEAK_HBM},
-        "sparse_mla": {"ms": float(stage_ms[2]), "bound": "mfma", "achieved_tflops": roof["achieved"],
-                       "frac": roof["frac"]},
+        "sparse_mla": {"ms": float(stage_ms[2]), "bound": "mfma", "achieved_tflops": wm["mla_flop"] / stage_ms[2] / 1e9,
+                       "frac": wm["mla_flop"] / (stage_ms[2] / 1e3) / PEAK_BF16},
     }
+    # dominant kernel: the stage that takes longest
+    dom = max(stages, key=lambda k: stages[k]["ms"])
+    if dom == "sparse_mla":
+        roof = {"kernel": "sparse_mla_kernel<%d,%d>" % (wl.D_qk, wl.D_v), "bound": "mfma",
+                "achieved": wm["mla_flop"] / (stage_ms[2] / 1e3) / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "traffic": traffic_from_profile() if wl.name == HEADLINE else None,
+                "algorithmic_flop_per_launch": wm["mla_flop"]}
+    elif dom == "indexer":
+        roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma",
+                "achieved": wm["indexer_flop"] / (stage_ms[0] / 1e3) / 1e12, "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s",
+                "traffic": None, "algorithmic_flop_per_launch": wm["indexer_flop"]}
+    else:
+        roof = {"kernel": "topk_chunk_kernel", "bound": "hbm",
+                "achieved": wm["topk_bytes"] / (stage_ms[1] / 1e3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "traffic": None, "algorithmic_bytes_per_launch": wm["topk_bytes"]}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["avg_launch_ms"] = float(stages[dom]["ms"])
+    step_ms = per.sum(axis=1)
+    return {
+        "value": T / (ms_step / 1e3), "ms_per_step": ms_step, "step_ms_events": percentiles(step_ms),
+        "roofline": roof, "stages": stages, "fused_ms_per_step": fused_ms,
+        "config": {"workload": wl.name, "T": T, "S": S, "q_start": wl.q_start, "H_I": wl.H_I, "D_I": wl.D_I,
+                   "topk": wl.topk, "H": wl.H, "D_qk": wl.D_qk, "D_v": wl.D_v, "parallelism": "single GPU"},
+    }
+
+
+def run_decode(wl, args, dev):
+    """Fused paged decode (dsa_decode_paged): one new token for each of the 64 sequences."""
+    import torch
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import decode_inputs
+
+    print("generating %s inputs" % wl.name, file=sys.stderr, flush=True)
+    inp = decode_inputs(wl)
+    cache = dsa.PagedKV(put(inp.k8_pool, dev), put(inp.ks_pool, dev), put(inp.kv_pool, dev).view(torch.bfloat16),
+                        put(inp.block_table, dev), put(inp.seq_lens, dev))
+    q8, qs, w = put(inp.q8, dev), put(inp.qs, dev), put(inp.w, dev)
+    q = put(inp.q, dev).view(torch.bfloat16)
+    lens = inp.seq_lens.astype(np.int64)
+    max_len = int(lens.max())
+    del inp
+    B = len(lens)
+    dims = dsa.make_dims(wl.H_I, wl.D_I, wl.H, wl.D_qk, wl.D_v, wl.topk, wl.sm_scale)
+    ws = torch.empty(dsa.decode_workspace_size(dims, B, max_len), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush_mall else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        dsa.dsa_decode_paged(cache, max_len, dims, q8, qs, w, q, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()  # evict the previous step's pool lines from the MALL (not timed)
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    n = lens
+    sel = np.minimum(n, wl.topk)
+    # HBM bytes any decode must move: the FP8 keys and scales of every visible position, the latent
+    # rows of the selected entries, queries, head weights and outputs (the logits kept between the
+    # indexer and the top-k, and the split-K partials, are this design's own and are not counted)
+    alg = float(n.sum() * (wl.D_I + 4) + sel.sum() * wl.D_qk * 2 + B * wl.H_I * (wl.D_I + 8)
+                + B * wl.H * (wl.D_qk + wl.D_v) * 2 + B * wl.H * 4)
+    med = float(np.median(ms))
+    roof = {"kernel": "dsa_decode_paged (indexer_decode + top-k + split-K MLA + combine)", "bound": "hbm",
+            "achieved": alg / (med / 1e3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s", "traffic": None,
+            "algorithmic_bytes_per_launch": alg, "avg_launch_ms": float(ms.mean())}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return {
+        "value": B / (med / 1e3), "ms_per_step": med, "step_ms_events": percentiles(ms), "roofline": roof,
+        "stages": None, "fused_ms_per_step": med, "mall_flush": bool(args.flush_mall),
+        "config": {"workload": wl.name, "B": B, "seq_len_min": int(lens.min()), "seq_len_max": max_len,
+                   "seq_len_mean": float(lens.mean()), "topk": wl.topk, "H_I": wl.H_I, "D_I": wl.D_I, "H": wl.H,
+                   "D_qk": wl.D_qk, "D_v": wl.D_v, "block_size": wl.block_size, "parallelism": "single GPU"},
+    }
+
+
+def run_one(name, args, dev, with_cpu: bool):
+    from dsa_inputs import get
+    wl = get(name)
+    res = run_decode(wl, args, dev) if wl.kind == "decode" else run_prefill(wl, args, dev)
     cpu = None
-    if not args.skip_cpu_baseline:
+    if with_cpu and wl.kind == "prefill":
         print("cpu baseline (oracle)", file=sys.stderr, flush=True)
         threads = max(1, min(16, os.cpu_count() or 1))
         cpu = cpu_baseline(wl, args.cpu_rows, threads)
-
-    res = {
-        "metric": "query tokens/s (indexer+top-2048+sparse MLA) at L=32K",
-        "value": T / (ms_step / 1e3),
+    line = {
+        "metric": METRIC if name == HEADLINE else "query tokens/s (%s)" % name,
+        "value": res["value"],
         "unit": "query tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8-e4m3 indexer, bf16/fp16 attention",
         "data": "synthetic (seeded PCG64 recipe, FP8 per-row absmax codes, bf16 N(0,1))",
-        "config": {"workload": wl.name, "T": T, "S": S, "q_start": wl.q_start, "H_I": wl.H_I, "D_I": wl.D_I,
-                   "topk": wl.topk, "H": wl.H, "D_qk": wl.D_qk, "D_v": wl.D_v, "parallelism": "single GPU"},
-        "roofline": roof,
-        "stages": stages,
-        "fused_ms_per_step": fused_ms,
+        "config": res["config"],
+        "roofline": res["roofline"],
+        "stages": res["stages"],
+        "step_ms_events": res["step_ms_events"],
+        "fused_ms_per_step": res["fused_ms_per_step"],
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res))
+    if "mall_flush" in res:
+        line["mall_flush"] = res["mall_flush"]
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--all-configs", action="store_true", help="one line per configuration (no CPU baseline)")
+    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-fused", action="store_true")
+    ap.add_argument("--flush-mall", action="store_true", help="decode: overwrite 512 MiB between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, copy 1 GiB device-to-device (counter scale reference)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dsa_lightning_indexer_02_amd as dsa
+    dev = torch.device("cuda:0")
+    dsa.load()
+    if args.all_configs:
+        for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64"]:
+            print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
+            torch.cuda.empty_cache()
+        return
+    print(json.dumps(run_one(args.workload, args, dev, with_cpu=not args.skip_cpu_baseline)))
 
 
 if __name__ == "__main__":

@@ -74,8 +74,12 @@ dsa_status_t check_topk(int64_t S, int32_t k) {
   return DSA_OK;
 }
 
+// Index-list splits per decode row: enough (B x nsplit) sparse-MLA workgroups for one per compute
+// unit of an MI355X (256), each over at least 64 indices.  More splits than that only add fp32
+// partial traffic (written by the attention, re-read by the combine).
 int32_t decode_splits(int32_t B, int32_t k) {
-  int32_t want = (512 + B - 1) / B;
+  constexpr int32_t kWorkgroups = 256;
+  int32_t want = (kWorkgroups + B - 1) / B;
   int32_t cap = std::max(1, k / 64);
   return std::max(1, std::min(want, cap));
 }
@@ -325,6 +329,7 @@ dsa_status_t dsa_decode_paged(const dsa_paged_cache_t* c, int32_t B, int64_t max
   dsa_status_t s = check_dims(d);
   if (s != DSA_OK) return s;
   REQUIRE(B >= 0 && max_seq_len >= 0, DSA_ERR_INVALID_ARGUMENT, "negative B or max_seq_len");
+  REQUIRE(B <= 16384, DSA_ERR_UNSUPPORTED, "B=%d sequences above 16384 per decode call", B);
   if (B == 0) return ok();
   REQUIRE(max_seq_len >= 1, DSA_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 1");
   s = check_cache(c, max_seq_len, B);

@@ -155,73 +155,256 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
 
 // ---------------------------------------------------------------------------------------
 // Decode: one query row per sequence.  The 64 (padded to a multiple of 16) heads are the MFMA
-// M dimension, held in registers; the waves stream disjoint 64-key groups of the sequence's
-// keys through its block table.  The head sum is a lane-local accumulation followed by a
-// reduction over the four lane groups.
+// M dimension, held in registers; a wave scores 64 keys of one sequence at a time (four 16-key
+// tiles), and the head sum is a lane-local accumulation followed by a reduction over the four
+// lane groups.
+//
+// The work is a stream of FP8 keys whose amount per sequence is only known on the device, so
+// the kernel balances it itself: every workgroup forms the prefix sum of the sequences' 64-key
+// group counts in LDS, and each wave of the (resident-sized) grid takes an equal contiguous
+// share of the flat list of groups.  A wave resolves up to 64 of its groups at a time, one per
+// lane (sequence, first key, and, when a block holds at least 64 rows so that a group never
+// straddles two blocks, the group's physical row from the block table), and picks them up with
+// readlane; it issues the loads of its next group before scoring the current one.  With blocks
+// of fewer than 64 rows each lane looks its rows up inside the group load.
 // ---------------------------------------------------------------------------------------
 constexpr int IDX_DECODE_WAVES = 4;
+constexpr int IDX_DECODE_THREADS = IDX_DECODE_WAVES * WAVE;
+constexpr int IDX_DECODE_MAX_B = 16384;  // sequences per call (LDS prefix table)
+#ifndef IDX_DECODE_DEPTH
+#define IDX_DECODE_DEPTH 3                 // 64-key groups in flight per wave
+#endif
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int j) {
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, j);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), j);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ int64_t shfl_up64(int64_t v, int o) {
+  const int lo = __shfl_up((int)(uint32_t)v, o);
+  const int hi = __shfl_up((int)(uint32_t)((uint64_t)v >> 32), o);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
 
 template <int NHT>
-__global__ __launch_bounds__(IDX_DECODE_WAVES * WAVE) void indexer_decode_kernel(
+__global__ __launch_bounds__(IDX_DECODE_THREADS, 2) void indexer_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int32_t* __restrict__ table,
-    int64_t max_blocks, int32_t block_shift, const int32_t* __restrict__ seq_lens, int32_t H_I,
-    int32_t D_I, int64_t max_len, float* __restrict__ logits, int64_t ld, int64_t key_chunk) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t max_blocks, int32_t block_shift, const int32_t* __restrict__ seq_lens, int32_t B,
+    int32_t H_I, int32_t D_I, int64_t max_len, float* __restrict__ logits, int64_t ld) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int64_t* gstart = reinterpret_cast<int64_t*>(smem);                      // [B + 1] group prefix
+  int32_t* nlen = reinterpret_cast<int32_t*>(smem + (size_t)(B + 1) * 8);  // [B] visible keys
+  __shared__ int64_t wave_tot[IDX_DECODE_WAVES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j16 = lane & 15, g = lane >> 4;
-  const int64_t b = blockIdx.y;
-  const int64_t n = min((int64_t)max(seq_lens[b], 0), max_len);
-  const int64_t c0 = (int64_t)blockIdx.x * key_chunk;
-  if (c0 >= n) return;
-  const int64_t c1 = min(n, c0 + key_chunk);
-  const RowMap map{table ? table + b * max_blocks : nullptr, block_shift};
+
+  // ---- prefix sum of per-sequence group counts (each thread a contiguous slice of sequences)
+  const int per = (B + IDX_DECODE_THREADS - 1) / IDX_DECODE_THREADS;
+  const int sb0 = tid * per;
+  int64_t mine = 0;
+  for (int i = 0; i < per; ++i) {
+    const int bb = sb0 + i;
+    if (bb < B) {
+      const int64_t n = min((int64_t)max(seq_lens[bb], 0), max_len);
+      nlen[bb] = (int32_t)n;
+      mine += (n + 63) >> 6;
+    }
+  }
+  int64_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int64_t t = shfl_up64(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == WAVE - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int64_t run = incl - mine;
+  for (int v = 0; v < wave; ++v) run += wave_tot[v];
+  for (int i = 0; i < per; ++i) {
+    const int bb = sb0 + i;
+    if (bb < B) {
+      gstart[bb] = run;
+      run += ((int64_t)nlen[bb] + 63) >> 6;
+    }
+  }
+  if (tid == 0) {
+    int64_t tot = 0;
+    for (int v = 0; v < IDX_DECODE_WAVES; ++v) tot += wave_tot[v];
+    gstart[B] = tot;
+  }
+  __syncthreads();
+
+  // ---- this wave's share of the flat group list
+  const int64_t total = uniform64(gstart[B]);
+  const int64_t nw = (int64_t)gridDim.x * IDX_DECODE_WAVES;
+  const int64_t wg = (int64_t)blockIdx.x * IDX_DECODE_WAVES + wave;
+  const int64_t f_beg = total * wg / nw, f_end = total * (wg + 1) / nw;
+  if (f_beg >= f_end) return;
+
+  // lane i of the window describes flat group ws + i
+  int64_t ws = f_beg;
+  int32_t wb = 0, wn = 0;
+  int64_t wbase = 0, wrow = 0;
+  auto window = [&](int64_t start) {
+    ws = start;
+    const int64_t f = start + lane;
+    wb = 0;
+    wn = 0;
+    wbase = 0;
+    wrow = 0;
+    if (f < f_end) {
+      int lo = 0, hi = B;  // gstart[lo] <= f < gstart[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (gstart[mid] <= f) lo = mid; else hi = mid;
+      }
+      wb = lo;
+      wn = nlen[lo];
+      wbase = (f - gstart[lo]) * 64;
+      wrow = wbase;
+      if (table && block_shift >= 6)
+        wrow = ((int64_t)table[(int64_t)lo * max_blocks + (wbase >> block_shift)] << block_shift) |
+               (wbase & ((1 << block_shift) - 1));
+    }
+  };
+
+  struct Grp {
+    int32_t b, n;
+    int64_t base, row0;
+  };
+  auto get = [&](int64_t f) {
+    const int j = (int)(f - ws);
+    return Grp{__builtin_amdgcn_readlane(wb, j), __builtin_amdgcn_readlane(wn, j), readlane64(wbase, j),
+               readlane64(wrow, j)};
+  };
 
   v8i A[NHT];
   float wv[NHT][4];
   const bool has_bytes = (g * 32) < D_I;
+  const int kofs = has_bytes ? g * 32 : D_I - 32;
+  auto load_query = [&](int64_t b) {
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const int head = ht * 16 + j16;
-    v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (head < H_I && has_bytes) a = *reinterpret_cast<const v8i*>(q8 + ((b * H_I + head) * D_I) + g * 32);
-    A[ht] = a;
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int head = ht * 16 + j16;
+      v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (head < H_I && has_bytes) a = *reinterpret_cast<const v8i*>(q8 + ((b * H_I + head) * D_I) + g * 32);
+      A[ht] = a;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hr = ht * 16 + 4 * g + r;
-      wv[ht][r] = hr < H_I ? w[b * H_I + hr] * qs[b * H_I + hr] : 0.0f;
+      for (int r = 0; r < 4; ++r) {
+        const int hr = ht * 16 + 4 * g + r;
+        wv[ht][r] = hr < H_I ? w[b * H_I + hr] * qs[b * H_I + hr] : 0.0f;
+      }
     }
-  }
-
-  for (int64_t base = c0 + (int64_t)wave * 64; base < c1; base += IDX_DECODE_WAVES * 64) {
-    v8i B[4];
-    float ksv[4];
+    // Complete these loads here: left pending past the branch that calls this, they would make
+    // the scoring after it wait for every load in flight, the next group's prefetch included.
+    // (one dword of each 16-byte load; a whole-vector operand would not pass the host compile)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t s = min(base + q * 16 + j16, n - 1);
-      const int64_t row = map(s);
-      v8i bb = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (has_bytes) bb = *reinterpret_cast<const v8i*>(k8 + row * D_I + g * 32);
-      B[q] = bb;
-      ksv[q] = ks[row];
+    for (int ht = 0; ht < NHT; ++ht) asm volatile("" ::"v"(A[ht][0]), "v"(A[ht][4]));
+  };
+
+  // keys base .. base+63 of the group (clamped to its last visible key) into registers, and the
+  // scale of the one key this lane stores (key base + 16 g + j16)
+  auto load = [&](const Grp& gr, v8i (&Bk)[4], float& kme) {
+    int64_t row[4], rme;
+    const int64_t sme = min(gr.base + g * 16 + j16, (int64_t)gr.n - 1);
+    if (!table || block_shift >= 6) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) row[q] = gr.row0 + (min(gr.base + q * 16 + j16, (int64_t)gr.n - 1) - gr.base);
+      rme = gr.row0 + (sme - gr.base);
+    } else {
+      const int32_t* tb = table + (int64_t)gr.b * max_blocks;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t s = min(gr.base + q * 16 + j16, (int64_t)gr.n - 1);
+        row[q] = ((int64_t)tb[s >> block_shift] << block_shift) | (s & ((1 << block_shift) - 1));
+      }
+      rme = ((int64_t)tb[sme >> block_shift] << block_shift) | (sme & ((1 << block_shift) - 1));
+    }
+    // Every lane loads, so no per-lane branch splits the group's loads: lanes whose k-range lies
+    // past D_I re-read the row's last 32 bytes (finite codes of the same key), which meet zero
+    // query bytes in the MFMA.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Bk[q] = *reinterpret_cast<const v8i*>(k8 + row[q] * D_I + kofs);
+    kme = ks[rme];
+  };
+
+  int32_t cur_b = -1;
+  auto score = [&](const Grp& gr, const v8i (&Bk)[4], float kme) {
+    if (gr.b != cur_b) {
+      load_query(gr.b);
+      cur_b = gr.b;
     }
     float res[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      v4f c[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) c[ht] = mfma_fp8_16x16x128(A[ht], Bk[q], (v4f){0.f, 0.f, 0.f, 0.f});
       float acc = 0.f;
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        const v4f c = mfma_fp8_16x16x128(A[ht], B[q], (v4f){0.f, 0.f, 0.f, 0.f});
-        acc = fmaf(wv[ht][0], fmaxf(c[0], 0.f), acc);
-        acc = fmaf(wv[ht][1], fmaxf(c[1], 0.f), acc);
-        acc = fmaf(wv[ht][2], fmaxf(c[2], 0.f), acc);
-        acc = fmaf(wv[ht][3], fmaxf(c[3], 0.f), acc);
-      }
-      res[q] = wave_sum_xor16_32(acc) * ksv[q];
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc = fmaf(wv[ht][r], __builtin_amdgcn_fmed3f(c[ht][r], 0.f, 3.402823466e38f), acc);
+      res[q] = wave_sum_xor16_32(acc);
+      // computed here, not sunk into the lane-group select below (whose divergent branches
+      // would otherwise wait for every load in flight)
+      asm volatile("" : "+v"(res[q]));
     }
     // lane group g stores tile g: 64 consecutive keys per store
-    const float v = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
-    const int64_t s = base + g * 16 + j16;
-    if (s < c1) logits[b * ld + s] = v;
+    float v = (g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3]) * kme;
+    asm volatile("" : "+v"(v));  // scaled before, not inside, the store's branch
+    const int64_t s = gr.base + g * 16 + j16;
+    if (s < gr.n) logits[(int64_t)gr.b * ld + s] = v;
+  };
+
+  // next group's descriptor, refilling the window when it runs out
+  auto advance = [&](int64_t f) {
+    if (f - ws >= WAVE) window(f);
+    return get(f);
+  };
+
+  // IDX_DECODE_DEPTH groups in flight per wave, in rotating register sets (the rotation is
+  // unrolled so every set has fixed registers).  The loads of group f + DEPTH are issued
+  // unconditionally before group f is scored (past the wave's last group they re-read the
+  // current one, which is cache-hot): a load under a branch would leave the compiler's wait
+  // counts for the joined paths at those of the path without it, i.e. waiting for the prefetch.
+  constexpr int NB = IDX_DECODE_DEPTH + 1;
+  v8i Bk[NB][4];
+  float km[NB];
+  Grp gq[NB];
+  window(f_beg);
+  gq[0] = get(f_beg);
+#pragma unroll
+  for (int d = 1; d < IDX_DECODE_DEPTH; ++d) gq[d] = f_beg + d < f_end ? advance(f_beg + d) : gq[d - 1];
+#pragma unroll
+  for (int d = 0; d < IDX_DECODE_DEPTH; ++d) load(gq[d], Bk[d], km[d]);
+  for (int64_t f = f_beg;;) {
+    bool done = false;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      constexpr int D = IDX_DECODE_DEPTH;
+      const int ls = (r + D) % NB;
+      gq[ls] = f + D < f_end ? advance(f + D) : gq[r];
+      load(gq[ls], Bk[ls], km[ls]);
+      score(gq[r], Bk[r], km[r]);
+      if (++f >= f_end) {
+        done = true;
+        break;
+      }
+    }
+    if (done) break;
   }
 }
 
@@ -267,18 +450,24 @@ hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float
                                  int32_t B, int64_t max_len, int32_t H_I, int32_t D_I, float* logits,
                                  int64_t ld, hipStream_t stream) {
   if (B <= 0) return hipSuccess;
-  const int64_t key_chunk = 4096;
-  dim3 grid((unsigned)((max_len + key_chunk - 1) / key_chunk), (unsigned)B);
+  if (B > IDX_DECODE_MAX_B) return hipErrorInvalidValue;
   const int nht = (H_I + 15) / 16;
-  if (nht <= 1)
-    hipLaunchKernelGGL(indexer_decode_kernel<1>, grid, dim3(IDX_DECODE_WAVES * WAVE), 0, stream, q8, qs,
-                       w, k8, ks, table, max_blocks, block_shift, seq_lens, H_I, D_I, max_len, logits, ld, key_chunk);
-  else if (nht <= 2)
-    hipLaunchKernelGGL(indexer_decode_kernel<2>, grid, dim3(IDX_DECODE_WAVES * WAVE), 0, stream, q8, qs,
-                       w, k8, ks, table, max_blocks, block_shift, seq_lens, H_I, D_I, max_len, logits, ld, key_chunk);
-  else
-    hipLaunchKernelGGL(indexer_decode_kernel<4>, grid, dim3(IDX_DECODE_WAVES * WAVE), 0, stream, q8, qs,
-                       w, k8, ks, table, max_blocks, block_shift, seq_lens, H_I, D_I, max_len, logits, ld, key_chunk);
+  auto kernel = nht <= 1 ? indexer_decode_kernel<1> : nht <= 2 ? indexer_decode_kernel<2> : indexer_decode_kernel<4>;
+  const size_t smem = (size_t)(B + 1) * 8 + (size_t)B * 4;
+  // a grid of exactly the resident workgroups: the waves split the work evenly among themselves
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int ncu = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, IDX_DECODE_THREADS, smem);
+  if (e != hipSuccess) return e;
+  const int64_t groups_max = (int64_t)B * ((max_len + 63) / 64);
+  const int64_t need = (groups_max + IDX_DECODE_WAVES - 1) / IDX_DECODE_WAVES;
+  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::max(per_cu, 1) * ncu, need));
+  hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(IDX_DECODE_THREADS), smem, stream, q8, qs, w, k8, ks,
+                     table, max_blocks, block_shift, seq_lens, B, H_I, D_I, max_len, logits, ld);
   return hipGetLastError();
 }
 

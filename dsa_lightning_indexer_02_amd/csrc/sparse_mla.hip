@@ -444,36 +444,47 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 }
 
 // Re-reduction of split partials in fp32: out = sum_s w_s out_s / sum_s w_s, w_s = exp(lse_s - max).
+// One workgroup per (row, group of heads); each thread owns four consecutive output columns of
+// one head, so the partial rows stream with 16-byte loads from many workgroups at once.
+constexpr int COMBINE_THREADS = 256;
+
 template <int DV>
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_out,
-                                                          const float* __restrict__ part_lse, int32_t nsplit,
-                                                          int32_t H, uint16_t* __restrict__ out,
-                                                          float* __restrict__ out_f32, float* __restrict__ lse) {
+__global__ __launch_bounds__(COMBINE_THREADS) void mla_combine_kernel(const float* __restrict__ part_out,
+                                                                      const float* __restrict__ part_lse,
+                                                                      int32_t nsplit, int32_t H,
+                                                                      uint16_t* __restrict__ out,
+                                                                      float* __restrict__ out_f32,
+                                                                      float* __restrict__ lse) {
+  constexpr int TPH = DV / 4;                  // threads per head
+  constexpr int HPB = COMBINE_THREADS / TPH;   // heads per workgroup
   const int64_t r = blockIdx.x;
-  for (int h = threadIdx.x / (DV / 4); h < H; h += 256 / (DV / 4)) {
-    const int d = (threadIdx.x % (DV / 4)) * 4;
-    float m = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[(r * nsplit + s) * (int64_t)H + h]);
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (m != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float ls = part_lse[(r * nsplit + s) * (int64_t)H + h];
-        const float wgt = ls == -INFINITY ? 0.f : expf(ls - m);
-        wsum += wgt;
-        const v4f v = *reinterpret_cast<const v4f*>(part_out + ((r * nsplit + s) * (int64_t)H + h) * DV + d);
-        acc += wgt * v;
-      }
+  const int h = blockIdx.y * HPB + (int)threadIdx.x / TPH;
+  if (h >= H) return;
+  const int d = ((int)threadIdx.x % TPH) * 4;
+  const float* pl = part_lse + r * nsplit * (int64_t)H + h;           // split s at pl[s * H]
+  const float* po = part_out + (r * nsplit * (int64_t)H + h) * DV + d;  // split s at po[s * H * DV]
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, pl[(int64_t)s * H]);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) {
+      const float ls = pl[(int64_t)s * H];
+      const float wgt = ls == -INFINITY ? 0.f : expf(ls - m);
+      wsum += wgt;
+      const v4f v = *reinterpret_cast<const v4f*>(po + (int64_t)s * H * DV);
+      acc += wgt * v;
     }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    const v4f o = acc * inv;
-    s16x4 ob;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) ob[rr] = (short)f32_to_bf16(o[rr]);
-    *reinterpret_cast<s16x4*>(out + (r * H + h) * (int64_t)DV + d) = ob;
-    if (out_f32) *reinterpret_cast<v4f*>(out_f32 + (r * H + h) * (int64_t)DV + d) = o;
-    if (d == 0 && lse) lse[r * H + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
   }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  const v4f o = acc * inv;
+  s16x4 ob;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) ob[rr] = (short)f32_to_bf16(o[rr]);
+  *reinterpret_cast<s16x4*>(out + (r * H + h) * (int64_t)DV + d) = ob;
+  if (out_f32) *reinterpret_cast<v4f*>(out_f32 + (r * H + h) * (int64_t)DV + d) = o;
+  if (d == 0 && lse) lse[r * H + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -497,8 +508,10 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
                      a.part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel<DV>, dim3((unsigned)a.R), dim3(256), 0, stream, a.part_out,
-                     a.part_lse, nsplit, a.H, a.out, a.out_f32, a.lse);
+  constexpr int HPB = COMBINE_THREADS / (DV / 4);
+  hipLaunchKernelGGL(mla_combine_kernel<DV>, dim3((unsigned)a.R, (unsigned)((a.H + HPB - 1) / HPB)),
+                     dim3(COMBINE_THREADS), 0, stream, a.part_out, a.part_lse, nsplit, a.H, a.out, a.out_f32,
+                     a.lse);
   return hipGetLastError();
 }
 

@@ -145,7 +145,7 @@ dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t *c, int32_t seq, const ds
  * keys (max_seq_len >= every seq_lens[b], used for grid and workspace sizing).
  * q8 [B][H_I][D_I], q_scale [B][H_I], w [B][H_I], q [B][H][D_qk], out [B][H][D_v],
  * out_f32 / lse / indices_out optional as above.  Sparse MLA is split over index chunks and the
- * partial results are re-reduced in fp32.
+ * partial results are re-reduced in fp32.  B <= 16384 (DSA_ERR_UNSUPPORTED above).
  */
 size_t dsa_decode_workspace_size(const dsa_dims_t *d, int32_t B, int64_t max_seq_len);
 dsa_status_t dsa_decode_paged(const dsa_paged_cache_t *c, int32_t B, int64_t max_seq_len,

@@ -115,3 +115,6 @@ def test_fused_argument_errors(lib):
              FAKE, need_d - 1, None) == WS_SMALL
     assert g(ctypes.byref(c2), 0, 131072, ctypes.byref(d), None, None, None, None, None, None, None, None,
              None, 0, None) == OK
+    assert g(ctypes.byref(c2), 16385, 131072, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+             FAKE, 1 << 40, None) == UNSUPPORTED
+    assert "16384" in _err(lib)

@@ -1,6 +1,7 @@
 """Fused paged decode vs the oracle, per sequence (needs an MI355X)."""
 from __future__ import annotations
 
+import dataclasses
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -63,3 +64,33 @@ def test_decode_64_full_size(dev):
     torch.cuda.synchronize()
     order = np.argsort(inp.seq_lens)
     _check(inp, res, [int(order[0]), int(order[1]), int(order[32]), int(order[-2]), int(order[-1])])
+
+
+@pytest.mark.parametrize("block_size", [16, 256])
+def test_decode_other_block_sizes(dev, block_size):
+    # blocks under 64 rows take the per-lane table lookup in the decode indexer; larger ones the
+    # per-workgroup block-id preload (a 64-key group never straddles two blocks)
+    wl = dataclasses.replace(get("decode_64"), block_size=block_size)
+    lens = np.array([1, 17, 64, 255, 257, 4097, 9000, 20001], dtype=np.int32)
+    print("case decode block_size", block_size, lens.tolist(), flush=True)
+    inp = decode_inputs(wl, seq_lens=lens)
+    d = DecodeDev(inp, dev)
+    res = d.run()
+    torch.cuda.synchronize()
+    _check(inp, res, range(len(lens)))
+
+
+@pytest.mark.parametrize("block_size", [16, 64])
+def test_decode_small_dims(dev, block_size):
+    # 4 indexer heads of width 32 (one 16-head MFMA tile, lanes past D_I re-read in-row bytes
+    # against zero query bytes), 8 attention heads of 80/64 and top-64: the combine over 64-wide
+    # partial rows
+    wl = dataclasses.replace(get("tiny"), kind="decode", T=7, S=5000, decode_len_lo=1, decode_len_hi=5000,
+                             block_size=block_size)
+    lens = np.array([1, 5, 64, 65, 300, 1000, 4097], dtype=np.int32)
+    print("case decode small dims block_size", block_size, lens.tolist(), flush=True)
+    inp = decode_inputs(wl, seq_lens=lens)
+    d = DecodeDev(inp, dev)
+    res = d.run()
+    torch.cuda.synchronize()
+    _check(inp, res, range(len(lens)))
