@@ -28,9 +28,13 @@ constexpr int64_t TK_CHUNK = (int64_t)TK_THREADS * TK_CHUNK_EPT;
 constexpr int TK_MERGE_EPT = 16;  // 8192 candidates per merge
 constexpr int TK_STAGE = 2048;    // index lists up to this length are staged in LDS
 
+constexpr int TK_CAND = 4096;     // candidate keys of the sampled threshold search
+constexpr int TK_CAND_EPT = TK_CAND / TK_THREADS;
+
 struct TopkShared {
   uint32_t hist[TK_BINS];
   int32_t stage[TK_STAGE];
+  uint32_t cand[TK_CAND];
   uint32_t wsum[TK_WAVES][2];
   uint32_t red[TK_WAVES][2];
   uint32_t sel_bin, sel_above;
@@ -60,23 +64,27 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
   return v;
 }
 
-// Exact threshold search.  keys: this thread's EPT keys (0 = no element).  Returns tau (the
-// k-th largest key) and k_rem (how many elements equal to tau are selected).  Requires at
-// least k valid elements.
+// Zero the histogram (once per workgroup; every select pass leaves it zeroed again).  The
+// barrier that makes it visible is the one in block_minmax.
+__device__ __forceinline__ void hist_clear(TopkShared& sh) {
+  for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
+}
+
+// Maximum and minimum of the valid keys (0 = no element) of the workgroup.
 template <int EPT>
-__device__ void radix_threshold(const uint32_t (&key)[EPT], uint32_t k, TopkShared& sh,
-                                uint32_t& tau, uint32_t& k_rem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t mx = 0, mn = 0xFFFFFFFFu;
+__device__ void block_minmax(const uint32_t (&key)[EPT], TopkShared& sh, uint32_t& mx, uint32_t& mn) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // no per-element validity test: 0 (no element) never raises the maximum, and key - 1 wraps it
+  // to the top for the minimum
+  mx = 0;
+  mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    if (key[e]) {
-      mx = max(mx, key[e]);
-      mn = min(mn, key[e]);
-    }
+    mx = max(mx, key[e]);
+    mn = min(mn, key[e] - 1u);
   }
   mx = wave_max_u32(mx);
-  mn = wave_min_u32(mn);
+  mn = wave_min_u32(mn) + 1u;  // 0 when the wave has no element
   if (lane == 0) {
     sh.red[wave][0] = mx;
     sh.red[wave][1] = mn;
@@ -86,9 +94,71 @@ __device__ void radix_threshold(const uint32_t (&key)[EPT], uint32_t k, TopkShar
   mn = 0xFFFFFFFFu;
   for (int i = 0; i < TK_WAVES; ++i) {
     mx = max(mx, sh.red[i][0]);
-    mn = min(mn, sh.red[i][1]);
+    mn = min(mn, sh.red[i][1] - 1u);
+  }
+  mn += 1u;
+}
+
+// One histogram pass of the radix select over the keys whose bits above shift + bits equal
+// prefix, binned by the `bits`-wide digit at `shift`.  The histogram is zero on entry and again
+// on exit (each thread clears the four bins it reads).  want(total) gives the rank, counted from
+// the top, sought among the `total` matching keys (0: none).  Returns the digit of the bin
+// holding that rank and the number of matching keys in higher bins.
+template <int EPT, typename Want>
+__device__ void hist_pass(const uint32_t (&key)[EPT], int shift, int bits, uint32_t prefix, TopkShared& sh,
+                          Want want, uint32_t& bin, uint32_t& above_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi_shift = shift + bits;
+  const uint32_t dmask = (1u << bits) - 1u;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t kk = key[e];
+    const bool match = kk != 0 && (hi_shift >= 32 ? true : ((kk >> hi_shift) == prefix));
+    if (match) atomicAdd(&sh.hist[(kk >> shift) & dmask], 1u);
   }
   __syncthreads();
+  // suffix counts: thread t owns the 4 bins 4*(511 - t) .. +3 (highest bins first)
+  const int b0 = 4 * (TK_THREADS - 1 - tid);
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = sh.hist[b0 + i];
+    sh.hist[b0 + i] = 0;
+  }
+  const uint32_t own = h[0] + h[1] + h[2] + h[3];
+  const uint32_t incl = wave_incl_scan(own, lane);
+  if (lane == 63) sh.wsum[wave][0] = incl;
+  __syncthreads();
+  uint32_t above = incl - own, total = 0;
+  for (int i = 0; i < TK_WAVES; ++i) {
+    const uint32_t w = sh.wsum[i][0];
+    if (i < wave) above += w;
+    total += w;
+  }
+  const uint32_t need = want(total);
+  if (above < need && need <= above + own) {
+    uint32_t a = above;
+    for (int i = 3; i >= 0; --i) {
+      if (need <= a + h[i]) {
+        sh.sel_bin = (uint32_t)(b0 + i);
+        sh.sel_above = a;
+        break;
+      }
+      a += h[i];
+    }
+  }
+  __syncthreads();
+  bin = sh.sel_bin;
+  above_out = sh.sel_above;
+}
+
+// Exact threshold search given the maximum mx and a lower bound mn (>= 1) of the valid keys
+// (keys 0 are no element; the valid ones all share the bits above the highest bit where mx and
+// mn differ).  Returns tau (the k-th largest key) and k_rem (how many elements equal to tau are
+// selected).  Requires at least k valid elements and a zero histogram.
+template <int EPT>
+__device__ void radix_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx, uint32_t mn, TopkShared& sh,
+                             uint32_t& tau, uint32_t& k_rem) {
   if (mx == mn) {  // every valid element is equal
     tau = mx;
     k_rem = k;
@@ -100,50 +170,91 @@ __device__ void radix_threshold(const uint32_t (&key)[EPT], uint32_t k, TopkShar
   uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));  // bits above the window
   uint32_t need = k;
   while (true) {
-    for (int i = tid; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
-    __syncthreads();
-    const int hi_shift = shift + bits;
-    const uint32_t dmask = (1u << bits) - 1u;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const uint32_t kk = key[e];
-      const bool match = kk != 0 && (hi_shift >= 32 ? true : ((kk >> hi_shift) == prefix));
-      if (match) atomicAdd(&sh.hist[(kk >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // suffix counts: thread t owns the 4 bins 4*(511 - t) .. +3 (highest bins first)
-    const int b0 = 4 * (TK_THREADS - 1 - tid);
-    uint32_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = sh.hist[b0 + i];
-    const uint32_t own = h[0] + h[1] + h[2] + h[3];
-    const uint32_t incl = wave_incl_scan(own, lane);
-    if (lane == 63) sh.wsum[wave][0] = incl;
-    __syncthreads();
-    uint32_t above = incl - own;
-    for (int i = 0; i < wave; ++i) above += sh.wsum[i][0];
-    if (above < need && need <= above + own) {
-      uint32_t a = above;
-      for (int i = 3; i >= 0; --i) {
-        if (need <= a + h[i]) {
-          sh.sel_bin = (uint32_t)(b0 + i);
-          sh.sel_above = a;
-          break;
-        }
-        a += h[i];
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = sh.sel_bin;
-    need -= sh.sel_above;
-    __syncthreads();
-    prefix = (hi_shift >= 32 ? 0u : (prefix << bits)) | bin;
+    uint32_t bin, above;
+    hist_pass<EPT>(key, shift, bits, prefix, sh, [&](uint32_t) { return need; }, bin, above);
+    need -= above;
+    prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
     if (shift == 0) break;
     bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
     shift -= bits;
   }
   tau = prefix;
   k_rem = need;
+}
+
+// Exact threshold search over a chunk of cn > k valid elements (maximum mx, minimum mn) that
+// touches most keys once: the radix select over a 1-in-16 sample of the keys puts a pivot (a
+// sample order statistic) a safe margin below the expected position of the k-th largest key;
+// the keys at or above the pivot are counted, and when there
+// are between k and TK_CAND of them they are compacted into LDS, where the radix select finds
+// tau and the tie count among them (every key >= tau is a candidate, so both are exact).
+// Outside that window (an unlucky or adversarial sample) the radix select runs over all keys.
+// Chunks of at most TK_CAND elements skip the sample.  The histogram is zero on entry and exit.
+template <int EPT>
+__device__ void sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32_t k, uint32_t mx, uint32_t mn,
+                                  TopkShared& sh, uint32_t& tau, uint32_t& k_rem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (mx == mn) {
+    tau = mx;
+    k_rem = k;
+    return;
+  }
+  uint32_t pivot = mn;  // every valid key
+  if (cn > TK_CAND) {
+    // sample element 17 i (i < 4) of every thread; lane l's copy sits at the lane-0 position + 4 l
+    // (elem_pos), so the number of valid samples follows from cn without a reduction
+    static_assert(EPT >= 52, "four sampled elements 17 apart");
+    uint32_t smp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) smp[i] = key[17 * i];
+    uint32_t m = 0;
+    for (int w = 0; w < TK_WAVES; ++w)
+      for (int i = 0; i < 4; ++i) {
+        const int64_t rest = cn - elem_pos<EPT>(w, 0, 17 * i);  // valid lanes: 4 l < rest
+        m += (uint32_t)min<int64_t>(WAVE, max<int64_t>(0, (rest + 3) / 4));
+      }
+    // rank sought among the m sampled keys: the expected rank of the k-th largest key plus four
+    // binomial standard deviations; none (the pivot stays mn) when the sample is too small
+    const float er = (float)k * (float)m / (float)cn;
+    const float w = er + 4.0f * sqrtf(er) + 16.0f;
+    if (w <= (float)m) {
+      uint32_t ts, tr;
+      radix_select<4>(smp, (uint32_t)w, mx, mn, sh, ts, tr);
+      pivot = ts;
+    }
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) c += key[e] >= pivot;  // pivot >= mn >= 1: valid keys only
+  // exclusive offsets of this thread's candidates
+  const uint32_t incl = wave_incl_scan(c, lane);
+  if (lane == 63) sh.wsum[wave][1] = incl;
+  __syncthreads();
+  uint32_t off = incl - c, total = 0;
+  for (int i = 0; i < TK_WAVES; ++i) {
+    const uint32_t w = sh.wsum[i][1];
+    if (i < wave) off += w;
+    total += w;
+  }
+  if (total < k || total > (uint32_t)TK_CAND) {  // workgroup-uniform
+    radix_select<EPT>(key, k, mx, mn, sh, tau, k_rem);
+    return;
+  }
+  // an opaque copy of the pivot: the counting loop's 64 compare masks are recomputed here rather
+  // than kept (in scalar registers) across the scan
+  uint32_t pv = __builtin_amdgcn_readfirstlane(pivot);
+  asm volatile("" : "+s"(pv));
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (key[e] >= pv) sh.cand[off++] = key[e];
+  __syncthreads();
+  uint32_t ck[TK_CAND_EPT];
+#pragma unroll
+  for (int j = 0; j < TK_CAND_EPT; ++j) {
+    const uint32_t i = (uint32_t)(tid + j * TK_THREADS);
+    ck[j] = i < total ? sh.cand[i] : 0u;
+  }
+  radix_select<TK_CAND_EPT>(ck, k, mx, pivot, sh, tau, k_rem);
 }
 
 // Number of set bits of a wave mask held by lanes below this one.
@@ -185,6 +296,7 @@ __device__ void emit_selected(const uint32_t (&key)[EPT], uint32_t tau, uint32_t
     ebase += sh.wsum[i][1];
   }
   const uint32_t n_gt = k - k_rem;
+  const bool wave_ties = __ballot(eqm != 0) != 0;  // ties sit in very few waves
 #pragma unroll 2
   for (int q = 0; q < EPT / 4; ++q) {
     const uint32_t ng = (uint32_t)(gtm >> (4 * q)) & 0xFu, ne = (uint32_t)(eqm >> (4 * q)) & 0xFu;
@@ -202,9 +314,10 @@ __device__ void emit_selected(const uint32_t (&key)[EPT], uint32_t tau, uint32_t
 #pragma unroll
       for (int c = 0; c < 4; ++c) gbase += (uint32_t)__builtin_popcountll(m[c]);
     }
+    if (!wave_ties) continue;
 #pragma unroll
     for (int c = 0; c < 4; ++c) m[c] = __ballot((ne >> c) & 1u);
-    if (m[0] | m[1] | m[2] | m[3]) {  // ties: rare
+    if (m[0] | m[1] | m[2] | m[3]) {
       uint32_t r = ebase;
 #pragma unroll
       for (int c = 0; c < 4; ++c) r = lanes_below(m[c], r);
@@ -284,9 +397,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     return;
   }
   uint32_t key[TK_CHUNK_EPT];
+  hist_clear(sh);
   load_keys<TK_CHUNK_EPT>(logits + t * ld + c0, cn, key);
-  uint32_t tau, k_rem;
-  radix_threshold<TK_CHUNK_EPT>(key, (uint32_t)k, sh, tau, k_rem);
+  uint32_t mx, mn, tau, k_rem;
+  block_minmax<TK_CHUNK_EPT>(key, sh, mx, mn);
+  sampled_threshold<TK_CHUNK_EPT>(key, cn, (uint32_t)k, mx, mn, sh, tau, k_rem);
   if (single) {
     if (k <= TK_STAGE) {
       emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh,
@@ -322,13 +437,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   const uint32_t* ck = cand_key + t * G * (int64_t)k;
   const int32_t* ci = cand_idx + t * G * (int64_t)k;
   uint32_t key[TK_MERGE_EPT];
+  hist_clear(sh);
 #pragma unroll
   for (int e = 0; e < TK_MERGE_EPT; ++e) {
     const int p = elem_pos<TK_MERGE_EPT>(wave, lane, e);
     key[e] = p < total ? ck[p] : 0u;
   }
-  uint32_t tau, k_rem;
-  radix_threshold<TK_MERGE_EPT>(key, (uint32_t)k, sh, tau, k_rem);
+  uint32_t mx, mn, tau, k_rem;
+  block_minmax<TK_MERGE_EPT>(key, sh, mx, mn);
+  radix_select<TK_MERGE_EPT>(key, (uint32_t)k, mx, mn, sh, tau, k_rem);
   int32_t* out_idx = indices + t * k;
   if (k <= TK_STAGE) {
     emit_selected<TK_MERGE_EPT>(key, tau, (uint32_t)k, k_rem, sh,

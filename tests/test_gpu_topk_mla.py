@@ -86,6 +86,22 @@ def test_topk_heavy_tail(dev):
     _topk_case(dev, s, 39990, 2048, "heavy tail")
 
 
+def test_topk_sample_adversarial(dev):
+    # The kernel picks its pivot from the scores at a fixed 1-in-16 sample of a row's positions
+    # (element 17 i, i < 4, of every thread: position 4096 w + 1024 i + 4 lane + i).  Rows that
+    # defeat that sample must still come out exact through the full select: sampled scores far
+    # above the rest leave too few candidates above the pivot, far below leave too many.
+    S = 32768
+    sampled = np.array([4096 * w + 1024 * i + 4 * l + i for w in range(8) for i in range(4) for l in range(64)])
+    g = block_rng(36, 0, 0)
+    s = g.standard_normal((4, S)).astype(np.float32)
+    s[0, sampled] += 100.0
+    s[1, sampled] -= 100.0
+    s[2, sampled] = 7.0        # sampled scores all tied, above the rest
+    s[3, sampled[::3]] += 50.0
+    _topk_case(dev, s, S - 4, 2048, "sample-adversarial rows")
+
+
 # ------------------------------------------------------------------------------------- MLA
 def _mla_case(dev, T, S, H, D_qk, D_v, k, idx, q_start, sm, name, seed=40):
     import dsa_lightning_indexer_02_amd as dsa
