@@ -50,6 +50,12 @@ def load(path: Optional[str] = None):
     lib.oracle_sparse_mla.argtypes = [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _i64,
                                       ctypes.c_float, _p, _p, _p, _i32]
     lib.oracle_sparse_mla.restype = ctypes.c_int
+    lib.oracle_e4m3_encode.argtypes = [_p, _p, _i64]
+    lib.oracle_e4m3_encode.restype = None
+    lib.oracle_quantize_rows.argtypes = [_p, _i64, _i32, _p, _p]
+    lib.oracle_quantize_rows.restype = None
+    lib.oracle_append_paged.argtypes = [_p, _p, _p, _i32, _p, _i64, _p, _p, _i64, _i32, _i32, _p, _p]
+    lib.oracle_append_paged.restype = _i64
     if path is None:
         _lib = lib
     return lib
@@ -174,3 +180,44 @@ def decode(inp, nthreads: int = 0, lib=None, seqs=None):
         o, ob, l = sparse_mla(inp.q[b:b + 1], ix, pos, kv, wl.D_v, wl.sm_scale, nthreads, lib)
         res.append((lg[0], ix[0], o[0], ob[0], l[0]))
     return res
+
+
+def e4m3_encode(y: np.ndarray, lib=None) -> np.ndarray:
+    """Nearest OCP E4M3 codes (ties to the even code) of finite fp32 values with |y| <= 448."""
+    lib = lib or load()
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib.oracle_e4m3_encode(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def quantize_rows(x_bf16: np.ndarray, lib=None):
+    """Per-row (last dim) absmax FP8 quantization of bf16 bit patterns: (uint8 codes, f32 scales)."""
+    lib = lib or load()
+    x = _c(x_bf16, np.uint16)
+    D = x.shape[-1]
+    rows = x.size // D if D else 0
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    lib.oracle_quantize_rows(_ptr(x), rows, D, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def append_paged(k8_pool, ks_pool, kv_pool, block_table, seq, pos, k_bf16, kv_bf16, lib=None):
+    """Copies of the three pools after appending tokens (seq[i], pos[i]) with indexer keys k_bf16
+    [n, D_I] (quantized here) and latent rows kv_bf16 [n, D_qk]."""
+    lib = lib or load()
+    k8 = np.array(k8_pool, dtype=np.uint8, copy=True, order="C")
+    ks = np.array(ks_pool, dtype=np.float32, copy=True, order="C")
+    kv = np.array(kv_pool, dtype=np.uint16, copy=True, order="C")
+    tbl = _c(block_table, np.int32)
+    seq = _c(seq, np.int32)
+    pos = _c(pos, np.int32)
+    k = _c(k_bf16, np.uint16)
+    v = _c(kv_bf16, np.uint16)
+    n = len(seq)
+    bad = lib.oracle_append_paged(_ptr(k8), _ptr(ks), _ptr(kv), k8.shape[1], _ptr(tbl), tbl.shape[1], _ptr(seq),
+                                  _ptr(pos), n, k8.shape[2], kv.shape[2], _ptr(k), _ptr(v))
+    if bad:
+        raise ValueError("oracle_append_paged: %d tokens fall in blocks with a negative id" % bad)
+    return k8, ks, kv

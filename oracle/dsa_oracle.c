@@ -317,3 +317,99 @@ int oracle_sparse_mla(const uint16_t *q, const int32_t *idx, const int64_t *pos,
     }
     return bad;
 }
+
+/* ---- NEXT step: FP8 quantization of the indexer inputs and the paged append -------------
+ * createthis gist page, indexer listing: the indexer's query and key vectors are cast to
+ * FP8 E4M3 along the last dimension with one scale per vector (per-row absmax); the cache
+ * then holds the codes and scales of every key, and the latent row of every token, at the
+ * token's slot of the paged layout. */
+
+/* Nearest E4M3 code of a finite y with 0 <= y <= 448.  The non-negative finite codes 0x00 ..
+ * 0x7E decode to strictly increasing values, so the nearest one is found by bisection over
+ * the decoded table; a y exactly halfway between two neighbouring codes takes the one whose
+ * code (low mantissa bit) is even, the nearest-even rule of a cast to the format. */
+static uint8_t e4m3_encode_abs(float y)
+{
+    int lo = 0, hi = 0x7E; /* g_e4m3[lo] <= y < g_e4m3[hi] during the search */
+    if (y >= g_e4m3[hi])
+        return (uint8_t)hi;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (g_e4m3[mid] <= y)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dl = (double)y - (double)g_e4m3[lo], dh = (double)g_e4m3[hi] - (double)y;
+    if (dl < dh)
+        return (uint8_t)lo;
+    if (dh < dl)
+        return (uint8_t)hi;
+    return (uint8_t)((lo & 1) ? hi : lo);
+}
+
+/* Code of a finite y with |y| <= 448 (the sign bit copied, also for -0). */
+static uint8_t e4m3_encode(float y)
+{
+    return (uint8_t)((signbit(y) ? 0x80 : 0) | e4m3_encode_abs(fabsf(y)));
+}
+
+void oracle_e4m3_encode(const float *y, uint8_t *out, int64_t n)
+{
+    e4m3_init();
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e4m3_encode(y[i]);
+}
+
+/* One row of D bf16 values: s = amax / 448 (1 for an all-zero row), code_i =
+ * e4m3(clamp(x_i / s, -448, 448)), the division and the clamp in fp32. */
+static void quantize_row(const uint16_t *x, int32_t D, uint8_t *codes, float *scale)
+{
+    float amax = 0.0f;
+    for (int32_t i = 0; i < D; ++i) {
+        float a = fabsf(bf16_value(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    *scale = s;
+    for (int32_t i = 0; i < D; ++i) {
+        float v = bf16_value(x[i]) / s;
+        if (v > 448.0f)
+            v = 448.0f;
+        if (v < -448.0f)
+            v = -448.0f;
+        codes[i] = e4m3_encode(v);
+    }
+}
+
+void oracle_quantize_rows(const uint16_t *x, int64_t rows, int32_t D, uint8_t *codes, float *scales)
+{
+    e4m3_init();
+    for (int64_t r = 0; r < rows; ++r)
+        quantize_row(x + r * D, D, codes + r * D, scales + r);
+}
+
+/* Append n tokens to a paged cache: token i (sequence seq[i], position pos[i]) goes to the
+ * physical row block_table[seq[i] * max_blocks + pos[i] / bs] * bs + pos[i] % bs of the pools:
+ * the quantized indexer key k[i] (codes and scale) and the latent row kv[i] copied as is.
+ * Returns the number of tokens whose block id is negative (those are not written). */
+int64_t oracle_append_paged(uint8_t *k8_pool, float *ks_pool, uint16_t *kv_pool, int32_t bs,
+                            const int32_t *block_table, int64_t max_blocks, const int32_t *seq,
+                            const int32_t *pos, int64_t n, int32_t D_I, int32_t D_qk,
+                            const uint16_t *k, const uint16_t *kv)
+{
+    e4m3_init();
+    int64_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t blk = block_table[(int64_t)seq[i] * max_blocks + pos[i] / bs];
+        if (blk < 0) {
+            ++bad;
+            continue;
+        }
+        int64_t row = (int64_t)blk * bs + pos[i] % bs;
+        quantize_row(k + i * D_I, D_I, k8_pool + row * D_I, ks_pool + row);
+        memcpy(kv_pool + row * D_qk, kv + i * D_qk, (size_t)D_qk * sizeof(uint16_t));
+    }
+    return bad;
+}

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from dsa_inputs import get, prefill_inputs
-from dsa_inputs.generate import block_rng, quantize_fp8_rows, to_bf16_bits
+from dsa_inputs.generate import bf16_bits_to_f32, block_rng, quantize_fp8_rows, to_bf16_bits
 
 import brute
 
@@ -278,3 +278,102 @@ def check_causal_end_to_end(lib):
         n = t + 1
         v = idx[t][idx[t] >= 0]
         assert len(v) == min(n, wl.topk) and len(set(v.tolist())) == len(v)
+
+
+# ---------------------------------------------------------------- FP8 quantize + paged append
+FP8_MAX = 448.0
+
+
+def _torch_e4m3(y: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def check_e4m3_encode_round_trip(lib):
+    t = oracle.e4m3_table(lib)
+    codes = np.arange(256, dtype=np.uint8)
+    fin = ~np.isnan(t)
+    assert fin.sum() == 254                      # 0x7F and 0xFF are NaN
+    assert np.array_equal(oracle.e4m3_encode(t[fin], lib), codes[fin]), "E4M3 encode does not invert decode"
+
+
+def check_e4m3_encode_midpoints(lib):
+    t = oracle.e4m3_table(lib).astype(np.float64)
+    lo = np.arange(0, 0x7E)
+    mid = ((t[lo] + t[lo + 1]) / 2).astype(np.float32)      # exact: at most 5 significant bits
+    assert np.array_equal(mid.astype(np.float64), (t[lo] + t[lo + 1]) / 2)
+    even = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    assert np.array_equal(oracle.e4m3_encode(mid, lib), even), "halfway values must take the even code"
+    assert np.array_equal(oracle.e4m3_encode(-mid, lib), even | 0x80)
+    above = np.nextafter(mid, np.float32(np.inf))
+    below = np.nextafter(mid, np.float32(0))
+    assert np.array_equal(oracle.e4m3_encode(above, lib), (lo + 1).astype(np.uint8))
+    assert np.array_equal(oracle.e4m3_encode(below[1:], lib), lo[1:].astype(np.uint8))
+    assert oracle.e4m3_encode(np.array([0.0, -0.0], np.float32), lib).tolist() == [0x00, 0x80]
+
+
+def check_e4m3_encode_vs_torch(lib):
+    g = block_rng(50, 0, 0)
+    u = g.uniform(-FP8_MAX, FP8_MAX, 200_000).astype(np.float32)
+    small = (g.choice([-1.0, 1.0], 100_000) * np.exp2(g.uniform(-12, 2, 100_000))).astype(np.float32)
+    t = oracle.e4m3_table(lib).astype(np.float64)
+    lo = np.arange(0, 0x7E)
+    mids = ((t[lo] + t[lo + 1]) / 2).astype(np.float32)
+    y = np.concatenate([u, small, mids, -mids, np.float32([FP8_MAX, -FP8_MAX, 0.0])])
+    assert np.array_equal(oracle.e4m3_encode(y, lib), _torch_e4m3(y)), "E4M3 encode differs from torch's cast"
+
+
+def check_quantize_rows_closed_forms(lib):
+    x = np.zeros((3, 128), np.float32)
+    x[1, 5] = -3.0
+    x[1, 7] = 1.5
+    x[2] = np.linspace(-2, 7, 128)
+    codes, scales = oracle.quantize_rows(to_bf16_bits(x), lib)
+    assert scales[0] == 1.0 and not codes[0].any()                       # all-zero row
+    assert scales[1] == np.float32(3.0) / np.float32(FP8_MAX)
+    assert codes[1, 5] == 0xFE and codes[1, 7] == _torch_e4m3(np.float32([224.0]))[0]
+    assert codes[2, 127] == 0x7E and (codes[2] & 0x7F).max() == 0x7E   # the row maximum codes 448
+    dec = oracle.e4m3_table(lib)[codes[2]].astype(np.float64) * scales[2]
+    xb = bf16_bits_to_f32(to_bf16_bits(x[2])).astype(np.float64)
+    # E4M3 keeps 4 significant bits: within 2^-4 relative (normal range) or half a subnormal step
+    assert np.all(np.abs(dec - xb) <= np.maximum(np.abs(xb) * 2.0 ** -4, 2.0 ** -10 * scales[2]))
+
+
+def check_quantize_rows_vs_generator(lib):
+    # the input generator quantizes the same definition through torch (fp32 division, RNE cast)
+    g = block_rng(51, 0, 0)
+    x = (g.standard_normal((257, 128)) * np.exp2(g.uniform(-6, 6, (257, 1)))).astype(np.float32)
+    x[3] = 0.0
+    x[4, :7] = 1e-30
+    bits = to_bf16_bits(x)
+    xv = bf16_bits_to_f32(bits)
+    codes, scales = oracle.quantize_rows(bits, lib)
+    gc, gs = quantize_fp8_rows(xv)
+    assert np.array_equal(scales, gs), "row scales differ from amax / 448"
+    assert np.array_equal(codes, gc), "row codes differ from the torch quantizer"
+
+
+def check_append_paged_round_trip(lib, bs=16):
+    g = block_rng(52, 0, bs)
+    D_I, D_qk, NB = 64, 80, 12
+    k8 = g.integers(0, 255, (NB, bs, D_I), dtype=np.uint8)
+    ks = g.uniform(0.1, 1.0, (NB, bs)).astype(np.float32)
+    kv = g.integers(0, 65535, (NB, bs, D_qk), dtype=np.uint16)
+    table = np.array([[3, 7, 1, -1], [0, 11, -1, -1]], np.int32)
+    seq = np.array([0, 0, 0, 1, 1], np.int32)
+    pos = np.array([0, bs + 2, 3 * bs - 1, 1, 2 * bs - 1], np.int32)
+    kn = to_bf16_bits(g.standard_normal((5, D_I)).astype(np.float32))
+    vn = g.integers(0, 65535, (5, D_qk), dtype=np.uint16)
+    k8n, ksn, kvn = oracle.append_paged(k8, ks, kv, table, seq, pos, kn, vn, lib)
+    qc, qsc = oracle.quantize_rows(kn, lib)
+    written = np.zeros((NB, bs), bool)
+    for i in range(5):
+        written[table[seq[i], pos[i] // bs], pos[i] % bs] = True
+        # through the paged gather: logical row pos[i] of sequence seq[i]
+        n = int(pos[i]) + 1
+        assert np.array_equal(oracle.gather_rows(k8n, table[seq[i]], n, lib)[-1], qc[i]), "appended codes misplaced"
+        assert oracle.gather_rows(ksn[..., None], table[seq[i]], n, lib)[-1, 0] == qsc[i]
+        assert np.array_equal(oracle.gather_rows(kvn, table[seq[i]], n, lib)[-1], vn[i]), "appended row misplaced"
+    assert np.array_equal(k8n[~written], k8[~written]), "append touched other slots"
+    assert np.array_equal(ksn[~written], ks[~written])
+    assert np.array_equal(kvn[~written], kv[~written])

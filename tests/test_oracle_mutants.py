@@ -38,6 +38,16 @@ MUTANTS = [
      "acc[d] += e * bf16_value(vr[d + (D_qk - D_v)]);", [pins.check_mla_brute]),
     ("mla_lse_no_max", "lse[t * H + h] = m + logf(l);", "lse[t * H + h] = logf(l);",
      [pins.check_mla_dense_equivalence]),
+    ("e4m3_ties_up", "return (uint8_t)((lo & 1) ? hi : lo);", "return (uint8_t)hi;",
+     [pins.check_e4m3_encode_midpoints, pins.check_e4m3_encode_vs_torch]),
+    ("e4m3_round_down", "    if (dl < dh)\n        return (uint8_t)lo;", "    if (dl <= dh + 1.0)\n        return (uint8_t)lo;",
+     [pins.check_e4m3_encode_midpoints, pins.check_e4m3_encode_vs_torch]),
+    ("quant_scale_447", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 447.0f : 1.0f",
+     [pins.check_quantize_rows_closed_forms, pins.check_quantize_rows_vs_generator]),
+    ("quant_sign_dropped", "return (uint8_t)((signbit(y) ? 0x80 : 0) | e4m3_encode_abs(fabsf(y)));",
+     "return (uint8_t)(e4m3_encode_abs(fabsf(y)));", [pins.check_e4m3_encode_round_trip]),
+    ("append_slot_shift", "int64_t row = (int64_t)blk * bs + pos[i] % bs;",
+     "int64_t row = (int64_t)blk * bs + (pos[i] + 1) % bs;", [pins.check_append_paged_round_trip]),
     ("mla_future_keys", "int64_t n = visible_keys(pos[t], S);\n        const int32_t *row",
      "int64_t n = S;\n        const int32_t *row", [pins.check_mla_brute]),
 ]
