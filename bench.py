@@ -9,8 +9,9 @@ and stay resident; nothing is generated, quantized or copied inside the timed re
 one JSON line.
 
 ``--workload`` selects another configuration (tiny, prefill_4k, chunked_131k, decode_64; decode
-times the fused paged decode call against its HBM roofline), and ``--all-configs`` prints one
-line per configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
+times the fused paged decode call against its HBM roofline; quantize_append_32k times the FP8
+quantization of the L = 32K queries and the paged append of its tokens), and ``--all-configs``
+prints one line per configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -282,8 +283,85 @@ def run_decode(wl, args, dev):
     }
 
 
+def run_quantize_append(args, dev):
+    """On-device FP8 quantization of the L = 32K prefill's indexer queries (32768 x 64 rows of 128)
+    and the paged append of its 32768 tokens (FP8 key + scale + 576-wide latent row, block 64, a
+    seeded permutation of blocks), each timed with HIP events against its algorithmic HBM bytes."""
+    import torch
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import get
+    wl = get(HEADLINE)
+    T, H_I, D_I, D_qk, bs = wl.T, wl.H_I, wl.D_I, wl.D_qk, 64
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    print("generating quantize/append inputs", file=sys.stderr, flush=True)
+    q = torch.randn((T, H_I, D_I), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((T, D_I), generator=g, device=dev).to(torch.bfloat16)
+    kv = torch.randn((T, D_qk), generator=g, device=dev).to(torch.bfloat16)
+    nb = T // bs
+    perm = torch.randperm(nb, generator=g, device=dev).to(torch.int32)
+    cache = dsa.PagedKV(torch.empty((nb, bs, D_I), dtype=torch.uint8, device=dev),
+                        torch.empty((nb, bs), dtype=torch.float32, device=dev),
+                        torch.empty((nb, bs, D_qk), dtype=torch.bfloat16, device=dev), perm[None].contiguous())
+    seq = torch.zeros(T, dtype=torch.int32, device=dev)
+    pos = torch.arange(T, dtype=torch.int32, device=dev)
+    codes = torch.empty((T, H_I, D_I), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, H_I), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dsa.dsa_quantize_fp8_rows(q, codes, scales)
+        if ev:
+            ev[1].record(stream)
+        dsa.dsa_append_paged(cache, seq, pos, k, kv)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in evs])
+    qms, ams = per.mean(axis=0)
+    q_bytes = float(T * H_I * (D_I * 2 + D_I + 4))
+    a_bytes = float(T * (D_I * 2 + D_I + 4 + D_qk * 2 * 2 + 8))
+    step_ms = per.sum(axis=1)
+    stages = {
+        "quantize_queries": {"ms": float(qms), "bound": "hbm", "achieved_gbs": q_bytes / qms / 1e6,
+                             "frac": q_bytes / (qms / 1e3) / PEAK_HBM, "bytes": q_bytes},
+        "append_paged": {"ms": float(ams), "bound": "hbm", "achieved_gbs": a_bytes / ams / 1e6,
+                         "frac": a_bytes / (ams / 1e3) / PEAK_HBM, "bytes": a_bytes},
+    }
+    roof = {"kernel": "quantize_rows_kernel", "bound": "hbm", "achieved": q_bytes / (qms / 1e3) / 1e9,
+            "peak": PEAK_HBM / 1e9, "unit": "GB/s", "traffic": None, "algorithmic_bytes_per_launch": q_bytes,
+            "avg_launch_ms": float(qms)}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    med = float(np.median(step_ms))
+    return {
+        "value": T / (med / 1e3), "ms_per_step": med, "step_ms_events": percentiles(step_ms), "roofline": roof,
+        "stages": stages, "fused_ms_per_step": None,
+        "config": {"workload": "quantize_append_32k", "T": T, "H_I": H_I, "D_I": D_I, "D_qk": D_qk,
+                   "block_size": bs, "parallelism": "single GPU"},
+    }
+
+
 def run_one(name, args, dev, with_cpu: bool):
     from dsa_inputs import get
+    if name == "quantize_append_32k":
+        res = run_quantize_append(args, dev)
+        line = {"metric": "query tokens/s (FP8 quantize of indexer queries + paged append, L=32K)",
+                "value": res["value"], "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp8-e4m3 out",
+                "data": "synthetic (seeded torch normal, bf16)", "config": res["config"], "roofline": res["roofline"],
+                "stages": res["stages"], "step_ms_events": res["step_ms_events"], "fused_ms_per_step": None,
+                "cpu_baseline": None}
+        return line
     wl = get(name)
     res = run_decode(wl, args, dev) if wl.kind == "decode" else run_prefill(wl, args, dev)
     cpu = None
@@ -340,7 +418,7 @@ def main():
     dev = torch.device("cuda:0")
     dsa.load()
     if args.all_configs:
-        for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64"]:
+        for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64", "quantize_append_32k"]:
             print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return

@@ -181,3 +181,36 @@ def dsa_decode_paged(cache: PagedKV, max_seq_len: int, dims: Dims, q8, q_scale, 
         _opt(out_f32), _opt(lse), _opt(idx), ws.data_ptr(), ws.numel(), _stream(q8))
     check("dsa_decode_paged", status)
     return out, out_f32, lse, idx
+
+
+# ------------------------------------------------------------------------------------------------
+def dsa_quantize_fp8_rows(x, codes=None, scales=None):
+    """Per-row FP8 E4M3 codes (uint8, x's shape) and fp32 scales (x's shape without the last dim)
+    of a bf16 tensor x [..., D]."""
+    lib = load()
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    nd = x.dim()
+    status = lib.dsa_quantize_fp8_rows(_dev(x, "x", nd, 2), rows, D, _dev(codes, "codes", nd, 1),
+                                       _dev(scales, "scales", nd - 1, 4) if nd > 1 else scales.data_ptr(),
+                                       _stream(x))
+    check("dsa_quantize_fp8_rows", status)
+    return codes, scales
+
+
+def dsa_append_paged(cache: PagedKV, seq_ids, positions, k, kv):
+    """Write tokens (seq_ids[i], positions[i]) into the cache's pools: the FP8 codes and scale of
+    their bf16 indexer keys k [n, D_I] and their bf16 latent rows kv [n, D_qk]."""
+    lib = load()
+    n, D_I = k.shape
+    D_qk = kv.shape[1]
+    B = cache.block_table.shape[0]
+    c = cache.struct()
+    status = lib.dsa_append_paged(ctypes.byref(c), B, _dev(seq_ids, "seq_ids", 1, 4),
+                                  _dev(positions, "positions", 1, 4), n, D_I, D_qk, _dev(k, "k", 2, 2),
+                                  _dev(kv, "kv", 2, 2), _stream(k))
+    check("dsa_append_paged", status)

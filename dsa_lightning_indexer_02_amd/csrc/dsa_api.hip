@@ -387,4 +387,37 @@ dsa_status_t dsa_decode_paged(const dsa_paged_cache_t* c, int32_t B, int64_t max
   return hip_status(dsa::launch_sparse_mla(a, stream), "sparse MLA launch");
 }
 
+dsa_status_t dsa_quantize_fp8_rows(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes, float* scales,
+                                   hipStream_t stream) {
+  REQUIRE(rows >= 0, DSA_ERR_INVALID_ARGUMENT, "negative rows");
+  REQUIRE(dsa::quantize_supported(D), DSA_ERR_UNSUPPORTED, "D=%d must be a multiple of 8 in [8, 512]", D);
+  if (rows == 0) return ok();
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  return hip_status(dsa::launch_quantize_rows(x, rows, D, codes, scales, stream), "quantize launch");
+}
+
+dsa_status_t dsa_append_paged(const dsa_paged_cache_t* c, int32_t B, const int32_t* seq_ids,
+                              const int32_t* positions, int64_t n, int32_t D_I, int32_t D_qk, const uint16_t* k,
+                              const uint16_t* kv, hipStream_t stream) {
+  REQUIRE(n >= 0 && B >= 0, DSA_ERR_INVALID_ARGUMENT, "negative n or B");
+  REQUIRE(dsa::quantize_supported(D_I), DSA_ERR_UNSUPPORTED, "D_I=%d must be a multiple of 8 in [8, 512]", D_I);
+  REQUIRE(D_qk >= 8 && D_qk % 8 == 0, DSA_ERR_UNSUPPORTED, "D_qk=%d must be a positive multiple of 8", D_qk);
+  if (n == 0) return ok();
+  REQUIRE(B >= 1, DSA_ERR_INVALID_ARGUMENT, "B must be >= 1 when tokens are appended");
+  dsa_status_t s = check_cache(c, 1, B);
+  if (s != DSA_OK) return s;
+  REQUIRE_PTR(seq_ids);
+  REQUIRE_PTR(positions);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(kv);
+  // the pools of the cache are written here (the struct's const is the readers' view)
+  return hip_status(dsa::launch_append_paged(const_cast<uint8_t*>(c->k8), const_cast<float*>(c->k_scale),
+                                             const_cast<uint16_t*>(c->kv), c->num_blocks,
+                                             block_shift_of(c->block_size), c->block_table, c->max_blocks_per_seq,
+                                             B, seq_ids, positions, n, D_I, D_qk, k, kv, stream),
+                    "append launch");
+}
+
 }  // extern "C"

@@ -22,6 +22,15 @@ hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float
                                  int32_t block_shift, const int32_t* seq_lens, int32_t B, int64_t max_len,
                                  int32_t H_I, int32_t D_I, float* logits, int64_t ld, hipStream_t stream);
 
+// ---- FP8 quantization and paged append
+bool quantize_supported(int32_t D);
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes, float* scales,
+                                hipStream_t stream);
+hipError_t launch_append_paged(uint8_t* k8_pool, float* ks_pool, uint16_t* kv_pool, int64_t num_blocks,
+                               int32_t block_shift, const int32_t* table, int64_t max_blocks, int32_t B,
+                               const int32_t* seq_ids, const int32_t* positions, int64_t n, int32_t D_I,
+                               int32_t D_qk, const uint16_t* k, const uint16_t* kv, hipStream_t stream);
+
 // ---- top-k
 int32_t topk_chunks(int64_t S);
 size_t topk_workspace_bytes(int64_t T, int64_t S, int32_t k);

@@ -154,6 +154,34 @@ dsa_status_t dsa_decode_paged(const dsa_paged_cache_t *c, int32_t B, int64_t max
                               float *lse, int32_t *indices_out, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * FP8 quantization of indexer vectors (createthis gist page, indexer listing: the query and key
+ * vectors are cast to FP8 E4M3 along the last dimension with one scale per vector).  Row r of
+ * x (bf16 [rows][D]) becomes scales[r] = max_i |x[r][i]| / 448 (1 for an all-zero row) and
+ * codes[r][i] = E4M3(clamp(x[r][i] / scales[r], -448, 448)): fp32 division, round to nearest
+ * even, OCP E4M3 bit patterns.  codes u8 [rows][D], scales f32 [rows], device pointers, 16-byte
+ * aligned.  D a multiple of 8 in [8, 512] (DSA_ERR_UNSUPPORTED otherwise).  For the indexer's
+ * queries pass rows = T * H_I, D = D_I; the result is the q8 / q_scale of the calls above.
+ */
+dsa_status_t dsa_quantize_fp8_rows(const uint16_t *x, int64_t rows, int32_t D, uint8_t *codes, float *scales,
+                                   hipStream_t stream);
+
+/*
+ * Paged append (summary page, section "Key claims": paged indexer caches).  Writes n new tokens
+ * into the cache c: token i of sequence seq_ids[i] (0 <= seq_ids[i] < B, a row of
+ * c->block_table) at position positions[i] gets, in physical row
+ * block_table[seq][pos / block_size] * block_size + pos % block_size of the pools, the FP8 codes
+ * and scale of its bf16 indexer key k[i] (D_I values, quantized as dsa_quantize_fp8_rows does)
+ * and its bf16 latent row kv[i] (D_qk values, copied).  The pools behind c are written (the
+ * const of the struct is the readers' view); seq_lens is not read or changed.  Tokens whose
+ * sequence, position or block id falls outside the table or the pool are skipped.  Two tokens
+ * mapped to the same slot race.  k bf16 [n][D_I], kv bf16 [n][D_qk], seq_ids / positions i32
+ * [n], device pointers, 16-byte aligned; D_I as above, D_qk a positive multiple of 8.
+ */
+dsa_status_t dsa_append_paged(const dsa_paged_cache_t *c, int32_t B, const int32_t *seq_ids,
+                              const int32_t *positions, int64_t n, int32_t D_I, int32_t D_qk, const uint16_t *k,
+                              const uint16_t *kv, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -118,3 +118,21 @@ def test_fused_argument_errors(lib):
     assert g(ctypes.byref(c2), 16385, 131072, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
              FAKE, 1 << 40, None) == UNSUPPORTED
     assert "16384" in _err(lib)
+
+
+def test_quantize_and_append_argument_errors(lib):
+    f = lib.dsa_quantize_fp8_rows
+    assert f(FAKE, 10, 12, FAKE, FAKE, None) == UNSUPPORTED          # D not a multiple of 8
+    assert f(FAKE, 10, 1024, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(None, 10, 128, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 10, 128, FAKE + 8, FAKE, None) == INVALID          # misaligned codes
+    assert f(None, 0, 128, None, None, None) == OK                    # nothing to do
+    g = lib.dsa_append_paged
+    c = PagedCache(FAKE, FAKE, FAKE, 100, 64, FAKE, 4, None)
+    assert g(ctypes.byref(c), 2, FAKE, FAKE, 5, 100, 576, FAKE, FAKE, None) == UNSUPPORTED   # D_I
+    assert g(ctypes.byref(c), 2, FAKE, FAKE, 5, 128, 570, FAKE, FAKE, None) == UNSUPPORTED   # D_qk
+    assert g(ctypes.byref(c), 2, None, FAKE, 5, 128, 576, FAKE, FAKE, None) == INVALID
+    bad_bs = PagedCache(FAKE, FAKE, FAKE, 100, 48, FAKE, 4, None)
+    assert g(ctypes.byref(bad_bs), 2, FAKE, FAKE, 5, 128, 576, FAKE, FAKE, None) == INVALID
+    assert g(ctypes.byref(c), 0, FAKE, FAKE, 5, 128, 576, FAKE, FAKE, None) == INVALID       # tokens, no sequences
+    assert g(None, 0, None, None, 0, 128, 576, None, None, None) == OK
