@@ -54,6 +54,8 @@ def load(path: Optional[str] = None):
     lib.oracle_e4m3_encode.restype = None
     lib.oracle_quantize_rows.argtypes = [_p, _i64, _i32, _p, _p]
     lib.oracle_quantize_rows.restype = None
+    lib.oracle_quantize_rows_ue8m0.argtypes = [_p, _i64, _i32, _p, _p, _p]
+    lib.oracle_quantize_rows_ue8m0.restype = None
     lib.oracle_append_paged.argtypes = [_p, _p, _p, _i32, _p, _i64, _p, _p, _i64, _i32, _i32, _p, _p]
     lib.oracle_append_paged.restype = _i64
     if path is None:
@@ -221,3 +223,17 @@ def append_paged(k8_pool, ks_pool, kv_pool, block_table, seq, pos, k_bf16, kv_bf
     if bad:
         raise ValueError("oracle_append_paged: %d tokens fall in blocks with a negative id" % bad)
     return k8, ks, kv
+
+
+def quantize_rows_ue8m0(x_bf16: np.ndarray, lib=None):
+    """Per-row FP8 quantization with power-of-two (UE8M0) scales: (uint8 codes, uint8 biased
+    exponents, f32 scales = 2^(exponent - 127))."""
+    lib = lib or load()
+    x = _c(x_bf16, np.uint16)
+    D = x.shape[-1]
+    rows = x.size // D if D else 0
+    codes = np.empty(x.shape, dtype=np.uint8)
+    exps = np.empty(x.shape[:-1], dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    lib.oracle_quantize_rows_ue8m0(_ptr(x), rows, D, _ptr(codes), _ptr(exps), _ptr(scales))
+    return codes, exps, scales

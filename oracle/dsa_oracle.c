@@ -390,6 +390,46 @@ void oracle_quantize_rows(const uint16_t *x, int64_t rows, int32_t D, uint8_t *c
         quantize_row(x + r * D, D, codes + r * D, scales + r);
 }
 
+/* Power-of-two variant (createthis gist page, indexer listing: the cast helper's use_ue8m0
+ * option, an unsigned exponent-only scale).  Reading: s = 2^p for the smallest p with
+ * 2^p >= t = amax / 448 (fp32 division; t = 1 for an all-zero row), p at least -127 so that s fits
+ * the format; the scale is stored as its biased exponent p + 127 and the codes are
+ * e4m3(clamp(x / s, -448, 448)) as above (the division by a power of two is exact). */
+static void quantize_row_ue8m0(const uint16_t *x, int32_t D, uint8_t *codes, uint8_t *exp8, float *scale)
+{
+    float amax = 0.0f;
+    for (int32_t i = 0; i < D; ++i) {
+        float a = fabsf(bf16_value(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    float t = amax > 0.0f ? amax / 448.0f : 1.0f;
+    int e;
+    float m = frexpf(t, &e); /* t = m 2^e, 0.5 <= m < 1 */
+    int p = m == 0.5f ? e - 1 : e;
+    if (p < -127)
+        p = -127;
+    float s = ldexpf(1.0f, p);
+    *scale = s;
+    *exp8 = (uint8_t)(p + 127);
+    for (int32_t i = 0; i < D; ++i) {
+        float v = bf16_value(x[i]) / s;
+        if (v > 448.0f)
+            v = 448.0f;
+        if (v < -448.0f)
+            v = -448.0f;
+        codes[i] = e4m3_encode(v);
+    }
+}
+
+void oracle_quantize_rows_ue8m0(const uint16_t *x, int64_t rows, int32_t D, uint8_t *codes, uint8_t *exps,
+                                float *scales)
+{
+    e4m3_init();
+    for (int64_t r = 0; r < rows; ++r)
+        quantize_row_ue8m0(x + r * D, D, codes + r * D, exps + r, scales + r);
+}
+
 /* Append n tokens to a paged cache: token i (sequence seq[i], position pos[i]) goes to the
  * physical row block_table[seq[i] * max_blocks + pos[i] / bs] * bs + pos[i] % bs of the pools:
  * the quantized indexer key k[i] (codes and scale) and the latent row kv[i] copied as is.

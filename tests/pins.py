@@ -377,3 +377,28 @@ def check_append_paged_round_trip(lib, bs=16):
     assert np.array_equal(k8n[~written], k8[~written]), "append touched other slots"
     assert np.array_equal(ksn[~written], ks[~written])
     assert np.array_equal(kvn[~written], kv[~written])
+
+
+def check_quantize_ue8m0(lib):
+    # UE8M0 reading: s = 2^p, the smallest power of two >= amax / 448 (p >= -127); codes as the
+    # plain quantizer with that scale.  Pinned to the closed form in float64 and torch's cast.
+    g = block_rng(53, 0, 0)
+    x = (g.standard_normal((300, 128)) * np.exp2(g.uniform(-30, 30, (300, 1)))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 3] = 448.0 * 2.0 ** -5          # amax / 448 exactly a power of two
+    x[2] = 0.0
+    x[2, 9] = -7.0                       # 7 / 448 = 2^-6 exactly
+    x[3] = np.float32(1e-38) * g.standard_normal(128).astype(np.float32)   # p clamps to -127
+    bits = to_bf16_bits(x)
+    xv = bf16_bits_to_f32(bits)
+    codes, exps, scales = oracle.quantize_rows_ue8m0(bits, lib)
+    amax = np.abs(xv).max(axis=1)
+    t = np.where(amax > 0, (amax / np.float32(FP8_MAX)).astype(np.float32), np.float32(1.0)).astype(np.float64)
+    p = np.maximum(np.ceil(np.log2(t)), -127).astype(np.int64)
+    assert np.array_equal(exps.astype(np.int64), p + 127), "E8M0 exponent is not ceil(log2(amax / 448))"
+    assert np.array_equal(scales.astype(np.float64), np.exp2(p.astype(np.float64))), "scale is not 2^p"
+    assert scales[1] == 2.0 ** -5 and scales[2] == 2.0 ** -6 and exps[0] == 127
+    y = np.clip(xv.astype(np.float64) / scales[:, None].astype(np.float64), -FP8_MAX, FP8_MAX).astype(np.float32)
+    assert np.array_equal(codes, _torch_e4m3(y)), "UE8M0 codes differ from the torch cast of x / 2^p"
+    assert np.all((codes & 0x7F) <= 0x7E)

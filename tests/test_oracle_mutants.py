@@ -42,10 +42,12 @@ MUTANTS = [
      [pins.check_e4m3_encode_midpoints, pins.check_e4m3_encode_vs_torch]),
     ("e4m3_round_down", "    if (dl < dh)\n        return (uint8_t)lo;", "    if (dl <= dh + 1.0)\n        return (uint8_t)lo;",
      [pins.check_e4m3_encode_midpoints, pins.check_e4m3_encode_vs_torch]),
-    ("quant_scale_447", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 447.0f : 1.0f",
+    ("quant_scale_447", "float s = amax > 0.0f ? amax / 448.0f : 1.0f", "float s = amax > 0.0f ? amax / 447.0f : 1.0f",
      [pins.check_quantize_rows_closed_forms, pins.check_quantize_rows_vs_generator]),
     ("quant_sign_dropped", "return (uint8_t)((signbit(y) ? 0x80 : 0) | e4m3_encode_abs(fabsf(y)));",
      "return (uint8_t)(e4m3_encode_abs(fabsf(y)));", [pins.check_e4m3_encode_round_trip]),
+    ("ue8m0_floor", "int p = m == 0.5f ? e - 1 : e;", "int p = e - 1;", [pins.check_quantize_ue8m0]),
+    ("ue8m0_no_clamp", "    if (p < -127)\n        p = -127;\n", "", [pins.check_quantize_ue8m0]),
     ("append_slot_shift", "int64_t row = (int64_t)blk * bs + pos[i] % bs;",
      "int64_t row = (int64_t)blk * bs + (pos[i] + 1) % bs;", [pins.check_append_paged_round_trip]),
     ("mla_future_keys", "int64_t n = visible_keys(pos[t], S);\n        const int32_t *row",

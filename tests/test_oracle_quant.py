@@ -19,7 +19,7 @@ from dsa_inputs import to_bf16_bits
 
 @pytest.mark.parametrize("check", [pins.check_e4m3_encode_round_trip, pins.check_e4m3_encode_midpoints,
                                    pins.check_e4m3_encode_vs_torch, pins.check_quantize_rows_closed_forms,
-                                   pins.check_quantize_rows_vs_generator],
+                                   pins.check_quantize_rows_vs_generator, pins.check_quantize_ue8m0],
                          ids=lambda c: c.__name__)
 def test_quantizer_pin(check):
     check(oracle.load())
