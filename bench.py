@@ -10,8 +10,9 @@ one JSON line.
 
 ``--workload`` selects another configuration (tiny, prefill_4k, chunked_131k, decode_64; decode
 times the fused paged decode call against its HBM roofline; quantize_append_32k times the FP8
-quantization of the L = 32K queries and the paged append of its tokens), and ``--all-configs``
-prints one line per configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
+quantization of the L = 32K queries and the paged append of its tokens; indexer_ue8m0_32k the
+indexer with power-of-two scales inside the MFMA), and ``--all-configs`` prints one line per
+configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -350,14 +351,77 @@ def run_quantize_append(args, dev):
     }
 
 
+def run_indexer_ue8m0(args, dev):
+    """The L = 32K prefill indexer with power-of-two (UE8M0) scales applied inside the FP8 MFMA
+    (dsa_indexer_logits_ue8m0), timed beside the fp32-scale indexer on the same codes (scales
+    2^(e - 127)); inputs are seeded bf16 vectors quantized on the device."""
+    import torch
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import get
+    wl = get(HEADLINE)
+    T, S, H_I, D_I = wl.T, wl.S, wl.H_I, wl.D_I
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    print("generating ue8m0 indexer inputs", file=sys.stderr, flush=True)
+    q = torch.randn((T, H_I, D_I), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((S, D_I), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.rand((T, H_I), generator=g, device=dev) / H_I).contiguous()
+    q8, qe, qs = dsa.dsa_quantize_fp8_rows_ue8m0(q)
+    k8, ke, ks = dsa.dsa_quantize_fp8_rows_ue8m0(k)
+    del q, k
+    logits = torch.empty((T, dsa.ld_for(S)), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dsa.dsa_indexer_logits_ue8m0(q8, qe, w, k8, ke, 0, logits)
+        if ev:
+            ev[1].record(stream)
+        dsa.dsa_indexer_logits(q8, qs, w, k8, ks, 0, logits)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in evs])
+    ums, fms = per.mean(axis=0)
+    wm = work_model(wl)
+    stages = {
+        "indexer_ue8m0": {"ms": float(ums), "bound": "mfma", "achieved_tflops": wm["indexer_flop"] / ums / 1e9,
+                          "frac": wm["indexer_flop"] / (ums / 1e3) / PEAK_FP8},
+        "indexer_fp32_scales": {"ms": float(fms), "bound": "mfma", "achieved_tflops": wm["indexer_flop"] / fms / 1e9,
+                                "frac": wm["indexer_flop"] / (fms / 1e3) / PEAK_FP8},
+    }
+    roof = {"kernel": "indexer_prefill_kernel (E8M0 operand scales)", "bound": "mfma",
+            "achieved": wm["indexer_flop"] / (ums / 1e3) / 1e12, "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s",
+            "traffic": None, "algorithmic_flop_per_launch": wm["indexer_flop"], "avg_launch_ms": float(ums)}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    ms = per[:, 0]
+    return {
+        "value": T / (float(np.median(ms)) / 1e3), "ms_per_step": float(np.median(ms)), "step_ms_events": percentiles(ms),
+        "roofline": roof, "stages": stages, "fused_ms_per_step": None,
+        "config": {"workload": "indexer_ue8m0_32k", "T": T, "S": S, "q_start": 0, "H_I": H_I, "D_I": D_I,
+                   "parallelism": "single GPU"},
+    }
+
+
 def run_one(name, args, dev, with_cpu: bool):
     from dsa_inputs import get
-    if name == "quantize_append_32k":
-        res = run_quantize_append(args, dev)
-        line = {"metric": "query tokens/s (FP8 quantize of indexer queries + paged append, L=32K)",
+    if name in ("quantize_append_32k", "indexer_ue8m0_32k"):
+        qa = name == "quantize_append_32k"
+        res = run_quantize_append(args, dev) if qa else run_indexer_ue8m0(args, dev)
+        line = {"metric": ("query tokens/s (FP8 quantize of indexer queries + paged append, L=32K)" if qa else
+                           "query tokens/s (indexer with UE8M0 scales in the MFMA, L=32K)"),
                 "value": res["value"], "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
-                "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp8-e4m3 out",
+                "scaling": "weak", "vs_baseline": None,
+                "dtype": "bf16 in, fp8-e4m3 out" if qa else "fp8-e4m3 with e8m0 scales",
                 "data": "synthetic (seeded torch normal, bf16)", "config": res["config"], "roofline": res["roofline"],
                 "stages": res["stages"], "step_ms_events": res["step_ms_events"], "fused_ms_per_step": None,
                 "cpu_baseline": None}
@@ -418,7 +482,8 @@ def main():
     dev = torch.device("cuda:0")
     dsa.load()
     if args.all_configs:
-        for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64", "quantize_append_32k"]:
+        for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64", "quantize_append_32k",
+                     "indexer_ue8m0_32k"]:
             print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return

@@ -7,5 +7,6 @@ binding: torch provides device memory and streams, the library does every step.
 from ._lib import DSAError, EXPORTS, LIB_PATH, load  # noqa: F401
 from .api import (  # noqa: F401
     PagedKV, decode_workspace_size, dsa_append_paged, dsa_decode_paged, dsa_indexer_logits, dsa_prefill_paged,
-    dsa_quantize_fp8_rows, dsa_sparse_mla_fwd, dsa_topk, ld_for, make_dims, prefill_workspace_size,
+    dsa_indexer_logits_ue8m0, dsa_quantize_fp8_rows, dsa_quantize_fp8_rows_ue8m0, dsa_sparse_mla_fwd, dsa_topk,
+    ld_for, make_dims, prefill_workspace_size,
 )

@@ -21,7 +21,7 @@ EXPORTS = [
     "dsa_status_string", "dsa_last_error", "dsa_abi_version", "dsa_indexer_logits",
     "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd",
     "dsa_prefill_workspace_size", "dsa_prefill_paged", "dsa_decode_workspace_size", "dsa_decode_paged",
-    "dsa_quantize_fp8_rows", "dsa_append_paged",
+    "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0", "dsa_indexer_logits_ue8m0",
 ]
 
 _p = ctypes.c_void_p
@@ -83,8 +83,11 @@ def load(path: str = LIB_PATH):
                                      _p, _p, _p, _p, _p, _p, _sz, _p]
     lib.dsa_quantize_fp8_rows.argtypes = [_p, _i64, _i32, _p, _p, _p]
     lib.dsa_append_paged.argtypes = [ctypes.POINTER(PagedCache), _i32, _p, _p, _i64, _i32, _i32, _p, _p, _p]
+    lib.dsa_quantize_fp8_rows_ue8m0.argtypes = [_p, _i64, _i32, _p, _p, _p, _p]
+    lib.dsa_indexer_logits_ue8m0.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i64, _p]
     for name in ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_paged",
-                 "dsa_decode_paged", "dsa_quantize_fp8_rows", "dsa_append_paged"):
+                 "dsa_decode_paged", "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0",
+                 "dsa_indexer_logits_ue8m0"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -214,3 +214,37 @@ def dsa_append_paged(cache: PagedKV, seq_ids, positions, k, kv):
                                   _dev(positions, "positions", 1, 4), n, D_I, D_qk, _dev(k, "k", 2, 2),
                                   _dev(kv, "kv", 2, 2), _stream(k))
     check("dsa_append_paged", status)
+
+
+def dsa_quantize_fp8_rows_ue8m0(x, codes=None, exps=None, scales=None, want_scales: bool = True):
+    """Per-row FP8 codes with power-of-two scales: (codes uint8 [..., D], biased exponents uint8
+    [...], scales fp32 [...] or None) of a bf16 tensor x [..., D]."""
+    lib = load()
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty(x.shape[:-1], dtype=torch.uint8, device=x.device)
+    if scales is None and want_scales:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    nd = x.dim()
+    status = lib.dsa_quantize_fp8_rows_ue8m0(_dev(x, "x", nd, 2), rows, D, _dev(codes, "codes", nd, 1),
+                                             _dev(exps, "exps", nd - 1, 1), _opt(scales), _stream(x))
+    check("dsa_quantize_fp8_rows_ue8m0", status)
+    return codes, exps, scales
+
+
+def dsa_indexer_logits_ue8m0(q8, q_exp, w, k8, k_exp, q_start: int = 0, logits=None) -> torch.Tensor:
+    """Index scores with UE8M0 exponent scales applied inside the FP8 MFMA (see dsa_indexer_logits)."""
+    lib = load()
+    T, H_I, D_I = q8.shape
+    S = k8.shape[0]
+    if logits is None:
+        logits = torch.empty((T, ld_for(S)), dtype=torch.float32, device=q8.device)
+    status = lib.dsa_indexer_logits_ue8m0(
+        _dev(q8, "q8", 3, 1), _dev(q_exp, "q_exp", 2, 1), _dev(w, "w", 2, 4), _dev(k8, "k8", 2, 1),
+        _dev(k_exp, "k_exp", 1, 1), T, S, H_I, D_I, q_start, _dev(logits, "logits", 2, 4), logits.shape[1],
+        _stream(q8))
+    check("dsa_indexer_logits_ue8m0", status)
+    return logits

@@ -186,6 +186,27 @@ dsa_status_t dsa_indexer_logits(const uint8_t* q8, const float* q_scale, const f
                     "indexer launch");
 }
 
+dsa_status_t dsa_indexer_logits_ue8m0(const uint8_t* q8, const uint8_t* q_exp, const float* w, const uint8_t* k8,
+                                      const uint8_t* k_exp, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
+                                      int64_t q_start, float* logits, int64_t ld_logits, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  dsa_status_t s = check_indexer_dims(H_I, D_I);
+  if (s != DSA_OK) return s;
+  if (T == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1 when T > 0");
+  REQUIRE(ld_logits >= S && ld_logits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_logits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_logits, (long long)S);
+  REQUIRE_PTR(q8);
+  REQUIRE_PTR(q_exp);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(k8);
+  REQUIRE_PTR(k_exp);
+  REQUIRE_PTR(logits);
+  return hip_status(dsa::launch_indexer_prefill(q8, nullptr, w, k8, nullptr, nullptr, 0, T, S, H_I, D_I, q_start,
+                                                logits, ld_logits, stream, q_exp, k_exp),
+                    "indexer launch");
+}
+
 size_t dsa_topk_workspace_size(int64_t T, int64_t S, int32_t k) {
   if (T <= 0 || S <= 0 || k <= 0) return 0;
   return dsa::topk_workspace_bytes(T, S, k);
@@ -395,7 +416,19 @@ dsa_status_t dsa_quantize_fp8_rows(const uint16_t* x, int64_t rows, int32_t D, u
   REQUIRE_PTR(x);
   REQUIRE_PTR(codes);
   REQUIRE_PTR(scales);
-  return hip_status(dsa::launch_quantize_rows(x, rows, D, codes, scales, stream), "quantize launch");
+  return hip_status(dsa::launch_quantize_rows(x, rows, D, codes, scales, nullptr, stream), "quantize launch");
+}
+
+dsa_status_t dsa_quantize_fp8_rows_ue8m0(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes,
+                                         uint8_t* exps, float* scales, hipStream_t stream) {
+  REQUIRE(rows >= 0, DSA_ERR_INVALID_ARGUMENT, "negative rows");
+  REQUIRE(dsa::quantize_supported(D), DSA_ERR_UNSUPPORTED, "D=%d must be a multiple of 8 in [8, 512]", D);
+  if (rows == 0) return ok();
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(exps);
+  OPTIONAL_PTR(scales);
+  return hip_status(dsa::launch_quantize_rows(x, rows, D, codes, scales, exps, stream), "quantize launch");
 }
 
 dsa_status_t dsa_append_paged(const dsa_paged_cache_t* c, int32_t B, const int32_t* seq_ids,

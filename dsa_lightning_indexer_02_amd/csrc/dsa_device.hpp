@@ -33,6 +33,12 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, co
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same product with E8M0 operand scales: lane l's byte sa (sb) multiplies the 32 A (B)
+// elements it supplies, i.e. row (column) l % 16 of its k-block, by 2^(byte - 127).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128_scaled(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(const s16x8& a, const s16x8& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

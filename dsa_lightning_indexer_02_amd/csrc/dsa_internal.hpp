@@ -12,11 +12,13 @@
 namespace dsa {
 
 // ---- lightning indexer
-size_t indexer_prefill_smem(int32_t H_I);
+size_t indexer_prefill_smem(int32_t H_I, bool e8);
+// q_exp / k_exp non-null: UE8M0 exponent scales applied in the MFMA (qs, ks unused)
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
                                   const float* ks, const int32_t* table, int32_t block_shift, int64_t T,
                                   int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, float* logits,
-                                  int64_t ld, hipStream_t stream);
+                                  int64_t ld, hipStream_t stream, const uint8_t* q_exp = nullptr,
+                                  const uint8_t* k_exp = nullptr);
 hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
                                  const float* ks, const int32_t* table, int64_t max_blocks,
                                  int32_t block_shift, const int32_t* seq_lens, int32_t B, int64_t max_len,
@@ -24,8 +26,9 @@ hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float
 
 // ---- FP8 quantization and paged append
 bool quantize_supported(int32_t D);
+// exps != nullptr: power-of-two (UE8M0) scales, biased exponents written to exps (scales may be null)
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes, float* scales,
-                                hipStream_t stream);
+                                uint8_t* exps, hipStream_t stream);
 hipError_t launch_append_paged(uint8_t* k8_pool, float* ks_pool, uint16_t* kv_pool, int64_t num_blocks,
                                int32_t block_shift, const int32_t* table, int64_t max_blocks, int32_t B,
                                const int32_t* seq_ids, const int32_t* positions, int64_t n, int32_t D_I,

@@ -24,15 +24,20 @@ constexpr int IDX_PREFILL_WAVES = 12;  // three waves per SIMD: VALU of one besi
 
 // HI > 0: the head count is a compile-time constant and the head loop is fully unrolled;
 // HI == 0: any head count (plain loop).
-template <int NK, int HI>
+// E8: the per-row scales are power-of-two exponents (UE8M0: q_exp [T][H_I], k_exp [S], value
+// 2^(e - 127)) applied inside the MFMA as its operand scales (lane l's byte scales the row or
+// column l % 16 it supplies), so the epilogue weighs by w alone and applies no key scale; qs and
+// ks are not read.  Otherwise the fp32 scales qs, ks are applied in the epilogue.
+template <int NK, int HI, bool E8>
 __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, RowMap keymap, int64_t T,
     int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, float* __restrict__ logits, int64_t ld,
-    int64_t key_chunk) {
+    int64_t key_chunk, const uint8_t* __restrict__ q_exp, const uint8_t* __restrict__ k_exp) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* qtile = smem;                                                        // [H_I][16][144]
   float* wq = reinterpret_cast<float*>(smem + (size_t)H_I * IDX_ROWS * IDX_QROW_BYTES);  // [H_I][16]
+  uint8_t* qe = reinterpret_cast<uint8_t*>(wq + H_I * IDX_ROWS);                // E8: [H_I][16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -58,14 +63,19 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
   for (int p = tid; p < H_I * IDX_ROWS; p += blockDim.x) {
     const int row = p & (IDX_ROWS - 1), head = p >> 4;
     const int64_t t = t0 + row;
-    wq[head * IDX_ROWS + row] = t < T ? w[t * H_I + head] * qs[t * H_I + head] : 0.0f;
+    if constexpr (E8) {
+      wq[head * IDX_ROWS + row] = t < T ? w[t * H_I + head] : 0.0f;
+      qe[head * IDX_ROWS + row] = t < T ? q_exp[t * H_I + head] : (uint8_t)127;
+    } else {
+      wq[head * IDX_ROWS + row] = t < T ? w[t * H_I + head] * qs[t * H_I + head] : 0.0f;
+    }
   }
   __syncthreads();
 
   const bool klane_has_bytes = (g * 32) < D_I;
   const int64_t pass_keys = (int64_t)IDX_PREFILL_WAVES * NK * 16;
-  // key tiles of one pass (MFMA B operands) and their scales
-  auto load_keys = [&](int64_t base, v8i (&B)[NK], float (&ksv)[NK]) {
+  // key tiles of one pass (MFMA B operands) and their scales (E8: exponent bytes)
+  auto load_keys = [&](int64_t base, v8i (&B)[NK], float (&ksv)[NK], int (&kb)[NK]) {
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) {
       const int64_t s = min(base + kt * 16 + j16, S - 1);
@@ -73,13 +83,17 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
       v8i b = {0, 0, 0, 0, 0, 0, 0, 0};
       if (klane_has_bytes) b = *reinterpret_cast<const v8i*>(k8 + row * D_I + g * 32);
       B[kt] = b;
-      ksv[kt] = ks[row];
+      if constexpr (E8)
+        kb[kt] = k_exp[row];
+      else
+        ksv[kt] = ks[row];
     }
   };
   for (int64_t base = c0 + (int64_t)wave * NK * 16; base < c1; base += pass_keys) {
     v8i B[NK];
     float ksv[NK];
-    load_keys(base, B, ksv);
+    int kb[NK];
+    load_keys(base, B, ksv, kb);
     v4f acc[NK];
 #pragma unroll
     for (int kt = 0; kt < NK; ++kt) acc[kt] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -94,6 +108,13 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
     auto load_a = [&](int head) {
       return *reinterpret_cast<const v8i*>(qtile + (head * IDX_ROWS + j16) * IDX_QROW_BYTES + g * 32);
     };
+    auto load_sa = [&](int head) { return E8 ? (int)qe[head * IDX_ROWS + j16] : 0; };
+    auto mfma = [&](const v8i& A, int sa, int kt) {
+      if constexpr (E8)
+        return mfma_fp8_16x16x128_scaled(A, B[kt], (v4f){0.f, 0.f, 0.f, 0.f}, sa, kb[kt]);
+      else
+        return mfma_fp8_16x16x128(A, B[kt], (v4f){0.f, 0.f, 0.f, 0.f});
+    };
     auto load_w = [&](int head) { return *reinterpret_cast<const v4f*>(wq + head * IDX_ROWS + 4 * g); };
     if constexpr (HI > 0) {
       // Software pipeline over the heads, two per iteration with static slots (last iteration
@@ -105,38 +126,43 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
       v4f c0[NK], c1[NK];
       v8i A0 = load_a(0), A1;
       v4f w0 = load_w(0), w1;
-      auto mma = [&](const v8i& A, v4f (&c)[NK]) {
+      int s0 = load_sa(0), s1;
+      auto mma = [&](const v8i& A, int sa, v4f (&c)[NK]) {
 #pragma unroll
-        for (int kt = 0; kt < NK; ++kt) c[kt] = mfma_fp8_16x16x128(A, B[kt], (v4f){0.f, 0.f, 0.f, 0.f});
+        for (int kt = 0; kt < NK; ++kt) c[kt] = mfma(A, sa, kt);
       };
-      mma(A0, c0);
+      mma(A0, s0, c0);
       for (int head = 0; head < HI - 2; head += 2) {
         A1 = load_a(head + 1);
         w1 = load_w(head + 1);
+        s1 = load_sa(head + 1);
         __builtin_amdgcn_sched_barrier(0);
-        mma(A1, c1);          // head + 1
+        mma(A1, s1, c1);      // head + 1
         relu_acc(w0, c0);     // head
         __builtin_amdgcn_sched_barrier(0);
         A0 = load_a(head + 2);
         w0 = load_w(head + 2);
+        s0 = load_sa(head + 2);
         __builtin_amdgcn_sched_barrier(0);
-        mma(A0, c0);          // head + 2
+        mma(A0, s0, c0);      // head + 2
         relu_acc(w1, c1);     // head + 1
         __builtin_amdgcn_sched_barrier(0);
       }
       A1 = load_a(HI - 1);
       w1 = load_w(HI - 1);
+      s1 = load_sa(HI - 1);
       __builtin_amdgcn_sched_barrier(0);
-      mma(A1, c1);
+      mma(A1, s1, c1);
       relu_acc(w0, c0);
       relu_acc(w1, c1);
     } else {
       for (int head = 0; head < H_I; ++head) {
         const v8i A = load_a(head);
         const v4f wv = load_w(head);
+        const int sa = load_sa(head);
         v4f c[NK];
 #pragma unroll
-        for (int kt = 0; kt < NK; ++kt) c[kt] = mfma_fp8_16x16x128(A, B[kt], (v4f){0.f, 0.f, 0.f, 0.f});
+        for (int kt = 0; kt < NK; ++kt) c[kt] = mfma(A, sa, kt);
         relu_acc(wv, c);
       }
     }
@@ -147,7 +173,7 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = t0 + 4 * g + r;
-        if (t < T && s < c1 && s < q_start + t + 1) logits[t * ld + s] = acc[kt][r] * ksv[kt];
+        if (t < T && s < c1 && s < q_start + t + 1) logits[t * ld + s] = E8 ? acc[kt][r] : acc[kt][r] * ksv[kt];
       }
     }
   }
@@ -409,14 +435,16 @@ __global__ __launch_bounds__(IDX_DECODE_THREADS, 2) void indexer_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-size_t indexer_prefill_smem(int32_t H_I) {
-  return (size_t)H_I * IDX_ROWS * IDX_QROW_BYTES + (size_t)H_I * IDX_ROWS * sizeof(float);
+size_t indexer_prefill_smem(int32_t H_I, bool e8) {
+  return (size_t)H_I * IDX_ROWS * IDX_QROW_BYTES + (size_t)H_I * IDX_ROWS * sizeof(float) +
+         (e8 ? (size_t)H_I * IDX_ROWS : 0);
 }
 
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
                                   const uint8_t* k8, const float* ks, const int32_t* table,
                                   int32_t block_shift, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
-                                  int64_t q_start, float* logits, int64_t ld, hipStream_t stream) {
+                                  int64_t q_start, float* logits, int64_t ld, hipStream_t stream,
+                                  const uint8_t* q_exp, const uint8_t* k_exp) {
   if (T <= 0) return hipSuccess;
   constexpr int NK = 4;
   const int64_t tiles = (T + IDX_ROWS - 1) / IDX_ROWS;
@@ -431,16 +459,18 @@ hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const floa
   key_chunk = std::max<int64_t>(key_chunk, 1);
   const int64_t chunks = (n_last + key_chunk - 1) / key_chunk;
   dim3 grid((unsigned)chunks, (unsigned)tiles);
-  const size_t smem = indexer_prefill_smem(H_I);
-  auto kernel = H_I == 64 ? indexer_prefill_kernel<NK, 64> : indexer_prefill_kernel<NK, 0>;
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[H_I == 64]) {
+  const bool e8 = q_exp != nullptr;
+  const size_t smem = indexer_prefill_smem(H_I, e8);
+  auto kernel = e8 ? (H_I == 64 ? indexer_prefill_kernel<NK, 64, true> : indexer_prefill_kernel<NK, 0, true>)
+                   : (H_I == 64 ? indexer_prefill_kernel<NK, 64, false> : indexer_prefill_kernel<NK, 0, false>);
+  static bool attr_set[2][2] = {{false, false}, {false, false}};
+  if (!attr_set[e8][H_I == 64]) {
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set[H_I == 64] = true;
+    attr_set[e8][H_I == 64] = true;
   }
   hipLaunchKernelGGL(kernel, grid, dim3(IDX_PREFILL_WAVES * WAVE), smem, stream, q8, qs, w, k8, ks,
-                     RowMap{table, block_shift}, T, S, H_I, D_I, q_start, logits, ld, key_chunk);
+                     RowMap{table, block_shift}, T, S, H_I, D_I, q_start, logits, ld, key_chunk, q_exp, k_exp);
   return hipGetLastError();
 }
 

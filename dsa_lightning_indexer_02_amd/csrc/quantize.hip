@@ -25,8 +25,11 @@ static int qz_lanes(int32_t D) {
 
 // Quantize the 8 values this lane holds (x: 8 bf16 bit patterns in a v4i) of a row whose lanes
 // are the aligned group of `lanes` lanes containing this one; `active`: this lane holds values.
-// Returns the 8 codes (two dwords); *scale receives the row scale.
-__device__ __forceinline__ v2i quantize8(v4i x, bool active, int lanes, float* scale) {
+// Returns the 8 codes (two dwords); *scale receives the row scale.  UE8M0: the scale is the
+// smallest power of two 2^p >= amax / 448 (p >= -127, createthis gist page, indexer listing: the
+// cast's use_ue8m0 option) and *exp8 receives p + 127.
+template <bool UE8M0>
+__device__ __forceinline__ v2i quantize8(v4i x, bool active, int lanes, float* scale, uint32_t* exp8) {
   float v[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -40,7 +43,14 @@ __device__ __forceinline__ v2i quantize8(v4i x, bool active, int lanes, float* s
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
   for (int o = 1; o < lanes; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const float s = amax > 0.0f ? __fdiv_rn(amax, QZ_FP8_MAX) : 1.0f;
+  float s = amax > 0.0f ? __fdiv_rn(amax, QZ_FP8_MAX) : 1.0f;
+  if constexpr (UE8M0) {
+    int e;
+    const float m = frexpf(s, &e);  // s = m 2^e, 0.5 <= m < 1
+    const int p = max(m == 0.5f ? e - 1 : e, -127);
+    s = ldexpf(1.0f, p);
+    *exp8 = (uint32_t)(p + 127);
+  }
   *scale = s;
   float y[8];
 #pragma unroll
@@ -58,9 +68,11 @@ __device__ __forceinline__ v2i quantize8(v4i x, bool active, int lanes, float* s
 // issues all of their loads before it converts any.
 constexpr int QZ_PIECES = 4;
 
+template <bool UE8M0>
 __global__ __launch_bounds__(QZ_THREADS) void quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                   int32_t D, int32_t lanes, uint8_t* __restrict__ codes,
-                                                                  float* __restrict__ scales) {
+                                                                  float* __restrict__ scales,
+                                                                  uint8_t* __restrict__ exps) {
   const int64_t g0 = (int64_t)blockIdx.x * QZ_THREADS * QZ_PIECES + threadIdx.x;
   v4i xv[QZ_PIECES];
   int64_t r[QZ_PIECES];
@@ -79,9 +91,13 @@ __global__ __launch_bounds__(QZ_THREADS) void quantize_rows_kernel(const uint16_
 #pragma unroll
   for (int u = 0; u < QZ_PIECES; ++u) {
     float s;
-    const v2i c = quantize8(xv[u], active[u], lanes, &s);
+    uint32_t e8 = 0;
+    const v2i c = quantize8<UE8M0>(xv[u], active[u], lanes, &s, &e8);
     if (active[u]) *reinterpret_cast<v2i*>(codes + r[u] * D + j[u] * 8) = c;
-    if (in_row[u] && j[u] == 0) scales[r[u]] = s;
+    if (in_row[u] && j[u] == 0) {
+      if (scales) scales[r[u]] = s;
+      if constexpr (UE8M0) exps[r[u]] = (uint8_t)e8;
+    }
   }
 }
 
@@ -106,7 +122,8 @@ __global__ __launch_bounds__(QZ_THREADS) void append_paged_kernel(
     v4i xv = {0, 0, 0, 0};
     if (active) xv = *reinterpret_cast<const v4i*>(k + i * D_I + lane * 8);
     float s;
-    const v2i c = quantize8(xv, active, lanes, &s);
+    uint32_t e8;
+    const v2i c = quantize8<false>(xv, active, lanes, &s, &e8);
     if (active) *reinterpret_cast<v2i*>(k8_pool + row * D_I + lane * 8) = c;
     if (lane == 0) ks_pool[row] = s;
   }
@@ -118,13 +135,17 @@ __global__ __launch_bounds__(QZ_THREADS) void append_paged_kernel(
 bool quantize_supported(int32_t D) { return D >= 8 && D <= 512 && D % 8 == 0; }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes, float* scales,
-                                hipStream_t stream) {
+                                uint8_t* exps, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   const int lanes = qz_lanes(D);
   const int64_t pieces = rows * lanes;
   const int64_t grid = (pieces + QZ_THREADS * QZ_PIECES - 1) / (QZ_THREADS * QZ_PIECES);
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, x, rows, D, lanes,
-                     codes, scales);
+  if (exps)
+    hipLaunchKernelGGL(quantize_rows_kernel<true>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, x, rows, D,
+                       lanes, codes, scales, exps);
+  else
+    hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, x, rows, D,
+                       lanes, codes, scales, exps);
   return hipGetLastError();
 }
 

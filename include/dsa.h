@@ -167,6 +167,26 @@ dsa_status_t dsa_quantize_fp8_rows(const uint16_t *x, int64_t rows, int32_t D, u
                                    hipStream_t stream);
 
 /*
+ * Power-of-two (UE8M0) variant of the quantizer (createthis gist page, indexer listing: the
+ * cast helper's use_ue8m0 option): the scale of row r is 2^p_r, p_r the smallest integer with
+ * 2^p_r >= max_i |x[r][i]| / 448 (fp32 division; 1 for an all-zero row), at least -127; exps[r] =
+ * p_r + 127 (u8 [rows]); scales[r] = 2^p_r (f32 [rows], optional: NULL skips it); codes as above
+ * with that scale.  Same shapes, alignment and D range as dsa_quantize_fp8_rows.
+ */
+dsa_status_t dsa_quantize_fp8_rows_ue8m0(const uint16_t *x, int64_t rows, int32_t D, uint8_t *codes,
+                                         uint8_t *exps, float *scales, hipStream_t stream);
+
+/*
+ * Lightning-indexer scores with UE8M0 scales: the same scores as dsa_indexer_logits with
+ * q_scale[t][j] = 2^(q_exp[t][j] - 127) and k_scale[s] = 2^(k_exp[s] - 127), the exponents
+ * applied as the FP8 MFMA's own operand scales (gfx950 v_mfma_scale_f32_16x16x128_f8f6f4) rather
+ * than in the epilogue.  q_exp u8 [T][H_I], k_exp u8 [S]; everything else as dsa_indexer_logits.
+ */
+dsa_status_t dsa_indexer_logits_ue8m0(const uint8_t *q8, const uint8_t *q_exp, const float *w, const uint8_t *k8,
+                                      const uint8_t *k_exp, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
+                                      int64_t q_start, float *logits, int64_t ld_logits, hipStream_t stream);
+
+/*
  * Paged append (summary page, section "Key claims": paged indexer caches).  Writes n new tokens
  * into the cache c: token i of sequence seq_ids[i] (0 <= seq_ids[i] < B, a row of
  * c->block_table) at position positions[i] gets, in physical row

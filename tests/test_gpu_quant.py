@@ -164,3 +164,48 @@ def test_quantize_append_then_decode(dev):
         parity.check_mla(g_out[b:b + 1], dget(f32)[b:b + 1], dget(lse)[b:b + 1], oo, ol,
                          "decode seq %d" % b)
 
+
+
+# ----------------------------------------------------------------- UE8M0 scales (next row 2)
+@pytest.mark.parametrize("D", [32, 128])
+def test_quantize_ue8m0_bit_exact(dev, D):
+    import dsa_lightning_indexer_02_amd as dsa
+    rng = block_rng(65, D, 0)
+    bits = _rows(rng, 777, D)
+    print("case quantize ue8m0", bits.shape, flush=True)
+    codes, exps, scales = dsa.dsa_quantize_fp8_rows_ue8m0(dput(bits, dev).view(torch.bfloat16))
+    oc, oe, osc = oracle.quantize_rows_ue8m0(bits)
+    assert np.array_equal(dget(exps), oe)
+    assert np.array_equal(dget(scales), osc)
+    assert np.array_equal(dget(codes), oc)
+
+
+@pytest.mark.parametrize("T,S,q_start,H_I,D_I", [(300, 700, 400, 64, 128), (77, 200, 123, 4, 32),
+                                                 (1000, 1000, 0, 64, 128)])
+def test_indexer_ue8m0_scaled_mfma(dev, T, S, q_start, H_I, D_I):
+    # scores from UE8M0-quantized inputs, exponents applied inside the MFMA, against the oracle
+    # indexer fed the same codes with fp32 scales 2^(e - 127)
+    import dsa_lightning_indexer_02_amd as dsa
+    import parity
+    rng = block_rng(66, T, H_I)
+    q = to_bf16_bits((rng.standard_normal((T, H_I, D_I)) * np.exp2(rng.uniform(-8, 8, (T, H_I, 1)))).astype(np.float32))
+    k = to_bf16_bits((rng.standard_normal((S, D_I)) * np.exp2(rng.uniform(-8, 8, (S, 1)))).astype(np.float32))
+    w = (rng.uniform(0, 1, (T, H_I)) / H_I).astype(np.float32)
+    print("case indexer ue8m0", T, S, q_start, H_I, D_I, flush=True)
+    q8, qe, qs = dsa.dsa_quantize_fp8_rows_ue8m0(dput(q, dev).view(torch.bfloat16))
+    k8, ke, ks = dsa.dsa_quantize_fp8_rows_ue8m0(dput(k, dev).view(torch.bfloat16))
+    lg = dsa.dsa_indexer_logits_ue8m0(q8, qe, dput(w, dev), k8, ke, q_start=q_start)
+    # the same scores through the fp32-scale entry point (scales 2^(e - 127), applied in the epilogue)
+    lg32 = dsa.dsa_indexer_logits(q8, qs, dput(w, dev), k8, ks, q_start=q_start)
+    torch.cuda.synchronize()
+    oq8, oqe, oqs = oracle.quantize_rows_ue8m0(q)
+    ok8, oke, oks = oracle.quantize_rows_ue8m0(k)
+    assert np.array_equal(dget(q8), oq8) and np.array_equal(dget(ke), oke)
+    pos = q_start + np.arange(T)
+    o = oracle.indexer(oq8, oqs, w, pos, ok8, oks)
+    A = parity.magnitude(oq8, oqs, w, ok8, oks, pos, S)
+    g = dget(lg)[:, :S]
+    parity.check_indexer(g, o, A, D_I, H_I, "indexer ue8m0")
+    m = ~np.isnan(o)
+    g32 = dget(lg32)[:, :S]
+    assert np.all(np.abs(g[m] - g32[m]) <= 2.0 ** -20 * A[m]), "scaled MFMA and epilogue scaling disagree"
