@@ -201,15 +201,16 @@ __device__ void sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32
   }
   uint32_t pivot = mn;  // every valid key
   if (cn > TK_CAND) {
-    // sample element 17 i (i < 4) of every thread; lane l's copy sits at the lane-0 position + 4 l
+    // sample element 17 i (i < EPT / 16) of every thread; lane l's copy sits at the lane-0 position + 4 l
     // (elem_pos), so the number of valid samples follows from cn without a reduction
-    static_assert(EPT >= 52, "four sampled elements 17 apart");
-    uint32_t smp[4];
+    constexpr int NS = EPT / 16;  // sampled elements per thread, 17 apart
+    static_assert(NS >= 1 && 17 * (NS - 1) < EPT, "sample positions");
+    uint32_t smp[NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) smp[i] = key[17 * i];
+    for (int i = 0; i < NS; ++i) smp[i] = key[17 * i];
     uint32_t m = 0;
     for (int w = 0; w < TK_WAVES; ++w)
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NS; ++i) {
         const int64_t rest = cn - elem_pos<EPT>(w, 0, 17 * i);  // valid lanes: 4 l < rest
         m += (uint32_t)min<int64_t>(WAVE, max<int64_t>(0, (rest + 3) / 4));
       }
@@ -219,7 +220,7 @@ __device__ void sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32
     const float w = er + 4.0f * sqrtf(er) + 16.0f;
     if (w <= (float)m) {
       uint32_t ts, tr;
-      radix_select<4>(smp, (uint32_t)w, mx, mn, sh, ts, tr);
+      radix_select<NS>(smp, (uint32_t)w, mx, mn, sh, ts, tr);
       pivot = ts;
     }
   }
@@ -347,21 +348,55 @@ __device__ __forceinline__ void store_staged(const TopkShared& sh, int32_t* __re
   }
 }
 
-// Load this thread's elements of scores[0 .. n) (n <= 512 * EPT) as keys.
+// Load this thread's elements of scores[0 .. n) (1 <= n <= 512 * EPT) as keys (0 past n).  The
+// loads are unconditional so that all of them are in flight before the first one is waited for:
+// a group of four past the end re-reads the row's last aligned group, which is in bounds because
+// rows start 16-byte aligned and their stride is a multiple of four floats.
 template <int EPT>
 __device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t n, uint32_t (&key)[EPT]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int last = (int)(((n + 3) & ~(int64_t)3) - 4);
+  v4f v[EPT / 4];
+#pragma unroll
+  for (int q = 0; q < EPT / 4; ++q)
+    v[q] = *reinterpret_cast<const v4f*>(row + min(elem_pos<EPT>(wave, lane, 4 * q), last));
 #pragma unroll
   for (int q = 0; q < EPT / 4; ++q) {
     const int p = elem_pos<EPT>(wave, lane, 4 * q);
-    if (p + 3 < n) {
-      const v4f v = *reinterpret_cast<const v4f*>(row + p);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) key[4 * q + c] = score_key(v[c]);
+    for (int c = 0; c < 4; ++c) key[4 * q + c] = p + c < n ? score_key(v[q][c]) : 0u;
+  }
+}
+
+// The selection of one chunk of cn (k < cn <= 512 EPT) elements with EPT elements per thread.
+template <int EPT>
+__device__ __forceinline__ void chunk_select(const float* __restrict__ logits, int64_t ld, int64_t t, int chunk,
+                                             int64_t c0, int64_t cn, bool single, int32_t k,
+                                             int32_t* __restrict__ out_idx, uint32_t* __restrict__ cand_key,
+                                             int32_t* __restrict__ cand_idx, int32_t G, TopkShared& sh) {
+  uint32_t key[EPT];
+  hist_clear(sh);
+  load_keys<EPT>(logits + t * ld + c0, cn, key);
+  uint32_t mx, mn, tau, k_rem;
+  block_minmax<EPT>(key, sh, mx, mn);
+  sampled_threshold<EPT>(key, cn, (uint32_t)k, mx, mn, sh, tau, k_rem);
+  if (single) {
+    if (k <= TK_STAGE) {
+      emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                                  [&](int pos, uint32_t slot) { sh.stage[slot] = (int32_t)(c0 + pos); });
+      store_staged(sh, out_idx, k);
     } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) key[4 * q + c] = (p + c < n) ? score_key(row[p + c]) : 0u;
+      emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh,
+                                  [&](int pos, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
     }
+  } else {
+    uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
+    int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
+    const float* row = logits + t * ld + c0;
+    emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh, [&](int pos, uint32_t slot) {
+      ck[slot] = score_key(row[pos]);  // re-read (L2): keeps the key array out of the loop
+      ci[slot] = (int32_t)(c0 + pos);
+    });
   }
 }
 
@@ -370,7 +405,7 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t
 // one chunk still write their final list.
 // mode 0: prefill rows (n_t = min(S, q_start + t + 1)); mode 1: decode rows (n = seq_lens[t]).
 template <bool SINGLE>
-__global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
+__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_chunk_kernel(
     const float* __restrict__ logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
     const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, int32_t G) {
@@ -396,30 +431,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     }
     return;
   }
-  uint32_t key[TK_CHUNK_EPT];
-  hist_clear(sh);
-  load_keys<TK_CHUNK_EPT>(logits + t * ld + c0, cn, key);
-  uint32_t mx, mn, tau, k_rem;
-  block_minmax<TK_CHUNK_EPT>(key, sh, mx, mn);
-  sampled_threshold<TK_CHUNK_EPT>(key, cn, (uint32_t)k, mx, mn, sh, tau, k_rem);
-  if (single) {
-    if (k <= TK_STAGE) {
-      emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh,
-                                  [&](int pos, uint32_t slot) { sh.stage[slot] = (int32_t)(c0 + pos); });
-      store_staged(sh, out_idx, k);
-    } else {
-      emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh,
-                                  [&](int pos, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
-    }
-  } else {
-    uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
-    int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
-    const float* row = logits + t * ld + c0;
-    emit_selected<TK_CHUNK_EPT>(key, tau, (uint32_t)k, k_rem, sh, [&](int pos, uint32_t slot) {
-      ck[slot] = score_key(row[pos]);  // re-read (L2): keeps the key array out of the loop
-      ci[slot] = (int32_t)(c0 + pos);
-    });
-  }
+  // the narrowest register layout that holds the chunk: the work per row follows its length
+  if (cn <= TK_CHUNK / 4)
+    chunk_select<TK_CHUNK_EPT / 4>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
+  else if (cn <= TK_CHUNK / 2)
+    chunk_select<TK_CHUNK_EPT / 2>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
+  else
+    chunk_select<TK_CHUNK_EPT>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
 }
 
 // Merge the chunk candidates of rows with more than one chunk.
@@ -438,11 +456,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   const int32_t* ci = cand_idx + t * G * (int64_t)k;
   uint32_t key[TK_MERGE_EPT];
   hist_clear(sh);
+  uint32_t raw[TK_MERGE_EPT];
 #pragma unroll
-  for (int e = 0; e < TK_MERGE_EPT; ++e) {
-    const int p = elem_pos<TK_MERGE_EPT>(wave, lane, e);
-    key[e] = p < total ? ck[p] : 0u;
-  }
+  for (int e = 0; e < TK_MERGE_EPT; ++e)  // unconditional loads (clamped index), masked below
+    raw[e] = ck[min<int64_t>(elem_pos<TK_MERGE_EPT>(wave, lane, e), total - 1)];
+#pragma unroll
+  for (int e = 0; e < TK_MERGE_EPT; ++e) key[e] = elem_pos<TK_MERGE_EPT>(wave, lane, e) < total ? raw[e] : 0u;
   uint32_t mx, mn, tau, k_rem;
   block_minmax<TK_MERGE_EPT>(key, sh, mx, mn);
   radix_select<TK_MERGE_EPT>(key, (uint32_t)k, mx, mn, sh, tau, k_rem);

@@ -86,20 +86,34 @@ def test_topk_heavy_tail(dev):
     _topk_case(dev, s, 39990, 2048, "heavy tail")
 
 
-def test_topk_sample_adversarial(dev):
-    # The kernel picks its pivot from the scores at a fixed 1-in-16 sample of a row's positions
-    # (element 17 i, i < 4, of every thread: position 4096 w + 1024 i + 4 lane + i).  Rows that
-    # defeat that sample must still come out exact through the full select: sampled scores far
-    # above the rest leave too few candidates above the pivot, far below leave too many.
-    S = 32768
-    sampled = np.array([4096 * w + 1024 * i + 4 * l + i for w in range(8) for i in range(4) for l in range(64)])
-    g = block_rng(36, 0, 0)
+@pytest.mark.parametrize("S", [8192, 16384, 32768])
+def test_topk_sample_adversarial(dev, S):
+    # A row of n <= 32768 scores is held as EPT = 16, 32 or 64 elements per thread (the narrowest
+    # that fits); the pivot comes from a fixed 1-in-16 sample of positions (element 17 i,
+    # i < EPT / 16, of every thread: position 64 EPT w + 1024 i + 4 lane + i).  Rows that defeat
+    # that sample must still come out exact through the full select: sampled scores far above the
+    # rest leave too few candidates above the pivot, far below leave too many.
+    ept = S // 512
+    sampled = np.array([64 * ept * w + 1024 * i + 4 * l + i
+                        for w in range(8) for i in range(ept // 16) for l in range(64)])
+    g = block_rng(36, 0, S)
     s = g.standard_normal((4, S)).astype(np.float32)
     s[0, sampled] += 100.0
     s[1, sampled] -= 100.0
     s[2, sampled] = 7.0        # sampled scores all tied, above the rest
     s[3, sampled[::3]] += 50.0
-    _topk_case(dev, s, S - 4, 2048, "sample-adversarial rows")
+    _topk_case(dev, s, S - 4, 2048, "sample-adversarial rows of %d" % S)
+
+
+def test_topk_row_lengths_across_layouts(dev):
+    # rows whose visible lengths select every register layout, on both sides of each boundary
+    g = block_rng(37, 0, 0)
+    for n in [4097, 5000, 8191, 8193, 12000, 16383, 16385, 20000]:
+        _topk_case(dev, g.standard_normal((1, n)).astype(np.float32), n - 1, 2048, "row of %d" % n)
+    # one launch whose consecutive row lengths cross a boundary (rows of 8161 .. 8224 and 16353 .. 16416)
+    for first in (8161, 16353):
+        _topk_case(dev, g.standard_normal((64, first + 63)).astype(np.float32), first - 1, 2048,
+                   "rows of %d .. %d" % (first, first + 63))
 
 
 # ------------------------------------------------------------------------------------- MLA
