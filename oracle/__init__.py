@@ -58,6 +58,12 @@ def load(path: Optional[str] = None):
     lib.oracle_quantize_rows_ue8m0.restype = None
     lib.oracle_append_paged.argtypes = [_p, _p, _p, _i32, _p, _i64, _p, _p, _i64, _i32, _i32, _p, _p]
     lib.oracle_append_paged.restype = _i64
+    lib.oracle_indexer_kl.argtypes = [_p, _p, _p, _i64, _i64, _i32, _i32, ctypes.c_double, _p, _i64, _p, _p,
+                                      _i64, _i32]
+    lib.oracle_indexer_kl.restype = ctypes.c_int
+    lib.oracle_indexer_bwd.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p,
+                                       _i32]
+    lib.oracle_indexer_bwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -237,3 +243,46 @@ def quantize_rows_ue8m0(x_bf16: np.ndarray, lib=None):
     scales = np.empty(x.shape[:-1], dtype=np.float32)
     lib.oracle_quantize_rows_ue8m0(_ptr(x), rows, D, _ptr(codes), _ptr(exps), _ptr(scales))
     return codes, exps, scales
+
+
+def indexer_kl(q, kv, pos, sm_scale: float, logits, nthreads: int = 0, lib=None):
+    """KL(p || softmax(I)) per query row and its gradient with respect to the scores.
+
+    q: bf16 bits [T, H, D_qk]; kv: bf16 bits [S, D_qk]; logits: fp32 [T, >= S] (each row's visible
+    entries are read).  Returns (loss float64 [T], dlogits float64 [T, S], NaN past each row's
+    visible range)."""
+    lib = lib or load()
+    q = _c(q, np.uint16)
+    T, H, D_qk = q.shape
+    kv = _c(kv, np.uint16)
+    S = kv.shape[0]
+    logits = _c(logits, np.float32)
+    pos = _c(pos, np.int64)
+    loss = np.empty(T, dtype=np.float64)
+    d = np.full((T, S), np.nan, dtype=np.float64)
+    rc = lib.oracle_indexer_kl(_ptr(q), _ptr(kv), _ptr(pos), T, S, H, D_qk, ctypes.c_double(sm_scale),
+                               _ptr(logits), logits.shape[1], _ptr(loss), _ptr(d), S, nthreads)
+    if rc:
+        raise RuntimeError("oracle_indexer_kl failed (%d)" % rc)
+    return loss, d
+
+
+def indexer_bwd(q8, qs, w, pos, k8, ks, dlogits, nthreads: int = 0, lib=None):
+    """Gradients (dq [T, H_I, D_I], dw [T, H_I], dk [S, D_I], float64) of a loss through the index
+    scores, given dlogits fp32 [T, >= S] = dL/dI on the visible entries."""
+    lib = lib or load()
+    q8 = _c(q8, np.uint8)
+    T, H_I, D_I = q8.shape
+    k8 = _c(k8, np.uint8)
+    S = k8.shape[0]
+    qs, w, ks = _c(qs, np.float32), _c(w, np.float32), _c(ks, np.float32)
+    dlogits = _c(dlogits, np.float32)
+    pos = _c(pos, np.int64)
+    dq = np.empty((T, H_I, D_I), dtype=np.float64)
+    dw = np.empty((T, H_I), dtype=np.float64)
+    dk = np.empty((S, D_I), dtype=np.float64)
+    rc = lib.oracle_indexer_bwd(_ptr(q8), _ptr(qs), _ptr(w), _ptr(pos), T, _ptr(k8), _ptr(ks), S, H_I, D_I,
+                                _ptr(dlogits), dlogits.shape[1], _ptr(dq), _ptr(dw), _ptr(dk), nthreads)
+    if rc:
+        raise RuntimeError("oracle_indexer_bwd failed (%d)" % rc)
+    return dq, dw, dk

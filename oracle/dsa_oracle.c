@@ -453,3 +453,180 @@ int64_t oracle_append_paged(uint8_t *k8_pool, float *ks_pool, uint16_t *kv_pool,
     }
     return bad;
 }
+
+/* ---- NEXT step: the indexer's training signal (dense warm-up) and its backward ------------
+ * DeepSeek-V3.2-Exp summary page, "Method" (continued pre-training): in a dense warm-up stage
+ * only the indexer is trained, against a KL-divergence target given by the main attention; in
+ * the sparse stage the indexer keeps its own graph.  The pages give no formula.  Reading:
+ *  - the target of query row t is the main attention's distribution over its visible keys
+ *    s < n_t averaged over the H heads,
+ *        p[t,s] = (1/H) sum_h softmax_s( sm_scale * q[t,h,:] . kv[s, :D_qk] ),
+ *    the attention of the sparse step taken over every visible key (MQA: K = the whole latent
+ *    row);
+ *  - the indexer's distribution is pi[t,.] = softmax_s(I[t,s]) over the same keys;
+ *  - the row's loss is KL(p || pi) = sum_s p (log p - log pi), with 0 log 0 = 0, and its
+ *    gradient with respect to the scores is dI[t,s] = pi[t,s] - p[t,s] (the p sum to one);
+ *  - the backward passes the FP8 quantization straight through: the gradients are taken with
+ *    respect to the dequantized vectors q_I = qs * dec(q8), k_I = ks * dec(k8) and the weights
+ *    w, and ReLU's derivative is 1 for a positive product and 0 otherwise.
+ * Arithmetic in double: every input value (bf16, dequantized FP8, fp32) is exact in double. */
+
+/* Loss and score gradient of every query row.  logits [T][ld] (fp32, the row's visible entries
+ * s < n_t are read); loss [T]; dlogits [T][ld_d] (entries s >= n_t untouched).  A row with no
+ * visible key has loss 0.  Returns 1 on a bad shape, 2 on a non-finite score, 3 on no memory. */
+int oracle_indexer_kl(const uint16_t *q, const uint16_t *kv, const int64_t *pos, int64_t T, int64_t S,
+                      int32_t H, int32_t D_qk, double sm_scale, const float *logits, int64_t ld,
+                      double *loss, double *dlogits, int64_t ld_d, int32_t nthreads)
+{
+    if (T < 0 || S < 0 || H <= 0 || D_qk <= 0 || ld < S || ld_d < S)
+        return 1;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = visible_keys(pos[t], S);
+        loss[t] = 0.0;
+        if (n <= 0)
+            continue;
+        double *z = (double *)malloc(sizeof(double) * (size_t)n);
+        double *p = (double *)calloc((size_t)n, sizeof(double));
+        if (!z || !p) {
+            bad = 3;
+            free(z);
+            free(p);
+            continue;
+        }
+        /* target: softmax of every head over the visible keys, averaged over the heads */
+        for (int32_t h = 0; h < H; ++h) {
+            const uint16_t *qh = q + (t * H + h) * (int64_t)D_qk;
+            double m = -INFINITY;
+            for (int64_t s = 0; s < n; ++s) {
+                const uint16_t *kr = kv + s * D_qk;
+                double dot = 0.0;
+                for (int32_t d = 0; d < D_qk; ++d)
+                    dot += (double)bf16_value(qh[d]) * (double)bf16_value(kr[d]);
+                z[s] = sm_scale * dot;
+                if (z[s] > m)
+                    m = z[s];
+            }
+            double l = 0.0;
+            for (int64_t s = 0; s < n; ++s)
+                l += exp(z[s] - m);
+            for (int64_t s = 0; s < n; ++s)
+                p[s] += exp(z[s] - m) / l / (double)H;
+        }
+        /* the indexer's log-probabilities over the same keys */
+        const float *I = logits + t * ld;
+        double mi = -INFINITY;
+        int finite = 1;
+        for (int64_t s = 0; s < n; ++s) {
+            if (!isfinite(I[s]))
+                finite = 0;
+            else if ((double)I[s] > mi)
+                mi = (double)I[s];
+        }
+        if (!finite) {
+            bad = 2;
+            free(z);
+            free(p);
+            continue;
+        }
+        double li = 0.0;
+        for (int64_t s = 0; s < n; ++s)
+            li += exp((double)I[s] - mi);
+        double lse_i = mi + log(li);
+        double acc = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            double log_pi = (double)I[s] - lse_i;
+            if (p[s] > 0.0)
+                acc += p[s] * (log(p[s]) - log_pi);
+            dlogits[t * ld_d + s] = exp(log_pi) - p[s];
+        }
+        loss[t] = acc;
+        free(z);
+        free(p);
+    }
+    return bad;
+}
+
+/* Gradients through the index scores I[t,s] = sum_j w[t,j] max(0, z), z = q_I[t,j] . k_I[s],
+ * given dlogits [T][ld] = dL/dI on the visible entries (s < n_t; others never read):
+ *     dw[t,j]     = sum_s dI[t,s] max(0, z)
+ *     dq[t,j,:]   = sum_{s: z > 0} dI[t,s] w[t,j] k_I[s,:]
+ *     dk[s,:]     = sum_{t, j: z > 0} dI[t,s] w[t,j] q_I[t,j,:]
+ * Outputs dq [T][H_I][D_I], dw [T][H_I], dk [S][D_I] (double).  Returns 1 on a bad shape, 3 on
+ * no memory. */
+int oracle_indexer_bwd(const uint8_t *q8, const float *qs, const float *w, const int64_t *pos, int64_t T,
+                       const uint8_t *k8, const float *ks, int64_t S, int32_t H_I, int32_t D_I,
+                       const float *dlogits, int64_t ld, double *dq, double *dw, double *dk, int32_t nthreads)
+{
+    if (T < 0 || S < 0 || H_I <= 0 || D_I <= 0 || ld < S)
+        return 1;
+    e4m3_init();
+    size_t nk = (size_t)(S > 0 ? S : 1) * (size_t)D_I, nq = (size_t)(T > 0 ? T : 1) * (size_t)H_I * (size_t)D_I;
+    double *kd = (double *)malloc(sizeof(double) * nk);
+    double *qd = (double *)malloc(sizeof(double) * nq);
+    if (!kd || !qd) {
+        free(kd);
+        free(qd);
+        return 3;
+    }
+    for (int64_t s = 0; s < S; ++s)
+        for (int32_t i = 0; i < D_I; ++i)
+            kd[s * D_I + i] = (double)ks[s] * (double)g_e4m3[k8[s * D_I + i]];
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < H_I; ++j)
+            for (int32_t i = 0; i < D_I; ++i)
+                qd[(t * H_I + j) * D_I + i] = (double)qs[t * H_I + j] * (double)g_e4m3[q8[(t * H_I + j) * D_I + i]];
+    set_threads(nthreads);
+    /* dq and dw: one query row per iteration */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = visible_keys(pos[t], S);
+        for (int32_t j = 0; j < H_I; ++j) {
+            const double *qv = qd + (t * H_I + j) * D_I;
+            double *g = dq + (t * H_I + j) * D_I;
+            double gw = 0.0;
+            for (int32_t i = 0; i < D_I; ++i)
+                g[i] = 0.0;
+            for (int64_t s = 0; s < n; ++s) {
+                const double *kv_ = kd + s * D_I;
+                double z = 0.0;
+                for (int32_t i = 0; i < D_I; ++i)
+                    z += qv[i] * kv_[i];
+                double di = (double)dlogits[t * ld + s];
+                if (z > 0.0) {
+                    gw += di * z;
+                    for (int32_t i = 0; i < D_I; ++i)
+                        g[i] += di * (double)w[t * H_I + j] * kv_[i];
+                }
+            }
+            dw[t * H_I + j] = gw;
+        }
+    }
+    /* dk: one key per iteration, over the query rows that see it */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t s = 0; s < S; ++s) {
+        double *g = dk + s * D_I;
+        const double *kv_ = kd + s * D_I;
+        for (int32_t i = 0; i < D_I; ++i)
+            g[i] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            if (s >= visible_keys(pos[t], S))
+                continue;
+            double di = (double)dlogits[t * ld + s];
+            for (int32_t j = 0; j < H_I; ++j) {
+                const double *qv = qd + (t * H_I + j) * D_I;
+                double z = 0.0;
+                for (int32_t i = 0; i < D_I; ++i)
+                    z += qv[i] * kv_[i];
+                if (z > 0.0)
+                    for (int32_t i = 0; i < D_I; ++i)
+                        g[i] += di * (double)w[t * H_I + j] * qv[i];
+            }
+        }
+    }
+    free(kd);
+    free(qd);
+    return 0;
+}

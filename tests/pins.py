@@ -402,3 +402,158 @@ def check_quantize_ue8m0(lib):
     y = np.clip(xv.astype(np.float64) / scales[:, None].astype(np.float64), -FP8_MAX, FP8_MAX).astype(np.float32)
     assert np.array_equal(codes, _torch_e4m3(y)), "UE8M0 codes differ from the torch cast of x / 2^p"
     assert np.all((codes & 0x7F) <= 0x7E)
+
+
+# ---------------------------------------------------------------- indexer training signal
+# Reading (DeepSeek-V3.2-Exp summary page, "Method", dense warm-up): the row loss is
+# KL(p || softmax(I)) with p the main attention's distribution averaged over the heads; the
+# backward passes the FP8 quantization straight through.
+def _kl_inputs(T, S, q_start, H, D, seed, scale=2.0):
+    g = block_rng(seed, T, S)
+    q = to_bf16_bits(g.standard_normal((T, H, D)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D)).astype(np.float32))
+    logits = (g.standard_normal((T, S)) * scale).astype(np.float32)
+    return q, kv, logits, q_start + np.arange(T)
+
+
+def torch_kl(q, kv, logits, pos, sm):
+    """(loss [T], dI [T, S]) by torch in float64: per-head softmax over the visible keys, mean over
+    heads, F.kl_div against log_softmax of the scores, gradient by autograd."""
+    qf = torch.from_numpy(brute.bf16_decode(q))
+    kf = torch.from_numpy(brute.bf16_decode(kv))
+    T, S = logits.shape
+    vis = torch.from_numpy(np.arange(S)[None, :] < np.minimum(S, pos + 1)[:, None])
+    z = torch.matmul(qf, kf.T) * sm                                    # [T, H, S]
+    p = torch.softmax(z.masked_fill(~vis[:, None, :], float("-inf")), dim=-1).mean(dim=1)
+    I = torch.from_numpy(logits.astype(np.float64)).requires_grad_(True)
+    logpi = torch.log_softmax(I.masked_fill(~vis, float("-inf")), dim=-1).masked_fill(~vis, 0.0)
+    loss = torch.nn.functional.kl_div(logpi, p, reduction="none").sum(dim=-1)
+    loss.sum().backward()
+    return loss.detach().numpy(), np.where(vis.numpy(), I.grad.numpy(), np.nan)
+
+
+def check_kl_vs_torch(lib):
+    for (T, S, q0, H, D, sm) in [(24, 40, 16, 4, 24, 0.3), (9, 9, 0, 3, 80, 80 ** -0.5)]:
+        q, kv, logits, pos = _kl_inputs(T, S, q0, H, D, 71)
+        loss, d = oracle.indexer_kl(q, kv, pos, sm, logits, lib=lib)
+        tl, td = torch_kl(q, kv, logits, pos, sm)
+        assert np.all(np.abs(loss - tl) <= 1e-12 * (1.0 + np.abs(tl))), "KL loss differs from torch kl_div"
+        m = ~np.isnan(td)
+        assert np.array_equal(m, ~np.isnan(d)), "visible region of dI is wrong"
+        assert np.max(np.abs(d[m] - td[m])) <= 1e-13, "dI differs from torch autograd"
+        assert np.all(loss >= -1e-15), "KL divergence must be non-negative"
+
+
+def check_kl_closed_forms(lib):
+    # a row that sees one key: both distributions are that key
+    q, kv, logits, pos = _kl_inputs(3, 8, 0, 2, 16, 72)
+    loss, d = oracle.indexer_kl(q, kv, pos, 0.25, logits, lib=lib)
+    assert loss[0] == 0.0 and d[0, 0] == 0.0
+    # identical heads and scores equal to that head's attention logits (+ a constant): pi = p
+    T, S, H, D, sm = 6, 20, 3, 16, 0.25
+    q, kv, _, pos = _kl_inputs(T, S, 14, H, D, 73)
+    q[:, 1:] = q[:, :1]
+    z = brute.bf16_decode(q)[:, 0] @ brute.bf16_decode(kv).T * sm
+    loss, d = oracle.indexer_kl(q, kv, pos, sm, (z + 1.5).astype(np.float32), lib=lib)
+    assert np.all(loss <= 1e-10) and np.nanmax(np.abs(d)) <= 1e-5, "pi = p must give zero loss"
+    # uniform scores: loss = log n + sum p log p, with p = 1/n - dI
+    q, kv, _, pos = _kl_inputs(T, S, 14, H, D, 74)
+    loss, d = oracle.indexer_kl(q, kv, pos, sm, np.full((T, S), 0.37, np.float32), lib=lib)
+    for t in range(T):
+        n = min(S, pos[t] + 1)
+        p = 1.0 / n - d[t, :n]
+        assert abs(p.sum() - 1.0) <= 1e-12
+        assert abs(loss[t] - (np.log(n) + np.sum(p * np.log(p)))) <= 1e-12
+    # two sharp heads on two different keys: p = 1/2 on each (head average, not a sum or a max)
+    S = 10
+    q = to_bf16_bits(np.array([[[60.0, 0.0], [0.0, 60.0]]], np.float32))
+    kvf = np.zeros((S, 2), np.float32)
+    kvf[3] = [1.0, 0.0]
+    kvf[7] = [0.0, 1.0]
+    logits = block_rng(75, 0, 0).standard_normal((1, S)).astype(np.float32)
+    loss, d = oracle.indexer_kl(q, to_bf16_bits(kvf), np.array([S - 1]), 1.0, logits, lib=lib)
+    lp = logits[0].astype(np.float64) - np.log(np.sum(np.exp(logits[0].astype(np.float64))))
+    ref = 0.5 * (np.log(0.5) - lp[3]) + 0.5 * (np.log(0.5) - lp[7])
+    assert abs(loss[0] - ref) <= 1e-12
+    pi = np.exp(lp)
+    assert abs(d[0, 3] - (pi[3] - 0.5)) <= 1e-12 and abs(d[0, 0] - pi[0]) <= 1e-12
+
+
+def check_kl_finite_difference(lib):
+    # dI against central differences of the oracle's own loss (the exact perturbation of the fp32
+    # score is used)
+    q, kv, logits, pos = _kl_inputs(4, 30, 26, 2, 16, 76)
+    sm = 0.3
+    _, d = oracle.indexer_kl(q, kv, pos, sm, logits, lib=lib)
+    for (t, s) in [(0, 0), (1, 5), (2, 28), (3, 29), (3, 11)]:
+        up, dn = logits.copy(), logits.copy()
+        up[t, s] = np.float32(logits[t, s] + np.float32(2.0 ** -9))
+        dn[t, s] = np.float32(logits[t, s] - np.float32(2.0 ** -9))
+        lu, _ = oracle.indexer_kl(q, kv, pos, sm, up, lib=lib)
+        ld_, _ = oracle.indexer_kl(q, kv, pos, sm, dn, lib=lib)
+        fd = (lu[t] - ld_[t]) / (float(up[t, s]) - float(dn[t, s]))
+        assert abs(fd - d[t, s]) <= 1e-5, "dI[%d,%d] differs from the finite difference" % (t, s)
+
+
+def _bwd_inputs(T, S, q_start, H_I, D_I, seed):
+    g = block_rng(seed, T, S)
+    q8, qs = quantize_fp8_rows(g.standard_normal((T, H_I, D_I)).astype(np.float32))
+    k8, ks = quantize_fp8_rows(g.standard_normal((S, D_I)).astype(np.float32))
+    w = (g.uniform(-1.0, 1.0, (T, H_I)) / H_I).astype(np.float32)      # any sign (weights are literal)
+    dI = (g.standard_normal((T, S)) * 1e-2).astype(np.float32)
+    return q8, qs, w, k8, ks, dI, q_start + np.arange(T)
+
+
+def _indexer_linear_form(qd, kd, w, dI, pos):
+    """L = sum over visible (t, s) of dI[t,s] I[t,s], in float64 from dequantized inputs."""
+    T, S = dI.shape
+    z = np.einsum("tjd,sd->tjs", qd, kd)
+    I = np.einsum("tj,tjs->ts", w.astype(np.float64), np.maximum(z, 0.0))
+    vis = np.arange(S)[None, :] < np.minimum(S, pos + 1)[:, None]
+    return float(np.sum(np.where(vis, dI.astype(np.float64) * I, 0.0)))
+
+
+def check_indexer_bwd_vs_torch(lib):
+    T, S, H_I, D_I = 20, 36, 4, 32
+    q8, qs, w, k8, ks, dI, pos = _bwd_inputs(T, S, 16, H_I, D_I, 77)
+    dq, dw, dk = oracle.indexer_bwd(q8, qs, w, pos, k8, ks, dI, lib=lib)
+    qd = torch.from_numpy(qs.astype(np.float64)[:, :, None] * brute.e4m3_decode(q8)).requires_grad_(True)
+    kd = torch.from_numpy(ks.astype(np.float64)[:, None] * brute.e4m3_decode(k8)).requires_grad_(True)
+    wt = torch.from_numpy(w.astype(np.float64)).requires_grad_(True)
+    vis = torch.from_numpy(np.arange(S)[None, :] < np.minimum(S, pos + 1)[:, None])
+    I = (wt[:, :, None] * torch.relu(torch.matmul(qd, kd.T))).sum(dim=1)
+    (torch.from_numpy(dI.astype(np.float64)) * I).masked_fill(~vis, 0.0).sum().backward()
+    for name, mine, ref in [("dq", dq, qd.grad.numpy()), ("dw", dw, wt.grad.numpy()), ("dk", dk, kd.grad.numpy())]:
+        assert np.max(np.abs(mine - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref))), "%s differs from autograd" % name
+
+
+def check_indexer_bwd_finite_difference(lib):
+    # I is linear in each row scale qs[t,j], key scale ks[s] and weight w[t,j] (positive scales do
+    # not move the ReLU kink), so central differences of L = sum dI * I are exact up to rounding
+    # and fix the projections dq[t,j] . dec(q8[t,j]), dk[s] . dec(k8[s]) and dw[t,j]
+    T, S, H_I, D_I = 10, 16, 3, 16
+    q8, qs, w, k8, ks, dI, pos = _bwd_inputs(T, S, 6, H_I, D_I, 78)
+    dq, dw, dk = oracle.indexer_bwd(q8, qs, w, pos, k8, ks, dI, lib=lib)
+    qdec, kdec = brute.e4m3_decode(q8), brute.e4m3_decode(k8)
+
+    def L(qs_, ks_, w_):
+        return _indexer_linear_form(qs_.astype(np.float64)[:, :, None] * qdec,
+                                    ks_.astype(np.float64)[:, None] * kdec, w_, dI, pos)
+    h = 1e-3
+    for (t, j) in [(0, 0), (4, 2), (9, 1)]:
+        a, b = qs.astype(np.float64).copy(), qs.astype(np.float64).copy()
+        a[t, j] += h
+        b[t, j] -= h
+        fd = (L(a, ks, w) - L(b, ks, w)) / (2 * h)
+        assert abs(fd - np.dot(dq[t, j], qdec[t, j])) <= 1e-9 * (1.0 + abs(fd)), "dq projection"
+        a, b = w.astype(np.float64).copy(), w.astype(np.float64).copy()
+        a[t, j] += h
+        b[t, j] -= h
+        fd = (L(qs, ks, a) - L(qs, ks, b)) / (2 * h)
+        assert abs(fd - dw[t, j]) <= 1e-9 * (1.0 + abs(fd)), "dw"
+    for s in [0, 7, 15]:
+        a, b = ks.astype(np.float64).copy(), ks.astype(np.float64).copy()
+        a[s] += h
+        b[s] -= h
+        fd = (L(qs, a, w) - L(qs, b, w)) / (2 * h)
+        assert abs(fd - np.dot(dk[s], kdec[s])) <= 1e-9 * (1.0 + abs(fd)), "dk projection"

@@ -52,6 +52,20 @@ MUTANTS = [
      "int64_t row = (int64_t)blk * bs + (pos[i] + 1) % bs;", [pins.check_append_paged_round_trip]),
     ("mla_future_keys", "int64_t n = visible_keys(pos[t], S);\n        const int32_t *row",
      "int64_t n = S;\n        const int32_t *row", [pins.check_mla_brute]),
+    ("kl_head_sum", "p[s] += exp(z[s] - m) / l / (double)H;", "p[s] += exp(z[s] - m) / l;",
+     [pins.check_kl_vs_torch]),
+    ("kl_reversed", "acc += p[s] * (log(p[s]) - log_pi);", "acc += exp(log_pi) * (log_pi - log(p[s]));",
+     [pins.check_kl_vs_torch, pins.check_kl_closed_forms]),
+    ("kl_grad_sign", "dlogits[t * ld_d + s] = exp(log_pi) - p[s];", "dlogits[t * ld_d + s] = p[s] - exp(log_pi);",
+     [pins.check_kl_vs_torch, pins.check_kl_finite_difference]),
+    ("kl_scale_dropped", "z[s] = sm_scale * dot;", "z[s] = dot;", [pins.check_kl_vs_torch]),
+    ("bwd_dk_unmasked", "if (z > 0.0)\n                    for", "if (1)\n                    for",
+     [pins.check_indexer_bwd_vs_torch, pins.check_indexer_bwd_finite_difference]),
+    ("bwd_dq_no_weight", "g[i] += di * (double)w[t * H_I + j] * kv_[i];", "g[i] += di * kv_[i];",
+     [pins.check_indexer_bwd_vs_torch, pins.check_indexer_bwd_finite_difference]),
+    ("bwd_dw_no_relu", "if (z > 0.0) {\n                    gw += di * z;",
+     "gw += di * z;\n                if (z > 0.0) {", [pins.check_indexer_bwd_vs_torch,
+                                                      pins.check_indexer_bwd_finite_difference]),
 ]
 
 
