@@ -248,3 +248,51 @@ def dsa_indexer_logits_ue8m0(q8, q_exp, w, k8, k_exp, q_start: int = 0, logits=N
         _stream(q8))
     check("dsa_indexer_logits_ue8m0", status)
     return logits
+
+
+def dsa_indexer_kl_loss(q, kv, logits, sm_scale: float, q_start: int = 0, dlogits=None, loss=None,
+                        in_place: bool = False):
+    """(loss f32 [T], dlogits f32 [T, ld]) of the indexer's KL loss toward the head-averaged main
+    attention; dlogits = softmax(logits) - p on each row's visible entries.  in_place overwrites
+    logits with dlogits."""
+    lib = load()
+    T, H, D_qk = q.shape
+    S = kv.shape[0]
+    if dlogits is None:
+        dlogits = logits if in_place else torch.empty_like(logits)
+    if loss is None:
+        loss = torch.empty((T,), dtype=torch.float32, device=q.device)
+    status = lib.dsa_indexer_kl_loss(
+        _dev(q, "q", 3, 2), _dev(kv, "kv", 2, 2), T, S, H, D_qk, ctypes.c_float(sm_scale), q_start,
+        _dev(logits, "logits", 2, 4), logits.shape[1], _dev(dlogits, "dlogits", 2, 4), _dev(loss, "loss", 1, 4),
+        _stream(q))
+    check("dsa_indexer_kl_loss", status)
+    return loss, dlogits
+
+
+def indexer_bwd_workspace_size(T: int, S: int, D_I: int) -> int:
+    return load().dsa_indexer_bwd_workspace_size(T, S, D_I)
+
+
+def dsa_indexer_bwd(q8, q_scale, w, k8, k_scale, dlogits, q_start: int = 0, dq=None, dw=None, dk=None,
+                    workspace=None):
+    """(dq [T, H_I, D_I], dw [T, H_I], dk [S, D_I]) f32: gradients through the index scores for
+    dlogits = dL/dlogits, with respect to the dequantized q_I, k_I and the weights w."""
+    lib = load()
+    T, H_I, D_I = q8.shape
+    S = k8.shape[0]
+    dev = q8.device
+    if dq is None:
+        dq = torch.empty((T, H_I, D_I), dtype=torch.float32, device=dev)
+    if dw is None:
+        dw = torch.empty((T, H_I), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((S, D_I), dtype=torch.float32, device=dev)
+    workspace = _workspace(lib.dsa_indexer_bwd_workspace_size(T, S, D_I), dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = lib.dsa_indexer_bwd(
+        _dev(q8, "q8", 3, 1), _dev(q_scale, "q_scale", 2, 4), _dev(w, "w", 2, 4), _dev(k8, "k8", 2, 1),
+        _dev(k_scale, "k_scale", 1, 4), T, S, H_I, D_I, q_start, _dev(dlogits, "dlogits", 2, 4), dlogits.shape[1],
+        _dev(dq, "dq", 3, 4), _dev(dw, "dw", 2, 4), _dev(dk, "dk", 2, 4), _opt(workspace), ws_bytes, _stream(q8))
+    check("dsa_indexer_bwd", status)
+    return dq, dw, dk

@@ -453,4 +453,59 @@ dsa_status_t dsa_append_paged(const dsa_paged_cache_t* c, int32_t B, const int32
                     "append launch");
 }
 
+dsa_status_t dsa_indexer_kl_loss(const uint16_t* q, const uint16_t* kv, int64_t T, int64_t S, int32_t H,
+                                 int32_t D_qk, float sm_scale, int64_t q_start, const float* logits,
+                                 int64_t ld_logits, float* dlogits, float* loss, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  REQUIRE(dsa::indexer_kl_supported(H, D_qk), DSA_ERR_UNSUPPORTED,
+          "KL loss with H=%d, D_qk=%d not supported (1 <= H <= 128, D_qk a multiple of 8 in [8, 576])", H, D_qk);
+  if (T == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1 when T > 0");
+  REQUIRE(ld_logits >= S && ld_logits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_logits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_logits, (long long)S);
+  REQUIRE(sm_scale > 0.0f && sm_scale < 1.0e30f, DSA_ERR_INVALID_ARGUMENT, "sm_scale must be positive and finite");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kv);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(dlogits);
+  REQUIRE_PTR(loss);
+  return hip_status(dsa::launch_indexer_kl(q, kv, T, S, H, D_qk, sm_scale, q_start, logits, ld_logits, dlogits, loss,
+                                           stream),
+                    "KL loss launch");
+}
+
+size_t dsa_indexer_bwd_workspace_size(int64_t T, int64_t S, int32_t D_I) {
+  if (T <= 0 || S <= 0 || D_I <= 0) return 0;
+  return dsa::indexer_bwd_workspace_bytes(T, S, D_I);
+}
+
+dsa_status_t dsa_indexer_bwd(const uint8_t* q8, const float* q_scale, const float* w, const uint8_t* k8,
+                             const float* k_scale, int64_t T, int64_t S, int32_t H_I, int32_t D_I, int64_t q_start,
+                             const float* dlogits, int64_t ld_dlogits, float* dq, float* dw, float* dk,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  dsa_status_t s = check_indexer_dims(H_I, D_I);
+  if (s != DSA_OK) return s;
+  if (T == 0 && S == 0) return ok();
+  REQUIRE(T >= 1 && S >= 1, DSA_ERR_INVALID_ARGUMENT, "T and S must both be >= 1 (or both 0)");
+  REQUIRE(ld_dlogits >= S && ld_dlogits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_dlogits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_dlogits, (long long)S);
+  REQUIRE_PTR(q8);
+  REQUIRE_PTR(q_scale);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(k8);
+  REQUIRE_PTR(k_scale);
+  REQUIRE_PTR(dlogits);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dw);
+  REQUIRE_PTR(dk);
+  const size_t need = dsa::indexer_bwd_workspace_bytes(T, S, D_I);
+  REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "indexer backward workspace %zu < %zu bytes",
+          workspace_bytes, need);
+  REQUIRE_PTR(workspace);
+  return hip_status(dsa::launch_indexer_bwd(q8, q_scale, w, k8, k_scale, T, S, H_I, D_I, q_start, dlogits,
+                                            ld_dlogits, dq, dw, dk, workspace, stream),
+                    "indexer backward launch");
+}
+
 }  // extern "C"

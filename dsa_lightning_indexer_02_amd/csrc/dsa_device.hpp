@@ -91,6 +91,48 @@ struct RowMap {
   }
 };
 
+// ---- LDS helpers
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave-wide global -> LDS transfer (gfx950 LDS DMA): lane l's 16 bytes at gaddr land at
+// lds_base + 16 l.  Completion is tracked by the vector-memory counter.
+__device__ __forceinline__ void lds_dma_16B(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gaddr) : "memory");
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding): at most N operations pending.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16 lanes, lane i
+// receives element i % 4 of the four 16-bit words addressed by lanes 4 j + i / 4 of its group,
+// j = 0..3.  With lane a of group g addressing row r0 + a / 4, columns c0 + 4 (a % 4) .. + 3 of a
+// row-major 16-bit matrix, lane i receives column c0 + i at rows r0 .. r0 + 3.
+__device__ __forceinline__ s16x4 lds_transpose_read16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+// Eight FP8 E4M3 codes (two dwords) -> eight bf16 values (exact: E4M3 values are bf16 values).
+__device__ __forceinline__ s16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  s16x8 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w = h ? hi : lo;
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);  // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);   // bytes 2, 3
+    r[4 * h + 0] = (short)(__float_as_uint(a[0]) >> 16);
+    r[4 * h + 1] = (short)(__float_as_uint(a[1]) >> 16);
+    r[4 * h + 2] = (short)(__float_as_uint(b[0]) >> 16);
+    r[4 * h + 3] = (short)(__float_as_uint(b[1]) >> 16);
+  }
+  return r;
+}
+
 __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);

@@ -34,6 +34,16 @@ hipError_t launch_append_paged(uint8_t* k8_pool, float* ks_pool, uint16_t* kv_po
                                const int32_t* seq_ids, const int32_t* positions, int64_t n, int32_t D_I,
                                int32_t D_qk, const uint16_t* k, const uint16_t* kv, hipStream_t stream);
 
+// ---- indexer training signal (KL loss toward the main attention) and backward
+bool indexer_kl_supported(int32_t H, int32_t D);
+hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t T, int64_t S, int32_t H, int32_t D,
+                             float sm_scale, int64_t q_start, const float* logits, int64_t ld, float* dlogits,
+                             float* loss, hipStream_t stream);
+size_t indexer_bwd_workspace_bytes(int64_t T, int64_t S, int32_t D_I);
+hipError_t launch_indexer_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
+                              int64_t T, int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, const float* dI,
+                              int64_t ld, float* dq, float* dw, float* dk, void* workspace, hipStream_t stream);
+
 // ---- top-k
 int32_t topk_chunks(int64_t S);
 size_t topk_workspace_bytes(int64_t T, int64_t S, int32_t k);

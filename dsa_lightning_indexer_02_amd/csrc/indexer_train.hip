@@ -1,0 +1,637 @@
+// Training signal of the lightning indexer and its backward (DeepSeek-V3.2-Exp summary page,
+// section "Method", continued pre-training: a dense warm-up stage trains only the indexer,
+// against a KL-divergence target given by the main attention; the sparse stage keeps the
+// indexer on its own graph).  The pages give no formula; the kernels compute:
+//
+//   p[t,s]  = (1/H) sum_h softmax_s( sm_scale * q[t,h,:] . kv[s,:] )     over s < n_t
+//   pi[t,s] = softmax_s( I[t,s] ),   loss[t] = KL(p || pi) = sum_s p (log p - log pi)
+//   dI[t,s] = pi[t,s] - p[t,s]
+//
+// and, for any dI, the gradients through I[t,s] = sum_j w[t,j] ReLU(z), z = q_I[t,j] . k_I[s]
+// with the FP8 quantization passed straight through (q_I = qs dec(q8), k_I = ks dec(k8)):
+//
+//   dw[t,j] = sum_s dI[t,s] max(0, z),   dq[t,j,:] = w[t,j] sum_{s: z>0} dI[t,s] k_I[s,:],
+//   dk[s,:] = sum_{t,j: z>0} dI[t,s] w[t,j] q_I[t,j,:].
+//
+// The target is the main attention over every visible key, so the loss kernel is a dense causal
+// QK^T over the 576-wide latent rows (bf16 MFMA), run twice: pass 1 finds each head's
+// log-normaliser, pass 2 sums the normalised probabilities over the heads and forms the loss and
+// dI.  The backward recomputes z with bf16 MFMA from the FP8 codes (exact in bf16) and feeds the
+// masked gradient tile, split into a bf16 high part and a bf16 remainder, straight from the
+// accumulator layout into the next MFMA as its A operand.
+#include "dsa_internal.hpp"
+
+namespace dsa {
+
+constexpr float KL_LOG2E = 1.4426950408889634f;
+constexpr float KL_LN2 = 0.69314718055994531f;
+constexpr float KL_NEG = -1.0e30f;  // start of a running maximum: finite and below every score
+
+// ---------------------------------------------------------------------------------------
+// Loss.  A workgroup takes two consecutive query rows (their causal ranges differ by one key)
+// and eight waves: wave (row, group) holds the queries of 32 heads of its row in registers for
+// the whole contraction (A operand of S = Q K^T, 32x32x16 MFMA), so the accumulator of a key
+// block gives each lane one key and 16 heads.  Blocks of 32 latent rows are copied HBM/L2 ->
+// LDS by DMA (double buffered, one barrier per block) and shared by both rows.
+// ---------------------------------------------------------------------------------------
+constexpr int KL_TOK = 2;
+constexpr int KL_GROUPS = 4;  // 32-head groups per row: H <= 128
+constexpr int KL_WAVES = KL_TOK * KL_GROUPS;
+constexpr int KL_THREADS = KL_WAVES * WAVE;
+constexpr int KL_KB = 32;
+
+template <int NKS>  // NKS 16-column contraction steps: the latent row padded to 16 NKS columns
+struct KlCfg {
+  static constexpr int DP = 16 * NKS;
+  static constexpr int RC = DP / 8;  // 16-byte chunks per row (even)
+  static constexpr int SWZ = RC % 8 == 0 ? 8 : (RC % 4 == 0 ? 4 : 2);
+  static constexpr int SLOTS = KL_KB * RC;  // a multiple of 64
+  static constexpr int K_BYTES = SLOTS * 16;
+  static constexpr int DMA_INSTR = SLOTS / WAVE;
+  static constexpr int RED_FLOATS = 2 * KL_TOK * KL_GROUPS * KL_KB;
+  static constexpr size_t SMEM = 2 * (size_t)K_BYTES + (RED_FLOATS + KL_TOK * KL_GROUPS * 2) * sizeof(float);
+};
+
+// Running log-sum-exp in log2 units: l = sum 2^(v - m).  v = -inf adds nothing.
+__device__ __forceinline__ void lse_push(float& m, float& l, float v) {
+  const float d = v - m;
+  const float e = __builtin_amdgcn_exp2f(-fabsf(d));
+  l = d > 0.f ? fmaf(l, e, 1.0f) : l + e;
+  m = fmaxf(m, v);
+}
+__device__ __forceinline__ void lse_merge(float& m, float& l, float mo, float lo) {
+  const float mn = fmaxf(m, mo);
+  l = l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+  m = mn;
+}
+
+template <int NKS>
+__global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t T, int64_t S, int32_t H,
+    int32_t D, float scale_log2, int64_t q_start, const float* logits, int64_t ld, float* dlogits,
+    float* __restrict__ loss) {
+  using C = KlCfg<NKS>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* Kbuf = smem;                                                   // [2][SLOTS] x 16 B
+  float* red = reinterpret_cast<float*>(smem + 2 * C::K_BYTES);          // [2][TOK][GROUPS][KB]
+  float* rowstat = red + C::RED_FLOATS;                                   // [TOK][GROUPS][2]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tok = wave / KL_GROUPS, grp = wave % KL_GROUPS;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int64_t pair = (int64_t)gridDim.x - 1 - blockIdx.x;  // latest rows (most keys) first
+  const int64_t t = pair * KL_TOK + tok;
+  const bool row_ok = t < T;
+  const int64_t n = row_ok ? min(S, q_start + t + 1) : 0;
+  const int64_t n_max = min(S, q_start + min(pair * KL_TOK + KL_TOK, T));
+  const int nblk = (int)((n_max + KL_KB - 1) / KL_KB);
+  const int ngrp = (H + 31) / 32;
+  const bool active = row_ok && grp < ngrp;  // wave-uniform
+  const float* Irow = logits + (row_ok ? t : 0) * ld;
+
+  // ---- log-normaliser of the row's index scores (log2 units), over the row's four waves
+  {
+    float m = KL_NEG, l = 0.f;
+    for (int64_t s = grp * WAVE + lane; s < n; s += KL_GROUPS * WAVE) lse_push(m, l, Irow[s] * KL_LOG2E);
+    for (int o = 32; o > 0; o >>= 1) lse_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
+    if (lane == 0) {
+      rowstat[(tok * KL_GROUPS + grp) * 2] = m;
+      rowstat[(tok * KL_GROUPS + grp) * 2 + 1] = l;
+    }
+  }
+  // padding chunks of both stages are zero (the DMA never writes them)
+  if (C::DP > D) {
+    for (int p = tid; p < 2 * C::SLOTS; p += KL_THREADS) {
+      const int sl = p % C::SLOTS, r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      if (c * 8 >= D) *reinterpret_cast<v4i*>(Kbuf + p * 16) = (v4i){0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+  float lse_i2;
+  {
+    float m = KL_NEG, l = 0.f;
+    for (int g = 0; g < KL_GROUPS; ++g)
+      lse_merge(m, l, rowstat[(tok * KL_GROUPS + g) * 2], rowstat[(tok * KL_GROUPS + g) * 2 + 1]);
+    lse_i2 = m + __builtin_amdgcn_logf(l);
+  }
+
+  // queries of this wave's 32 heads: lane supplies head 32 grp + l32, columns 16 ks + 8 lh .. + 7
+  const int head = grp * 32 + l32;
+  s16x8 Qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int col = 16 * ks + 8 * lh;
+    s16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active && head < H && col < D) v = *reinterpret_cast<const s16x8*>(q + (t * H + head) * (int64_t)D + col);
+    asm volatile("" : "+v"(v));  // resident for both passes
+    Qf[ks] = v;
+  }
+
+  const uint32_t kbuf_lds = lds_offset(Kbuf);
+  auto issue = [&](int blk) {
+    const uint32_t base = kbuf_lds + (uint32_t)((blk & 1) * C::K_BYTES);
+    for (int i = wave; i < C::DMA_INSTR; i += KL_WAVES) {
+      const int sl = i * WAVE + lane;
+      const int r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      const int64_t s = min((int64_t)blk * KL_KB + r, S - 1);
+      if (c * 8 < D) lds_dma_16B(kv + s * D + c * 8, base + (uint32_t)(i * WAVE * 16));
+    }
+  };
+  // B operand of step ks: key row l32, chunk 2 ks + lh.  XOR-ing the row into the low log2(SWZ)
+  // chunk bits leaves steps SWZ / 2 apart a constant distance apart.
+  constexpr int KP = C::SWZ / 2;
+  const int kx = l32 & (C::SWZ - 1);
+  int kbase[KP];
+#pragma unroll
+  for (int u = 0; u < KP; ++u) kbase[u] = (l32 * C::RC + ((2 * u + lh) ^ kx)) * 16;
+  auto koff = [&](int ks) { return kbase[ks % KP] + (ks / KP) * (2 * KP * 16); };
+
+  float st_m[16], st_l[16], lse2[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    st_m[r] = KL_NEG;
+    st_l[r] = 0.f;
+    lse2[r] = INFINITY;
+  }
+  const float inv_h = 1.0f / (float)H;
+  float lacc = 0.f;  // loss of the row (log2 units), lanes 0..31 of the row's first wave
+  auto finalize = [&](int blk) {
+    const int64_t s = (int64_t)blk * KL_KB + l32;
+    if (grp == 0 && lh == 0 && s < n) {
+      const float* rb = red + ((blk & 1) * KL_TOK + tok) * KL_GROUPS * KL_KB + l32;
+      float ps = 0.f;
+      for (int g = 0; g < ngrp; ++g) ps += rb[g * KL_KB];
+      const float p = ps * inv_h;
+      const float lpi2 = fmaf(Irow[s], KL_LOG2E, -lse_i2);
+      const float pi = __builtin_amdgcn_exp2f(lpi2);
+      // terms below 1e-30 are negligible (and log2 of a subnormal is not reliable)
+      if (p > 1e-30f) lacc += p * (__builtin_amdgcn_logf(p) - lpi2);
+      dlogits[t * ld + s] = pi - p;
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+    if (nblk > 0) issue(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+      vm_wait<0>();
+      __syncthreads();  // block blk is in LDS; every wave is done with block blk - 1
+      if (pass == 1 && blk > 0 && row_ok) finalize(blk - 1);
+      if (blk + 1 < nblk) issue(blk + 1);
+      if (!active) continue;
+      const uint8_t* Kst = Kbuf + (blk & 1) * C::K_BYTES;
+      v16f acc = {};
+      constexpr int LA = 3;  // fragments in flight
+      s16x8 Bf[LA];
+#pragma unroll
+      for (int i = 0; i < LA - 1; ++i) Bf[i] = *reinterpret_cast<const s16x8*>(Kst + koff(i));
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + LA - 1 < NKS) Bf[(ks + LA - 1) % LA] = *reinterpret_cast<const s16x8*>(Kst + koff(ks + LA - 1));
+        acc = mfma_bf16_32x32x16(Qf[ks], Bf[ks % LA], acc);
+      }
+      // lane: key blk * KB + l32; element r: head 32 grp + 8 (r / 4) + 4 lh + r % 4
+      const bool valid = (int64_t)blk * KL_KB + l32 < n;
+      if (pass == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lse_push(st_m[r], st_l[r], valid ? acc[r] * scale_log2 : -INFINITY);
+      } else {
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ps += __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -lse2[r]));
+        ps = valid ? ps : 0.f;
+        ps += __shfl_xor(ps, 32);
+        if (lh == 0) red[((blk & 1) * KL_TOK + tok) * KL_GROUPS * KL_KB + grp * KL_KB + l32] = ps;
+      }
+    }
+    if (pass == 0) {
+      // each head's normaliser: merge the 32 lanes that hold it (one key column each)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float m = st_m[r], l = st_l[r];
+        for (int o = 1; o < 32; o <<= 1) lse_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
+        const int hh = grp * 32 + 8 * (r / 4) + 4 * lh + r % 4;
+        lse2[r] = (hh < H && l > 0.f) ? m + __builtin_amdgcn_logf(l) : INFINITY;
+      }
+      __syncthreads();  // both stages free before pass 2 refills them
+    } else {
+      vm_wait<0>();
+      __syncthreads();
+      if (row_ok && nblk > 0) finalize(nblk - 1);
+    }
+  }
+  if (grp == 0 && row_ok) {
+    float v = lh == 0 ? lacc : 0.f;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) loss[t] = v * KL_LN2;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward.  z is recomputed from the FP8 codes converted to bf16 (exact) with the 16x16x32 bf16
+// MFMA; the scales, the weights and dI enter in fp32.  A 16x16 accumulator holds, in lane l,
+// column l % 16 and rows 4 (l / 16) + r: computing z with the rows that are contracted next on
+// the M side puts them, four per lane for each of two 16-row sub-blocks, exactly where the A
+// operand of the next 16x16x32 MFMA expects its eight contraction elements (element e of lane
+// group g: sub-block e / 4, row 4 g + e % 4).  The matching B operand comes from the streamed
+// rows in LDS (bf16, row-major) by transposing reads.  The gradient tile is split as
+// hi = bf16 truncation, lo = bf16(g - hi), so hi + lo carries 16 significant bits.
+// ---------------------------------------------------------------------------------------
+constexpr int BW_ROWS = 16;   // owned rows of one 16x16 tile
+constexpr int BW_BLK = 32;    // streamed rows per block (two sub-blocks of 16)
+constexpr int BQ_WAVES = 8;   // dq / dw: 16 query rows x 2 heads per wave
+constexpr int BQ_HPW = 2;
+constexpr int BK_WAVES = 4;   // dk: 32 keys per wave, all heads
+constexpr int BK_KPW = 32;
+constexpr int BK_HC = 8;      // heads of a query block staged at once
+
+template <int DI>
+struct BwCfg {
+  static constexpr int NDT = DI / 16;   // 16-column output tiles
+  static constexpr int NZS = DI / 32;   // contraction steps of z
+  static constexpr int STRIDE = DI * 2 + 16;  // bytes per bf16 row in LDS (pad: bank spread)
+  static constexpr size_t BK_SMEM = (size_t)BK_HC * BW_BLK * STRIDE + BK_HC * BW_BLK * sizeof(float);
+};
+
+__device__ __forceinline__ void split_bf16(float v, short& hi, short& lo) {
+  const uint32_t u = __float_as_uint(v) & 0xFFFF0000u;
+  hi = (short)(u >> 16);
+  lo = (short)f32_to_bf16(v - __uint_as_float(u));  // the difference is exact
+}
+
+// 16 FP8 codes of one row -> 16 bf16 values at dst (32 bytes, 16-byte aligned).
+__device__ __forceinline__ void stage_row16(uint8_t* dst, v4i raw) {
+  *reinterpret_cast<s16x8*>(dst) = e4m3x8_to_bf16((uint32_t)raw[0], (uint32_t)raw[1]);
+  *reinterpret_cast<s16x8*>(dst + 16) = e4m3x8_to_bf16((uint32_t)raw[2], (uint32_t)raw[3]);
+}
+
+// B operand of a 16x16x32 MFMA over the 32 rows of a staged block (contraction = rows in the
+// order of the A operand above), for output columns c0 .. c0 + 15.
+template <int STRIDE>
+__device__ __forceinline__ s16x8 block_columns(const uint8_t* blk, int lane, int c0) {
+  const int g = (lane >> 4) & 3, a = lane & 15;
+  const uint8_t* p = blk + (4 * g + (a >> 2)) * STRIDE + (c0 + 4 * (a & 3)) * 2;
+  const s16x4 x0 = lds_transpose_read16(p), x1 = lds_transpose_read16(p + 16 * STRIDE);
+  return (s16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+
+// A operand of step zs of z over a staged block: sub-block sub, row l % 16, columns 32 zs + 8 g.
+template <int STRIDE>
+__device__ __forceinline__ s16x8 block_rows(const uint8_t* blk, int lane, int sub, int zs) {
+  return *reinterpret_cast<const s16x8*>(blk + (16 * sub + (lane & 15)) * STRIDE + (32 * zs + 8 * (lane >> 4)) * 2);
+}
+
+// dq and dw: a workgroup owns 16 query rows and 16 heads (two per wave) and streams the keys.
+template <int DI>
+__global__ __launch_bounds__(BQ_WAVES * WAVE, 1) void indexer_bwd_q_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
+    const uint8_t* __restrict__ k8, const float* __restrict__ ks, int64_t T, int64_t S, int32_t H_I,
+    int64_t q_start, const float* __restrict__ dI, int64_t ld, float* __restrict__ dq, float* __restrict__ dw) {
+  using C = BwCfg<DI>;
+  __shared__ __align__(16) uint8_t kt[BW_BLK * C::STRIDE];
+  __shared__ float kss[BW_BLK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int64_t t0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * BW_ROWS;  // latest rows first
+  const int64_t t = t0 + j16;
+  const bool t_ok = t < T;
+  const int64_t n_t = t_ok ? min(S, q_start + t + 1) : 0;
+  const int64_t n_max = min(S, q_start + min(t0 + BW_ROWS, T));
+  const int jw = (blockIdx.y * BQ_WAVES + wave) * BQ_HPW;
+
+  // owned queries, B operands of z^T = K Q^T: lane = query t, columns 32 zs + 8 g .. + 7
+  s16x8 Qb[BQ_HPW][C::NZS];
+#pragma unroll
+  for (int h = 0; h < BQ_HPW; ++h)
+#pragma unroll
+    for (int zs = 0; zs < C::NZS; ++zs) {
+      s16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (t_ok && jw + h < H_I) {
+        const v2i raw = *reinterpret_cast<const v2i*>(q8 + (t * H_I + jw + h) * DI + 32 * zs + 8 * g);
+        v = e4m3x8_to_bf16((uint32_t)raw[0], (uint32_t)raw[1]);
+      }
+      Qb[h][zs] = v;
+    }
+  v4f acc[BQ_HPW][C::NDT];
+  float dwa[BQ_HPW];
+#pragma unroll
+  for (int h = 0; h < BQ_HPW; ++h) {
+    dwa[h] = 0.f;
+#pragma unroll
+    for (int n = 0; n < C::NDT; ++n) acc[h][n] = (v4f){0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int64_t kb = 0; kb < n_max; kb += BW_BLK) {
+    __syncthreads();  // the previous block is consumed
+    for (int p = tid; p < BW_BLK * (DI / 16); p += BQ_WAVES * WAVE) {
+      const int r = p / (DI / 16), c = p % (DI / 16);
+      const int64_t s = min(kb + r, S - 1);
+      stage_row16(kt + r * C::STRIDE + c * 32, *reinterpret_cast<const v4i*>(k8 + s * DI + c * 16));
+    }
+    if (tid < BW_BLK) kss[tid] = ks[min(kb + tid, S - 1)];
+    __syncthreads();
+    // key factors dI[t,s] ks[s] of this lane's eight (row, key) pairs; 0 outside the causal range
+    float u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kr = (e < 4 ? 0 : 16) + 4 * g + (e & 3);
+      u[e] = kb + kr < n_t ? dI[t * ld + kb + kr] * kss[kr] : 0.f;
+    }
+    s16x8 Ka[2][C::NZS], Kb[C::NDT];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int zs = 0; zs < C::NZS; ++zs) Ka[sub][zs] = block_rows<C::STRIDE>(kt, lane, sub, zs);
+#pragma unroll
+    for (int nt = 0; nt < C::NDT; ++nt) Kb[nt] = block_columns<C::STRIDE>(kt, lane, 16 * nt);
+#pragma unroll
+    for (int h = 0; h < BQ_HPW; ++h) {
+      if (jw + h >= H_I) break;  // wave-uniform
+      v4f z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int zs = 0; zs < C::NZS; ++zs) {
+        z0 = mfma_bf16_16x16x32(Ka[0][zs], Qb[h][zs], z0);
+        z1 = mfma_bf16_16x16x32(Ka[1][zs], Qb[h][zs], z1);
+      }
+      s16x8 ghi, glo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float zz = e < 4 ? z0[e] : z1[e - 4];
+        dwa[h] = fmaf(u[e], fmaxf(zz, 0.f), dwa[h]);
+        short hi, lo;
+        split_bf16(zz > 0.f ? u[e] : 0.f, hi, lo);
+        ghi[e] = hi;
+        glo[e] = lo;
+      }
+#pragma unroll
+      for (int nt = 0; nt < C::NDT; ++nt) {
+        acc[h][nt] = mfma_bf16_16x16x32(ghi, Kb[nt], acc[h][nt]);
+        acc[h][nt] = mfma_bf16_16x16x32(glo, Kb[nt], acc[h][nt]);
+      }
+    }
+  }
+  // dq rows t0 + 4 g + r, columns 16 nt + j16; dw row t (reduced over the four lane groups)
+#pragma unroll
+  for (int h = 0; h < BQ_HPW; ++h) {
+    const int j = jw + h;
+    if (j >= H_I) break;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t tr = t0 + 4 * g + r;
+      if (tr < T) {
+        const float wv = w[tr * H_I + j];
+#pragma unroll
+        for (int nt = 0; nt < C::NDT; ++nt) dq[(tr * H_I + j) * DI + 16 * nt + j16] = acc[h][nt][r] * wv;
+      }
+    }
+    const float v = wave_sum_xor16_32(dwa[h]);
+    if (g == 0 && t_ok) dw[t * H_I + j] = v * qs[t * H_I + j];
+  }
+}
+
+// Queries [qc qchunk, (qc + 1) qchunk) that can see keys of key group kg (keys 128 kg ..): the
+// chunk contributes a partial dk for the group iff this range is not empty.
+__host__ __device__ __forceinline__ void bk_query_range(int64_t kg, int64_t qc, int64_t qchunk, int64_t T,
+                                                        int64_t q_start, int64_t& tb, int64_t& te) {
+  tb = max(qc * qchunk, kg * (BK_WAVES * BK_KPW) - q_start);
+  te = min(T, (qc + 1) * qchunk);
+}
+
+// dk partials: a workgroup owns 128 keys (32 per wave) and streams the query rows of one chunk,
+// all heads, eight heads at a time; part [nqc][S][DI].
+template <int DI>
+__global__ __launch_bounds__(BK_WAVES * WAVE, 2) void indexer_bwd_k_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
+    const uint8_t* __restrict__ k8, int64_t T, int64_t S, int32_t H_I, int64_t q_start,
+    const float* __restrict__ dI, int64_t ld, int64_t qchunk, float* __restrict__ part) {
+  using C = BwCfg<DI>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* qt = smem;                                                          // [HC][32][STRIDE]
+  float* wq = reinterpret_cast<float*>(smem + (size_t)BK_HC * BW_BLK * C::STRIDE);  // [HC][32]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int64_t kg = blockIdx.x, qc = blockIdx.y;
+  int64_t tb0, t_end;
+  bk_query_range(kg, qc, qchunk, T, q_start, tb0, t_end);
+  if (tb0 >= t_end) return;  // workgroup-uniform: no partial for this chunk
+  const int64_t s_w = kg * (BK_WAVES * BK_KPW) + wave * BK_KPW;
+
+  // owned keys, B operands of z = Q K^T: lane = key s_w + 16 u + j16, columns 32 zs + 8 g .. + 7
+  s16x8 Kb[2][C::NZS];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int zs = 0; zs < C::NZS; ++zs) {
+      const int64_t s = min(s_w + 16 * u + j16, S - 1);
+      const v2i raw = *reinterpret_cast<const v2i*>(k8 + s * DI + 32 * zs + 8 * g);
+      Kb[u][zs] = e4m3x8_to_bf16((uint32_t)raw[0], (uint32_t)raw[1]);
+    }
+  v4f acc[2][C::NDT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int nt = 0; nt < C::NDT; ++nt) acc[u][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t tb = tb0; tb < t_end; tb += BW_BLK) {
+    // dI of this lane's 16 (row, key) pairs; 0 outside the chunk or the causal range
+    float dv[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t tq = tb + (e < 4 ? 0 : 16) + 4 * g + (e & 3);
+        const int64_t s = s_w + 16 * u + j16;
+        dv[u][e] = (tq < t_end && s < min(S, q_start + tq + 1)) ? dI[tq * ld + s] : 0.f;
+      }
+    for (int hc = 0; hc < H_I; hc += BK_HC) {
+      __syncthreads();  // the previous heads are consumed
+      for (int p = tid; p < BK_HC * BW_BLK * (DI / 16); p += BK_WAVES * WAVE) {
+        const int c = p % (DI / 16), rq = (p / (DI / 16)) % BW_BLK, hh = p / (DI / 16) / BW_BLK;
+        const int64_t tq = tb + rq;
+        const int j = hc + hh;
+        v4i raw = {0, 0, 0, 0};
+        if (tq < t_end && j < H_I) raw = *reinterpret_cast<const v4i*>(q8 + (tq * H_I + j) * DI + c * 16);
+        stage_row16(qt + (hh * BW_BLK + rq) * C::STRIDE + c * 32, raw);
+      }
+      for (int p = tid; p < BK_HC * BW_BLK; p += BK_WAVES * WAVE) {
+        const int rq = p % BW_BLK, hh = p / BW_BLK;
+        const int64_t tq = tb + rq;
+        const int j = hc + hh;
+        wq[p] = (tq < t_end && j < H_I) ? w[tq * H_I + j] * qs[tq * H_I + j] : 0.f;
+      }
+      __syncthreads();
+      for (int hh = 0; hh < BK_HC && hc + hh < H_I; ++hh) {
+        const uint8_t* qh = qt + hh * BW_BLK * C::STRIDE;
+        s16x8 Qa[2][C::NZS], Qc[C::NDT];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int zs = 0; zs < C::NZS; ++zs) Qa[sub][zs] = block_rows<C::STRIDE>(qh, lane, sub, zs);
+#pragma unroll
+        for (int nt = 0; nt < C::NDT; ++nt) Qc[nt] = block_columns<C::STRIDE>(qh, lane, 16 * nt);
+        float wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = wq[hh * BW_BLK + (e < 4 ? 0 : 16) + 4 * g + (e & 3)];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          v4f z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int zs = 0; zs < C::NZS; ++zs) {
+            z0 = mfma_bf16_16x16x32(Qa[0][zs], Kb[u][zs], z0);
+            z1 = mfma_bf16_16x16x32(Qa[1][zs], Kb[u][zs], z1);
+          }
+          s16x8 ghi, glo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float zz = e < 4 ? z0[e] : z1[e - 4];
+            short hi, lo;
+            split_bf16(zz > 0.f ? dv[u][e] * wv[e] : 0.f, hi, lo);
+            ghi[e] = hi;
+            glo[e] = lo;
+          }
+#pragma unroll
+          for (int nt = 0; nt < C::NDT; ++nt) {
+            acc[u][nt] = mfma_bf16_16x16x32(ghi, Qc[nt], acc[u][nt]);
+            acc[u][nt] = mfma_bf16_16x16x32(glo, Qc[nt], acc[u][nt]);
+          }
+        }
+      }
+    }
+  }
+  // keys s_w + 16 u + 4 g + r, columns 16 nt + j16
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t s = s_w + 16 * u + 4 * g + r;
+      if (s < S) {
+#pragma unroll
+        for (int nt = 0; nt < C::NDT; ++nt) part[(qc * S + s) * DI + 16 * nt + j16] = acc[u][nt][r];
+      }
+    }
+}
+
+// dk[s] = sum of the partials of the chunks that see the key's group (0 when none does).
+__global__ __launch_bounds__(256) void indexer_bwd_k_reduce_kernel(const float* __restrict__ part, int64_t S,
+                                                                   int32_t DI, int64_t T, int64_t q_start,
+                                                                   int64_t qchunk, int32_t nqc,
+                                                                   float* __restrict__ dk) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
+  if (i * 4 >= S * DI) return;
+  const int64_t s = i * 4 / DI, kg = s / (BK_WAVES * BK_KPW);
+  v4f sum = {0.f, 0.f, 0.f, 0.f};
+  for (int qc = 0; qc < nqc; ++qc) {
+    int64_t tb, te;
+    bk_query_range(kg, qc, qchunk, T, q_start, tb, te);
+    if (tb < te) sum += *reinterpret_cast<const v4f*>(part + (int64_t)qc * S * DI + i * 4);
+  }
+  *reinterpret_cast<v4f*>(dk + i * 4) = sum;
+}
+
+// ---------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------
+static const int kKlSteps[] = {2, 4, 5, 8, 12, 16, 24, 32, 36};
+
+bool indexer_kl_supported(int32_t H, int32_t D) { return H >= 1 && H <= 128 && D >= 8 && D <= 576 && D % 8 == 0; }
+
+template <int NKS>
+static hipError_t launch_kl(const uint16_t* q, const uint16_t* kv, int64_t T, int64_t S, int32_t H, int32_t D,
+                            float sm_scale, int64_t q_start, const float* logits, int64_t ld, float* dlogits,
+                            float* loss, hipStream_t stream) {
+  using C = KlCfg<NKS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&indexer_kl_kernel<NKS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::SMEM);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t grid = (T + KL_TOK - 1) / KL_TOK;
+  hipLaunchKernelGGL(indexer_kl_kernel<NKS>, dim3((unsigned)grid), dim3(KL_THREADS), C::SMEM, stream, q, kv, T, S,
+                     H, D, sm_scale * KL_LOG2E, q_start, logits, ld, dlogits, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t T, int64_t S, int32_t H, int32_t D,
+                             float sm_scale, int64_t q_start, const float* logits, int64_t ld, float* dlogits,
+                             float* loss, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int need = (D + 15) / 16;
+  int nks = 0;
+  for (int c : kKlSteps)
+    if (c >= need) {
+      nks = c;
+      break;
+    }
+  switch (nks) {
+#define KL_CASE(N) \
+  case N: return launch_kl<N>(q, kv, T, S, H, D, sm_scale, q_start, logits, ld, dlogits, loss, stream);
+    KL_CASE(2) KL_CASE(4) KL_CASE(5) KL_CASE(8) KL_CASE(12) KL_CASE(16) KL_CASE(24) KL_CASE(32) KL_CASE(36)
+#undef KL_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Query chunk of the dk partials: about 16 chunks (enough workgroups for the chip at the
+// workloads' sizes), a multiple of the 32-row block.
+int64_t indexer_bwd_qchunk(int64_t T) {
+  const int64_t c = (T + 15) / 16;
+  return std::max<int64_t>(128, (c + BW_BLK - 1) / BW_BLK * BW_BLK);
+}
+
+size_t indexer_bwd_workspace_bytes(int64_t T, int64_t S, int32_t D_I) {
+  if (T <= 0 || S <= 0) return 0;
+  const int64_t qchunk = indexer_bwd_qchunk(T);
+  const int64_t nqc = (T + qchunk - 1) / qchunk;
+  return (size_t)nqc * (size_t)S * (size_t)D_I * sizeof(float);
+}
+
+template <int DI>
+static hipError_t launch_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
+                             int64_t T, int64_t S, int32_t H_I, int64_t q_start, const float* dI, int64_t ld,
+                             float* dq, float* dw, float* dk, void* workspace, hipStream_t stream) {
+  using C = BwCfg<DI>;
+  const int64_t qtiles = (T + BW_ROWS - 1) / BW_ROWS;
+  const int hgroups = (H_I + BQ_WAVES * BQ_HPW - 1) / (BQ_WAVES * BQ_HPW);
+  hipLaunchKernelGGL(indexer_bwd_q_kernel<DI>, dim3((unsigned)qtiles, (unsigned)hgroups), dim3(BQ_WAVES * WAVE), 0,
+                     stream, q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static bool attr_set = false;
+  if (!attr_set) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&indexer_bwd_k_kernel<DI>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BK_SMEM);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t qchunk = indexer_bwd_qchunk(T);
+  const int32_t nqc = (int32_t)((T + qchunk - 1) / qchunk);
+  const int64_t kgroups = (S + BK_WAVES * BK_KPW - 1) / (BK_WAVES * BK_KPW);
+  float* part = reinterpret_cast<float*>(workspace);
+  hipLaunchKernelGGL(indexer_bwd_k_kernel<DI>, dim3((unsigned)kgroups, (unsigned)nqc), dim3(BK_WAVES * WAVE),
+                     C::BK_SMEM, stream, q8, qs, w, k8, T, S, H_I, q_start, dI, ld, qchunk, part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n4 = S * DI / 4;
+  hipLaunchKernelGGL(indexer_bwd_k_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, part, S,
+                     DI, T, q_start, qchunk, nqc, dk);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
+                              int64_t T, int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, const float* dI,
+                              int64_t ld, float* dq, float* dw, float* dk, void* workspace, hipStream_t stream) {
+  if (T <= 0 || S <= 0) return hipSuccess;
+  switch (D_I) {
+    case 32: return launch_bwd<32>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
+    case 64: return launch_bwd<64>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
+    case 96: return launch_bwd<96>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
+    case 128: return launch_bwd<128>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsa

@@ -202,6 +202,44 @@ dsa_status_t dsa_append_paged(const dsa_paged_cache_t *c, int32_t B, const int32
                               const int32_t *positions, int64_t n, int32_t D_I, int32_t D_qk, const uint16_t *k,
                               const uint16_t *kv, hipStream_t stream);
 
+/*
+ * Indexer training signal (summary page, section "Method", continued pre-training: in the dense
+ * warm-up only the indexer is trained, against a KL-divergence target given by the main
+ * attention).  Reading: for query row t and its visible keys s < n_t,
+ *   p[t][s]  = (1/H) sum_h softmax_s(sm_scale * q[t][h][:] . kv[s][:])   (the main attention over
+ *              every visible key, MQA: K = the whole latent row, averaged over the heads),
+ *   pi[t][s] = softmax_s(logits[t][s]),
+ *   loss[t]  = KL(p || pi) = sum_s p (log p - log pi)   (natural log; 0 log 0 = 0),
+ *   dlogits[t][s] = pi[t][s] - p[t][s]   (the gradient of loss[t] with respect to logits[t][s]).
+ *   q [T][H][D_qk] bf16, kv [S][D_qk] bf16, logits and dlogits [T][ld_logits] f32 (ld_logits >= S,
+ *   a multiple of 4; dlogits may be logits itself, overwritten in place; entries s >= n_t are
+ *   neither read nor written), loss [T] f32.  Scores must be finite.  Supported: 1 <= H <= 128,
+ *   D_qk a multiple of 8 in [8, 576], S >= 1 when T > 0.
+ */
+dsa_status_t dsa_indexer_kl_loss(const uint16_t *q, const uint16_t *kv, int64_t T, int64_t S, int32_t H,
+                                 int32_t D_qk, float sm_scale, int64_t q_start, const float *logits,
+                                 int64_t ld_logits, float *dlogits, float *loss, hipStream_t stream);
+
+/*
+ * Indexer backward (the same training stages): gradients of a loss through the scores of
+ * dsa_indexer_logits given dlogits = dL/dlogits on the visible entries (s < n_t; others never
+ * read).  Reading: the FP8 quantization is passed straight through, so the gradients are with
+ * respect to the dequantized vectors q_I = q_scale dec(q8), k_I = k_scale dec(k8) and w, and
+ * ReLU's derivative is 1 for a positive product and 0 otherwise; with z = q_I[t][j] . k_I[s]:
+ *   dw[t][j] = sum_s dlogits[t][s] max(0, z),
+ *   dq[t][j][:] = w[t][j] sum_{s: z > 0} dlogits[t][s] k_I[s][:],
+ *   dk[s][:] = sum_{t, j: z > 0} dlogits[t][s] w[t][j] q_I[t][j][:].
+ *   Inputs as dsa_indexer_logits (scales positive), dlogits [T][ld_dlogits] f32; outputs dq
+ *   [T][H_I][D_I], dw [T][H_I], dk [S][D_I] f32 (every entry written).  The workspace (device,
+ *   dsa_indexer_bwd_workspace_size() bytes) holds per-chunk partial key gradients; the result is
+ *   deterministic.  Supported: as dsa_indexer_logits, T and S both >= 1 (or both 0).
+ */
+size_t dsa_indexer_bwd_workspace_size(int64_t T, int64_t S, int32_t D_I);
+dsa_status_t dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const float *w, const uint8_t *k8,
+                             const float *k_scale, int64_t T, int64_t S, int32_t H_I, int32_t D_I, int64_t q_start,
+                             const float *dlogits, int64_t ld_dlogits, float *dq, float *dw, float *dk,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -119,3 +119,73 @@ def check_mla(g_bf16: np.ndarray, g_f32: np.ndarray, g_lse: np.ndarray, o_f32: n
     le = np.abs(g_lse[fin].astype(np.float64) - o_lse[fin]) / np.maximum(1.0, np.abs(o_lse[fin]))
     assert le.size == 0 or le.max() <= LSE_TOL, "%s: lse error %.3e" % (what, le.max())
     return float(abs_err.max()), float(rel.max())
+
+
+# ------------------------------------------------------------ indexer training signal / backward
+KL_REL = 1e-3   # the project's relative bar, applied to each quantity's magnitude scale
+
+
+def check_kl(loss_g, d_g, loss_o, d_o, logits, pos, name):
+    """GPU KL loss / dI against the oracle (float64) for the same scores.  p = pi - dI_o with
+    pi = softmax of the (fp32) scores in float64; bars: |d dI| <= KL_REL (p + pi) + 1e-9 per entry,
+    |d loss| <= KL_REL sum_s p (|ln p - ln pi| + 1) + 1e-9 per row."""
+    T, S = d_o.shape
+    worst = 0.0
+    for t in range(T):
+        n = min(S, int(pos[t]) + 1)
+        x = logits[t, :n].astype(np.float64)
+        lpi = x - x.max() - np.log(np.sum(np.exp(x - x.max())))
+        pi = np.exp(lpi)
+        p = pi - d_o[t, :n]
+        err = np.abs(d_g[t, :n].astype(np.float64) - d_o[t, :n])
+        tol = KL_REL * (np.maximum(p, 0.0) + pi) + 1e-9
+        assert np.all(err <= tol), "%s: dI row %d off by %.3e (bar %.3e)" % (name, t, err.max(), tol[np.argmax(err / tol)])
+        worst = max(worst, float(np.max(err / tol)))
+        with np.errstate(divide="ignore", invalid="ignore"):
+            lp = np.where(p > 0, np.log(np.maximum(p, 1e-300)), 0.0)
+        A = np.sum(np.maximum(p, 0.0) * (np.abs(lp - lpi) + 1.0))
+        e = abs(float(loss_g[t]) - loss_o[t])
+        assert e <= KL_REL * A + 1e-9, "%s: loss row %d off by %.3e (bar %.3e)" % (name, t, e, KL_REL * A)
+        worst = max(worst, e / (KL_REL * A + 1e-9))
+    return worst
+
+
+Z_BOUND = 2.0 ** -14   # sign allowance of z relative to sum_i |q_i k_i| (bf16-MFMA accumulation of exact products)
+
+
+def check_indexer_bwd(dq_g, dw_g, dk_g, dq_o, dw_o, dk_o, q8, qs, w, k8, ks, dI, pos, name):
+    """GPU indexer backward against the oracle (float64) for the same dI.  Bars: KL_REL times each
+    output's magnitude scale (the sum of the absolute values of its terms), plus the absolute terms
+    of the (t, j, s) whose ReLU sign is within the accumulation error of z (either side is right)."""
+    tab = e4m3_abs_table().astype(np.float64)
+    sgn = np.where(np.arange(256) & 0x80, -1.0, 1.0)
+    dec = tab * sgn
+    qd = dec[q8] * qs.astype(np.float64)[..., None]           # [T, H, D]
+    kd = dec[k8] * ks.astype(np.float64)[:, None]             # [S, D]
+    T, H, D = q8.shape
+    S = k8.shape[0]
+    vis = np.arange(S)[None, :] < np.minimum(S, np.asarray(pos) + 1)[:, None]
+    dIv = np.where(vis, dI.astype(np.float64), 0.0)           # [T, S]
+    z = np.einsum("tjd,sd->tjs", qd, kd)
+    zabs = np.einsum("tjd,sd->tjs", np.abs(qd), np.abs(kd))
+    amb = np.abs(z) <= Z_BOUND * zabs                          # either ReLU side is right
+    on = (z > 0) | amb
+    wa = np.abs(w.astype(np.float64))
+    # dw: terms |dI| max(z, 0)
+    A_dw = np.einsum("ts,tjs->tj", np.abs(dIv), np.maximum(z, 0.0) + amb * np.abs(z))
+    e = np.abs(dw_g - dw_o)
+    assert np.all(e <= KL_REL * A_dw + 1e-12), "%s: dw off by %.3e" % (name, e.max())
+    worst = float(np.max(e / (KL_REL * A_dw + 1e-12)))
+    # dq[t,j,:]: terms |dI w k| over the keys on either side of the mask
+    A_dq = np.einsum("ts,tjs,sd->tjd", np.abs(dIv), on.astype(np.float64), np.abs(kd), optimize=True) * wa[..., None]
+    X_dq = np.einsum("ts,tjs,sd->tjd", np.abs(dIv), amb.astype(np.float64), np.abs(kd), optimize=True) * wa[..., None]
+    e = np.abs(dq_g - dq_o)
+    assert np.all(e <= KL_REL * A_dq + X_dq + 1e-12), "%s: dq off by %.3e" % (name, e.max())
+    worst = max(worst, float(np.max(e / (KL_REL * A_dq + X_dq + 1e-12))))
+    # dk[s,:]: terms |dI w q|
+    A_dk = np.einsum("ts,tjs,tj,tjd->sd", np.abs(dIv), on.astype(np.float64), wa, np.abs(qd), optimize=True)
+    X_dk = np.einsum("ts,tjs,tj,tjd->sd", np.abs(dIv), amb.astype(np.float64), wa, np.abs(qd), optimize=True)
+    e = np.abs(dk_g - dk_o)
+    assert np.all(e <= KL_REL * A_dk + X_dk + 1e-12), "%s: dk off by %.3e" % (name, e.max())
+    worst = max(worst, float(np.max(e / (KL_REL * A_dk + X_dk + 1e-12))))
+    return int(amb.sum()), worst

@@ -136,3 +136,36 @@ def test_quantize_and_append_argument_errors(lib):
     assert g(ctypes.byref(bad_bs), 2, FAKE, FAKE, 5, 128, 576, FAKE, FAKE, None) == INVALID
     assert g(ctypes.byref(c), 0, FAKE, FAKE, 5, 128, 576, FAKE, FAKE, None) == INVALID       # tokens, no sequences
     assert g(None, 0, None, None, 0, 128, 576, None, None, None) == OK
+
+
+def test_kl_loss_and_backward_argument_errors(lib):
+    f = lib.dsa_indexer_kl_loss
+    sm = ctypes.c_float(0.07)
+    assert f(FAKE, FAKE, 4, 8, 129, 576, sm, 0, FAKE, 8, FAKE, FAKE, None) == UNSUPPORTED   # H > 128
+    assert f(FAKE, FAKE, 4, 8, 128, 580, sm, 0, FAKE, 8, FAKE, FAKE, None) == UNSUPPORTED   # D_qk
+    assert f(FAKE, FAKE, 4, 8, 128, 576, sm, 0, FAKE, 6, FAKE, FAKE, None) == INVALID       # ld < S
+    assert f(FAKE, FAKE, 4, 0, 128, 576, sm, 0, FAKE, 8, FAKE, FAKE, None) == INVALID       # no keys
+    assert f(FAKE, FAKE, 4, 8, 128, 576, ctypes.c_float(0.0), 0, FAKE, 8, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 4, 8, 128, 576, sm, 0, FAKE, 8, FAKE, None, None) == INVALID       # loss
+    assert "loss" in _err(lib)
+    assert f(None, None, 0, 8, 128, 576, sm, 0, None, 8, None, None, None) == OK            # T = 0
+    g = lib.dsa_indexer_bwd
+    need = lib.dsa_indexer_bwd_workspace_size(64, 64, 128)
+    assert need > 0 and lib.dsa_indexer_bwd_workspace_size(0, 64, 128) == 0
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 128, 0, FAKE, 64, FAKE, FAKE, FAKE, FAKE, need, None]
+    bad = list(args)
+    bad[8] = 100                                                                            # D_I
+    assert g(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[16] = need - 1
+    assert g(*bad) == WS_SMALL
+    bad = list(args)
+    bad[14] = None                                                                          # dk
+    assert g(*bad) == INVALID
+    bad = list(args)
+    bad[5] = 0                                                                              # T = 0, S > 0
+    assert g(*bad) == INVALID
+    bad = list(args)
+    bad[11] = 66                                                                            # ld % 4
+    assert g(*bad) == INVALID
+    assert g(None, None, None, None, None, 0, 0, 64, 128, 0, None, 4, None, None, None, None, 0, None) == OK

@@ -1,0 +1,147 @@
+"""The indexer's training signal (KL loss toward the head-averaged main attention) and the indexer
+backward through the C ABI against the oracle (needs an MI355X).
+
+Shapes cover the workloads' widths (H = 128 heads of 576-wide latent rows, H_I = 64 indexer heads
+of 128) and the small configuration's (8 heads of 80, 4 indexer heads of 32), an odd number of
+query rows (the last workgroup holds one row), partial head groups, a latent row width that is
+not a multiple of 16, every supported D_I, rows that end inside a key block, the in-place score
+gradient, and the whole chain (indexer -> loss -> backward) at the 4K prefill shape on sampled
+rows."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from dsa_inputs.generate import block_rng, quantize_fp8_rows, to_bf16_bits
+from gpu_helpers import dget, dput
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dsa_lightning_indexer_02_amd as dsa
+    dsa.load()
+    return torch.device("cuda:0")
+
+
+def _kl_case(dev, T, S, q_start, H, D, sm, seed, scale=2.0, in_place=False):
+    import dsa_lightning_indexer_02_amd as dsa
+    print("case kl", T, S, q_start, H, D, "in_place" if in_place else "", flush=True)
+    g = block_rng(seed, T, S)
+    q = to_bf16_bits(g.standard_normal((T, H, D)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D)).astype(np.float32))
+    ld = dsa.ld_for(S)
+    logits = np.zeros((T, ld), np.float32)
+    logits[:, :S] = (g.standard_normal((T, S)) * scale).astype(np.float32)
+    lg = dput(logits, dev)
+    loss, d = dsa.dsa_indexer_kl_loss(dput(q, dev).view(torch.bfloat16), dput(kv, dev).view(torch.bfloat16), lg,
+                                      sm, q_start=q_start, in_place=in_place)
+    torch.cuda.synchronize()
+    pos = q_start + np.arange(T)
+    lo, do = oracle.indexer_kl(q, kv, pos, sm, logits[:, :S])
+    worst = parity.check_kl(dget(loss), dget(d)[:, :S], lo, do, logits[:, :S], pos, "kl %dx%d H=%d D=%d" % (T, S, H, D))
+    print("  worst error / bar: %.3e" % worst, flush=True)
+    if in_place:
+        assert d.data_ptr() == lg.data_ptr()
+
+
+@pytest.mark.parametrize("T,S,q_start,H,D,sm", [
+    (40, 64, 24, 8, 80, 80 ** -0.5),          # the small configuration's attention shape
+    (67, 300, 250, 128, 576, 192 ** -0.5),    # full width, odd row count, rows ending mid-block
+    (33, 100, 80, 20, 72, 0.11),              # partial head group, row width padded to 80
+    (16, 16, 0, 128, 576, 192 ** -0.5),       # causal from the first key (rows of 1 .. 16 keys)
+])
+def test_kl_loss_vs_oracle(dev, T, S, q_start, H, D, sm):
+    _kl_case(dev, T, S, q_start, H, D, sm, 81)
+
+
+def test_kl_loss_in_place_and_sharp(dev):
+    _kl_case(dev, 31, 97, 70, 64, 576, 192 ** -0.5, 82, in_place=True)
+    # sharp indexer distributions (scores spread over ~60 nats)
+    _kl_case(dev, 20, 50, 30, 16, 80, 0.5, 83, scale=20.0)
+
+
+def _bwd_case(dev, T, S, q_start, H_I, D_I, seed):
+    import dsa_lightning_indexer_02_amd as dsa
+    print("case bwd", T, S, q_start, H_I, D_I, flush=True)
+    g = block_rng(seed, T, S)
+    q8, qs = quantize_fp8_rows(g.standard_normal((T, H_I, D_I)).astype(np.float32))
+    k8, ks = quantize_fp8_rows(g.standard_normal((S, D_I)).astype(np.float32))
+    w = (g.uniform(0.0, 1.0, (T, H_I)) / H_I).astype(np.float32)
+    ld = dsa.ld_for(S)
+    dI = np.zeros((T, ld), np.float32)
+    dI[:, :S] = (g.standard_normal((T, S)) * 1e-2).astype(np.float32)
+    dq, dw, dk = dsa.dsa_indexer_bwd(dput(q8, dev), dput(qs, dev), dput(w, dev), dput(k8, dev), dput(ks, dev),
+                                     dput(dI, dev), q_start=q_start)
+    torch.cuda.synchronize()
+    pos = q_start + np.arange(T)
+    oq, ow, ok = oracle.indexer_bwd(q8, qs, w, pos, k8, ks, dI[:, :S])
+    amb, worst = parity.check_indexer_bwd(dget(dq), dget(dw), dget(dk), oq, ow, ok, q8, qs, w, k8, ks, dI[:, :S], pos,
+                                   "bwd %dx%d H_I=%d D_I=%d" % (T, S, H_I, D_I))
+    print("  ambiguous ReLU signs: %d, worst error / bar: %.3e" % (amb, worst), flush=True)
+
+
+@pytest.mark.parametrize("T,S,q_start,H_I,D_I", [
+    (256, 256, 0, 4, 32),        # the small configuration
+    (100, 300, 200, 64, 128),    # full heads; ragged rows, keys and query chunks
+    (50, 50, 0, 20, 64),         # partial head group
+    (40, 170, 130, 8, 96),
+    (300, 700, 400, 64, 128),    # several dk query chunks, key groups that no row sees
+])
+def test_indexer_bwd_vs_oracle(dev, T, S, q_start, H_I, D_I):
+    _bwd_case(dev, T, S, q_start, H_I, D_I, 84)
+
+
+def test_train_chain_prefill_4k_rows(dev):
+    """indexer -> KL loss (in place) -> backward at the 4K prefill shape; the loss and dI of
+    sampled rows against the oracle (its own scores), the backward against the oracle fed the same
+    GPU-independent inputs on a slice of the rows."""
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import get, prefill_inputs
+    wl = get("prefill_4k")
+    inp = prefill_inputs(wl)
+    print("case train chain prefill_4k", flush=True)
+    lg = dsa.dsa_indexer_logits(dput(inp.q8, dev), dput(inp.qs, dev), dput(inp.w, dev), dput(inp.k8, dev),
+                                dput(inp.ks, dev), 0)
+    q = dput(inp.q, dev).view(torch.bfloat16)
+    kv = dput(inp.kv, dev).view(torch.bfloat16)
+    loss, d = dsa.dsa_indexer_kl_loss(q, kv, lg, wl.sm_scale, in_place=True)
+    dq, dw, dk = dsa.dsa_indexer_bwd(dput(inp.q8, dev), dput(inp.qs, dev), dput(inp.w, dev), dput(inp.k8, dev),
+                                     dput(inp.ks, dev), d)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 17, 1000, 2047, 3333, 4095])
+    pos = rows.astype(np.int64)
+    o_lg = oracle.indexer(inp.q8[rows], inp.qs[rows], inp.w[rows], pos, inp.k8, inp.ks)
+    o_lg = np.nan_to_num(o_lg, nan=0.0)
+    lo, do = oracle.indexer_kl(inp.q[rows], inp.kv, pos, wl.sm_scale, o_lg)
+    # the GPU's scores differ from the oracle's within the indexer bar; the loss moves by at most
+    # sum |dI| |dlogit| <= 2 max |dlogit|, dI by at most (e - 1)-relative of pi
+    A = parity.magnitude(inp.q8[rows], inp.qs[rows], inp.w[rows], inp.k8, inp.ks, pos, wl.S)
+    dmax = np.nanmax(A, axis=1) * (parity.MFMA_FP8_BOUND + 2.0 ** -20)
+    g_loss, g_d = dget(loss)[rows], dget(d)[rows, :wl.S]
+    for i, t in enumerate(rows):
+        n = t + 1
+        x = o_lg[i, :n].astype(np.float64)
+        pi = np.exp(x - x.max()) / np.sum(np.exp(x - x.max()))
+        p = pi - do[i, :n]
+        tol = parity.KL_REL * (np.abs(p) + pi) + pi * (np.exp(2 * dmax[i]) - 1) + 1e-9
+        assert np.all(np.abs(g_d[i, :n] - do[i, :n]) <= tol), "chain dI row %d" % t
+        assert abs(g_loss[i] - lo[i]) <= parity.KL_REL * (lo[i] + 1.0) + 2 * dmax[i], "chain loss row %d" % t
+    assert np.all(np.isfinite(dget(dq))) and np.all(np.isfinite(dget(dw))) and np.all(np.isfinite(dget(dk)))
+    # the backward on the GPU's own dI is checked elementwise by the shape tests above; at full size
+    # it must satisfy Euler's identity: I is homogeneous of degree 2 in (q_I, k_I) jointly and of
+    # degree 1 in w, so (sum dq . q_I + sum dk . k_I) / 2 = sum dI I = sum dw . w
+    tab = parity.e4m3_abs_table().astype(np.float64) * np.where(np.arange(256) & 0x80, -1.0, 1.0)
+    qd = tab[inp.q8] * inp.qs.astype(np.float64)[..., None]
+    kd = tab[inp.k8] * inp.ks.astype(np.float64)[:, None]
+    gq, gk, gw = (dget(x).astype(np.float64) for x in (dq, dk, dw))
+    lhs = (np.sum(gq * qd) + np.sum(gk * kd)) / 2.0
+    rhs = np.sum(gw * inp.w.astype(np.float64))
+    scale = (np.sum(np.abs(gq * qd)) + np.sum(np.abs(gk * kd))) / 2.0 + np.sum(np.abs(gw * inp.w))
+    assert abs(lhs - rhs) <= parity.KL_REL * scale, "Euler identity of the backward: %.6e vs %.6e" % (lhs, rhs)
