@@ -11,8 +11,9 @@ one JSON line.
 ``--workload`` selects another configuration (tiny, prefill_4k, chunked_131k, decode_64; decode
 times the fused paged decode call against its HBM roofline; quantize_append_32k times the FP8
 quantization of the L = 32K queries and the paged append of its tokens; indexer_ue8m0_32k the
-indexer with power-of-two scales inside the MFMA), and ``--all-configs`` prints one line per
-configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
+indexer with power-of-two scales inside the MFMA; indexer_train_4k / indexer_train_32k one
+training step of the indexer: scores, KL loss toward the main attention, backward), and
+``--all-configs`` prints one line per configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -411,6 +412,78 @@ def run_indexer_ue8m0(args, dev):
     }
 
 
+def run_indexer_train(name, args, dev):
+    """One training step of the indexer at a prefill shape (dense warm-up signal): scores ->
+    KL loss toward the head-averaged main attention (dI in place of the scores) -> backward to
+    q_I, k_I and w.  The inputs of the prefill configuration; stages timed with events."""
+    import torch
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import get, prefill_inputs
+    wl = get(name.replace("indexer_train_", "prefill_"))
+    print("generating %s inputs" % wl.name, file=sys.stderr, flush=True)
+    inp = prefill_inputs(wl)
+    q8, qs, w, k8, ks = (put(x, dev) for x in (inp.q8, inp.qs, inp.w, inp.k8, inp.ks))
+    q = put(inp.q, dev).view(torch.bfloat16)
+    kv = put(inp.kv, dev).view(torch.bfloat16)
+    del inp
+    T, S = wl.T, wl.S
+    logits = torch.empty((T, dsa.ld_for(S)), dtype=torch.float32, device=dev)
+    loss = torch.empty((T,), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, wl.H_I, wl.D_I), dtype=torch.float32, device=dev)
+    dw = torch.empty((T, wl.H_I), dtype=torch.float32, device=dev)
+    dk = torch.empty((S, wl.D_I), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, dsa.indexer_bwd_workspace_size(T, S, wl.D_I)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dsa.dsa_indexer_logits(q8, qs, w, k8, ks, wl.q_start, logits)
+        if ev:
+            ev[1].record(stream)
+        dsa.dsa_indexer_kl_loss(q, kv, logits, wl.sm_scale, wl.q_start, dlogits=logits, loss=loss)
+        if ev:
+            ev[2].record(stream)
+        dsa.dsa_indexer_bwd(q8, qs, w, k8, ks, logits, wl.q_start, dq, dw, dk, ws)
+        if ev:
+            ev[3].record(stream)
+
+    print("warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print("timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    step_ms = per.sum(axis=1)
+    ims, kms, bms = per.mean(axis=0)
+    wm = work_model(wl)
+    pairs = wm["visible_pairs"]
+    kl_flop = 2.0 * wl.H * wl.D_qk * pairs            # one Q K^T over every visible pair
+    bwd_flop = 3 * 2.0 * wl.H_I * wl.D_I * pairs      # z, dq and dk contractions
+    stages = {
+        "indexer": {"ms": float(ims), "bound": "mfma", "achieved_tflops": wm["indexer_flop"] / ims / 1e9,
+                    "frac": wm["indexer_flop"] / (ims / 1e3) / PEAK_FP8},
+        "kl_loss": {"ms": float(kms), "bound": "mfma", "achieved_tflops": kl_flop / kms / 1e9,
+                    "frac": kl_flop / (kms / 1e3) / PEAK_BF16},
+        "indexer_bwd": {"ms": float(bms), "bound": "mfma", "achieved_tflops": bwd_flop / bms / 1e9,
+                        "frac": bwd_flop / (bms / 1e3) / PEAK_BF16},
+    }
+    roof = {"kernel": "indexer_kl_kernel<36>", "bound": "mfma", "achieved": kl_flop / (kms / 1e3) / 1e12,
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "traffic": None, "algorithmic_flop_per_launch": kl_flop,
+            "avg_launch_ms": float(kms)}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return {
+        "value": T / (float(np.median(step_ms)) / 1e3), "ms_per_step": float(np.median(step_ms)),
+        "step_ms_events": percentiles(step_ms), "roofline": roof, "stages": stages,
+        "config": {"workload": name, "T": T, "S": S, "q_start": wl.q_start, "H": wl.H, "D_qk": wl.D_qk,
+                   "H_I": wl.H_I, "D_I": wl.D_I, "parallelism": "single GPU"},
+    }
+
+
 def run_one(name, args, dev, with_cpu: bool):
     from dsa_inputs import get
     if name in ("quantize_append_32k", "indexer_ue8m0_32k"):
@@ -426,6 +499,16 @@ def run_one(name, args, dev, with_cpu: bool):
                 "stages": res["stages"], "step_ms_events": res["step_ms_events"], "fused_ms_per_step": None,
                 "cpu_baseline": None}
         return line
+    if name.startswith("indexer_train_"):
+        res = run_indexer_train(name, args, dev)
+        return {"metric": "query tokens/s (indexer training step: scores + KL loss + backward, %s)" % name,
+                "value": res["value"], "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None,
+                "dtype": "fp8-e4m3 indexer, bf16 MFMA loss and backward, fp32 gradients",
+                "data": "synthetic (seeded PCG64 recipe, FP8 per-row absmax codes, bf16 N(0,1))",
+                "config": res["config"], "roofline": res["roofline"], "stages": res["stages"],
+                "step_ms_events": res["step_ms_events"], "fused_ms_per_step": None, "cpu_baseline": None}
     wl = get(name)
     res = run_decode(wl, args, dev) if wl.kind == "decode" else run_prefill(wl, args, dev)
     cpu = None
@@ -483,7 +566,7 @@ def main():
     dsa.load()
     if args.all_configs:
         for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64", "quantize_append_32k",
-                     "indexer_ue8m0_32k"]:
+                     "indexer_ue8m0_32k", "indexer_train_4k"]:
             print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return

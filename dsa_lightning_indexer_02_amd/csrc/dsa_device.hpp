@@ -109,6 +109,29 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wait until at most n (wave-uniform, 0 <= n) vector-memory operations of this wave are pending;
+// n above 15 waits for 15.
+__device__ __forceinline__ void vm_wait_pending(int n) {
+  switch (n) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<1>(); break;
+    case 2: vm_wait<2>(); break;
+    case 3: vm_wait<3>(); break;
+    case 4: vm_wait<4>(); break;
+    case 5: vm_wait<5>(); break;
+    case 6: vm_wait<6>(); break;
+    case 7: vm_wait<7>(); break;
+    case 8: vm_wait<8>(); break;
+    case 9: vm_wait<9>(); break;
+    case 10: vm_wait<10>(); break;
+    case 11: vm_wait<11>(); break;
+    case 12: vm_wait<12>(); break;
+    case 13: vm_wait<13>(); break;
+    case 14: vm_wait<14>(); break;
+    default: vm_wait<15>(); break;
+  }
+}
+
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16 lanes, lane i
 // receives element i % 4 of the four 16-bit words addressed by lanes 4 j + i / 4 of its group,
 // j = 0..3.  With lane a of group g addressing row r0 + a / 4, columns c0 + 4 (a % 4) .. + 3 of a

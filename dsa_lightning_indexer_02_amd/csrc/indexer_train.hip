@@ -32,13 +32,17 @@ constexpr float KL_NEG = -1.0e30f;  // start of a running maximum: finite and be
 // and eight waves: wave (row, group) holds the queries of 32 heads of its row in registers for
 // the whole contraction (A operand of S = Q K^T, 32x32x16 MFMA), so the accumulator of a key
 // block gives each lane one key and 16 heads.  Blocks of 32 latent rows are copied HBM/L2 ->
-// LDS by DMA (double buffered, one barrier per block) and shared by both rows.
+// LDS by DMA, KL_STAGES deep with one barrier per block, and shared by both rows.  The copies are
+// issued by the six waves of groups 1..3; the first wave of each row, which reads the row's scores
+// and writes its results, issues none, so waiting for its own loads never waits for the key stream.
 // ---------------------------------------------------------------------------------------
 constexpr int KL_TOK = 2;
 constexpr int KL_GROUPS = 4;  // 32-head groups per row: H <= 128
 constexpr int KL_WAVES = KL_TOK * KL_GROUPS;
 constexpr int KL_THREADS = KL_WAVES * WAVE;
 constexpr int KL_KB = 32;
+constexpr int KL_STAGES = 4;
+constexpr int KL_ISSUERS = KL_WAVES - KL_TOK;  // waves with grp != 0
 
 template <int NKS>  // NKS 16-column contraction steps: the latent row padded to 16 NKS columns
 struct KlCfg {
@@ -49,7 +53,8 @@ struct KlCfg {
   static constexpr int K_BYTES = SLOTS * 16;
   static constexpr int DMA_INSTR = SLOTS / WAVE;
   static constexpr int RED_FLOATS = 2 * KL_TOK * KL_GROUPS * KL_KB;
-  static constexpr size_t SMEM = 2 * (size_t)K_BYTES + (RED_FLOATS + KL_TOK * KL_GROUPS * 2) * sizeof(float);
+  static constexpr size_t SMEM =
+      (size_t)KL_STAGES * K_BYTES + (RED_FLOATS + KL_TOK * KL_GROUPS * 2) * sizeof(float);
 };
 
 // Running log-sum-exp in log2 units: l = sum 2^(v - m).  v = -inf adds nothing.
@@ -72,8 +77,8 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
     float* __restrict__ loss) {
   using C = KlCfg<NKS>;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* Kbuf = smem;                                                   // [2][SLOTS] x 16 B
-  float* red = reinterpret_cast<float*>(smem + 2 * C::K_BYTES);          // [2][TOK][GROUPS][KB]
+  uint8_t* Kbuf = smem;                                                   // [STAGES][SLOTS] x 16 B
+  float* red = reinterpret_cast<float*>(smem + KL_STAGES * C::K_BYTES);  // [2][TOK][GROUPS][KB]
   float* rowstat = red + C::RED_FLOATS;                                   // [TOK][GROUPS][2]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -100,9 +105,9 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
       rowstat[(tok * KL_GROUPS + grp) * 2 + 1] = l;
     }
   }
-  // padding chunks of both stages are zero (the DMA never writes them)
+  // padding chunks of every stage are zero (the DMA never writes them)
   if (C::DP > D) {
-    for (int p = tid; p < 2 * C::SLOTS; p += KL_THREADS) {
+    for (int p = tid; p < KL_STAGES * C::SLOTS; p += KL_THREADS) {
       const int sl = p % C::SLOTS, r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
       if (c * 8 >= D) *reinterpret_cast<v4i*>(Kbuf + p * 16) = (v4i){0, 0, 0, 0};
     }
@@ -129,9 +134,12 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
   }
 
   const uint32_t kbuf_lds = lds_offset(Kbuf);
+  const int issuer = tok * (KL_GROUPS - 1) + grp - 1;  // 0 .. KL_ISSUERS - 1; -1: issues nothing
+  const int my_dma = grp == 0 ? 0 : (C::DMA_INSTR - issuer + KL_ISSUERS - 1) / KL_ISSUERS;
   auto issue = [&](int blk) {
-    const uint32_t base = kbuf_lds + (uint32_t)((blk & 1) * C::K_BYTES);
-    for (int i = wave; i < C::DMA_INSTR; i += KL_WAVES) {
+    if (grp == 0) return;
+    const uint32_t base = kbuf_lds + (uint32_t)((blk % KL_STAGES) * C::K_BYTES);
+    for (int i = issuer; i < C::DMA_INSTR; i += KL_ISSUERS) {
       const int sl = i * WAVE + lane;
       const int r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
       const int64_t s = min((int64_t)blk * KL_KB + r, S - 1);
@@ -172,14 +180,17 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
   };
 
   for (int pass = 0; pass < 2; ++pass) {
-    if (nblk > 0) issue(0);
+    for (int b = 0; b < KL_STAGES - 1 && b < nblk; ++b) issue(b);
     for (int blk = 0; blk < nblk; ++blk) {
-      vm_wait<0>();
+      // this wave's copies of block blk are done once at most those of the blocks after it are
+      // pending (issued in order)
+      const int later = min(KL_STAGES - 2, nblk - 1 - blk);
+      vm_wait_pending(later * my_dma);
       __syncthreads();  // block blk is in LDS; every wave is done with block blk - 1
       if (pass == 1 && blk > 0 && row_ok) finalize(blk - 1);
-      if (blk + 1 < nblk) issue(blk + 1);
+      if (blk + KL_STAGES - 1 < nblk) issue(blk + KL_STAGES - 1);
       if (!active) continue;
-      const uint8_t* Kst = Kbuf + (blk & 1) * C::K_BYTES;
+      const uint8_t* Kst = Kbuf + (blk % KL_STAGES) * C::K_BYTES;
       v16f acc = {};
       constexpr int LA = 3;  // fragments in flight
       s16x8 Bf[LA];
@@ -322,21 +333,36 @@ __global__ __launch_bounds__(BQ_WAVES * WAVE, 1) void indexer_bwd_q_kernel(
     for (int n = 0; n < C::NDT; ++n) acc[h][n] = (v4f){0.f, 0.f, 0.f, 0.f};
   }
 
+  // The loads of key block kb + 32 (codes, scales, this lane's dI) are issued before the MFMAs of
+  // block kb, into registers; staging them into LDS waits for the next barrier.  Loads are
+  // unconditional with clamped addresses (rows start 16-byte aligned, ld is a multiple of 4).
+  static_assert(BW_BLK * (DI / 16) <= BQ_WAVES * WAVE, "one 16-byte piece per thread");
+  const int pr = tid / (DI / 16), pc = tid % (DI / 16);
+  const bool stager = tid < BW_BLK * (DI / 16);
+  const float* drow = dI + min(t, T - 1) * ld;
+  v4i nraw = {0, 0, 0, 0};
+  float nks = 0.f;
+  v4f nd0, nd1;
+  auto prefetch = [&](int64_t kb) {
+    if (stager) nraw = *reinterpret_cast<const v4i*>(k8 + min(kb + pr, S - 1) * DI + pc * 16);
+    if (tid < BW_BLK) nks = ks[min(kb + tid, S - 1)];
+    nd0 = *reinterpret_cast<const v4f*>(drow + min(kb + 4 * g, ld - 4));
+    nd1 = *reinterpret_cast<const v4f*>(drow + min(kb + 16 + 4 * g, ld - 4));
+  };
+  prefetch(0);
   for (int64_t kb = 0; kb < n_max; kb += BW_BLK) {
     __syncthreads();  // the previous block is consumed
-    for (int p = tid; p < BW_BLK * (DI / 16); p += BQ_WAVES * WAVE) {
-      const int r = p / (DI / 16), c = p % (DI / 16);
-      const int64_t s = min(kb + r, S - 1);
-      stage_row16(kt + r * C::STRIDE + c * 32, *reinterpret_cast<const v4i*>(k8 + s * DI + c * 16));
-    }
-    if (tid < BW_BLK) kss[tid] = ks[min(kb + tid, S - 1)];
+    if (stager) stage_row16(kt + pr * C::STRIDE + pc * 32, nraw);
+    if (tid < BW_BLK) kss[tid] = nks;
+    const v4f d0 = nd0, d1 = nd1;
     __syncthreads();
+    if (kb + BW_BLK < n_max) prefetch(kb + BW_BLK);
     // key factors dI[t,s] ks[s] of this lane's eight (row, key) pairs; 0 outside the causal range
     float u[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int kr = (e < 4 ? 0 : 16) + 4 * g + (e & 3);
-      u[e] = kb + kr < n_t ? dI[t * ld + kb + kr] * kss[kr] : 0.f;
+      u[e] = kb + kr < n_t ? (e < 4 ? d0[e] : d1[e - 4]) * kss[kr] : 0.f;
     }
     s16x8 Ka[2][C::NZS], Kb[C::NDT];
 #pragma unroll
