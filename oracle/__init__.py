@@ -64,6 +64,9 @@ def load(path: Optional[str] = None):
     lib.oracle_indexer_bwd.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _i64, _i32, _i32, _p, _i64, _p, _p, _p,
                                        _i32]
     lib.oracle_indexer_bwd.restype = ctypes.c_int
+    lib.oracle_indexer_kl_sparse.argtypes = [_p, _p, _p, _i64, _i64, _i32, _i32, ctypes.c_double, _p, _i32, _p,
+                                             _i64, _p, _p, _i64, _i32]
+    lib.oracle_indexer_kl_sparse.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -286,3 +289,26 @@ def indexer_bwd(q8, qs, w, pos, k8, ks, dlogits, nthreads: int = 0, lib=None):
     if rc:
         raise RuntimeError("oracle_indexer_bwd failed (%d)" % rc)
     return dq, dw, dk
+
+
+def indexer_kl_sparse(q, kv, pos, sm_scale: float, idx, logits, nthreads: int = 0, lib=None):
+    """Sparse-stage loss: KL over each row's index-list entries (see oracle_indexer_kl_sparse).
+
+    idx: int32 [T, k].  Returns (loss float64 [T], dlogits float64 [T, S], 0 on visible keys not
+    listed, NaN past each row's visible range)."""
+    lib = lib or load()
+    q = _c(q, np.uint16)
+    T, H, D_qk = q.shape
+    kv = _c(kv, np.uint16)
+    S = kv.shape[0]
+    idx = _c(idx, np.int32)
+    logits = _c(logits, np.float32)
+    pos = _c(pos, np.int64)
+    loss = np.empty(T, dtype=np.float64)
+    d = np.full((T, S), np.nan, dtype=np.float64)
+    rc = lib.oracle_indexer_kl_sparse(_ptr(q), _ptr(kv), _ptr(pos), T, S, H, D_qk, ctypes.c_double(sm_scale),
+                                      _ptr(idx), idx.shape[1], _ptr(logits), logits.shape[1], _ptr(loss), _ptr(d),
+                                      S, nthreads)
+    if rc:
+        raise RuntimeError("oracle_indexer_kl_sparse failed (%d)" % rc)
+    return loss, d

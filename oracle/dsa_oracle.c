@@ -630,3 +630,106 @@ int oracle_indexer_bwd(const uint8_t *q8, const float *qs, const float *w, const
     free(qd);
     return 0;
 }
+
+/* Sparse stage (summary page, "Method": with top-k on, the indexer keeps its own graph; the
+ * pages print no formula).  Reading: the loss is restricted to the entries of each row's index
+ * list.  For row t and its valid entries i (0 <= idx[t][i] < n_t; others skipped, a repeated key
+ * counts once per entry, as in the sparse attention):
+ *     p_i  = (1/H) sum_h exp(z_hi) / sum_j exp(z_hj),  z_hi = sm_scale q[t,h,:] . kv[idx_i, :D_qk]
+ *            (the sparse attention's probabilities averaged over the heads),
+ *     pi_i = exp(I[t, idx_i]) / sum_j exp(I[t, idx_j]),
+ *     loss[t] = sum_i p_i (log p_i - log pi_i),
+ *     dlogits[t][s] = sum_{i: idx_i = s} (pi_i - p_i) for s < n_t (0 for keys not listed).
+ * A row without valid entries has loss 0 and dlogits 0.  Arithmetic in double.  Returns 1 on a bad
+ * shape, 2 on a non-finite listed score, 3 on no memory. */
+int oracle_indexer_kl_sparse(const uint16_t *q, const uint16_t *kv, const int64_t *pos, int64_t T, int64_t S,
+                             int32_t H, int32_t D_qk, double sm_scale, const int32_t *idx, int32_t k,
+                             const float *logits, int64_t ld, double *loss, double *dlogits, int64_t ld_d,
+                             int32_t nthreads)
+{
+    if (T < 0 || S < 0 || H <= 0 || D_qk <= 0 || k <= 0 || ld < S || ld_d < S)
+        return 1;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = visible_keys(pos[t], S);
+        const int32_t *row = idx + t * k;
+        loss[t] = 0.0;
+        for (int64_t s = 0; s < n; ++s)
+            dlogits[t * ld_d + s] = 0.0;
+        double *z = (double *)malloc(sizeof(double) * (size_t)k);
+        double *p = (double *)calloc((size_t)k, sizeof(double));
+        if (!z || !p) {
+            bad = 3;
+            free(z);
+            free(p);
+            continue;
+        }
+        int any = 0;
+        for (int32_t i = 0; i < k; ++i)
+            if (row[i] >= 0 && row[i] < n)
+                any = 1;
+        if (!any) {
+            free(z);
+            free(p);
+            continue;
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            const uint16_t *qh = q + (t * H + h) * (int64_t)D_qk;
+            double m = -INFINITY;
+            for (int32_t i = 0; i < k; ++i) {
+                if (row[i] < 0 || row[i] >= n)
+                    continue;
+                const uint16_t *kr = kv + (int64_t)row[i] * D_qk;
+                double dot = 0.0;
+                for (int32_t d = 0; d < D_qk; ++d)
+                    dot += (double)bf16_value(qh[d]) * (double)bf16_value(kr[d]);
+                z[i] = sm_scale * dot;
+                if (z[i] > m)
+                    m = z[i];
+            }
+            double l = 0.0;
+            for (int32_t i = 0; i < k; ++i)
+                if (row[i] >= 0 && row[i] < n)
+                    l += exp(z[i] - m);
+            for (int32_t i = 0; i < k; ++i)
+                if (row[i] >= 0 && row[i] < n)
+                    p[i] += exp(z[i] - m) / l / (double)H;
+        }
+        const float *I = logits + t * ld;
+        double mi = -INFINITY;
+        int finite = 1;
+        for (int32_t i = 0; i < k; ++i) {
+            if (row[i] < 0 || row[i] >= n)
+                continue;
+            if (!isfinite(I[row[i]]))
+                finite = 0;
+            else if ((double)I[row[i]] > mi)
+                mi = (double)I[row[i]];
+        }
+        if (!finite) {
+            bad = 2;
+            free(z);
+            free(p);
+            continue;
+        }
+        double li = 0.0;
+        for (int32_t i = 0; i < k; ++i)
+            if (row[i] >= 0 && row[i] < n)
+                li += exp((double)I[row[i]] - mi);
+        double lse_i = mi + log(li), acc = 0.0;
+        for (int32_t i = 0; i < k; ++i) {
+            if (row[i] < 0 || row[i] >= n)
+                continue;
+            double log_pi = (double)I[row[i]] - lse_i;
+            if (p[i] > 0.0)
+                acc += p[i] * (log(p[i]) - log_pi);
+            dlogits[t * ld_d + row[i]] += exp(log_pi) - p[i];
+        }
+        loss[t] = acc;
+        free(z);
+        free(p);
+    }
+    return bad;
+}

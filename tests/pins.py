@@ -557,3 +557,90 @@ def check_indexer_bwd_finite_difference(lib):
         b[s] -= h
         fd = (L(qs, a, w) - L(qs, b, w)) / (2 * h)
         assert abs(fd - np.dot(dk[s], kdec[s])) <= 1e-9 * (1.0 + abs(fd)), "dk projection"
+
+
+# Sparse stage (reading: the loss restricted to each row's index-list entries).
+def torch_kl_sparse(q, kv, logits, pos, sm, idx):
+    """(loss [T], dI [T, S]) by torch in float64 over the valid entries of idx (rows with at least
+    one valid entry): gathered scores, per-head softmax over the entries, head mean, kl_div against
+    log_softmax of the gathered scores, autograd through the gather (repeated keys accumulate)."""
+    qf = torch.from_numpy(brute.bf16_decode(q))
+    kf = torch.from_numpy(brute.bf16_decode(kv))
+    T, S = logits.shape
+    n = np.minimum(S, pos + 1)
+    valid = torch.from_numpy((idx >= 0) & (idx < n[:, None]))
+    ic = torch.from_numpy(np.where(idx >= 0, np.minimum(idx, S - 1), 0).astype(np.int64))
+    z = torch.einsum("thd,tkd->thk", qf, kf[ic]) * sm
+    p = torch.softmax(z.masked_fill(~valid[:, None, :], float("-inf")), dim=-1).mean(dim=1)
+    I = torch.from_numpy(logits.astype(np.float64)).requires_grad_(True)
+    g = torch.gather(I, 1, ic).masked_fill(~valid, float("-inf"))
+    logpi = torch.log_softmax(g, dim=-1).masked_fill(~valid, 0.0)
+    loss = torch.nn.functional.kl_div(logpi, p, reduction="none").sum(dim=-1)
+    loss.sum().backward()
+    vis = np.arange(S)[None, :] < n[:, None]
+    return loss.detach().numpy(), np.where(vis, I.grad.numpy(), np.nan)
+
+
+def _sparse_lists(T, S, pos, k, seed):
+    g = block_rng(seed, T, k)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = min(S, pos[t] + 1)
+        m = min(n, k)
+        idx[t, :m] = g.permutation(n)[:m]
+        if m > 3:
+            idx[t, 1] = idx[t, 0]               # a repeated key
+            idx[t, 2] = n + 5                   # beyond the causal range: skipped
+    return idx
+
+
+def check_kl_sparse_vs_torch(lib):
+    T, S, q0, H, D, sm, k = 12, 40, 20, 3, 24, 0.3, 16
+    q, kv, logits, pos = _kl_inputs(T, S, q0, H, D, 91)
+    idx = _sparse_lists(T, S, pos, k, 92)
+    loss, d = oracle.indexer_kl_sparse(q, kv, pos, sm, idx, logits, lib=lib)
+    tl, td = torch_kl_sparse(q, kv, logits, pos, sm, idx)
+    assert np.all(np.abs(loss - tl) <= 1e-12 * (1.0 + np.abs(tl))), "sparse KL loss differs from torch"
+    m = ~np.isnan(td)
+    assert np.array_equal(m, ~np.isnan(d)), "visible region of the sparse dI is wrong"
+    assert np.max(np.abs(d[m] - td[m])) <= 1e-13, "sparse dI differs from torch autograd"
+    for t in range(T):                          # keys not listed get exactly 0
+        listed = set(int(x) for x in idx[t] if 0 <= x < min(S, pos[t] + 1))
+        for s in range(min(S, pos[t] + 1)):
+            if s not in listed:
+                assert d[t, s] == 0.0
+
+
+def check_kl_sparse_closed_forms(lib):
+    T, S, q0, H, D, sm = 8, 30, 22, 4, 16, 0.25
+    q, kv, logits, pos = _kl_inputs(T, S, q0, H, D, 93)
+    # every visible key listed once (any order, -1 padding): the dense loss
+    k = 40
+    g = block_rng(94, 0, 0)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = min(S, pos[t] + 1)
+        idx[t, :n] = g.permutation(n)
+    ls, ds = oracle.indexer_kl_sparse(q, kv, pos, sm, idx, logits, lib=lib)
+    ld_, dd = oracle.indexer_kl(q, kv, pos, sm, logits, lib=lib)
+    assert np.all(np.abs(ls - ld_) <= 1e-12 * (1 + np.abs(ld_))), "full list must give the dense loss"
+    m = ~np.isnan(dd)
+    assert np.max(np.abs(ds[m] - dd[m])) <= 1e-14
+    # no valid entry: 0; one valid entry: 0
+    idx = np.full((T, 4), -1, np.int32)
+    idx[1, 2] = 5
+    ls, ds = oracle.indexer_kl_sparse(q, kv, pos, sm, idx, logits, lib=lib)
+    assert ls[0] == 0.0 and np.all(ds[0][~np.isnan(ds[0])] == 0.0)
+    assert ls[1] == 0.0 and ds[1, 5] == 0.0
+    # a key listed twice next to another with the same row: p = 1/3 per entry
+    kvf = np.zeros((S, D), np.float32)
+    kvf[3] = kvf[9] = 1.0
+    idx = np.array([[3, 3, 9, -1]] * T, np.int32)
+    ls, ds = oracle.indexer_kl_sparse(q, to_bf16_bits(kvf), pos, sm, idx, logits, lib=lib)
+    for t in range(T):
+        a, b = float(logits[t, 3]), float(logits[t, 9])
+        zt = 2 * np.exp(a) + np.exp(b)
+        pa, pb = np.exp(a) / zt, np.exp(b) / zt
+        ref = 2 * (1 / 3) * (np.log(1 / 3) - np.log(pa)) + (1 / 3) * (np.log(1 / 3) - np.log(pb))
+        assert abs(ls[t] - ref) <= 1e-12
+        assert abs(ds[t, 3] - 2 * (pa - 1 / 3)) <= 1e-12 and abs(ds[t, 9] - (pb - 1 / 3)) <= 1e-12

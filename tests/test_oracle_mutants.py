@@ -66,6 +66,11 @@ MUTANTS = [
     ("bwd_dw_no_relu", "if (z > 0.0) {\n                    gw += di * z;",
      "gw += di * z;\n                if (z > 0.0) {", [pins.check_indexer_bwd_vs_torch,
                                                       pins.check_indexer_bwd_finite_difference]),
+    ("kl_sparse_repeat_overwrites", "dlogits[t * ld_d + row[i]] += exp(log_pi) - p[i];",
+     "dlogits[t * ld_d + row[i]] = exp(log_pi) - p[i];", [pins.check_kl_sparse_vs_torch,
+                                                          pins.check_kl_sparse_closed_forms]),
+    ("kl_sparse_all_keys", "p[i] += exp(z[i] - m) / l / (double)H;", "p[i] += exp(z[i] - m) / l / (double)(H + 1);",
+     [pins.check_kl_sparse_vs_torch]),
 ]
 
 
