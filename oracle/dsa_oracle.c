@@ -685,7 +685,7 @@ int oracle_indexer_kl_sparse(const uint16_t *q, const uint16_t *kv, const int64_
                 double dot = 0.0;
                 for (int32_t d = 0; d < D_qk; ++d)
                     dot += (double)bf16_value(qh[d]) * (double)bf16_value(kr[d]);
-                z[i] = sm_scale * dot;
+                z[i] = dot * sm_scale;
                 if (z[i] > m)
                     m = z[i];
             }
