@@ -653,8 +653,8 @@ int oracle_indexer_kl_sparse(const uint16_t *q, const uint16_t *kv, const int64_
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t t = 0; t < T; ++t) {
-        int64_t n = visible_keys(pos[t], S);
         const int32_t *row = idx + t * k;
+        int64_t n = visible_keys(pos[t], S);
         loss[t] = 0.0;
         for (int64_t s = 0; s < n; ++s)
             dlogits[t * ld_d + s] = 0.0;
