@@ -12,7 +12,9 @@ one JSON line.
 times the fused paged decode call against its HBM roofline; quantize_append_32k times the FP8
 quantization of the L = 32K queries and the paged append of its tokens; indexer_ue8m0_32k the
 indexer with power-of-two scales inside the MFMA; indexer_train_4k / indexer_train_32k one
-training step of the indexer: scores, KL loss toward the main attention, backward), and
+training step of the indexer: scores, KL loss toward the main attention, backward;
+indexer_train_sparse_4k / _32k the sparse-stage step: scores, top-k, sparse attention, the loss over
+the selected entries, backward), and
 ``--all-configs`` prints one line per configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -419,7 +421,8 @@ def run_indexer_train(name, args, dev):
     import torch
     import dsa_lightning_indexer_02_amd as dsa
     from dsa_inputs import get, prefill_inputs
-    wl = get(name.replace("indexer_train_", "prefill_"))
+    sparse = name.startswith("indexer_train_sparse_")
+    wl = get(name.replace("indexer_train_sparse_", "prefill_").replace("indexer_train_", "prefill_"))
     print("generating %s inputs" % wl.name, file=sys.stderr, flush=True)
     inp = prefill_inputs(wl)
     q8, qs, w, k8, ks = (put(x, dev) for x in (inp.q8, inp.qs, inp.w, inp.k8, inp.ks))
@@ -434,35 +437,50 @@ def run_indexer_train(name, args, dev):
     dk = torch.empty((S, wl.D_I), dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, dsa.indexer_bwd_workspace_size(T, S, wl.D_I)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if sparse:  # sparse stage: top-k lists and the sparse attention's normaliser feed the loss
+        idx = torch.empty((T, wl.topk), dtype=torch.int32, device=dev)
+        out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+        tk_ws = torch.empty(max(1, dsa.load().dsa_topk_workspace_size(T, S, wl.topk)), dtype=torch.uint8, device=dev)
+    nstage = 5 if sparse else 3
 
     def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+        def mark(i):
+            if ev:
+                ev[i].record(stream)
+        mark(0)
         dsa.dsa_indexer_logits(q8, qs, w, k8, ks, wl.q_start, logits)
-        if ev:
-            ev[1].record(stream)
-        dsa.dsa_indexer_kl_loss(q, kv, logits, wl.sm_scale, wl.q_start, dlogits=logits, loss=loss)
-        if ev:
-            ev[2].record(stream)
+        mark(1)
+        if sparse:
+            dsa.dsa_topk(logits, wl.topk, S, wl.q_start, idx, tk_ws)
+            mark(2)
+            dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v, wl.q_start, out=out, lse=lse)
+            mark(3)
+            dsa.dsa_indexer_kl_loss_sparse(q, kv, idx, lse, logits, wl.sm_scale, wl.q_start, dlogits=logits,
+                                           loss=loss)
+        else:
+            dsa.dsa_indexer_kl_loss(q, kv, logits, wl.sm_scale, wl.q_start, dlogits=logits, loss=loss)
+        mark(nstage - 1)
         dsa.dsa_indexer_bwd(q8, qs, w, k8, ks, logits, wl.q_start, dq, dw, dk, ws)
-        if ev:
-            ev[3].record(stream)
+        mark(nstage)
 
     print("warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nstage + 1)] for _ in range(args.steps)]
     print("timing %d steps" % args.steps, file=sys.stderr, flush=True)
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nstage)] for e in evs])
     step_ms = per.sum(axis=1)
-    ims, kms, bms = per.mean(axis=0)
+    mean = per.mean(axis=0)
+    ims, kms, bms = mean[0], mean[nstage - 2], mean[nstage - 1]
     wm = work_model(wl)
     pairs = wm["visible_pairs"]
-    kl_flop = 2.0 * wl.H * wl.D_qk * pairs            # one Q K^T over every visible pair
+    # the loss: one Q K^T over every visible pair (dense) or every selected entry (sparse stage)
+    kl_flop = 2.0 * wl.H * wl.D_qk * (wm["selected_rows"] if sparse else pairs)
     bwd_flop = 3 * 2.0 * wl.H_I * wl.D_I * pairs      # z, dq and dk contractions
     stages = {
         "indexer": {"ms": float(ims), "bound": "mfma", "achieved_tflops": wm["indexer_flop"] / ims / 1e9,
@@ -472,7 +490,12 @@ def run_indexer_train(name, args, dev):
         "indexer_bwd": {"ms": float(bms), "bound": "mfma", "achieved_tflops": bwd_flop / bms / 1e9,
                         "frac": bwd_flop / (bms / 1e3) / PEAK_BF16},
     }
-    roof = {"kernel": "indexer_kl_kernel<36>", "bound": "mfma", "achieved": kl_flop / (kms / 1e3) / 1e12,
+    if sparse:
+        stages["topk"] = {"ms": float(mean[1]), "bound": "hbm", "frac": wm["topk_bytes"] / (mean[1] / 1e3) / PEAK_HBM}
+        stages["sparse_mla"] = {"ms": float(mean[2]), "bound": "mfma",
+                                "frac": wm["mla_flop"] / (mean[2] / 1e3) / PEAK_BF16}
+    kname = "indexer_kl_sparse_kernel<36>" if sparse else "indexer_kl_kernel<36>"
+    roof = {"kernel": kname, "bound": "mfma", "achieved": kl_flop / (kms / 1e3) / 1e12,
             "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "traffic": None, "algorithmic_flop_per_launch": kl_flop,
             "avg_launch_ms": float(kms)}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -501,7 +524,9 @@ def run_one(name, args, dev, with_cpu: bool):
         return line
     if name.startswith("indexer_train_"):
         res = run_indexer_train(name, args, dev)
-        return {"metric": "query tokens/s (indexer training step: scores + KL loss + backward, %s)" % name,
+        what = ("scores + top-k + sparse attention + sparse-stage KL loss + backward"
+                if name.startswith("indexer_train_sparse_") else "scores + KL loss + backward")
+        return {"metric": "query tokens/s (indexer training step: %s, %s)" % (what, name),
                 "value": res["value"], "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
                 "scaling": "weak", "vs_baseline": None,
@@ -566,7 +591,7 @@ def main():
     dsa.load()
     if args.all_configs:
         for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64", "quantize_append_32k",
-                     "indexer_ue8m0_32k", "indexer_train_4k"]:
+                     "indexer_ue8m0_32k", "indexer_train_4k", "indexer_train_sparse_32k"]:
             print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return

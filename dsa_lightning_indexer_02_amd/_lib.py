@@ -22,7 +22,7 @@ EXPORTS = [
     "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd",
     "dsa_prefill_workspace_size", "dsa_prefill_paged", "dsa_decode_workspace_size", "dsa_decode_paged",
     "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0", "dsa_indexer_logits_ue8m0",
-    "dsa_indexer_kl_loss", "dsa_indexer_bwd_workspace_size", "dsa_indexer_bwd",
+    "dsa_indexer_kl_loss", "dsa_indexer_bwd_workspace_size", "dsa_indexer_bwd", "dsa_indexer_kl_loss_sparse",
 ]
 
 _p = ctypes.c_void_p
@@ -87,13 +87,16 @@ def load(path: str = LIB_PATH):
     lib.dsa_quantize_fp8_rows_ue8m0.argtypes = [_p, _i64, _i32, _p, _p, _p, _p]
     lib.dsa_indexer_logits_ue8m0.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i64, _p]
     lib.dsa_indexer_kl_loss.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _f32, _i64, _p, _i64, _p, _p, _p]
+    lib.dsa_indexer_kl_loss_sparse.argtypes = [_p, _p, _p, _i32, _p, _i64, _i64, _i32, _i32, _f32, _i64, _p, _i64,
+                                               _p, _p, _p]
     lib.dsa_indexer_bwd_workspace_size.argtypes = [_i64, _i64, _i32]
     lib.dsa_indexer_bwd_workspace_size.restype = _sz
     lib.dsa_indexer_bwd.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i64, _p, _p, _p, _p,
                                     _sz, _p]
     for name in ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_paged",
                  "dsa_decode_paged", "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0",
-                 "dsa_indexer_logits_ue8m0", "dsa_indexer_kl_loss", "dsa_indexer_bwd"):
+                 "dsa_indexer_logits_ue8m0", "dsa_indexer_kl_loss", "dsa_indexer_bwd",
+                 "dsa_indexer_kl_loss_sparse"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

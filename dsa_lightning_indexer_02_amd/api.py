@@ -270,6 +270,26 @@ def dsa_indexer_kl_loss(q, kv, logits, sm_scale: float, q_start: int = 0, dlogit
     return loss, dlogits
 
 
+def dsa_indexer_kl_loss_sparse(q, kv, indices, lse, logits, sm_scale: float, q_start: int = 0, dlogits=None,
+                               loss=None, in_place: bool = False):
+    """(loss f32 [T], dlogits f32 [T, ld]) of the sparse-stage indexer loss over each row's index-list
+    entries; lse is the sparse forward's [T, H] log-normaliser over the same lists."""
+    lib = load()
+    T, H, D_qk = q.shape
+    S = kv.shape[0]
+    k = indices.shape[1]
+    if dlogits is None:
+        dlogits = logits if in_place else torch.empty_like(logits)
+    if loss is None:
+        loss = torch.empty((T,), dtype=torch.float32, device=q.device)
+    status = lib.dsa_indexer_kl_loss_sparse(
+        _dev(q, "q", 3, 2), _dev(kv, "kv", 2, 2), _dev(indices, "indices", 2, 4), k, _dev(lse, "lse", 2, 4), T, S, H,
+        D_qk, ctypes.c_float(sm_scale), q_start, _dev(logits, "logits", 2, 4), logits.shape[1],
+        _dev(dlogits, "dlogits", 2, 4), _dev(loss, "loss", 1, 4), _stream(q))
+    check("dsa_indexer_kl_loss_sparse", status)
+    return loss, dlogits
+
+
 def indexer_bwd_workspace_size(T: int, S: int, D_I: int) -> int:
     return load().dsa_indexer_bwd_workspace_size(T, S, D_I)
 

@@ -474,6 +474,31 @@ dsa_status_t dsa_indexer_kl_loss(const uint16_t* q, const uint16_t* kv, int64_t 
                     "KL loss launch");
 }
 
+dsa_status_t dsa_indexer_kl_loss_sparse(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int32_t k,
+                                        const float* lse, int64_t T, int64_t S, int32_t H, int32_t D_qk,
+                                        float sm_scale, int64_t q_start, const float* logits, int64_t ld_logits,
+                                        float* dlogits, float* loss, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  REQUIRE(dsa::indexer_kl_sparse_supported(H, D_qk, k), DSA_ERR_UNSUPPORTED,
+          "sparse KL loss with H=%d, D_qk=%d, k=%d not supported (1 <= H <= 128, D_qk a multiple of 8 in "
+          "[8, 576], 1 <= k <= 2048)", H, D_qk, k);
+  if (T == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1 when T > 0");
+  REQUIRE(ld_logits >= S && ld_logits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_logits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_logits, (long long)S);
+  REQUIRE(sm_scale > 0.0f && sm_scale < 1.0e30f, DSA_ERR_INVALID_ARGUMENT, "sm_scale must be positive and finite");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kv);
+  REQUIRE_PTR(indices);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(dlogits);
+  REQUIRE_PTR(loss);
+  return hip_status(dsa::launch_indexer_kl_sparse(q, kv, indices, k, lse, T, S, H, D_qk, sm_scale, q_start, logits,
+                                                  ld_logits, dlogits, loss, stream),
+                    "sparse KL loss launch");
+}
+
 size_t dsa_indexer_bwd_workspace_size(int64_t T, int64_t S, int32_t D_I) {
   if (T <= 0 || S <= 0 || D_I <= 0) return 0;
   return dsa::indexer_bwd_workspace_bytes(T, S, D_I);

@@ -39,6 +39,11 @@ bool indexer_kl_supported(int32_t H, int32_t D);
 hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t T, int64_t S, int32_t H, int32_t D,
                              float sm_scale, int64_t q_start, const float* logits, int64_t ld, float* dlogits,
                              float* loss, hipStream_t stream);
+bool indexer_kl_sparse_supported(int32_t H, int32_t D, int32_t k);
+hipError_t launch_indexer_kl_sparse(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int32_t k,
+                                    const float* lse, int64_t T, int64_t S, int32_t H, int32_t D, float sm_scale,
+                                    int64_t q_start, const float* logits, int64_t ld, float* dlogits, float* loss,
+                                    hipStream_t stream);
 size_t indexer_bwd_workspace_bytes(int64_t T, int64_t S, int32_t D_I);
 hipError_t launch_indexer_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
                               int64_t T, int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, const float* dI,

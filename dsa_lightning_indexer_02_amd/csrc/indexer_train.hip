@@ -239,6 +239,185 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
+// Sparse stage: the same loss over the entries of each row's index list (the attention that the
+// sparse step computes, averaged over the heads, against the softmax of the listed scores).  The
+// per-head normaliser is the sparse forward's log-sum-exp (an input), so one pass suffices.  One
+// workgroup per row: four waves of 32 heads, the listed latent rows gathered by DMA (KLS_STAGES
+// deep).  The pre-pass keeps the listed scores in LDS (so the gradient may overwrite the scores),
+// then zeroes the row's visible range; each entry adds pi - p to its key's gradient (repeated keys
+// accumulate).
+// ---------------------------------------------------------------------------------------
+constexpr int KLS_WAVES = 4;
+constexpr int KLS_THREADS = KLS_WAVES * WAVE;
+constexpr int KLS_STAGES = 3;
+constexpr int KLS_MAX_K = 2048;
+
+template <int NKS>
+constexpr size_t kls_smem_bytes() {
+  return (size_t)KLS_STAGES * KlCfg<NKS>::K_BYTES + (size_t)KLS_MAX_K * 8 +
+         (2 * KL_GROUPS * KL_KB + 2 * KLS_WAVES + 2 * KLS_WAVES) * sizeof(float);
+}
+
+template <int NKS>
+__global__ __launch_bounds__(KLS_THREADS, 1) void indexer_kl_sparse_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, int32_t k,
+    const float* __restrict__ lse, int64_t T, int64_t S, int32_t H, int32_t D, float scale_log2, int64_t q_start,
+    const float* logits, int64_t ld, float* dlogits, float* __restrict__ loss) {
+  using C = KlCfg<NKS>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* Kbuf = smem;                                                              // [STAGES][SLOTS] x 16 B
+  int32_t* rows = reinterpret_cast<int32_t*>(smem + KLS_STAGES * C::K_BYTES);       // [k]: key or -1
+  float* isel = reinterpret_cast<float*>(rows + KLS_MAX_K);                          // [k]: listed scores
+  float* red = isel + KLS_MAX_K;                                                     // [2][GROUPS][KB]
+  float* wstat = red + 2 * KL_GROUPS * KL_KB;                                        // [WAVES][2]
+  int32_t* wlast = reinterpret_cast<int32_t*>(wstat + 2 * KLS_WAVES);                // [WAVES]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave, l32 = lane & 31, lh = lane >> 5;
+  const int64_t t = blockIdx.x;
+  const int64_t n = min(S, q_start + t + 1);
+  const int ngrp = (H + 31) / 32;
+  const bool active = grp < ngrp;
+
+  // ---- the list, its scores (log2 units), the normaliser of the listed scores, the last entry
+  float m = KL_NEG, l = 0.f;
+  int last = 0;
+  for (int i = tid; i < k; i += KLS_THREADS) {
+    const int32_t li = idx[t * k + i];
+    const bool v = li >= 0 && li < n;
+    rows[i] = v ? li : -1;
+    const float x = v ? logits[t * ld + li] * KL_LOG2E : 0.f;
+    isel[i] = x;
+    if (v) {
+      lse_push(m, l, x);
+      last = i + 1;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    lse_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
+    last = max(last, __shfl_xor(last, o));
+  }
+  if (lane == 0) {
+    wstat[2 * wave] = m;
+    wstat[2 * wave + 1] = l;
+    wlast[wave] = last;
+  }
+  __syncthreads();  // every listed score is in LDS before the row is overwritten
+  float lse_i2;
+  int k_used = 0;
+  {
+    float mm = KL_NEG, ll = 0.f;
+    for (int w = 0; w < KLS_WAVES; ++w) {
+      lse_merge(mm, ll, wstat[2 * w], wstat[2 * w + 1]);
+      k_used = max(k_used, wlast[w]);
+    }
+    lse_i2 = mm + __builtin_amdgcn_logf(ll);
+  }
+  for (int64_t s = tid; s < n; s += KLS_THREADS) dlogits[t * ld + s] = 0.f;
+  if (C::DP > D) {
+    for (int p = tid; p < KLS_STAGES * C::SLOTS; p += KLS_THREADS) {
+      const int sl = p % C::SLOTS, r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      if (c * 8 >= D) *reinterpret_cast<v4i*>(Kbuf + p * 16) = (v4i){0, 0, 0, 0};
+    }
+  }
+  const int nblk = (k_used + KL_KB - 1) / KL_KB;
+
+  const int head = grp * 32 + l32;
+  s16x8 Qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int col = 16 * ks + 8 * lh;
+    s16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active && head < H && col < D) v = *reinterpret_cast<const s16x8*>(q + (t * H + head) * (int64_t)D + col);
+    asm volatile("" : "+v"(v));
+    Qf[ks] = v;
+  }
+  float lse2[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int hh = grp * 32 + 8 * (r / 4) + 4 * lh + r % 4;
+    lse2[r] = (active && hh < H) ? lse[t * H + hh] * KL_LOG2E : INFINITY;
+  }
+  vm_wait<0>();     // the zeroing stores have completed before any entry's gradient is added
+  __syncthreads();  // zeroed row and padding visible; list complete
+
+  const uint32_t kbuf_lds = lds_offset(Kbuf);
+  auto issue = [&](int blk) {
+    const uint32_t base = kbuf_lds + (uint32_t)((blk % KLS_STAGES) * C::K_BYTES);
+    for (int i = wave; i < C::DMA_INSTR; i += KLS_WAVES) {
+      const int sl = i * WAVE + lane;
+      const int r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      const int e = blk * KL_KB + r;
+      const int32_t kr = e < k ? rows[e] : -1;
+      const int64_t s = kr >= 0 ? kr : 0;  // skipped entries read row 0 (masked)
+      if (c * 8 < D) lds_dma_16B(kv + s * D + c * 8, base + (uint32_t)(i * WAVE * 16));
+    }
+  };
+  constexpr int KP = C::SWZ / 2;
+  const int kx = l32 & (C::SWZ - 1);
+  int kbase[KP];
+#pragma unroll
+  for (int u = 0; u < KP; ++u) kbase[u] = (l32 * C::RC + ((2 * u + lh) ^ kx)) * 16;
+  auto koff = [&](int ks) { return kbase[ks % KP] + (ks / KP) * (2 * KP * 16); };
+  const int my_dma = (C::DMA_INSTR - wave + KLS_WAVES - 1) / KLS_WAVES;
+
+  const float inv_h = 1.0f / (float)H;
+  float lacc = 0.f;
+  auto finalize = [&](int blk) {
+    const int e = blk * KL_KB + l32;
+    if (grp == 0 && lh == 0 && e < k) {
+      const int32_t kr = rows[e];
+      if (kr >= 0) {
+        const float* rb = red + (blk & 1) * KL_GROUPS * KL_KB + l32;
+        float ps = 0.f;
+        for (int g = 0; g < ngrp; ++g) ps += rb[g * KL_KB];
+        const float p = ps * inv_h;
+        const float lpi2 = isel[e] - lse_i2;
+        if (p > 1e-30f) lacc += p * (__builtin_amdgcn_logf(p) - lpi2);
+        atomicAdd(dlogits + t * ld + kr, __builtin_amdgcn_exp2f(lpi2) - p);
+      }
+    }
+  };
+
+  for (int b = 0; b < KLS_STAGES - 1 && b < nblk; ++b) issue(b);
+  for (int blk = 0; blk < nblk; ++blk) {
+    vm_wait_pending(min(KLS_STAGES - 2, nblk - 1 - blk) * my_dma);
+    __syncthreads();
+    if (blk > 0) finalize(blk - 1);
+    if (blk + KLS_STAGES - 1 < nblk) issue(blk + KLS_STAGES - 1);
+    if (!active) continue;
+    const uint8_t* Kst = Kbuf + (blk % KLS_STAGES) * C::K_BYTES;
+    v16f acc = {};
+    constexpr int LA = 3;
+    s16x8 Bf[LA];
+#pragma unroll
+    for (int i = 0; i < LA - 1; ++i) Bf[i] = *reinterpret_cast<const s16x8*>(Kst + koff(i));
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + LA - 1 < NKS) Bf[(ks + LA - 1) % LA] = *reinterpret_cast<const s16x8*>(Kst + koff(ks + LA - 1));
+      acc = mfma_bf16_32x32x16(Qf[ks], Bf[ks % LA], acc);
+    }
+    const int e = blk * KL_KB + l32;
+    const bool valid = e < k && rows[e] >= 0;
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ps += __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -lse2[r]));
+    ps = valid ? ps : 0.f;
+    ps += __shfl_xor(ps, 32);
+    if (lh == 0) red[(blk & 1) * KL_GROUPS * KL_KB + grp * KL_KB + l32] = ps;
+  }
+  vm_wait<0>();
+  __syncthreads();
+  if (nblk > 0) finalize(nblk - 1);
+  if (grp == 0) {
+    float v = lh == 0 ? lacc : 0.f;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) loss[t] = v * KL_LN2;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Backward.  z is recomputed from the FP8 codes converted to bf16 (exact) with the 16x16x32 bf16
 // MFMA; the scales, the weights and dI enter in fp32.  A 16x16 accumulator holds, in lane l,
 // column l % 16 and rows 4 (l / 16) + r: computing z with the rows that are contracted next on
@@ -597,6 +776,51 @@ hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t T, i
   case N: return launch_kl<N>(q, kv, T, S, H, D, sm_scale, q_start, logits, ld, dlogits, loss, stream);
     KL_CASE(2) KL_CASE(4) KL_CASE(5) KL_CASE(8) KL_CASE(12) KL_CASE(16) KL_CASE(24) KL_CASE(32) KL_CASE(36)
 #undef KL_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NKS>
+static hipError_t launch_kl_sparse(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int32_t k,
+                                   const float* lse, int64_t T, int64_t S, int32_t H, int32_t D, float sm_scale,
+                                   int64_t q_start, const float* logits, int64_t ld, float* dlogits, float* loss,
+                                   hipStream_t stream) {
+  constexpr size_t smem = kls_smem_bytes<NKS>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&indexer_kl_sparse_kernel<NKS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(indexer_kl_sparse_kernel<NKS>, dim3((unsigned)T), dim3(KLS_THREADS), smem, stream, q, kv, idx,
+                     k, lse, T, S, H, D, sm_scale * KL_LOG2E, q_start, logits, ld, dlogits, loss);
+  return hipGetLastError();
+}
+
+bool indexer_kl_sparse_supported(int32_t H, int32_t D, int32_t k) {
+  return indexer_kl_supported(H, D) && k >= 1 && k <= KLS_MAX_K;
+}
+
+hipError_t launch_indexer_kl_sparse(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int32_t k,
+                                    const float* lse, int64_t T, int64_t S, int32_t H, int32_t D, float sm_scale,
+                                    int64_t q_start, const float* logits, int64_t ld, float* dlogits, float* loss,
+                                    hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int need = (D + 15) / 16;
+  int nks = 0;
+  for (int c : kKlSteps)
+    if (c >= need) {
+      nks = c;
+      break;
+    }
+  switch (nks) {
+#define KLS_CASE(N)                                                                                            \
+  case N:                                                                                                      \
+    return launch_kl_sparse<N>(q, kv, idx, k, lse, T, S, H, D, sm_scale, q_start, logits, ld, dlogits, loss, \
+                               stream);
+    KLS_CASE(2) KLS_CASE(4) KLS_CASE(5) KLS_CASE(8) KLS_CASE(12) KLS_CASE(16) KLS_CASE(24) KLS_CASE(32) KLS_CASE(36)
+#undef KLS_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -221,6 +221,25 @@ dsa_status_t dsa_indexer_kl_loss(const uint16_t *q, const uint16_t *kv, int64_t 
                                  int64_t ld_logits, float *dlogits, float *loss, hipStream_t stream);
 
 /*
+ * Sparse-stage indexer loss (summary page, "Method": once top-k is on, the indexer keeps its own
+ * graph).  Reading: the loss of dsa_indexer_kl_loss restricted to the entries of each row's index
+ * list.  For the valid entries i of indices[t] (0 <= idx < n_t; anything else is skipped; a key
+ * listed twice counts once per entry, as in the sparse attention):
+ *   p_i  = (1/H) sum_h exp(sm_scale * q[t][h][:] . kv[idx_i][:] - lse[t][h]),
+ *   pi_i = softmax over the entries of logits[t][idx_i],   loss[t] = sum_i p_i (log p_i - log pi_i),
+ *   dlogits[t][s] = sum_{i: idx_i = s} (pi_i - p_i) for s < n_t, 0 for visible keys not listed.
+ *   lse [T][H] f32 is the natural-log normaliser of the sparse attention over the same lists (the
+ *   lse output of dsa_sparse_mla_fwd); indices [T][k] i32; other arguments as dsa_indexer_kl_loss
+ *   (dlogits may be logits itself).  A row without valid entries gets loss 0 and dlogits 0.
+ *   Repeated keys are summed with atomic adds (their order is not fixed).  Supported: as
+ *   dsa_indexer_kl_loss, 1 <= k <= 2048.
+ */
+dsa_status_t dsa_indexer_kl_loss_sparse(const uint16_t *q, const uint16_t *kv, const int32_t *indices, int32_t k,
+                                        const float *lse, int64_t T, int64_t S, int32_t H, int32_t D_qk,
+                                        float sm_scale, int64_t q_start, const float *logits, int64_t ld_logits,
+                                        float *dlogits, float *loss, hipStream_t stream);
+
+/*
  * Indexer backward (the same training stages): gradients of a loss through the scores of
  * dsa_indexer_logits given dlogits = dL/dlogits on the visible entries (s < n_t; others never
  * read).  Reading: the FP8 quantization is passed straight through, so the gradients are with

@@ -189,3 +189,39 @@ def check_indexer_bwd(dq_g, dw_g, dk_g, dq_o, dw_o, dk_o, q8, qs, w, k8, ks, dI,
     assert np.all(e <= KL_REL * A_dk + X_dk + 1e-12), "%s: dk off by %.3e" % (name, e.max())
     worst = max(worst, float(np.max(e / (KL_REL * A_dk + X_dk + 1e-12))))
     return int(amb.sum()), worst
+
+
+def check_kl_sparse(loss_g, d_g, loss_o, d_o, logits, pos, idx, name):
+    """Sparse-stage loss / dI against the oracle.  Per key s the oracle's pi_s (the softmax of the
+    listed scores summed over the key's entries) and p_s = pi_s - dI_s; bars as check_kl on those
+    sums (the entries of one key share p / pi, so the loss bar is the same); keys not listed must be
+    exactly 0."""
+    T, S = d_o.shape
+    worst = 0.0
+    for t in range(T):
+        n = min(S, int(pos[t]) + 1)
+        ent = idx[t][(idx[t] >= 0) & (idx[t] < n)]
+        listed = np.zeros(n, bool)
+        listed[ent] = True
+        assert np.all(d_g[t, :n][~listed] == 0.0), "%s: row %d has gradient on keys it does not list" % (name, t)
+        if len(ent) == 0:
+            assert loss_g[t] == 0.0
+            continue
+        x = logits[t, ent].astype(np.float64)
+        e = np.exp(x - x.max())
+        pi_e = e / e.sum()
+        pi = np.zeros(n)
+        np.add.at(pi, ent, pi_e)
+        p = pi - d_o[t, :n]
+        err = np.abs(d_g[t, :n].astype(np.float64) - d_o[t, :n])
+        tol = KL_REL * (np.maximum(p, 0.0) + pi) + 1e-9
+        assert np.all(err <= tol), "%s: dI row %d off by %.3e" % (name, t, err.max())
+        worst = max(worst, float(np.max(err / tol)))
+        pk, pik = np.maximum(p[listed], 0.0), pi[listed]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            lr = np.where(pk > 0, np.log(np.maximum(pk, 1e-300)) - np.log(pik), 0.0)
+        A = np.sum(pk * (np.abs(lr) + 1.0))
+        el = abs(float(loss_g[t]) - loss_o[t])
+        assert el <= KL_REL * A + 1e-9, "%s: loss row %d off by %.3e" % (name, t, el)
+        worst = max(worst, el / (KL_REL * A + 1e-9))
+    return worst

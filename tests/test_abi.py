@@ -169,3 +169,13 @@ def test_kl_loss_and_backward_argument_errors(lib):
     bad[11] = 66                                                                            # ld % 4
     assert g(*bad) == INVALID
     assert g(None, None, None, None, None, 0, 0, 64, 128, 0, None, 4, None, None, None, None, 0, None) == OK
+
+
+def test_kl_sparse_argument_errors(lib):
+    f = lib.dsa_indexer_kl_loss_sparse
+    sm = ctypes.c_float(0.07)
+    assert f(FAKE, FAKE, FAKE, 4096, FAKE, 4, 8, 128, 576, sm, 0, FAKE, 8, FAKE, FAKE, None) == UNSUPPORTED   # k
+    assert f(FAKE, FAKE, FAKE, 64, None, 4, 8, 128, 576, sm, 0, FAKE, 8, FAKE, FAKE, None) == INVALID         # lse
+    assert "lse" in _err(lib)
+    assert f(FAKE, FAKE, None, 64, FAKE, 4, 8, 128, 576, sm, 0, FAKE, 8, FAKE, FAKE, None) == INVALID         # indices
+    assert f(None, None, None, 64, None, 0, 8, 128, 576, sm, 0, None, 8, None, None, None) == OK              # T = 0

@@ -145,3 +145,87 @@ def test_train_chain_prefill_4k_rows(dev):
     rhs = np.sum(gw * inp.w.astype(np.float64))
     scale = (np.sum(np.abs(gq * qd)) + np.sum(np.abs(gk * kd))) / 2.0 + np.sum(np.abs(gw * inp.w))
     assert abs(lhs - rhs) <= parity.KL_REL * scale, "Euler identity of the backward: %.6e vs %.6e" % (lhs, rhs)
+
+
+# ------------------------------------------------------------------ sparse-stage loss
+def _sparse_lists(T, S, pos, k, seed):
+    g = block_rng(seed, T, k)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = min(S, int(pos[t]) + 1)
+        m = min(n, k)
+        idx[t, :m] = g.permutation(n)[:m]
+        if m > 3:
+            idx[t, 1] = idx[t, 0]           # a repeated key
+            idx[t, 2] = n + 5               # beyond the causal range: skipped
+    return idx
+
+
+def _kl_sparse_case(dev, T, S, q_start, H, D, D_v, k, sm, seed, in_place=False, gpu_lse=True):
+    import dsa_lightning_indexer_02_amd as dsa
+    print("case kl sparse", T, S, q_start, H, D, k, "in_place" if in_place else "", flush=True)
+    g = block_rng(seed, T, S)
+    q = to_bf16_bits(g.standard_normal((T, H, D)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D)).astype(np.float32))
+    pos = q_start + np.arange(T)
+    idx = _sparse_lists(T, S, pos, k, seed + 1)
+    ld = dsa.ld_for(S)
+    logits = np.zeros((T, ld), np.float32)
+    logits[:, :S] = (g.standard_normal((T, S)) * 2.0).astype(np.float32)
+    qd, kvd, idd = dput(q, dev).view(torch.bfloat16), dput(kv, dev).view(torch.bfloat16), dput(idx, dev)
+    if gpu_lse:   # the sparse forward's normaliser over the same lists
+        _, _, lse = dsa.dsa_sparse_mla_fwd(qd, kvd, idd, sm, D_v, q_start=q_start)
+    else:         # a width the forward does not take: the oracle forward's normaliser as the input
+        _, _, lse_o = oracle.sparse_mla(q, idx, pos, kv, D_v, sm)
+        lse = dput(lse_o, dev)
+    lg = dput(logits, dev)
+    loss, d = dsa.dsa_indexer_kl_loss_sparse(qd, kvd, idd, lse, lg, sm, q_start=q_start, in_place=in_place)
+    torch.cuda.synchronize()
+    lo, do = oracle.indexer_kl_sparse(q, kv, pos, sm, idx, logits[:, :S])
+    worst = parity.check_kl_sparse(dget(loss), dget(d)[:, :S], lo, do, logits[:, :S], pos, idx,
+                                   "kl sparse %dx%d H=%d D=%d k=%d" % (T, S, H, D, k))
+    print("  worst error / bar: %.3e" % worst, flush=True)
+
+
+@pytest.mark.parametrize("T,S,q_start,H,D,D_v,k,sm,gpu_lse", [
+    (40, 64, 24, 8, 80, 64, 16, 80 ** -0.5, True),          # the small configuration's shapes
+    (21, 3000, 2900, 128, 576, 512, 2048, 192 ** -0.5, True),  # full width and k
+    (33, 100, 80, 20, 72, 64, 48, 0.11, False),             # partial head group, padded width
+    (10, 40, 0, 128, 576, 512, 64, 192 ** -0.5, True),      # rows shorter than their lists (-1 padded)
+])
+def test_kl_sparse_vs_oracle(dev, T, S, q_start, H, D, D_v, k, sm, gpu_lse):
+    _kl_sparse_case(dev, T, S, q_start, H, D, D_v, k, sm, 85, gpu_lse=gpu_lse)
+
+
+def test_kl_sparse_in_place(dev):
+    _kl_sparse_case(dev, 17, 500, 450, 64, 576, 512, 256, 192 ** -0.5, 86, in_place=True)
+
+
+def test_sparse_stage_chain_prefill_4k(dev):
+    """indexer -> top-2048 -> sparse attention (lse) -> sparse-stage loss in place -> backward at the
+    4K prefill shape.  Invariants of every row: keys outside the list get exactly 0, the gradient
+    sums to 0 (both distributions sum to 1), the loss is non-negative, all finite."""
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import get, prefill_inputs
+    wl = get("prefill_4k")
+    inp = prefill_inputs(wl)
+    print("case sparse-stage chain prefill_4k", flush=True)
+    q8, qs, w, k8, ks = (dput(x, dev) for x in (inp.q8, inp.qs, inp.w, inp.k8, inp.ks))
+    q = dput(inp.q, dev).view(torch.bfloat16)
+    kv = dput(inp.kv, dev).view(torch.bfloat16)
+    lg = dsa.dsa_indexer_logits(q8, qs, w, k8, ks, 0)
+    idx = dsa.dsa_topk(lg, wl.topk, wl.S)
+    _, _, lse = dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v)
+    loss, d = dsa.dsa_indexer_kl_loss_sparse(q, kv, idx, lse, lg, wl.sm_scale, in_place=True)
+    dq, dw, dk = dsa.dsa_indexer_bwd(q8, qs, w, k8, ks, d)
+    torch.cuda.synchronize()
+    L, D, I = dget(loss), dget(d)[:, :wl.S], dget(idx)
+    assert np.all(np.isfinite(L)) and np.all(L >= -1e-5), "sparse-stage loss must be finite and non-negative"
+    for t in [0, 1, 100, 2047, 2048, 3000, 4095]:
+        n = t + 1
+        listed = np.zeros(n, bool)
+        listed[I[t][I[t] >= 0]] = True
+        assert np.all(D[t, :n][~listed] == 0.0)
+        assert abs(float(np.sum(D[t, :n].astype(np.float64)))) <= 1e-5, "row %d gradient does not sum to 0" % t
+    for x in (dq, dw, dk):
+        assert np.all(np.isfinite(dget(x)))
