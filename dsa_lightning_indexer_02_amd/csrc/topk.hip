@@ -31,10 +31,15 @@ constexpr int TK_STAGE = 2048;    // index lists up to this length are staged in
 constexpr int TK_CAND = 4096;     // candidate keys of the sampled threshold search
 constexpr int TK_CAND_EPT = TK_CAND / TK_THREADS;
 
+constexpr int TK_MAP_WORDS = TK_CHUNK_EPT * TK_THREADS / 32;  // one bit per position of a chunk
+
 struct TopkShared {
   uint32_t hist[TK_BINS];
   int32_t stage[TK_STAGE];
   uint32_t cand[TK_CAND];
+  uint32_t cpos[TK_CAND];           // position of each candidate in the chunk
+  uint32_t gtmap[TK_MAP_WORDS];     // selected positions above tau
+  uint32_t eqmap[TK_MAP_WORDS];     // positions equal to tau
   uint32_t wsum[TK_WAVES][2];
   uint32_t red[TK_WAVES][2];
   uint32_t sel_bin, sel_above;
@@ -68,6 +73,10 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 // barrier that makes it visible is the one in block_minmax.
 __device__ __forceinline__ void hist_clear(TopkShared& sh) {
   for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
+  for (int i = threadIdx.x; i < TK_MAP_WORDS; i += TK_THREADS) {
+    sh.gtmap[i] = 0;
+    sh.eqmap[i] = 0;
+  }
 }
 
 // Maximum and minimum of the valid keys (0 = no element) of the workgroup.
@@ -183,7 +192,8 @@ __device__ void radix_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx
 }
 
 // Exact threshold search over a chunk of cn > k valid elements (maximum mx, minimum mn) that
-// touches most keys once: the radix select over a 1-in-16 sample of the keys puts a pivot (a
+// touches most keys once (returns the number of candidates left in sh.cand / sh.cpos, or 0 when
+// the select ran over all keys instead): the radix select over a 1-in-16 sample of the keys puts a pivot (a
 // sample order statistic) a safe margin below the expected position of the k-th largest key;
 // the keys at or above the pivot are counted, and when there
 // are between k and TK_CAND of them they are compacted into LDS, where the radix select finds
@@ -191,13 +201,13 @@ __device__ void radix_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx
 // Outside that window (an unlucky or adversarial sample) the radix select runs over all keys.
 // Chunks of at most TK_CAND elements skip the sample.  The histogram is zero on entry and exit.
 template <int EPT>
-__device__ void sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32_t k, uint32_t mx, uint32_t mn,
-                                  TopkShared& sh, uint32_t& tau, uint32_t& k_rem) {
+__device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32_t k, uint32_t mx, uint32_t mn,
+                                      TopkShared& sh, uint32_t& tau, uint32_t& k_rem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (mx == mn) {
     tau = mx;
     k_rem = k;
-    return;
+    return 0;
   }
   uint32_t pivot = mn;  // every valid key
   if (cn > TK_CAND) {
@@ -239,7 +249,7 @@ __device__ void sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32
   }
   if (total < k || total > (uint32_t)TK_CAND) {  // workgroup-uniform
     radix_select<EPT>(key, k, mx, mn, sh, tau, k_rem);
-    return;
+    return 0;
   }
   // an opaque copy of the pivot: the counting loop's 64 compare masks are recomputed here rather
   // than kept (in scalar registers) across the scan
@@ -247,7 +257,11 @@ __device__ void sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32
   asm volatile("" : "+s"(pv));
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
-    if (key[e] >= pv) sh.cand[off++] = key[e];
+    if (key[e] >= pv) {
+      sh.cand[off] = key[e];
+      sh.cpos[off] = (uint32_t)elem_pos<EPT>(wave, lane, e);
+      ++off;
+    }
   __syncthreads();
   uint32_t ck[TK_CAND_EPT];
 #pragma unroll
@@ -256,6 +270,42 @@ __device__ void sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32
     ck[j] = i < total ? sh.cand[i] : 0u;
   }
   radix_select<TK_CAND_EPT>(ck, k, mx, pivot, sh, tau, k_rem);
+  return total;
+}
+
+// Ordered emission from the candidate list (every selected element is a candidate): each
+// candidate above tau sets its position's bit in one LDS bitmap, each equal to tau in another;
+// thread t then owns positions 64 t .. 64 t + 63 (two words of each map), and one block scan of
+// its two bit counts (packed in one word) gives its output offsets: every position above tau in
+// ascending order, then the first k_rem positions equal to tau.  The maps are zero on entry.
+template <typename Emit>
+__device__ void emit_candidates(TopkShared& sh, uint32_t total, uint32_t tau, uint32_t k, uint32_t k_rem,
+                                Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (uint32_t i = (uint32_t)tid; i < total; i += TK_THREADS) {
+    const uint32_t kk = sh.cand[i], p = sh.cpos[i];
+    if (kk > tau)
+      atomicOr(&sh.gtmap[p >> 5], 1u << (p & 31));
+    else if (kk == tau)
+      atomicOr(&sh.eqmap[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  static_assert(TK_MAP_WORDS == 2 * TK_THREADS, "two map words per thread");
+  uint32_t g0 = sh.gtmap[2 * tid], g1 = sh.gtmap[2 * tid + 1];
+  uint32_t e0 = sh.eqmap[2 * tid], e1 = sh.eqmap[2 * tid + 1];
+  const uint32_t cnt = (uint32_t)(__popc(g0) + __popc(g1)) | ((uint32_t)(__popc(e0) + __popc(e1)) << 16);
+  const uint32_t incl = wave_incl_scan(cnt, lane);
+  if (lane == 63) sh.wsum[wave][0] = incl;
+  __syncthreads();
+  uint32_t off = incl - cnt;
+  for (int i = 0; i < wave; ++i) off += sh.wsum[i][0];
+  uint32_t go = off & 0xFFFFu, eo = off >> 16;
+  const int base = 64 * tid;
+  for (; g0; g0 &= g0 - 1) emit(base + __builtin_ctz(g0), go++);
+  for (; g1; g1 &= g1 - 1) emit(base + 32 + __builtin_ctz(g1), go++);
+  const uint32_t n_gt = k - k_rem;
+  for (; e0 && eo < k_rem; e0 &= e0 - 1) emit(base + __builtin_ctz(e0), n_gt + eo++);
+  for (; e1 && eo < k_rem; e1 &= e1 - 1) emit(base + 32 + __builtin_ctz(e1), n_gt + eo++);
 }
 
 // Number of set bits of a wave mask held by lanes below this one.
@@ -379,21 +429,26 @@ __device__ __forceinline__ void chunk_select(const float* __restrict__ logits, i
   load_keys<EPT>(logits + t * ld + c0, cn, key);
   uint32_t mx, mn, tau, k_rem;
   block_minmax<EPT>(key, sh, mx, mn);
-  sampled_threshold<EPT>(key, cn, (uint32_t)k, mx, mn, sh, tau, k_rem);
+  const uint32_t ncand = sampled_threshold<EPT>(key, cn, (uint32_t)k, mx, mn, sh, tau, k_rem);
+  // emission from the candidates when they hold the selection, else from the registers
+  auto emit = [&](auto&& f) {
+    if (ncand)
+      emit_candidates(sh, ncand, tau, (uint32_t)k, k_rem, f);
+    else
+      emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh, f);
+  };
   if (single) {
     if (k <= TK_STAGE) {
-      emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh,
-                                  [&](int pos, uint32_t slot) { sh.stage[slot] = (int32_t)(c0 + pos); });
+      emit([&](int pos, uint32_t slot) { sh.stage[slot] = (int32_t)(c0 + pos); });
       store_staged(sh, out_idx, k);
     } else {
-      emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh,
-                                  [&](int pos, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
+      emit([&](int pos, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
     }
   } else {
     uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
     int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
     const float* row = logits + t * ld + c0;
-    emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh, [&](int pos, uint32_t slot) {
+    emit([&](int pos, uint32_t slot) {
       ck[slot] = score_key(row[pos]);  // re-read (L2): keeps the key array out of the loop
       ci[slot] = (int32_t)(c0 + pos);
     });
