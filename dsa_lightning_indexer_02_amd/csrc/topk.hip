@@ -42,7 +42,9 @@ struct TopkShared {
   uint32_t eqmap[TK_MAP_WORDS];     // positions equal to tau
   uint32_t wsum[TK_WAVES][2];
   uint32_t red[TK_WAVES][2];
-  uint32_t sel_bin, sel_above;
+  uint32_t sel_bin, sel_above, sel_cnt;
+  uint32_t small[WAVE];             // keys of a bin small enough to rank in one wave
+  uint32_t small_n;
   uint32_t kmax, kmin;
 };
 
@@ -73,6 +75,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 // barrier that makes it visible is the one in block_minmax.
 __device__ __forceinline__ void hist_clear(TopkShared& sh) {
   for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
+  if (threadIdx.x == 0) sh.small_n = 0;
   for (int i = threadIdx.x; i < TK_MAP_WORDS; i += TK_THREADS) {
     sh.gtmap[i] = 0;
     sh.eqmap[i] = 0;
@@ -115,7 +118,7 @@ __device__ void block_minmax(const uint32_t (&key)[EPT], TopkShared& sh, uint32_
 // holding that rank and the number of matching keys in higher bins.
 template <int EPT, typename Want>
 __device__ void hist_pass(const uint32_t (&key)[EPT], int shift, int bits, uint32_t prefix, TopkShared& sh,
-                          Want want, uint32_t& bin, uint32_t& above_out) {
+                          Want want, uint32_t& bin, uint32_t& above_out, uint32_t* count_out = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi_shift = shift + bits;
   const uint32_t dmask = (1u << bits) - 1u;
@@ -151,6 +154,7 @@ __device__ void hist_pass(const uint32_t (&key)[EPT], int shift, int bits, uint3
       if (need <= a + h[i]) {
         sh.sel_bin = (uint32_t)(b0 + i);
         sh.sel_above = a;
+        sh.sel_cnt = h[i];
         break;
       }
       a += h[i];
@@ -159,6 +163,40 @@ __device__ void hist_pass(const uint32_t (&key)[EPT], int shift, int bits, uint3
   __syncthreads();
   bin = sh.sel_bin;
   above_out = sh.sel_above;
+  if (count_out) *count_out = sh.sel_cnt;
+}
+
+// The end of an exact select once the bin holding the sought rank has cnt <= 64 keys: they (the
+// valid keys whose bits from shift up equal prefix) are collected in LDS and one wave ranks them:
+// tau is the key with fewer than `need` keys above it and at least `need` at or above it, k_rem
+// the count of its copies to take.  sh.small_n is zero on entry and on exit.
+template <int EPT>
+__device__ void small_finish(const uint32_t (&key)[EPT], int shift, uint32_t prefix, uint32_t cnt, uint32_t need,
+                             TopkShared& sh, uint32_t& tau, uint32_t& k_rem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t kk = key[e];
+    if (kk != 0 && (kk >> shift) == prefix) sh.small[atomicAdd(&sh.small_n, 1u)] = kk;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t x = (uint32_t)lane < cnt ? sh.small[lane] : 0u;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t m = 0; m < cnt; ++m) {
+      const uint32_t y = sh.small[m];
+      gt += y > x;
+      eq += y == x;
+    }
+    if ((uint32_t)lane < cnt && gt < need && need <= gt + eq) {  // every copy of tau writes the same
+      sh.sel_bin = x;
+      sh.sel_above = need - gt;
+    }
+    if (lane == 0) sh.small_n = 0;
+  }
+  __syncthreads();
+  tau = sh.sel_bin;
+  k_rem = sh.sel_above;
 }
 
 // Exact threshold search given the maximum mx and a lower bound mn (>= 1) of the valid keys
@@ -179,11 +217,15 @@ __device__ void radix_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx
   uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));  // bits above the window
   uint32_t need = k;
   while (true) {
-    uint32_t bin, above;
-    hist_pass<EPT>(key, shift, bits, prefix, sh, [&](uint32_t) { return need; }, bin, above);
+    uint32_t bin, above, cnt;
+    hist_pass<EPT>(key, shift, bits, prefix, sh, [&](uint32_t) { return need; }, bin, above, &cnt);
     need -= above;
     prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
     if (shift == 0) break;
+    if (cnt <= (uint32_t)WAVE) {  // workgroup-uniform
+      small_finish<EPT>(key, shift, prefix, cnt, need, sh, tau, k_rem);
+      return;
+    }
     bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
     shift -= bits;
   }
@@ -229,9 +271,26 @@ __device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, ui
     const float er = (float)k * (float)m / (float)cn;
     const float w = er + 4.0f * sqrtf(er) + 16.0f;
     if (w <= (float)m) {
-      uint32_t ts, tr;
-      radix_select<NS>(smp, (uint32_t)w, mx, mn, sh, ts, tr);
-      pivot = ts;
+      // Digit passes over the samples toward the one of rank w, stopped as soon as the lower edge
+      // of the bin holding it leaves few enough samples at or above it: the pivot only has to keep
+      // between k and TK_CAND keys, not be that sample exactly.
+      const int hb = 31 - __clz(mx ^ mn);  // mx > mn here
+      int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
+      int bits = hb - shift + 1;
+      uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));
+      const uint32_t w0 = (uint32_t)w;
+      uint32_t need = w0;
+      const float per_sample = (float)cn / (float)m;
+      while (true) {
+        uint32_t bin, above, cnt;
+        hist_pass<NS>(smp, shift, bits, prefix, sh, [&](uint32_t) { return need; }, bin, above, &cnt);
+        need -= above;
+        prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
+        if (shift == 0 || (float)(w0 - need + cnt) * per_sample <= 0.75f * (float)TK_CAND) break;
+        bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
+        shift -= bits;
+      }
+      pivot = max(prefix << shift, mn);  // lower edge of the bin (prefix holds every bit above shift)
     }
   }
   uint32_t c = 0;
