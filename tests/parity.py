@@ -166,13 +166,13 @@ def check_indexer_bwd(dq_g, dw_g, dk_g, dq_o, dw_o, dk_o, q8, qs, w, k8, ks, dI,
     S = k8.shape[0]
     vis = np.arange(S)[None, :] < np.minimum(S, np.asarray(pos) + 1)[:, None]
     dIv = np.where(vis, dI.astype(np.float64), 0.0)           # [T, S]
-    z = np.einsum("tjd,sd->tjs", qd, kd)
-    zabs = np.einsum("tjd,sd->tjs", np.abs(qd), np.abs(kd))
+    z = np.einsum("tjd,sd->tjs", qd, kd, optimize=True)
+    zabs = np.einsum("tjd,sd->tjs", np.abs(qd), np.abs(kd), optimize=True)
     amb = np.abs(z) <= Z_BOUND * zabs                          # either ReLU side is right
     on = (z > 0) | amb
     wa = np.abs(w.astype(np.float64))
     # dw: terms |dI| max(z, 0)
-    A_dw = np.einsum("ts,tjs->tj", np.abs(dIv), np.maximum(z, 0.0) + amb * np.abs(z))
+    A_dw = np.einsum("ts,tjs->tj", np.abs(dIv), np.maximum(z, 0.0) + amb * np.abs(z), optimize=True)
     e = np.abs(dw_g - dw_o)
     assert np.all(e <= KL_REL * A_dw + 1e-12), "%s: dw off by %.3e" % (name, e.max())
     worst = float(np.max(e / (KL_REL * A_dw + 1e-12)))

@@ -229,3 +229,42 @@ def test_sparse_stage_chain_prefill_4k(dev):
         assert abs(float(np.sum(D[t, :n].astype(np.float64)))) <= 1e-5, "row %d gradient does not sum to 0" % t
     for x in (dq, dw, dk):
         assert np.all(np.isfinite(dget(x)))
+
+
+def test_train_long_context_rows(dev):
+    """The chunked-prefill shape: 64 query rows at positions 131008 .. 131071 over a 131072-key
+    context (4096 key blocks per row in the loss, key groups and query chunks far from the origin
+    in the backward); loss and dI of two rows against the oracle, the backward on a 16-row slice."""
+    import dsa_lightning_indexer_02_amd as dsa
+    T, S, H, D, H_I, D_I = 64, 131072, 128, 576, 64, 128
+    q_start = S - T
+    sm = 192 ** -0.5
+    print("case long context", T, S, flush=True)
+    g = block_rng(87, T, S)
+    q = to_bf16_bits(g.standard_normal((T, H, D)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D)).astype(np.float32))
+    ld = dsa.ld_for(S)
+    logits = (g.standard_normal((T, ld)) * 2.0).astype(np.float32)
+    loss, d = dsa.dsa_indexer_kl_loss(dput(q, dev).view(torch.bfloat16), dput(kv, dev).view(torch.bfloat16),
+                                      dput(logits, dev), sm, q_start=q_start)
+    torch.cuda.synchronize()
+    rows = np.array([0, T - 1])
+    pos = q_start + rows
+    lo, do = oracle.indexer_kl(q[rows], kv, pos, sm, logits[rows, :S])
+    worst = parity.check_kl(dget(loss)[rows], dget(d)[rows, :S], lo, do, logits[rows, :S], pos, "kl long context")
+    print("  loss worst error / bar: %.3e" % worst, flush=True)
+    # backward over the same context for 16 rows (q_start leaves them 131056 .. 131071)
+    Tb = 16
+    q8, qs = quantize_fp8_rows(g.standard_normal((Tb, H_I, D_I)).astype(np.float32))
+    k8, ks = quantize_fp8_rows(g.standard_normal((S, D_I)).astype(np.float32))
+    w = (g.uniform(0.0, 1.0, (Tb, H_I)) / H_I).astype(np.float32)
+    dI = (g.standard_normal((Tb, ld)) * 1e-4).astype(np.float32)
+    dq, dw, dk = dsa.dsa_indexer_bwd(dput(q8, dev), dput(qs, dev), dput(w, dev), dput(k8, dev), dput(ks, dev),
+                                     dput(dI, dev), q_start=S - Tb)
+    torch.cuda.synchronize()
+    posb = S - Tb + np.arange(Tb)
+    oq, ow, ok = oracle.indexer_bwd(q8, qs, w, posb, k8, ks, dI[:, :S])
+    # the dk of 1024 sampled keys and every dq / dw (the magnitude scales need the whole sum)
+    amb, worst = parity.check_indexer_bwd(dget(dq), dget(dw), dget(dk), oq, ow, ok, q8, qs, w, k8, ks, dI[:, :S],
+                                          posb, "bwd long context")
+    print("  backward: ambiguous ReLU signs %d, worst error / bar %.3e" % (amb, worst), flush=True)
