@@ -433,7 +433,7 @@ constexpr int BQ_WAVES = 8;   // dq / dw: 16 query rows x 2 heads per wave
 constexpr int BQ_HPW = 2;
 constexpr int BK_WAVES = 4;   // dk: 32 keys per wave, all heads
 constexpr int BK_KPW = 32;
-constexpr int BK_HC = 8;      // heads of a query block staged at once
+constexpr int BK_HC = 4;      // heads of a query block staged at once
 
 template <int DI>
 struct BwCfg {
@@ -639,6 +639,31 @@ __global__ __launch_bounds__(BK_WAVES * WAVE, 2) void indexer_bwd_k_kernel(
 #pragma unroll
     for (int nt = 0; nt < C::NDT; ++nt) acc[u][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+  // Query codes and weights of the next (query block, head chunk) are loaded into registers before
+  // the MFMAs of the current one; staging them into LDS waits for the next barrier.
+  constexpr int BK_PPT = BK_HC * BW_BLK * (DI / 16) / (BK_WAVES * WAVE);  // 16-byte pieces per thread
+  static_assert(BK_PPT * BK_WAVES * WAVE == BK_HC * BW_BLK * (DI / 16), "whole pieces per thread");
+  static_assert(BK_HC * BW_BLK <= BK_WAVES * WAVE, "one weight per thread");
+  v4i nraw[BK_PPT];
+  float nwq = 0.f;
+  auto prefetch = [&](int64_t tbn, int hcn) {
+#pragma unroll
+    for (int u = 0; u < BK_PPT; ++u) {
+      const int p = tid + u * BK_WAVES * WAVE;
+      const int c = p % (DI / 16), rq = (p / (DI / 16)) % BW_BLK, hh = p / (DI / 16) / BW_BLK;
+      const int64_t tq = tbn + rq;
+      const int j = hcn + hh;
+      nraw[u] = (v4i){0, 0, 0, 0};
+      if (tq < t_end && j < H_I) nraw[u] = *reinterpret_cast<const v4i*>(q8 + (tq * H_I + j) * DI + c * 16);
+    }
+    if (tid < BK_HC * BW_BLK) {
+      const int rq = tid % BW_BLK, hh = tid / BW_BLK;
+      const int64_t tq = tbn + rq;
+      const int j = hcn + hh;
+      nwq = (tq < t_end && j < H_I) ? w[tq * H_I + j] * qs[tq * H_I + j] : 0.f;
+    }
+  };
+  prefetch(tb0, 0);
   for (int64_t tb = tb0; tb < t_end; tb += BW_BLK) {
     // dI of this lane's 16 (row, key) pairs; 0 outside the chunk or the causal range
     float dv[2][8];
@@ -652,33 +677,31 @@ __global__ __launch_bounds__(BK_WAVES * WAVE, 2) void indexer_bwd_k_kernel(
       }
     for (int hc = 0; hc < H_I; hc += BK_HC) {
       __syncthreads();  // the previous heads are consumed
-      for (int p = tid; p < BK_HC * BW_BLK * (DI / 16); p += BK_WAVES * WAVE) {
+#pragma unroll
+      for (int u = 0; u < BK_PPT; ++u) {
+        const int p = tid + u * BK_WAVES * WAVE;
         const int c = p % (DI / 16), rq = (p / (DI / 16)) % BW_BLK, hh = p / (DI / 16) / BW_BLK;
-        const int64_t tq = tb + rq;
-        const int j = hc + hh;
-        v4i raw = {0, 0, 0, 0};
-        if (tq < t_end && j < H_I) raw = *reinterpret_cast<const v4i*>(q8 + (tq * H_I + j) * DI + c * 16);
-        stage_row16(qt + (hh * BW_BLK + rq) * C::STRIDE + c * 32, raw);
+        stage_row16(qt + (hh * BW_BLK + rq) * C::STRIDE + c * 32, nraw[u]);
       }
-      for (int p = tid; p < BK_HC * BW_BLK; p += BK_WAVES * WAVE) {
-        const int rq = p % BW_BLK, hh = p / BW_BLK;
-        const int64_t tq = tb + rq;
-        const int j = hc + hh;
-        wq[p] = (tq < t_end && j < H_I) ? w[tq * H_I + j] * qs[tq * H_I + j] : 0.f;
-      }
+      if (tid < BK_HC * BW_BLK) wq[tid] = nwq;
       __syncthreads();
+      // the next chunk's loads go out before this chunk's MFMAs
+      if (hc + BK_HC < H_I)
+        prefetch(tb, hc + BK_HC);
+      else if (tb + BW_BLK < t_end)
+        prefetch(tb + BW_BLK, 0);
       for (int hh = 0; hh < BK_HC && hc + hh < H_I; ++hh) {
         const uint8_t* qh = qt + hh * BW_BLK * C::STRIDE;
-        s16x8 Qa[2][C::NZS], Qc[C::NDT];
+        s16x8 Qa[2][C::NZS];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int zs = 0; zs < C::NZS; ++zs) Qa[sub][zs] = block_rows<C::STRIDE>(qh, lane, sub, zs);
-#pragma unroll
-        for (int nt = 0; nt < C::NDT; ++nt) Qc[nt] = block_columns<C::STRIDE>(qh, lane, 16 * nt);
         float wv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) wv[e] = wq[hh * BW_BLK + (e < 4 ? 0 : 16) + 4 * g + (e & 3)];
+        // the gradient tiles of both key tiles first, then one B fragment at a time for both
+        s16x8 ghi[2], glo[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           v4f z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
@@ -687,19 +710,22 @@ __global__ __launch_bounds__(BK_WAVES * WAVE, 2) void indexer_bwd_k_kernel(
             z0 = mfma_bf16_16x16x32(Qa[0][zs], Kb[u][zs], z0);
             z1 = mfma_bf16_16x16x32(Qa[1][zs], Kb[u][zs], z1);
           }
-          s16x8 ghi, glo;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float zz = e < 4 ? z0[e] : z1[e - 4];
             short hi, lo;
             split_bf16(zz > 0.f ? dv[u][e] * wv[e] : 0.f, hi, lo);
-            ghi[e] = hi;
-            glo[e] = lo;
+            ghi[u][e] = hi;
+            glo[u][e] = lo;
           }
+        }
 #pragma unroll
-          for (int nt = 0; nt < C::NDT; ++nt) {
-            acc[u][nt] = mfma_bf16_16x16x32(ghi, Qc[nt], acc[u][nt]);
-            acc[u][nt] = mfma_bf16_16x16x32(glo, Qc[nt], acc[u][nt]);
+        for (int nt = 0; nt < C::NDT; ++nt) {
+          const s16x8 qcol = block_columns<C::STRIDE>(qh, lane, 16 * nt);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            acc[u][nt] = mfma_bf16_16x16x32(ghi[u], qcol, acc[u][nt]);
+            acc[u][nt] = mfma_bf16_16x16x32(glo[u], qcol, acc[u][nt]);
           }
         }
       }
