@@ -591,7 +591,7 @@ def main():
     dsa.load()
     if args.all_configs:
         for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64", "quantize_append_32k",
-                     "indexer_ue8m0_32k", "indexer_train_4k", "indexer_train_sparse_32k"]:
+                     "indexer_ue8m0_32k", "indexer_train_4k", "indexer_train_sparse_4k"]:
             print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return
