@@ -461,7 +461,10 @@ def run_indexer_train(name, args, dev):
         else:
             dsa.dsa_indexer_kl_loss(q, kv, logits, wl.sm_scale, wl.q_start, dlogits=logits, loss=loss)
         mark(nstage - 1)
-        dsa.dsa_indexer_bwd(q8, qs, w, k8, ks, logits, wl.q_start, dq, dw, dk, ws)
+        if sparse:  # dI vanishes off the lists: dq / dw over the listed keys only
+            dsa.dsa_indexer_bwd_listed(q8, qs, w, k8, ks, idx, logits, wl.q_start, dq, dw, dk, ws)
+        else:
+            dsa.dsa_indexer_bwd(q8, qs, w, k8, ks, logits, wl.q_start, dq, dw, dk, ws)
         mark(nstage)
 
     print("warmup", file=sys.stderr, flush=True)
@@ -481,7 +484,9 @@ def run_indexer_train(name, args, dev):
     pairs = wm["visible_pairs"]
     # the loss: one Q K^T over every visible pair (dense) or every selected entry (sparse stage)
     kl_flop = 2.0 * wl.H * wl.D_qk * (wm["selected_rows"] if sparse else pairs)
-    bwd_flop = 3 * 2.0 * wl.H_I * wl.D_I * pairs      # z, dq and dk contractions
+    # z, dq and dk contractions over the pairs with a nonzero dI (the listed entries in the sparse
+    # stage, although its dk kernel still walks every visible pair)
+    bwd_flop = 3 * 2.0 * wl.H_I * wl.D_I * (wm["selected_rows"] if sparse else pairs)
     stages = {
         "indexer": {"ms": float(ims), "bound": "mfma", "achieved_tflops": wm["indexer_flop"] / ims / 1e9,
                     "frac": wm["indexer_flop"] / (ims / 1e3) / PEAK_FP8},

@@ -23,6 +23,7 @@ EXPORTS = [
     "dsa_prefill_workspace_size", "dsa_prefill_paged", "dsa_decode_workspace_size", "dsa_decode_paged",
     "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0", "dsa_indexer_logits_ue8m0",
     "dsa_indexer_kl_loss", "dsa_indexer_bwd_workspace_size", "dsa_indexer_bwd", "dsa_indexer_kl_loss_sparse",
+    "dsa_indexer_bwd_listed",
 ]
 
 _p = ctypes.c_void_p
@@ -93,10 +94,12 @@ def load(path: str = LIB_PATH):
     lib.dsa_indexer_bwd_workspace_size.restype = _sz
     lib.dsa_indexer_bwd.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i64, _p, _p, _p, _p,
                                     _sz, _p]
+    lib.dsa_indexer_bwd_listed.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i32, _p, _i64, _p,
+                                           _p, _p, _p, _sz, _p]
     for name in ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_prefill_paged",
                  "dsa_decode_paged", "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0",
                  "dsa_indexer_logits_ue8m0", "dsa_indexer_kl_loss", "dsa_indexer_bwd",
-                 "dsa_indexer_kl_loss_sparse"):
+                 "dsa_indexer_kl_loss_sparse", "dsa_indexer_bwd_listed"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -316,3 +316,29 @@ def dsa_indexer_bwd(q8, q_scale, w, k8, k_scale, dlogits, q_start: int = 0, dq=N
         _dev(dq, "dq", 3, 4), _dev(dw, "dw", 2, 4), _dev(dk, "dk", 2, 4), _opt(workspace), ws_bytes, _stream(q8))
     check("dsa_indexer_bwd", status)
     return dq, dw, dk
+
+
+def dsa_indexer_bwd_listed(q8, q_scale, w, k8, k_scale, indices, dlogits, q_start: int = 0, dq=None, dw=None,
+                           dk=None, workspace=None):
+    """dsa_indexer_bwd for a dlogits that vanishes off each row's index list (indices [T, k] i32,
+    distinct valid entries per row): dq and dw are summed over the listed keys only."""
+    lib = load()
+    T, H_I, D_I = q8.shape
+    S = k8.shape[0]
+    k = indices.shape[1]
+    dev = q8.device
+    if dq is None:
+        dq = torch.empty((T, H_I, D_I), dtype=torch.float32, device=dev)
+    if dw is None:
+        dw = torch.empty((T, H_I), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((S, D_I), dtype=torch.float32, device=dev)
+    workspace = _workspace(lib.dsa_indexer_bwd_workspace_size(T, S, D_I), dev, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = lib.dsa_indexer_bwd_listed(
+        _dev(q8, "q8", 3, 1), _dev(q_scale, "q_scale", 2, 4), _dev(w, "w", 2, 4), _dev(k8, "k8", 2, 1),
+        _dev(k_scale, "k_scale", 1, 4), T, S, H_I, D_I, q_start, _dev(indices, "indices", 2, 4), k,
+        _dev(dlogits, "dlogits", 2, 4), dlogits.shape[1], _dev(dq, "dq", 3, 4), _dev(dw, "dw", 2, 4),
+        _dev(dk, "dk", 2, 4), _opt(workspace), ws_bytes, _stream(q8))
+    check("dsa_indexer_bwd_listed", status)
+    return dq, dw, dk

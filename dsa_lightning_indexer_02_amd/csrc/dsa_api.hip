@@ -533,4 +533,36 @@ dsa_status_t dsa_indexer_bwd(const uint8_t* q8, const float* q_scale, const floa
                     "indexer backward launch");
 }
 
+dsa_status_t dsa_indexer_bwd_listed(const uint8_t* q8, const float* q_scale, const float* w, const uint8_t* k8,
+                                    const float* k_scale, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
+                                    int64_t q_start, const int32_t* indices, int32_t k, const float* dlogits,
+                                    int64_t ld_dlogits, float* dq, float* dw, float* dk, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  dsa_status_t s = check_indexer_dims(H_I, D_I);
+  if (s != DSA_OK) return s;
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 1", k);
+  if (T == 0 && S == 0) return ok();
+  REQUIRE(T >= 1 && S >= 1, DSA_ERR_INVALID_ARGUMENT, "T and S must both be >= 1 (or both 0)");
+  REQUIRE(ld_dlogits >= S && ld_dlogits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_dlogits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_dlogits, (long long)S);
+  REQUIRE_PTR(q8);
+  REQUIRE_PTR(q_scale);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(k8);
+  REQUIRE_PTR(k_scale);
+  REQUIRE_PTR(indices);
+  REQUIRE_PTR(dlogits);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dw);
+  REQUIRE_PTR(dk);
+  const size_t need = dsa::indexer_bwd_workspace_bytes(T, S, D_I);
+  REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "indexer backward workspace %zu < %zu bytes",
+          workspace_bytes, need);
+  REQUIRE_PTR(workspace);
+  return hip_status(dsa::launch_indexer_bwd(q8, q_scale, w, k8, k_scale, T, S, H_I, D_I, q_start, dlogits,
+                                            ld_dlogits, dq, dw, dk, workspace, stream, indices, k),
+                    "indexer backward launch");
+}
+
 }  // extern "C"

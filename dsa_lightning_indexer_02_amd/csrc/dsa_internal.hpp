@@ -45,9 +45,11 @@ hipError_t launch_indexer_kl_sparse(const uint16_t* q, const uint16_t* kv, const
                                     int64_t q_start, const float* logits, int64_t ld, float* dlogits, float* loss,
                                     hipStream_t stream);
 size_t indexer_bwd_workspace_bytes(int64_t T, int64_t S, int32_t D_I);
+// idx non-null: dq / dw over the listed keys of each row only (idx [T][k], distinct entries)
 hipError_t launch_indexer_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
                               int64_t T, int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, const float* dI,
-                              int64_t ld, float* dq, float* dw, float* dk, void* workspace, hipStream_t stream);
+                              int64_t ld, float* dq, float* dw, float* dk, void* workspace, hipStream_t stream,
+                              const int32_t* idx = nullptr, int32_t k = 0);
 
 // ---- top-k
 int32_t topk_chunks(int64_t S);

@@ -595,6 +595,122 @@ __global__ __launch_bounds__(BQ_WAVES * WAVE, 1) void indexer_bwd_q_kernel(
   }
 }
 
+// dq and dw over each row's listed keys only (the sparse stage, where dI vanishes off the index
+// lists; lists with distinct entries).  A workgroup owns one query row and 64 heads (16 per wave,
+// the MFMA M dimension of dq); blocks of 32 listed keys are gathered, their FP8 codes staged as
+// bf16 rows, with dI[t, key] ks[key] per entry (0 for a skipped entry).
+constexpr int BL_WAVES = 4;
+
+template <int DI>
+__global__ __launch_bounds__(BL_WAVES * WAVE, 2) void indexer_bwd_q_listed_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
+    const uint8_t* __restrict__ k8, const float* __restrict__ ks, int64_t T, int64_t S, int32_t H_I,
+    int64_t q_start, const int32_t* __restrict__ idx, int32_t k, const float* __restrict__ dI, int64_t ld,
+    float* __restrict__ dq, float* __restrict__ dw) {
+  using C = BwCfg<DI>;
+  __shared__ __align__(16) uint8_t kt[BW_BLK * C::STRIDE];
+  __shared__ float us[BW_BLK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int64_t t = blockIdx.x;
+  const int64_t n = min(S, q_start + t + 1);
+  const int jw = (blockIdx.y * BL_WAVES + wave) * 16;  // waves past H_I still stage (zero queries)
+  const int jl = jw + j16;  // this lane's head as the column of z^T = K Q^T
+  // owned queries, B operands of z^T: lane = head jl, columns 32 zs + 8 g .. + 7
+  s16x8 Qb[C::NZS];
+#pragma unroll
+  for (int zs = 0; zs < C::NZS; ++zs) {
+    s16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (jl < H_I) {
+      const v2i raw = *reinterpret_cast<const v2i*>(q8 + (t * H_I + jl) * DI + 32 * zs + 8 * g);
+      v = e4m3x8_to_bf16((uint32_t)raw[0], (uint32_t)raw[1]);
+    }
+    Qb[zs] = v;
+  }
+  v4f acc[C::NDT];
+#pragma unroll
+  for (int nt = 0; nt < C::NDT; ++nt) acc[nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float dwa = 0.f;
+
+  // Block b + 1's codes and key factors are loaded into registers before block b's MFMAs, with
+  // the list entries they need read one block earlier still.  A thread stages piece pc of row
+  // pr, and thread tid < 32 the key factor of row tid; skipped entries (negative or not visible)
+  // load row 0 and get the factor 0.
+  static_assert(BW_BLK * (DI / 16) <= BL_WAVES * WAVE, "one 16-byte piece per thread");
+  const int pr = tid / (DI / 16), pc = tid % (DI / 16);
+  const bool stager = tid < BW_BLK * (DI / 16);
+  const int32_t* lrow = idx + t * k;
+  const float* drow = dI + t * ld;
+  auto entry = [&](int e) -> int32_t {  // the listed key of entry e, -1 when skipped
+    const int32_t key = lrow[min(e, k - 1)];
+    return (e < k && key >= 0 && key < n) ? key : -1;
+  };
+  int32_t kp = entry(pr), ku = entry(tid & (BW_BLK - 1));  // block 0
+  v4i nraw = *reinterpret_cast<const v4i*>(k8 + (int64_t)max(kp, 0) * DI + pc * 16);
+  auto factor = [&](int32_t key) {  // loads are unconditional, the select comes after them
+    const int32_t kk = max(key, 0);
+    const float v = drow[kk] * ks[kk];
+    return key >= 0 ? v : 0.f;
+  };
+  float nu = factor(ku);
+  kp = entry(BW_BLK + pr);  // block 1
+  ku = entry(BW_BLK + (tid & (BW_BLK - 1)));
+  for (int e0 = 0; e0 < k; e0 += BW_BLK) {
+    __syncthreads();  // the previous block is consumed
+    if (stager) stage_row16(kt + pr * C::STRIDE + pc * 32, nraw);
+    if (tid < BW_BLK) us[tid] = nu;
+    __syncthreads();
+    if (e0 + BW_BLK < k) {
+      nraw = *reinterpret_cast<const v4i*>(k8 + (int64_t)max(kp, 0) * DI + pc * 16);
+      nu = factor(ku);
+      kp = entry(e0 + 2 * BW_BLK + pr);
+      ku = entry(e0 + 2 * BW_BLK + (tid & (BW_BLK - 1)));
+    }
+    s16x8 Ka[2][C::NZS];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int zs = 0; zs < C::NZS; ++zs) Ka[sub][zs] = block_rows<C::STRIDE>(kt, lane, sub, zs);
+    v4f z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int zs = 0; zs < C::NZS; ++zs) {
+      z0 = mfma_bf16_16x16x32(Ka[0][zs], Qb[zs], z0);
+      z1 = mfma_bf16_16x16x32(Ka[1][zs], Qb[zs], z1);
+    }
+    // lane: head jl, entries e0 + 4 g + r (sub-block 0) and e0 + 16 + 4 g + r (sub-block 1)
+    s16x8 ghi, glo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float zz = e < 4 ? z0[e] : z1[e - 4];
+      const float u = us[(e < 4 ? 0 : 16) + 4 * g + (e & 3)];
+      dwa = fmaf(u, fmaxf(zz, 0.f), dwa);
+      short hi, lo;
+      split_bf16(zz > 0.f ? u : 0.f, hi, lo);
+      ghi[e] = hi;
+      glo[e] = lo;
+    }
+#pragma unroll
+    for (int nt = 0; nt < C::NDT; ++nt) {
+      const s16x8 kcol = block_columns<C::STRIDE>(kt, lane, 16 * nt);
+      acc[nt] = mfma_bf16_16x16x32(ghi, kcol, acc[nt]);
+      acc[nt] = mfma_bf16_16x16x32(glo, kcol, acc[nt]);
+    }
+  }
+  // dq: heads jw + 4 g + r, columns 16 nt + j16; dw: head jl (reduced over the lane groups)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int jh = jw + 4 * g + r;
+    if (jh < H_I) {
+      const float wv = w[t * H_I + jh];
+#pragma unroll
+      for (int nt = 0; nt < C::NDT; ++nt) dq[(t * H_I + jh) * DI + 16 * nt + j16] = acc[nt][r] * wv;
+    }
+  }
+  const float v = wave_sum_xor16_32(dwa);
+  if (g == 0 && jl < H_I) dw[t * H_I + jl] = v * qs[t * H_I + jl];
+}
+
 // Queries [qc qchunk, (qc + 1) qchunk) that can see keys of key group kg (keys 128 kg ..): the
 // chunk contributes a partial dk for the group iff this range is not empty.
 __host__ __device__ __forceinline__ void bk_query_range(int64_t kg, int64_t qc, int64_t qchunk, int64_t T,
@@ -868,12 +984,19 @@ size_t indexer_bwd_workspace_bytes(int64_t T, int64_t S, int32_t D_I) {
 template <int DI>
 static hipError_t launch_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
                              int64_t T, int64_t S, int32_t H_I, int64_t q_start, const float* dI, int64_t ld,
-                             float* dq, float* dw, float* dk, void* workspace, hipStream_t stream) {
+                             float* dq, float* dw, float* dk, void* workspace, const int32_t* idx, int32_t k,
+                             hipStream_t stream) {
   using C = BwCfg<DI>;
-  const int64_t qtiles = (T + BW_ROWS - 1) / BW_ROWS;
-  const int hgroups = (H_I + BQ_WAVES * BQ_HPW - 1) / (BQ_WAVES * BQ_HPW);
-  hipLaunchKernelGGL(indexer_bwd_q_kernel<DI>, dim3((unsigned)qtiles, (unsigned)hgroups), dim3(BQ_WAVES * WAVE), 0,
-                     stream, q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw);
+  if (idx) {  // dq / dw over the listed keys only
+    const int hgroups = (H_I + BL_WAVES * 16 - 1) / (BL_WAVES * 16);
+    hipLaunchKernelGGL(indexer_bwd_q_listed_kernel<DI>, dim3((unsigned)T, (unsigned)hgroups), dim3(BL_WAVES * WAVE), 0, stream, q8, qs,
+                       w, k8, ks, T, S, H_I, q_start, idx, k, dI, ld, dq, dw);
+  } else {
+    const int64_t qtiles = (T + BW_ROWS - 1) / BW_ROWS;
+    const int hgroups = (H_I + BQ_WAVES * BQ_HPW - 1) / (BQ_WAVES * BQ_HPW);
+    hipLaunchKernelGGL(indexer_bwd_q_kernel<DI>, dim3((unsigned)qtiles, (unsigned)hgroups), dim3(BQ_WAVES * WAVE), 0,
+                       stream, q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static bool attr_set = false;
@@ -899,13 +1022,14 @@ static hipError_t launch_bwd(const uint8_t* q8, const float* qs, const float* w,
 
 hipError_t launch_indexer_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
                               int64_t T, int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, const float* dI,
-                              int64_t ld, float* dq, float* dw, float* dk, void* workspace, hipStream_t stream) {
+                              int64_t ld, float* dq, float* dw, float* dk, void* workspace, hipStream_t stream,
+                              const int32_t* idx, int32_t k) {
   if (T <= 0 || S <= 0) return hipSuccess;
   switch (D_I) {
-    case 32: return launch_bwd<32>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
-    case 64: return launch_bwd<64>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
-    case 96: return launch_bwd<96>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
-    case 128: return launch_bwd<128>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, stream);
+#define BWD_CASE(N) \
+  case N: return launch_bwd<N>(q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw, dk, workspace, idx, k, stream);
+    BWD_CASE(32) BWD_CASE(64) BWD_CASE(96) BWD_CASE(128)
+#undef BWD_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -259,6 +259,21 @@ dsa_status_t dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const floa
                              const float *dlogits, int64_t ld_dlogits, float *dq, float *dw, float *dk,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Indexer backward of the sparse stage (summary page, "Method": the sparse-stage loss only sees
+ * the selected keys, so dlogits vanishes off each row's index list).  Same gradients and
+ * arguments as dsa_indexer_bwd, for a dlogits that is 0 at every visible key not in indices[t]
+ * (as dsa_indexer_kl_loss_sparse writes it): dq and dw are summed over the valid entries of
+ * indices [T][k] i32 only (0 <= idx < n_t; others skipped), dk as in dsa_indexer_bwd.  The
+ * valid entries of a row must be distinct (top-k lists are): a key listed twice would be counted
+ * twice in dq and dw.  Supported: as dsa_indexer_bwd, k >= 1.
+ */
+dsa_status_t dsa_indexer_bwd_listed(const uint8_t *q8, const float *q_scale, const float *w, const uint8_t *k8,
+                                    const float *k_scale, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
+                                    int64_t q_start, const int32_t *indices, int32_t k, const float *dlogits,
+                                    int64_t ld_dlogits, float *dq, float *dw, float *dk, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

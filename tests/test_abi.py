@@ -169,6 +169,24 @@ def test_kl_loss_and_backward_argument_errors(lib):
     bad[11] = 66                                                                            # ld % 4
     assert g(*bad) == INVALID
     assert g(None, None, None, None, None, 0, 0, 64, 128, 0, None, 4, None, None, None, None, 0, None) == OK
+    h = lib.dsa_indexer_bwd_listed
+    largs = args[:10] + [FAKE, 2048] + args[10:]
+    assert len(largs) == 20
+    bad = list(largs)
+    bad[11] = 0                                                                             # k
+    assert h(*bad) == INVALID
+    bad = list(largs)
+    bad[10] = None                                                                          # indices
+    assert h(*bad) == INVALID
+    assert "indices" in _err(lib)
+    bad = list(largs)
+    bad[18] = need - 1
+    assert h(*bad) == WS_SMALL
+    bad = list(largs)
+    bad[8] = 100                                                                            # D_I
+    assert h(*bad) == UNSUPPORTED
+    assert h(None, None, None, None, None, 0, 0, 64, 128, 0, None, 16, None, 4, None, None, None, None, 0,
+             None) == OK
 
 
 def test_kl_sparse_argument_errors(lib):

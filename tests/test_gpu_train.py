@@ -98,6 +98,54 @@ def test_indexer_bwd_vs_oracle(dev, T, S, q_start, H_I, D_I):
     _bwd_case(dev, T, S, q_start, H_I, D_I, 84)
 
 
+def _distinct_lists(T, S, pos, k, seed):
+    """Index lists with distinct valid entries (as top-k writes them), -1 padding and one entry
+    beyond the causal range per row."""
+    g = block_rng(seed, T, k)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = min(S, int(pos[t]) + 1)
+        m = min(n, k)
+        idx[t, :m] = g.permutation(n)[:m]
+        if m > 3:
+            idx[t, 2] = n + 5
+    return idx
+
+
+def _bwd_listed_case(dev, T, S, q_start, H_I, D_I, k, seed):
+    import dsa_lightning_indexer_02_amd as dsa
+    print("case bwd listed", T, S, q_start, H_I, D_I, k, flush=True)
+    g = block_rng(seed, T, S)
+    q8, qs = quantize_fp8_rows(g.standard_normal((T, H_I, D_I)).astype(np.float32))
+    k8, ks = quantize_fp8_rows(g.standard_normal((S, D_I)).astype(np.float32))
+    w = (g.uniform(0.0, 1.0, (T, H_I)) / H_I).astype(np.float32)
+    pos = q_start + np.arange(T)
+    idx = _distinct_lists(T, S, pos, k, seed + 1)
+    ld = dsa.ld_for(S)
+    dI = np.zeros((T, ld), np.float32)      # nonzero at the valid listed keys only
+    for t in range(T):
+        keys = idx[t][(idx[t] >= 0) & (idx[t] < pos[t] + 1) & (idx[t] < S)]
+        dI[t, keys] = (g.standard_normal(keys.size) * 1e-2).astype(np.float32)
+    dq, dw, dk = dsa.dsa_indexer_bwd_listed(dput(q8, dev), dput(qs, dev), dput(w, dev), dput(k8, dev),
+                                            dput(ks, dev), dput(idx, dev), dput(dI, dev), q_start=q_start)
+    torch.cuda.synchronize()
+    oq, ow, ok = oracle.indexer_bwd(q8, qs, w, pos, k8, ks, dI[:, :S])
+    amb, worst = parity.check_indexer_bwd(dget(dq), dget(dw), dget(dk), oq, ow, ok, q8, qs, w, k8, ks, dI[:, :S], pos,
+                                          "bwd listed %dx%d H_I=%d D_I=%d k=%d" % (T, S, H_I, D_I, k))
+    print("  ambiguous ReLU signs: %d, worst error / bar: %.3e" % (amb, worst), flush=True)
+
+
+@pytest.mark.parametrize("T,S,q_start,H_I,D_I,k", [
+    (256, 256, 0, 4, 32, 64),        # the small configuration (rows shorter than their lists)
+    (40, 3000, 2900, 64, 128, 2048),  # full heads and list length
+    (50, 50, 0, 20, 64, 16),         # partial head group, one list block
+    (40, 170, 130, 8, 96, 48),       # a ragged list block
+    (33, 300, 100, 60, 128, 100),    # a partial wave of heads
+])
+def test_indexer_bwd_listed_vs_oracle(dev, T, S, q_start, H_I, D_I, k):
+    _bwd_listed_case(dev, T, S, q_start, H_I, D_I, k, 88)
+
+
 def test_train_chain_prefill_4k_rows(dev):
     """indexer -> KL loss (in place) -> backward at the 4K prefill shape; the loss and dI of
     sampled rows against the oracle (its own scores), the backward against the oracle fed the same
@@ -229,6 +277,14 @@ def test_sparse_stage_chain_prefill_4k(dev):
         assert abs(float(np.sum(D[t, :n].astype(np.float64)))) <= 1e-5, "row %d gradient does not sum to 0" % t
     for x in (dq, dw, dk):
         assert np.all(np.isfinite(dget(x)))
+    # the listed backward on the same lists: dk through the same kernels, dq / dw summed in
+    # another order over the same nonzero terms
+    lq, lw, lk = dsa.dsa_indexer_bwd_listed(q8, qs, w, k8, ks, idx, d)
+    torch.cuda.synchronize()
+    assert np.array_equal(dget(lk), dget(dk))
+    for a, b, name in ((lq, dq, "dq"), (lw, dw, "dw")):
+        a, b = dget(a), dget(b)
+        assert np.max(np.abs(a - b)) <= 1e-4 * np.max(np.abs(b)), "listed %s differs from the dense backward" % name
 
 
 def test_train_long_context_rows(dev):
