@@ -49,6 +49,11 @@ struct KlCfg {
   static constexpr int DP = 16 * NKS;
   static constexpr int RC = DP / 8;  // 16-byte chunks per row (even)
   static constexpr int SWZ = RC % 8 == 0 ? 8 : (RC % 4 == 0 ? 4 : 2);
+  // Chunk XOR of staged row r (within aligned groups of SWZ chunks).  gfx950's LDS serves a
+  // 16-byte-per-lane read 16 lanes at a time over 64 four-byte banks; a 576-wide row moves the
+  // bank map by half the banks, so the 16 rows of one fragment-read pass are conflict-free when
+  // rows of equal parity get distinct XORs mod 8 (row bits 1-3 do that, row bits 0-2 do not).
+  static __device__ __forceinline__ int swz(int r) { return ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) & (SWZ - 1); }
   static constexpr int SLOTS = KL_KB * RC;  // a multiple of 64
   static constexpr int K_BYTES = SLOTS * 16;
   static constexpr int DMA_INSTR = SLOTS / WAVE;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
   // padding chunks of every stage are zero (the DMA never writes them)
   if (C::DP > D) {
     for (int p = tid; p < KL_STAGES * C::SLOTS; p += KL_THREADS) {
-      const int sl = p % C::SLOTS, r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      const int sl = p % C::SLOTS, r = sl / C::RC, c = (sl % C::RC) ^ C::swz(r);
       if (c * 8 >= D) *reinterpret_cast<v4i*>(Kbuf + p * 16) = (v4i){0, 0, 0, 0};
     }
   }
@@ -141,15 +146,15 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
     const uint32_t base = kbuf_lds + (uint32_t)((blk % KL_STAGES) * C::K_BYTES);
     for (int i = issuer; i < C::DMA_INSTR; i += KL_ISSUERS) {
       const int sl = i * WAVE + lane;
-      const int r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      const int r = sl / C::RC, c = (sl % C::RC) ^ C::swz(r);
       const int64_t s = min((int64_t)blk * KL_KB + r, S - 1);
       if (c * 8 < D) lds_dma_16B(kv + s * D + c * 8, base + (uint32_t)(i * WAVE * 16));
     }
   };
-  // B operand of step ks: key row l32, chunk 2 ks + lh.  XOR-ing the row into the low log2(SWZ)
+  // B operand of step ks: key row l32, chunk 2 ks + lh.  XOR-ing the row swizzle into the low log2(SWZ)
   // chunk bits leaves steps SWZ / 2 apart a constant distance apart.
   constexpr int KP = C::SWZ / 2;
-  const int kx = l32 & (C::SWZ - 1);
+  const int kx = C::swz(l32);
   int kbase[KP];
 #pragma unroll
   for (int u = 0; u < KP; ++u) kbase[u] = (l32 * C::RC + ((2 * u + lh) ^ kx)) * 16;
@@ -317,7 +322,7 @@ __global__ __launch_bounds__(KLS_THREADS, 1) void indexer_kl_sparse_kernel(
   for (int64_t s = tid; s < n; s += KLS_THREADS) dlogits[t * ld + s] = 0.f;
   if (C::DP > D) {
     for (int p = tid; p < KLS_STAGES * C::SLOTS; p += KLS_THREADS) {
-      const int sl = p % C::SLOTS, r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      const int sl = p % C::SLOTS, r = sl / C::RC, c = (sl % C::RC) ^ C::swz(r);
       if (c * 8 >= D) *reinterpret_cast<v4i*>(Kbuf + p * 16) = (v4i){0, 0, 0, 0};
     }
   }
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(KLS_THREADS, 1) void indexer_kl_sparse_kernel(
     const uint32_t base = kbuf_lds + (uint32_t)((blk % KLS_STAGES) * C::K_BYTES);
     for (int i = wave; i < C::DMA_INSTR; i += KLS_WAVES) {
       const int sl = i * WAVE + lane;
-      const int r = sl / C::RC, c = (sl % C::RC) ^ (r & (C::SWZ - 1));
+      const int r = sl / C::RC, c = (sl % C::RC) ^ C::swz(r);
       const int e = blk * KL_KB + r;
       const int32_t kr = e < k ? rows[e] : -1;
       const int64_t s = kr >= 0 ? kr : 0;  // skipped entries read row 0 (masked)
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(KLS_THREADS, 1) void indexer_kl_sparse_kernel(
     }
   };
   constexpr int KP = C::SWZ / 2;
-  const int kx = l32 & (C::SWZ - 1);
+  const int kx = C::swz(l32);
   int kbase[KP];
 #pragma unroll
   for (int u = 0; u < KP; ++u) kbase[u] = (l32 * C::RC + ((2 * u + lh) ^ kx)) * 16;

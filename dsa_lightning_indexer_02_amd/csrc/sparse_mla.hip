@@ -51,9 +51,17 @@ struct MlaCfg {
   static constexpr int VT_BYTES = DV * VT_STRIDE;
   static_assert(DQK % 8 == 0 && DV % 64 == 0 && DV <= DQK && DV <= 64 * MLA_WAVES, "unsupported MLA dims");
   static_assert(SLOTS % WAVE == 0, "gather slots must fill whole waves");
+  // Chunk XOR of gathered row r.  gfx950's LDS serves a 16-byte-per-lane read 16 lanes at a time
+  // over 64 four-byte banks, and a 576-wide row (288 dwords) moves the bank map by half the banks:
+  // the 16 rows of one K-fragment read pass are conflict-free when rows of equal parity get
+  // distinct XORs mod 8, and the transposing reads of rows 4 j .. 4 j + 3 when rows 4 j and 4 j + 2
+  // differ in XOR bit 2.  (row bit 1 -> XOR bit 2, row bits 2-3 -> XOR bits 0-1) does both.
+  static __host__ __device__ __forceinline__ constexpr int swz(int r) {
+    return ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) & (SWZ - 1);
+  }
   // 16-byte slot of chunk c of gathered row r: rows are contiguous, chunks XOR-swizzled within
   // aligned groups of SWZ.
-  static __device__ __forceinline__ int slot(int r, int c) { return r * RC + (c ^ (r & (SWZ - 1))); }
+  static __device__ __forceinline__ int slot(int r, int c) { return r * RC + (c ^ swz(r)); }
 };
 
 template <int DQK, int DV>
@@ -207,11 +215,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   const uint32_t kbuf_lds = lds_addr(Kbuf);
   const int my_dma = (C::DMA_INSTR - wave + MLA_WAVES - 1) / MLA_WAVES;  // this wave's transfers per block
   static_assert(C::SWZ == 8 || C::SWZ == 4 || C::SWZ == 1, "swizzle span");
-  // K fragment of step ks (A operand): row l32, chunk cb + 2 ks.  XOR-ing the row into the low
+  // K fragment of step ks (A operand): row l32, chunk cb + 2 ks.  XOR-ing the row swizzle into the low
   // log2(SWZ) chunk bits leaves steps that are SWZ chunks apart a constant distance apart, so the
   // offset is one of KP per-lane bases plus a compile-time constant.
   constexpr int KP = C::SWZ >= 2 ? C::SWZ / 2 : 1;
-  const int kx = l32 & (C::SWZ - 1);
+  const int kx = C::swz(l32);
   const int kcb = hf * (C::DH / 8) + lh;
   int kbase[KP];
 #pragma unroll
@@ -227,12 +235,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   const int tg = (lane >> 4) & 3, ti = lane & 15;
   const int trow = (lane & 15) >> 2;                                   // + 4 j'
   const int tch = (wave * 64 + 16 * tg) / 8 + ((lane & 3) >> 1);      // chunk of the addressed columns
-  // row 4 jq + trow: its swizzle bits are trow | 4 (jq & 1) when SWZ is 8, trow when SWZ is 4
-  constexpr int TQ = C::SWZ >= 8 ? 2 : 1;
-  int tb[TQ];
-#pragma unroll
-  for (int e = 0; e < TQ; ++e) tb[e] = (trow * C::RC + (tch ^ ((trow | 4 * e) & (C::SWZ - 1)))) * 16 + 8 * (lane & 1);
-  auto tr_off = [&](int jq) { return tb[jq % TQ] + 4 * jq * C::RC * 16; };  // key quad jq: rows 4 jq + 0..3
+  // row 4 jq + trow (trow < 4) has the swizzle swz(trow) ^ swz(4 jq): the two take disjoint bits
+  static_assert(C::swz(4 * 3 + 3) == (C::swz(3) ^ C::swz(12)) && C::swz(4 * 2 + 1) == (C::swz(1) ^ C::swz(8)),
+                "row swizzle splits into the quad and the row within it");
+  const int tbase = trow * C::RC * 16 + 8 * (lane & 1);
+  const int tc0 = tch ^ C::swz(trow);
+  auto tr_off = [&](int jq) {  // key quad jq (a compile-time constant): rows 4 jq + 0..3
+    return tbase + 16 * (tc0 ^ C::swz(4 * jq)) + 4 * jq * C::RC * 16;
+  };
   uint8_t* vt_dst = Vt + (wave * 64 + 16 * tg + ti) * C::VT_STRIDE;
   // Gather of block blk.  Transfer i covers slots [64 i, 64 i + 64).  When a row holds at least
   // 64 slots that is at most two gathered rows, (64 i) / RC and (64 i + 63) / RC: gather_rows then
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       for (int i = wave; i < C::DMA_INSTR; i += MLA_WAVES) {
         const int s = i * WAVE + lane;
         const int rr = s / C::RC;
-        const int c = (s % C::RC) ^ (rr & (C::SWZ - 1));
+        const int c = (s % C::RC) ^ C::swz(rr);
         const int e = blk * MLA_KB + rr;
         const int32_t pr = e < cnt ? phys[e] : -1;
         const uint16_t* src = kv + (int64_t)(pr >= 0 ? pr : safe_row) * DQK + c * 8;
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       if (i < C::DMA_INSTR) {  // wave-uniform
         const int s = i * WAVE + ln;
         const int rr = s / C::RC;
-        const int c = (s % C::RC) ^ (rr & (C::SWZ - 1));
+        const int c = (s % C::RC) ^ C::swz(rr);
         const int first = (i * WAVE) / C::RC;
         const int32_t pa = __builtin_amdgcn_readlane(prow, 2 * j), pb = __builtin_amdgcn_readlane(prow, 2 * j + 1);
         const uint16_t* src = kv + (int64_t)(rr == first ? pa : pb) * DQK + c * 8;
