@@ -290,7 +290,8 @@ def test_sparse_stage_chain_prefill_4k(dev):
 def test_train_long_context_rows(dev):
     """The chunked-prefill shape: 64 query rows at positions 131008 .. 131071 over a 131072-key
     context (4096 key blocks per row in the loss, key groups and query chunks far from the origin
-    in the backward); loss and dI of two rows against the oracle, the backward on a 16-row slice."""
+    in the backward); loss and dI of two rows against the oracle, the backward on a 16-row slice and
+    the listed backward (2048-entry lists over the whole context) on 8 rows."""
     import dsa_lightning_indexer_02_amd as dsa
     T, S, H, D, H_I, D_I = 64, 131072, 128, 576, 64, 128
     q_start = S - T
@@ -324,3 +325,18 @@ def test_train_long_context_rows(dev):
     amb, worst = parity.check_indexer_bwd(dget(dq), dget(dw), dget(dk), oq, ow, ok, q8, qs, w, k8, ks, dI[:, :S],
                                           posb, "bwd long context")
     print("  backward: ambiguous ReLU signs %d, worst error / bar %.3e" % (amb, worst), flush=True)
+    # the listed backward over 2048-entry lists spread across the whole context (8 rows)
+    Tl = 8
+    posl = S - Tl + np.arange(Tl)
+    idx = _distinct_lists(Tl, S, posl, 2048, 89)
+    dIl = np.zeros((Tl, ld), np.float32)
+    for t in range(Tl):
+        keys = idx[t][(idx[t] >= 0) & (idx[t] <= posl[t])]
+        dIl[t, keys] = (g.standard_normal(keys.size) * 1e-2).astype(np.float32)
+    lq, lw, lk = dsa.dsa_indexer_bwd_listed(dput(q8[:Tl], dev), dput(qs[:Tl], dev), dput(w[:Tl], dev), dput(k8, dev),
+                                            dput(ks, dev), dput(idx, dev), dput(dIl, dev), q_start=S - Tl)
+    torch.cuda.synchronize()
+    oq, ow, ok = oracle.indexer_bwd(q8[:Tl], qs[:Tl], w[:Tl], posl, k8, ks, dIl[:, :S])
+    amb, worst = parity.check_indexer_bwd(dget(lq), dget(lw), dget(lk), oq, ow, ok, q8[:Tl], qs[:Tl], w[:Tl], k8, ks,
+                                          dIl[:, :S], posl, "bwd listed long context")
+    print("  listed backward: ambiguous ReLU signs %d, worst error / bar %.3e" % (amb, worst), flush=True)
