@@ -15,7 +15,7 @@ indexer with power-of-two scales inside the MFMA; indexer_train_4k / indexer_tra
 training step of the indexer: scores, KL loss toward the main attention, backward;
 indexer_train_sparse_4k / _32k the sparse-stage step: scores, top-k, sparse attention, the loss over
 the selected entries, backward), and
-``--all-configs`` prints one line per configuration.  ``--gpus`` above 1 is rejected: this build runs on one GPU.
+``--all-configs`` prints one line per configuration.  ``--gpus`` above 1 is rejected: the library runs on one GPU (no multi-GPU path).
 """
 from __future__ import annotations
 
@@ -586,7 +586,7 @@ def main():
                     help="after timing, copy 1 GiB device-to-device (counter scale reference)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus,
+        print("bench.py runs on one GPU: the library has no multi-GPU path (asked for --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
