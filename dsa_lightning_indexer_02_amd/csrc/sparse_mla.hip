@@ -143,8 +143,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hg = wave >> 1, hf = wave & 1;                    // head group, contraction half
   const int l32 = lane & 31, lh = lane >> 5;
-  const int64_t r = blockIdx.y;
-  const int sp = blockIdx.x;
+  const int64_t r = blockIdx.x;  // rows on x: up to 2^31 - 1 of them in one launch
+  const int sp = blockIdx.y;
   const int64_t n = seq_lens ? min((int64_t)max(seq_lens[r], 0), S) : min(S, q_start + r + 1);
   const int i0 = sp * keys_per_split;
   const int i1 = min(k, i0 + keys_per_split);
@@ -511,7 +511,7 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
     attr_set = true;
   }
   const float scale_log2 = a.sm_scale * 1.4426950408889634f;
-  dim3 grid((unsigned)nsplit, (unsigned)a.R);
+  dim3 grid((unsigned)a.R, (unsigned)nsplit);
   hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), grid, dim3(MLA_THREADS), smem, stream, a.q, a.kv,
                      a.idx, a.table, a.max_blocks, a.block_shift, a.per_row_table, a.seq_lens, a.S,
                      a.q_start, a.H, a.k, scale_log2, nsplit, kps, a.out, a.out_f32, a.lse, a.part_out,

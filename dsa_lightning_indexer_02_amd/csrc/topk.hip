@@ -524,8 +524,8 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4
     const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, int32_t G) {
   __shared__ TopkShared sh;
-  const int64_t t = blockIdx.y;
-  const int chunk = blockIdx.x;
+  const int64_t t = blockIdx.x;  // rows on x: up to 2^31 - 1 of them in one launch
+  const int chunk = blockIdx.y;
   const int64_t n = seq_lens ? min((int64_t)max(seq_lens[t], 0), S) : min(S, q_start + t + 1);
   const int64_t c0 = (int64_t)chunk * TK_CHUNK;
   if (c0 >= n && chunk > 0) return;
@@ -615,10 +615,10 @@ hipError_t launch_topk(const float* logits, int64_t ld, int64_t T, int64_t S, in
     ci = reinterpret_cast<int32_t*>(ck + (size_t)T * G * k);
   }
   if (G <= 1)
-    hipLaunchKernelGGL(topk_chunk_kernel<true>, dim3(1, (unsigned)T), dim3(TK_THREADS), 0, stream, logits, ld,
+    hipLaunchKernelGGL(topk_chunk_kernel<true>, dim3((unsigned)T, 1), dim3(TK_THREADS), 0, stream, logits, ld,
                        T, S, q_start, seq_lens, k, indices, ck, ci, G);
   else
-    hipLaunchKernelGGL(topk_chunk_kernel<false>, dim3((unsigned)G, (unsigned)T), dim3(TK_THREADS), 0, stream,
+    hipLaunchKernelGGL(topk_chunk_kernel<false>, dim3((unsigned)T, (unsigned)G), dim3(TK_THREADS), 0, stream,
                        logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || G <= 1) return e;

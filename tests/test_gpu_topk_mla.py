@@ -155,3 +155,30 @@ def test_mla_k1_and_large_logits(dev):
     f32, lse = _mla_case(dev, T, S, 128, 576, 512, 1, idx1, S, 1 / np.sqrt(192), "k=1")
     idx = np.stack([g.permutation(S)[:256] for _ in range(T)])
     _mla_case(dev, T, S, 128, 576, 512, 256, idx, S, 2.0, "sharp softmax (rescale path)")
+
+
+def test_many_rows_one_launch(dev):
+    """70,000 query rows in one call (one workgroup per row, more than 65,536 of them): top-k and
+    sparse attention at small widths, the oracle on rows on both sides of 65,536."""
+    import dsa_lightning_indexer_02_amd as dsa
+    T, S, k, q_start = 70000, 200, 64, 100
+    print("case many rows", T, flush=True)
+    g = block_rng(44, T, S)
+    scores = g.standard_normal((T, S)).astype(np.float32)
+    ld = dsa.ld_for(S)
+    host = np.zeros((T, ld), np.float32)
+    host[:, :S] = scores
+    gi = dget(dsa.dsa_topk(dput(host, dev), k, S, q_start=q_start))
+    rows = np.array([0, 1, 65534, 65535, 65536, 65537, T - 1])
+    pos = q_start + rows
+    parity.check_topk_exact(gi[rows], oracle.topk(scores[rows], pos, k), "top-k, many rows")
+    H, D_qk, D_v, km = 8, 80, 64, 16
+    q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
+    idx = g.integers(-2, S, size=(T, km)).astype(np.int32)   # some skipped and some non-causal entries
+    sm = 1 / np.sqrt(80)
+    out, f32, lse = dsa.dsa_sparse_mla_fwd(dput(q, dev).view(torch.bfloat16), dput(kv, dev).view(torch.bfloat16),
+                                           dput(idx, dev), sm, D_v, q_start=q_start, want_f32=True)
+    torch.cuda.synchronize()
+    o, _, ol = oracle.sparse_mla(q[rows], idx[rows], pos, kv, D_v, sm)
+    parity.check_mla(bf16_vals(out)[rows], dget(f32)[rows], dget(lse)[rows], o, ol, "MLA, many rows")
