@@ -169,6 +169,8 @@ dsa_status_t dsa_indexer_logits(const uint8_t* q8, const float* q_scale, const f
                                 const float* k_scale, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
                                 int64_t q_start, float* logits, int64_t ld_logits, hipStream_t stream) {
   REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  REQUIRE(T <= dsa::indexer_prefill_max_rows(), DSA_ERR_UNSUPPORTED, "T=%lld exceeds %lld query rows per call",
+          (long long)T, (long long)dsa::indexer_prefill_max_rows());
   dsa_status_t s = check_indexer_dims(H_I, D_I);
   if (s != DSA_OK) return s;
   if (T == 0) return ok();
@@ -190,6 +192,8 @@ dsa_status_t dsa_indexer_logits_ue8m0(const uint8_t* q8, const uint8_t* q_exp, c
                                       const uint8_t* k_exp, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
                                       int64_t q_start, float* logits, int64_t ld_logits, hipStream_t stream) {
   REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  REQUIRE(T <= dsa::indexer_prefill_max_rows(), DSA_ERR_UNSUPPORTED, "T=%lld exceeds %lld query rows per call",
+          (long long)T, (long long)dsa::indexer_prefill_max_rows());
   dsa_status_t s = check_indexer_dims(H_I, D_I);
   if (s != DSA_OK) return s;
   if (T == 0) return ok();
@@ -285,6 +289,8 @@ dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t* c, int32_t seq, const ds
   dsa_status_t s = check_dims(d);
   if (s != DSA_OK) return s;
   REQUIRE(T >= 0 && q_start >= 0 && seq >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, q_start or seq");
+  REQUIRE(T <= dsa::indexer_prefill_max_rows(), DSA_ERR_UNSUPPORTED, "T=%lld exceeds %lld query rows per call",
+          (long long)T, (long long)dsa::indexer_prefill_max_rows());
   if (T == 0) return ok();
   const int64_t S = q_start + T;
   s = check_cache(c, S, seq + 1);

@@ -14,6 +14,9 @@ namespace dsa {
 // ---- lightning indexer
 size_t indexer_prefill_smem(int32_t H_I, bool e8);
 // q_exp / k_exp non-null: UE8M0 exponent scales applied in the MFMA (qs, ks unused)
+// Query rows one indexer-prefill call takes: its 16-row query tiles run on the grid's second
+// dimension, which gfx950 caps at 65536 workgroups.
+int64_t indexer_prefill_max_rows();
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
                                   const float* ks, const int32_t* table, int32_t block_shift, int64_t T,
                                   int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, float* logits,

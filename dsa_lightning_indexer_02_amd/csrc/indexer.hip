@@ -440,6 +440,8 @@ size_t indexer_prefill_smem(int32_t H_I, bool e8) {
          (e8 ? (size_t)H_I * IDX_ROWS : 0);
 }
 
+int64_t indexer_prefill_max_rows() { return (int64_t)IDX_ROWS * 65536; }
+
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
                                   const uint8_t* k8, const float* ks, const int32_t* table,
                                   int32_t block_shift, int64_t T, int64_t S, int32_t H_I, int32_t D_I,

@@ -58,7 +58,9 @@ int dsa_abi_version(void);
  * for s < n_t.  Entries s >= n_t of each logits row are not written.
  *   q8 [T][H_I][D_I] u8, q_scale [T][H_I] f32, w [T][H_I] f32 (used as given, any sign),
  *   k8 [S][D_I] u8, k_scale [S] f32, logits [T][ld_logits] f32 with ld_logits >= S and a
- *   multiple of 4.  Supported: 1 <= H_I <= 64, D_I in {32, 64, 96, 128}.
+ *   multiple of 4.  Supported: 1 <= H_I <= 64, D_I in {32, 64, 96, 128}, T <= 1,048,576 per call
+ *   (16-row query tiles on the launch grid's second dimension, which the GPU caps at 65,536; more
+ *   rows return DSA_ERR_UNSUPPORTED and are split by the caller).
  */
 dsa_status_t dsa_indexer_logits(const uint8_t *q8, const float *q_scale, const float *w,
                                 const uint8_t *k8, const float *k_scale, int64_t T, int64_t S,
@@ -131,7 +133,7 @@ typedef struct {
  * kernels as the three standalone calls.  q8/q_scale/w/q as in the standalone calls,
  * out [T][H][D_v] bf16, out_f32 (optional), lse [T][H] (optional), indices_out [T][topk]
  * (optional; written when non-NULL).  Workspace: dsa_prefill_workspace_size() bytes, 256-byte
- * aligned.
+ * aligned.  T <= 1,048,576 per call, as dsa_indexer_logits.
  */
 size_t dsa_prefill_workspace_size(const dsa_dims_t *d, int64_t T, int64_t S);
 dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t *c, int32_t seq, const dsa_dims_t *d, int64_t T,
@@ -251,7 +253,7 @@ dsa_status_t dsa_indexer_kl_loss_sparse(const uint16_t *q, const uint16_t *kv, c
  *   Inputs as dsa_indexer_logits (scales positive), dlogits [T][ld_dlogits] f32; outputs dq
  *   [T][H_I][D_I], dw [T][H_I], dk [S][D_I] f32 (every entry written).  The workspace (device,
  *   dsa_indexer_bwd_workspace_size() bytes) holds per-chunk partial key gradients; the result is
- *   deterministic.  Supported: as dsa_indexer_logits, T and S both >= 1 (or both 0).
+ *   deterministic.  Supported: H_I and D_I as dsa_indexer_logits, T and S both >= 1 (or both 0).
  */
 size_t dsa_indexer_bwd_workspace_size(int64_t T, int64_t S, int32_t D_I);
 dsa_status_t dsa_indexer_bwd(const uint8_t *q8, const float *q_scale, const float *w, const uint8_t *k8,

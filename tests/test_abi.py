@@ -63,6 +63,9 @@ def test_indexer_argument_errors(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 10, 64, 128, 0, FAKE, 10, None) == INVALID  # ld % 4
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 64, 128, 0, FAKE, 8, None) == INVALID
     assert f(None, None, None, None, None, 0, 8, 64, 128, 0, None, 8, None) == OK         # T = 0
+    # more query rows than one launch's 16-row tiles cover on the grid's second dimension
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 16 * 65536 + 1, 8, 64, 128, 0, FAKE, 8, None) == UNSUPPORTED
+    assert "query rows per call" in _err(lib)
 
 
 def test_topk_argument_errors(lib):
