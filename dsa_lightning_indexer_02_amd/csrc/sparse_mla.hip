@@ -294,7 +294,13 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 
   v16f O[C::NDT];
   float mref, mlane = -INFINITY, lsum;  // mlane: this lane's running maximum (its head, its keys)
-  const int nblk = (cnt + MLA_KB - 1) / MLA_KB;
+  // blocks up to the last one holding a valid entry (all later entries are masked: a row with fewer
+  // visible keys than list entries skips its padding); one validity word per lane, the same answer
+  // in every wave
+  static_assert(MLA_MAX_K / MLA_KB <= WAVE, "one block word per lane");
+  const int nblk_all = (cnt + MLA_KB - 1) / MLA_KB;
+  const uint64_t live = __ballot(lane < nblk_all && vmask_lds[lane] != 0u);
+  const int nblk = live ? 64 - __clzll(live) : 0;
   int32_t* overflow_flag = phys + MLA_MAX_K;  // one int after the row list
   const v4f* Sx_mine = reinterpret_cast<const v4f*>(Sx) + wave * 4 * WAVE + lane;
   const v4f* Sx_peer = reinterpret_cast<const v4f*>(Sx) + (wave ^ 1) * 4 * WAVE + lane;
