@@ -143,7 +143,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hg = wave >> 1, hf = wave & 1;                    // head group, contraction half
   const int l32 = lane & 31, lh = lane >> 5;
-  const int64_t r = blockIdx.x;  // rows on x: up to 2^31 - 1 of them in one launch
+  // Rows on x (up to 2^31 - 1 in one launch), latest first: rows with full lists start together
+  // and walk their ascending index lists in near lockstep, so the gathered rows of the workgroups
+  // in flight overlap in L2; rows shorter than their lists (which stop early) come last.
+  const int64_t r = (int64_t)gridDim.x - 1 - blockIdx.x;
   const int sp = blockIdx.y;
   const int64_t n = seq_lens ? min((int64_t)max(seq_lens[r], 0), S) : min(S, q_start + r + 1);
   const int i0 = sp * keys_per_split;
