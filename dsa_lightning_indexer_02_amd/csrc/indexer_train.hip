@@ -647,6 +647,19 @@ __global__ __launch_bounds__(BL_WAVES * WAVE, 2) void indexer_bwd_q_listed_kerne
   const bool stager = tid < BW_BLK * (DI / 16);
   const int32_t* lrow = idx + t * k;
   const float* drow = dI + t * ld;
+  // entries past the row's last valid one are not visited (rows with fewer visible keys than list
+  // entries end in padding)
+  __shared__ int32_t klast[BL_WAVES];
+  int last = 0;
+  for (int i = tid; i < k; i += BL_WAVES * WAVE) {
+    const int32_t key = lrow[i];
+    if (key >= 0 && key < n) last = i + 1;  // i grows: the thread's last valid entry
+  }
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o));
+  if (lane == 0) klast[wave] = last;
+  __syncthreads();
+  int k_used = 0;
+  for (int w = 0; w < BL_WAVES; ++w) k_used = max(k_used, klast[w]);
   auto entry = [&](int e) -> int32_t {  // the listed key of entry e, -1 when skipped
     const int32_t key = lrow[min(e, k - 1)];
     return (e < k && key >= 0 && key < n) ? key : -1;
@@ -661,12 +674,12 @@ __global__ __launch_bounds__(BL_WAVES * WAVE, 2) void indexer_bwd_q_listed_kerne
   float nu = factor(ku);
   kp = entry(BW_BLK + pr);  // block 1
   ku = entry(BW_BLK + (tid & (BW_BLK - 1)));
-  for (int e0 = 0; e0 < k; e0 += BW_BLK) {
+  for (int e0 = 0; e0 < k_used; e0 += BW_BLK) {
     __syncthreads();  // the previous block is consumed
     if (stager) stage_row16(kt + pr * C::STRIDE + pc * 32, nraw);
     if (tid < BW_BLK) us[tid] = nu;
     __syncthreads();
-    if (e0 + BW_BLK < k) {
+    if (e0 + BW_BLK < k_used) {
       nraw = *reinterpret_cast<const v4i*>(k8 + (int64_t)max(kp, 0) * DI + pc * 16);
       nu = factor(ku);
       kp = entry(e0 + 2 * BW_BLK + pr);
