@@ -67,6 +67,9 @@ def load(path: Optional[str] = None):
     lib.oracle_indexer_kl_sparse.argtypes = [_p, _p, _p, _i64, _i64, _i32, _i32, ctypes.c_double, _p, _i32, _p,
                                              _i64, _p, _p, _i64, _i32]
     lib.oracle_indexer_kl_sparse.restype = ctypes.c_int
+    lib.oracle_sparse_mla_bwd.argtypes = [_p, _p, _p, _i64, _i32, _i32, _i32, _i32, _p, _i64, ctypes.c_double, _p,
+                                          _p, _p, _i32]
+    lib.oracle_sparse_mla_bwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -312,3 +315,25 @@ def indexer_kl_sparse(q, kv, pos, sm_scale: float, idx, logits, nthreads: int = 
     if rc:
         raise RuntimeError("oracle_indexer_kl_sparse failed (%d)" % rc)
     return loss, d
+
+
+def sparse_mla_bwd(q, idx, pos, kv, D_v: int, sm_scale: float, dout, nthreads: int = 0, lib=None):
+    """Gradients of the sparse MLA forward (see oracle_sparse_mla_bwd) for dL/dout = dout (bf16 bits
+    [T, H, D_v]): (dq float64 [T, H, D_qk], dkv float64 [S, D_qk])."""
+    lib = lib or load()
+    q = _c(q, np.uint16)
+    T, H, D_qk = q.shape
+    idx = _c(idx, np.int32)
+    k = idx.shape[1]
+    kv = _c(kv, np.uint16)
+    S = kv.shape[0]
+    pos = _c(pos, np.int64)
+    dout = _c(dout, np.uint16)
+    dq = np.empty((T, H, D_qk), dtype=np.float64)
+    dkv = np.empty((S, D_qk), dtype=np.float64)
+    rc = lib.oracle_sparse_mla_bwd(_ptr(q), _ptr(idx), _ptr(pos), T, H, D_qk, D_v, k, _ptr(kv), S,
+                                   ctypes.c_double(sm_scale), _ptr(dout), _ptr(dq), _ptr(dkv), nthreads)
+    if rc:
+        raise RuntimeError("oracle_sparse_mla_bwd failed (%d)" % rc)
+    return dq, dkv
+

@@ -733,3 +733,133 @@ int oracle_indexer_kl_sparse(const uint16_t *q, const uint16_t *kv, const int64_
     }
     return bad;
 }
+
+/* ---- NEXT step: backward of the sparse MLA forward ---------------------------------------------
+ * DeepSeek-V3.2-Exp summary page, section "Method": in the sparse training stage the main model
+ * trains with top-k selection on, its attention reading only the selected latent rows (AMD article,
+ * section "Training Approach", sparse stage).  The forward of oracle_sparse_mla, for query row t,
+ * head h and the valid entries i of its list (0 <= idx_i < n_t; each entry its own term):
+ *     z_i = sm_scale q . k_i,  p = softmax(z),  out = sum_i p_i v_i   (k_i = kv[idx_i][:D_qk],
+ *                                                                       v_i = kv[idx_i][:D_v]).
+ * Given g = dL/dout[t][h] (bf16 bits), the chain rule through the softmax gives
+ *     dp_i = g . v_i,   D = sum_i p_i dp_i  (= g . out),   ds_i = p_i (dp_i - D),
+ *     dq[t][h][:]  = sm_scale sum_i ds_i k_i,
+ *     dkv[s][:]   += sm_scale ds_i q[t][h][:]        for every entry i with idx_i = s (all D_qk columns)
+ *     dkv[s][:D_v] += p_i g                         (the value columns of the same row).
+ * Rows with no valid entry contribute nothing (dq = 0).  Arithmetic in double, the softmax with
+ * its row maximum subtracted.  Each row's contributions are summed over its heads per entry, then
+ * added to dkv in ascending entry order, rows in ascending order: the result does not depend on the
+ * thread count.  dq [T][H][D_qk], dkv [S][D_qk] (every entry written).  Returns 1 on a bad shape, 3
+ * on no memory. */
+static int mla_bwd_row(const uint16_t *q, const int32_t *row, int64_t n, int32_t H, int32_t D_qk, int32_t D_v,
+                       int32_t k, const uint16_t *kv, double sm_scale, const uint16_t *g, double *dq,
+                       double *contrib)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)k);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!z || !dp) {
+        free(z);
+        free(dp);
+        return 3;
+    }
+    for (int64_t e = 0; e < (int64_t)k * D_qk; ++e)
+        contrib[e] = 0.0;
+    for (int32_t h = 0; h < H; ++h) {
+        const uint16_t *qh = q + (int64_t)h * D_qk;
+        const uint16_t *gh = g + (int64_t)h * D_v;
+        double *dqh = dq + (int64_t)h * D_qk;
+        for (int32_t d = 0; d < D_qk; ++d)
+            dqh[d] = 0.0;
+        double m = -INFINITY;
+        for (int32_t i = 0; i < k; ++i) {
+            if (row[i] < 0 || row[i] >= n)
+                continue;
+            const uint16_t *kr = kv + (int64_t)row[i] * D_qk;
+            double dot = 0.0;
+            for (int32_t d = 0; d < D_qk; ++d)
+                dot += (double)bf16_value(qh[d]) * (double)bf16_value(kr[d]);
+            z[i] = sm_scale * dot;
+            if (z[i] > m)
+                m = z[i];
+        }
+        if (m == -INFINITY)
+            continue;
+        double l = 0.0;
+        for (int32_t i = 0; i < k; ++i)
+            if (row[i] >= 0 && row[i] < n)
+                l += exp(z[i] - m);
+        double D = 0.0;
+        for (int32_t i = 0; i < k; ++i) {
+            if (row[i] < 0 || row[i] >= n)
+                continue;
+            const uint16_t *vr = kv + (int64_t)row[i] * D_qk;
+            double dot = 0.0;
+            for (int32_t d = 0; d < D_v; ++d)
+                dot += (double)bf16_value(gh[d]) * (double)bf16_value(vr[d]);
+            dp[i] = dot;
+            D += exp(z[i] - m) / l * dot;
+        }
+        for (int32_t i = 0; i < k; ++i) {
+            if (row[i] < 0 || row[i] >= n)
+                continue;
+            const double p = exp(z[i] - m) / l;
+            const double ds = p * (dp[i] - D);
+            const uint16_t *kr = kv + (int64_t)row[i] * D_qk;
+            double *c = contrib + (int64_t)i * D_qk;
+            for (int32_t d = 0; d < D_qk; ++d) {
+                dqh[d] += sm_scale * ds * (double)bf16_value(kr[d]);
+                c[d] += sm_scale * ds * (double)bf16_value(qh[d]);
+            }
+            for (int32_t d = 0; d < D_v; ++d)
+                c[d] += p * (double)bf16_value(gh[d]);
+        }
+    }
+    free(z);
+    free(dp);
+    return 0;
+}
+
+int oracle_sparse_mla_bwd(const uint16_t *q, const int32_t *idx, const int64_t *pos, int64_t T, int32_t H,
+                          int32_t D_qk, int32_t D_v, int32_t k, const uint16_t *kv, int64_t S, double sm_scale,
+                          const uint16_t *dout, double *dq, double *dkv, int32_t nthreads)
+{
+    if (T < 0 || S < 0 || H <= 0 || D_qk <= 0 || D_v <= 0 || D_v > D_qk || k <= 0)
+        return 1;
+    set_threads(nthreads);
+    for (int64_t e = 0; e < S * (int64_t)D_qk; ++e)
+        dkv[e] = 0.0;
+    int nt = 1;
+#ifdef _OPENMP
+    nt = omp_get_max_threads();
+#endif
+    /* rows in batches of nt: contributions in parallel, added to dkv serially in row order */
+    double *contrib = (double *)malloc(sizeof(double) * (size_t)nt * (size_t)k * (size_t)D_qk);
+    if (!contrib)
+        return 3;
+    int bad = 0;
+    for (int64_t t0 = 0; t0 < T && !bad; t0 += nt) {
+        int64_t t1 = t0 + nt < T ? t0 + nt : T;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t t = t0; t < t1; ++t) {
+            int rc = mla_bwd_row(q + t * H * (int64_t)D_qk, idx + t * k, visible_keys(pos[t], S), H, D_qk, D_v, k,
+                                 kv, sm_scale, dout + t * H * (int64_t)D_v, dq + t * H * (int64_t)D_qk,
+                                 contrib + (t - t0) * (int64_t)k * D_qk);
+            if (rc)
+                bad = rc;
+        }
+        for (int64_t t = t0; t < t1 && !bad; ++t) {
+            const int32_t *row = idx + t * k;
+            int64_t n = visible_keys(pos[t], S);
+            for (int32_t i = 0; i < k; ++i) {
+                if (row[i] < 0 || row[i] >= n)
+                    continue;
+                const double *c = contrib + ((t - t0) * (int64_t)k + i) * D_qk;
+                double *dst = dkv + (int64_t)row[i] * D_qk;
+                for (int32_t d = 0; d < D_qk; ++d)
+                    dst[d] += c[d];
+            }
+        }
+    }
+    free(contrib);
+    return bad;
+}

@@ -644,3 +644,155 @@ def check_kl_sparse_closed_forms(lib):
         ref = 2 * (1 / 3) * (np.log(1 / 3) - np.log(pa)) + (1 / 3) * (np.log(1 / 3) - np.log(pb))
         assert abs(ls[t] - ref) <= 1e-12
         assert abs(ds[t, 3] - 2 * (pa - 1 / 3)) <= 1e-12 and abs(ds[t, 9] - (pb - 1 / 3)) <= 1e-12
+
+
+# ---------------------------------------------------------------- sparse MLA backward
+def _mla_bwd_case(T, S, H, D_qk, D_v, k, seed, dup=True):
+    """Inputs with duplicates, entries past the causal range and -1 padding in the lists."""
+    g = block_rng(seed, 5, 0)
+    q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
+    dout = to_bf16_bits(g.standard_normal((T, H, D_v)).astype(np.float32))
+    pos = g.integers(k // 2, S, size=T).astype(np.int64)
+    idx = g.integers(-2, S, size=(T, k)).astype(np.int32)
+    if dup:
+        idx[:, 1] = idx[:, 0]
+        idx[:, 5] = idx[:, 4]
+    idx[:, -1] = -1
+    return q, kv, dout, pos, idx
+
+
+def torch_mla_bwd(q, kv, dout, pos, idx, D_v, sm):
+    """(dq, dkv) by torch autograd in float64 through the gather of each row's valid entries."""
+    qf = torch.from_numpy(brute.bf16_decode(q)).requires_grad_(True)
+    kvf = torch.from_numpy(brute.bf16_decode(kv)).requires_grad_(True)
+    gf = torch.from_numpy(brute.bf16_decode(dout))
+    S = kvf.shape[0]
+    n = np.minimum(S, pos + 1)
+    total = 0.0
+    for t in range(q.shape[0]):
+        sel = [int(s) for s in idx[t] if 0 <= s < n[t]]
+        if not sel:
+            continue
+        K = kvf[torch.tensor(sel)]                              # [m, D_qk], repeated rows allowed
+        p = torch.softmax(sm * qf[t] @ K.T, dim=-1)             # [H, m]
+        total = total + (p @ K[:, :D_v] * gf[t]).sum()
+    if isinstance(total, torch.Tensor):
+        total.backward()
+    dq = qf.grad.numpy() if qf.grad is not None else np.zeros(qf.shape)
+    dkv = kvf.grad.numpy() if kvf.grad is not None else np.zeros(kvf.shape)
+    return dq, dkv
+
+
+def check_mla_bwd_vs_torch(lib):
+    T, S, H, D_qk, D_v, k, sm = 6, 50, 3, 24, 16, 20, 0.3
+    q, kv, dout, pos, idx = _mla_bwd_case(T, S, H, D_qk, D_v, k, 95)
+    dq, dkv = oracle.sparse_mla_bwd(q, idx, pos, kv, D_v, sm, dout, lib=lib)
+    tq, tkv = torch_mla_bwd(q, kv, dout, pos, idx, D_v, sm)
+    assert np.max(np.abs(dq - tq)) <= 1e-12 * (1 + np.abs(tq).max()), "sparse MLA dq differs from torch autograd"
+    assert np.max(np.abs(dkv - tkv)) <= 1e-12 * (1 + np.abs(tkv).max()), "sparse MLA dkv differs from torch autograd"
+
+
+def _mla_loss_f64(qd, kvd, gd, pos, idx, D_v, sm):
+    """L = sum_{t,h} g[t,h] . out[t,h] of the forward's definition, float64 inputs."""
+    S = kvd.shape[0]
+    n = np.minimum(S, pos + 1)
+    L = 0.0
+    for t in range(qd.shape[0]):
+        sel = [int(s) for s in idx[t] if 0 <= s < n[t]]
+        if not sel:
+            continue
+        K = kvd[sel]
+        z = sm * qd[t] @ K.T
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        L += float(np.sum((p @ K[:, :D_v]) * gd[t]))
+    return L
+
+
+def check_mla_bwd_finite_difference(lib):
+    """Central differences of L = sum g . out along single coordinates of q and of listed kv rows."""
+    T, S, H, D_qk, D_v, k, sm = 4, 30, 2, 12, 8, 10, 0.4
+    q, kv, dout, pos, idx = _mla_bwd_case(T, S, H, D_qk, D_v, k, 96)
+    dq, dkv = oracle.sparse_mla_bwd(q, idx, pos, kv, D_v, sm, dout, lib=lib)
+    qd, kvd, gd = brute.bf16_decode(q), brute.bf16_decode(kv), brute.bf16_decode(dout)
+    h = 1e-6
+    g = block_rng(97, 0, 0)
+    for _ in range(12):
+        t, hh, d = int(g.integers(T)), int(g.integers(H)), int(g.integers(D_qk))
+        a, b = qd.copy(), qd.copy()
+        a[t, hh, d] += h
+        b[t, hh, d] -= h
+        fd = (_mla_loss_f64(a, kvd, gd, pos, idx, D_v, sm) - _mla_loss_f64(b, kvd, gd, pos, idx, D_v, sm)) / (2 * h)
+        assert abs(fd - dq[t, hh, d]) <= 1e-6 * (1 + abs(fd)), "dq vs central difference"
+    listed = sorted(set(int(s) for t in range(T) for s in idx[t] if 0 <= s <= pos[t]))
+    for _ in range(12):
+        s, d = listed[int(g.integers(len(listed)))], int(g.integers(D_qk))
+        a, b = kvd.copy(), kvd.copy()
+        a[s, d] += h
+        b[s, d] -= h
+        fd = (_mla_loss_f64(qd, a, gd, pos, idx, D_v, sm) - _mla_loss_f64(qd, b, gd, pos, idx, D_v, sm)) / (2 * h)
+        assert abs(fd - dkv[s, d]) <= 1e-6 * (1 + abs(fd)), "dkv vs central difference"
+
+
+def check_mla_bwd_dense_equivalence(lib):
+    """Every visible key listed once (k >= n_t): the gradients of dense causal attention, torch SDPA
+    autograd in float64 with K = kv and V = kv[:, :D_v] shared by every head."""
+    T = S = 24
+    H, D_qk, D_v, sm = 4, 20, 16, 1.0 / np.sqrt(20.0)
+    g = block_rng(98, 0, 0)
+    q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
+    dout = to_bf16_bits(g.standard_normal((T, H, D_v)).astype(np.float32))
+    idx = np.full((T, S), -1, np.int32)
+    for t in range(T):
+        idx[t, :t + 1] = g.permutation(t + 1)
+    dq, dkv = oracle.sparse_mla_bwd(q, idx, np.arange(T), kv, D_v, sm, dout, lib=lib)
+    Q = torch.from_numpy(brute.bf16_decode(q)).permute(1, 0, 2).contiguous().requires_grad_(True)   # [H,T,D]
+    KV = torch.from_numpy(brute.bf16_decode(kv)).requires_grad_(True)
+    out = torch.nn.functional.scaled_dot_product_attention(Q, KV[None].expand(H, S, D_qk),
+                                                           KV[None, :, :D_v].expand(H, S, D_v),
+                                                           is_causal=True, scale=sm)
+    (out * torch.from_numpy(brute.bf16_decode(dout)).permute(1, 0, 2)).sum().backward()
+    assert np.max(np.abs(dq - Q.grad.permute(1, 0, 2).numpy())) <= 1e-12, "dq differs from dense attention"
+    assert np.max(np.abs(dkv - KV.grad.numpy())) <= 1e-12, "dkv differs from dense attention"
+
+
+def check_mla_bwd_closed_forms(lib):
+    T, S, H, D_qk, D_v = 5, 40, 3, 16, 8
+    g = block_rng(99, 0, 0)
+    q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
+    kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
+    dout = to_bf16_bits(g.standard_normal((T, H, D_v)).astype(np.float32))
+    gd, qd = brute.bf16_decode(dout), brute.bf16_decode(q)
+    pos = np.full(T, S - 1)
+    # one valid entry: p = 1, ds = 0, so dq = 0 and the key gets sum_h g in its value columns
+    idx1 = np.array([[3 * t + 1, -1, S + 2] for t in range(T)], np.int32)
+    dq, dkv = oracle.sparse_mla_bwd(q, idx1, pos, kv, D_v, 0.2, dout, lib=lib)
+    assert np.all(dq == 0.0)
+    ref = np.zeros((S, D_qk))
+    for t in range(T):
+        ref[3 * t + 1, :D_v] += gd[t].sum(axis=0)
+    assert np.max(np.abs(dkv - ref)) <= 1e-12
+    # q = 0: uniform p over the m entries, the key columns of dkv get nothing (ds q = 0), each
+    # entry's value columns get sum_h g / m
+    m = 7
+    idx = np.stack([np.arange(m) * 5 + t for t in range(T)]).astype(np.int32)
+    dq0, dkv0 = oracle.sparse_mla_bwd(np.zeros_like(q), idx, pos, kv, D_v, 0.2, dout, lib=lib)
+    ref = np.zeros((S, D_qk))
+    for t in range(T):
+        for s in idx[t]:
+            ref[s, :D_v] += gd[t].sum(axis=0) / m
+    assert np.max(np.abs(dkv0 - ref)) <= 1e-12
+    # the softmax gradient sums to zero over a row's entries: summed over all keys, the columns past
+    # D_v vanish and the value columns add up to sum_{t,h} g (rows with a valid entry)
+    q_, kv_, dout_, pos_, idx_ = _mla_bwd_case(8, 60, 4, 24, 16, 24, 100)
+    dq_, dkv_ = oracle.sparse_mla_bwd(q_, idx_, pos_, kv_, 16, 0.3, dout_, lib=lib)
+    has = np.array([np.any((r >= 0) & (r <= p)) for r, p in zip(idx_, pos_)])
+    assert np.abs(dkv_[:, 16:].sum(axis=0)).max() <= 1e-10
+    assert np.abs(dkv_[:, :16].sum(axis=0) - brute.bf16_decode(dout_)[has].sum(axis=(0, 1))).max() <= 1e-10
+    # rows without a valid entry: dq = 0 and no contribution
+    none = np.full((T, 3), -1, np.int32)
+    dqn, dkvn = oracle.sparse_mla_bwd(q, none, pos, kv, D_v, 0.2, dout, lib=lib)
+    assert np.all(dqn == 0.0) and np.all(dkvn == 0.0)
+    del qd

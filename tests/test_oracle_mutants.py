@@ -69,6 +69,18 @@ MUTANTS = [
     ("kl_sparse_repeat_overwrites", "dlogits[t * ld_d + row[i]] += exp(log_pi) - p[i];",
      "dlogits[t * ld_d + row[i]] = exp(log_pi) - p[i];", [pins.check_kl_sparse_vs_torch,
                                                           pins.check_kl_sparse_closed_forms]),
+    ("mla_bwd_no_delta", "const double ds = p * (dp[i] - D);", "const double ds = p * dp[i];",
+     [pins.check_mla_bwd_vs_torch, pins.check_mla_bwd_finite_difference, pins.check_mla_bwd_closed_forms]),
+    ("mla_bwd_dq_unscaled", "dqh[d] += sm_scale * ds * (double)bf16_value(kr[d]);",
+     "dqh[d] += ds * (double)bf16_value(kr[d]);",
+     [pins.check_mla_bwd_vs_torch, pins.check_mla_bwd_finite_difference, pins.check_mla_bwd_dense_equivalence]),
+    ("mla_bwd_dv_without_p", "c[d] += p * (double)bf16_value(gh[d]);", "c[d] += (double)bf16_value(gh[d]);",
+     [pins.check_mla_bwd_vs_torch, pins.check_mla_bwd_closed_forms]),
+    ("mla_bwd_dk_from_key", "c[d] += sm_scale * ds * (double)bf16_value(qh[d]);",
+     "c[d] += sm_scale * ds * (double)bf16_value(kr[d]);",
+     [pins.check_mla_bwd_vs_torch, pins.check_mla_bwd_finite_difference]),
+    ("mla_bwd_repeat_once", "                dst[d] += c[d];", "                dst[d] = c[d];",
+     [pins.check_mla_bwd_vs_torch, pins.check_mla_bwd_closed_forms]),
     ("kl_sparse_all_keys", "p[i] += exp(z[i] - m) / l / (double)H;", "p[i] += exp(z[i] - m) / l / (double)(H + 1);",
      [pins.check_kl_sparse_vs_torch]),
 ]
