@@ -778,9 +778,10 @@ static int mla_bwd_row(const uint16_t *q, const int32_t *row, int64_t n, int32_t
             double dot = 0.0;
             for (int32_t d = 0; d < D_qk; ++d)
                 dot += (double)bf16_value(qh[d]) * (double)bf16_value(kr[d]);
-            z[i] = sm_scale * dot;
-            if (z[i] > m)
-                m = z[i];
+            const double zi = sm_scale * dot;
+            z[i] = zi;
+            if (zi > m)
+                m = zi;
         }
         if (m == -INFINITY)
             continue;
