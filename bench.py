@@ -83,9 +83,27 @@ def percentiles(ms):
             "p90": float(np.percentile(ms, 90))}
 
 
+def host_cpu():
+    """The host cores the oracle may use (this process's CPU affinity), nproc and the CPU model."""
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"threads": max(1, threads), "nproc": os.cpu_count(), "model": model}
+
+
 def cpu_baseline(wl, n_rows: int, threads: int):
     """The oracle (as it stands) on a uniform sample of query rows, scaled to the whole workload by the
-    exact per-stage work model."""
+    exact per-stage work model (all rows when n_rows >= T)."""
     import oracle
     from dsa_inputs import prefill_inputs
     rows = np.unique(np.linspace(0, wl.T - 1, min(n_rows, wl.T)).round().astype(np.int64))
@@ -106,10 +124,28 @@ def cpu_baseline(wl, n_rows: int, threads: int):
     sample = ("all %d query rows" % wl.T if len(rows) == wl.T else
               "%d query rows evenly spaced over the %d-token batch (full indexer, top-k and MLA per row), "
               "scaled per stage by visible / selected key counts" % (len(rows), wl.T))
+    cpu = host_cpu()
     return {
         "value": wl.T / est, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+        "mode": "full" if len(rows) == wl.T else "sampled",
         "sample": sample + "; %.1f s measured" % (t3 - t0), "sample_seconds": t3 - t0,
+        "nproc": cpu["nproc"], "cpu_model": cpu["model"],
     }
+
+
+def cpu_baseline_decode(inp, threads: int):
+    """The oracle (as it stands) over every sequence of a decode batch: scores of all visible keys
+    read through the block tables, top-k, attention; timed in full."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.decode(inp, nthreads=threads)
+    dt = time.perf_counter() - t0
+    cpu = host_cpu()
+    B = len(inp.seq_lens)
+    return {"value": B / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle", "mode": "full",
+            "sample": "all %d sequences (%d visible keys), one query each; %.1f s measured"
+                      % (B, int(inp.seq_lens.astype(np.int64).sum()), dt),
+            "sample_seconds": dt, "nproc": cpu["nproc"], "cpu_model": cpu["model"]}
 
 
 def put(a, dev):
@@ -229,8 +265,9 @@ def run_prefill(wl, args, dev):
     }
 
 
-def run_decode(wl, args, dev):
-    """Fused paged decode (dsa_decode_paged): one new token for each of the 64 sequences."""
+def run_decode(wl, args, dev, cpu_threads: int = 0):
+    """Fused paged decode (dsa_decode_paged): one new token for each of the 64 sequences.  A second,
+    profiled pass brackets each kernel of the call with stage events for its own achieved GB/s."""
     import torch
     import dsa_lightning_indexer_02_amd as dsa
     from dsa_inputs import decode_inputs
@@ -243,7 +280,6 @@ def run_decode(wl, args, dev):
     q = put(inp.q, dev).view(torch.bfloat16)
     lens = inp.seq_lens.astype(np.int64)
     max_len = int(lens.max())
-    del inp
     B = len(lens)
     dims = dsa.make_dims(wl.H_I, wl.D_I, wl.H, wl.D_qk, wl.D_v, wl.topk, wl.sm_scale)
     ws = torch.empty(dsa.decode_workspace_size(dims, B, max_len), dtype=torch.uint8, device=dev)
@@ -266,8 +302,46 @@ def run_decode(wl, args, dev):
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    # profiled pass: an event before the call and one after each of its kernels
+    nk = 8
+    prof = []
+    names = []
+    for _ in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        evp = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
+        evp[0].record(stream)
+        dsa.dsa_profile_begin(evp[1:])
+        step()
+        names = dsa.dsa_profile_end()
+        prof.append(evp[:len(names) + 1])
+    torch.cuda.synchronize()
+    kms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(names))] for e in prof]).mean(axis=0)
     n = lens
     sel = np.minimum(n, wl.topk)
+    nsplit = max(1, min(-(-256 // B), wl.topk // 64))
+    G = -(-max_len // 32768)
+    # each kernel's own reads and writes (the logits and split partials included: they are this
+    # design's intermediates, so the fused roofline below leaves them out)
+    kbytes = {
+        "indexer_decode_kernel": float(n.sum() * (wl.D_I + 4) + B * wl.H_I * (wl.D_I + 8)
+                                       + ((n + 63) // 64).sum() * 4 + 4 * n.sum()),
+        "topk_chunk_kernel<whole row>": float(4 * n.sum() + 4 * B * wl.topk),
+        # rows over 32768 keys: per-chunk candidates (key + index) written, then merged
+        "topk_chunk_kernel<chunk>": float(4 * n.sum() + B * G * wl.topk * 8),
+        "topk_merge_kernel": float(B * G * wl.topk * 8 + 4 * B * wl.topk),
+        "sparse_mla_kernel": float(sel.sum() * wl.D_qk * 2 + B * wl.H * wl.D_qk * 2 + B * wl.topk * 4
+                                   + B * nsplit * wl.H * (wl.D_v + 1) * 4),
+        "mla_combine_kernel": float(B * nsplit * wl.H * (wl.D_v + 1) * 4 + B * wl.H * (wl.D_v * 2 + 4)),
+    }
+    kernels = []
+    for name, t in zip(names, kms):
+        rec = {"kernel": name, "ms": float(t)}
+        if name in kbytes:
+            rec["bytes"] = kbytes[name]
+            rec["achieved_gbs"] = rec["bytes"] / (t / 1e3) / 1e9
+            rec["frac"] = rec["achieved_gbs"] * 1e9 / PEAK_HBM
+        kernels.append(rec)
     # HBM bytes any decode must move: the FP8 keys and scales of every visible position, the latent
     # rows of the selected entries, queries, head weights and outputs (the logits kept between the
     # indexer and the top-k, and the split-K partials, are this design's own and are not counted)
@@ -278,9 +352,12 @@ def run_decode(wl, args, dev):
             "achieved": alg / (med / 1e3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s", "traffic": None,
             "algorithmic_bytes_per_launch": alg, "avg_launch_ms": float(ms.mean())}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    cpu = cpu_baseline_decode(inp, cpu_threads) if cpu_threads > 0 else None
+    del inp
     return {
         "value": B / (med / 1e3), "ms_per_step": med, "step_ms_events": percentiles(ms), "roofline": roof,
-        "stages": None, "fused_ms_per_step": med, "mall_flush": bool(args.flush_mall),
+        "stages": None, "kernels": kernels, "fused_ms_per_step": med, "mall_flush": bool(args.flush_mall),
+        "cpu_baseline": cpu,
         "config": {"workload": wl.name, "B": B, "seq_len_min": int(lens.min()), "seq_len_max": max_len,
                    "seq_len_mean": float(lens.mean()), "topk": wl.topk, "H_I": wl.H_I, "D_I": wl.D_I, "H": wl.H,
                    "D_qk": wl.D_qk, "D_v": wl.D_v, "block_size": wl.block_size, "parallelism": "single GPU"},
@@ -540,12 +617,17 @@ def run_one(name, args, dev, with_cpu: bool):
                 "config": res["config"], "roofline": res["roofline"], "stages": res["stages"],
                 "step_ms_events": res["step_ms_events"], "fused_ms_per_step": None, "cpu_baseline": None}
     wl = get(name)
-    res = run_decode(wl, args, dev) if wl.kind == "decode" else run_prefill(wl, args, dev)
-    cpu = None
-    if with_cpu and wl.kind == "prefill":
-        print("cpu baseline (oracle)", file=sys.stderr, flush=True)
-        threads = max(1, min(16, os.cpu_count() or 1))
-        cpu = cpu_baseline(wl, args.cpu_rows, threads)
+    threads = host_cpu()["threads"]
+    if wl.kind == "decode":
+        res = run_decode(wl, args, dev, cpu_threads=threads if with_cpu else 0)
+        cpu = res.get("cpu_baseline")
+    else:
+        res = run_prefill(wl, args, dev)
+        cpu = None
+        if with_cpu:
+            print("cpu baseline (oracle)", file=sys.stderr, flush=True)
+            rows = args.cpu_rows if name == HEADLINE else (128 if name == "chunked_131k" else wl.T)
+            cpu = cpu_baseline(wl, rows, threads)
     line = {
         "metric": METRIC if name == HEADLINE else "query tokens/s (%s)" % name,
         "value": res["value"],
@@ -568,7 +650,15 @@ def run_one(name, args, dev, with_cpu: bool):
     }
     if "mall_flush" in res:
         line["mall_flush"] = res["mall_flush"]
+    if res.get("kernels"):
+        line["kernels"] = res["kernels"]
     return line
+
+
+def summary(line):
+    """The fields of another workload's line that the headline line carries beside its own."""
+    keep = ("value", "unit", "ms_per_step", "roofline", "stages", "kernels", "cpu_baseline", "config", "mall_flush")
+    return {k: line[k] for k in keep if k in line}
 
 
 def main():
@@ -581,6 +671,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1536)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-fused", action="store_true")
+    ap.add_argument("--skip-other-workloads", action="store_true",
+                    help="headline run: leave out the decode_64 and chunked_131k summaries")
     ap.add_argument("--flush-mall", action="store_true", help="decode: overwrite 512 MiB between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy 1 GiB device-to-device (counter scale reference)")
@@ -600,7 +692,15 @@ def main():
             print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return
-    print(json.dumps(run_one(args.workload, args, dev, with_cpu=not args.skip_cpu_baseline)))
+    line = run_one(args.workload, args, dev, with_cpu=not args.skip_cpu_baseline)
+    if args.workload == HEADLINE and not args.skip_other_workloads:
+        # the decode and chunked-prefill workloads, each with its own oracle baseline, beside the headline
+        other = {}
+        for name in ("decode_64", "chunked_131k"):
+            torch.cuda.empty_cache()
+            other[name] = summary(run_one(name, args, dev, with_cpu=not args.skip_cpu_baseline))
+        line["other_workloads"] = other
+    print(json.dumps(line))
 
 
 if __name__ == "__main__":

@@ -18,7 +18,8 @@ STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPOR
                 3: "DSA_ERR_WORKSPACE_TOO_SMALL", 4: "DSA_ERR_HIP"}
 
 EXPORTS = [
-    "dsa_status_string", "dsa_last_error", "dsa_abi_version", "dsa_indexer_logits",
+    "dsa_status_string", "dsa_last_error", "dsa_abi_version", "dsa_profile_begin", "dsa_profile_end",
+    "dsa_profile_kernel_name", "dsa_indexer_logits",
     "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd",
     "dsa_prefill_workspace_size", "dsa_prefill_paged", "dsa_decode_workspace_size", "dsa_decode_paged",
     "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0", "dsa_indexer_logits_ue8m0",
@@ -67,6 +68,12 @@ def load(path: str = LIB_PATH):
     lib.dsa_last_error.restype = ctypes.c_char_p
     lib.dsa_abi_version.argtypes = []
     lib.dsa_abi_version.restype = ctypes.c_int
+    lib.dsa_profile_begin.argtypes = [_p, _i32]
+    lib.dsa_profile_begin.restype = ctypes.c_int
+    lib.dsa_profile_end.argtypes = []
+    lib.dsa_profile_end.restype = _i32
+    lib.dsa_profile_kernel_name.argtypes = [_i32]
+    lib.dsa_profile_kernel_name.restype = ctypes.c_char_p
     lib.dsa_indexer_logits.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i64, _p]
     lib.dsa_topk_workspace_size.argtypes = [_i64, _i64, _i32]
     lib.dsa_topk_workspace_size.restype = _sz

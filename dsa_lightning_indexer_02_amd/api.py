@@ -46,6 +46,35 @@ def ld_for(S: int) -> int:
 
 
 # ------------------------------------------------------------------------------------------------
+_profile_handles = None  # the event-handle array the library records into (kept alive while active)
+
+
+def dsa_profile_begin(events) -> None:
+    """Start stage timing on this thread: the kernels of the following dsa_* calls record
+    ``events`` (torch.cuda.Event(enable_timing=True) objects) in launch order, one after each kernel."""
+    global _profile_handles
+    lib = load()
+    handles = []
+    for ev in events:
+        if not ev.cuda_event:       # torch creates the HIP event at its first record
+            ev.record()
+        handles.append(ev.cuda_event)
+    _profile_handles = (ctypes.c_void_p * len(handles))(*handles)
+    check("dsa_profile_begin", lib.dsa_profile_begin(ctypes.cast(_profile_handles, ctypes.c_void_p), len(handles)))
+
+
+def dsa_profile_end():
+    """Stop stage timing; returns the kernel names behind the events recorded, in order."""
+    lib = load()
+    n = lib.dsa_profile_end()
+    return [lib.dsa_profile_kernel_name(i).decode() for i in range(n)]
+
+
+def dsa_profile_kernel_name(i: int) -> str:
+    return load().dsa_profile_kernel_name(i).decode()
+
+
+# ------------------------------------------------------------------------------------------------
 def dsa_indexer_logits(q8, q_scale, w, k8, k_scale, q_start: int = 0, logits=None) -> torch.Tensor:
     """Index scores into ``logits`` [T, ld >= S] float32 (entries past each row's causal range untouched)."""
     lib = load()
@@ -181,6 +210,17 @@ def dsa_decode_paged(cache: PagedKV, max_seq_len: int, dims: Dims, q8, q_scale, 
         _opt(out_f32), _opt(lse), _opt(idx), ws.data_ptr(), ws.numel(), _stream(q8))
     check("dsa_decode_paged", status)
     return out, out_f32, lse, idx
+
+
+def decode_scores(workspace: torch.Tensor, B: int, max_seq_len: int) -> torch.Tensor:
+    """The index scores a completed dsa_decode_paged call left at the start of its workspace:
+    fp32 [B, ld] with ld = ld_for(max_seq_len); entries s < seq_lens[b] of row b are the scores
+    the top-k selected from (the layout include/dsa.h documents for the decode workspace)."""
+    ld = ld_for(max_seq_len)
+    nbytes = B * ld * 4
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace smaller than the %d-byte score prefix" % nbytes)
+    return workspace.view(torch.uint8).reshape(-1)[:nbytes].view(torch.float32).view(B, ld)
 
 
 # ------------------------------------------------------------------------------------------------

@@ -165,6 +165,30 @@ const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
 int dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
+dsa_status_t dsa_profile_begin(hipEvent_t* events, int32_t capacity) {
+  REQUIRE(events != nullptr && capacity >= 1, DSA_ERR_INVALID_ARGUMENT, "events must be non-null, capacity >= 1");
+  dsa::ProfileState& ps = dsa::profile_state();
+  ps.events = events;
+  ps.capacity = capacity;
+  ps.count = 0;
+  ps.names.clear();
+  return ok();
+}
+
+int32_t dsa_profile_end(void) {
+  dsa::ProfileState& ps = dsa::profile_state();
+  const int32_t n = ps.events ? ps.count : 0;
+  ps.events = nullptr;
+  ps.capacity = 0;
+  return n;
+}
+
+const char* dsa_profile_kernel_name(int32_t i) {
+  const dsa::ProfileState& ps = dsa::profile_state();
+  if (i < 0 || i >= (int32_t)ps.names.size()) return "";
+  return ps.names[i];
+}
+
 dsa_status_t dsa_indexer_logits(const uint8_t* q8, const float* q_scale, const float* w, const uint8_t* k8,
                                 const float* k_scale, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
                                 int64_t q_start, float* logits, int64_t ld_logits, hipStream_t stream) {
@@ -183,7 +207,7 @@ dsa_status_t dsa_indexer_logits(const uint8_t* q8, const float* q_scale, const f
   REQUIRE_PTR(k8);
   REQUIRE_PTR(k_scale);
   REQUIRE_PTR(logits);
-  return hip_status(dsa::launch_indexer_prefill(q8, q_scale, w, k8, k_scale, nullptr, 0, T, S, H_I, D_I,
+  return hip_status(dsa::launch_indexer_prefill(q8, q_scale, w, k8, k_scale, nullptr, 0, 0, T, S, H_I, D_I,
                                                 q_start, logits, ld_logits, stream),
                     "indexer launch");
 }
@@ -206,7 +230,7 @@ dsa_status_t dsa_indexer_logits_ue8m0(const uint8_t* q8, const uint8_t* q_exp, c
   REQUIRE_PTR(k8);
   REQUIRE_PTR(k_exp);
   REQUIRE_PTR(logits);
-  return hip_status(dsa::launch_indexer_prefill(q8, nullptr, w, k8, nullptr, nullptr, 0, T, S, H_I, D_I, q_start,
+  return hip_status(dsa::launch_indexer_prefill(q8, nullptr, w, k8, nullptr, nullptr, 0, 0, T, S, H_I, D_I, q_start,
                                                 logits, ld_logits, stream, q_exp, k_exp),
                     "indexer launch");
 }
@@ -316,8 +340,9 @@ dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t* c, int32_t seq, const ds
   const int32_t* table = c->block_table + (int64_t)seq * c->max_blocks_per_seq;
   const int shift = block_shift_of(c->block_size);
 
-  hipError_t e = dsa::launch_indexer_prefill(q8, q_scale, w, c->k8, c->k_scale, table, shift, T, S, d->H_I,
-                                             d->D_I, q_start, logits, L.ld, stream);
+  dsa::trace_call("dsa_prefill_paged", workspace_bytes, L.total);
+  hipError_t e = dsa::launch_indexer_prefill(q8, q_scale, w, c->k8, c->k_scale, table, shift, c->num_blocks, T, S,
+                                             d->H_I, d->D_I, q_start, logits, L.ld, stream);
   if (e != hipSuccess) return hip_status(e, "indexer launch");
   e = dsa::launch_topk(logits, L.ld, T, S, q_start, nullptr, d->topk, idx, ws + L.topk, stream);
   if (e != hipSuccess) return hip_status(e, "top-k launch");
@@ -328,6 +353,7 @@ dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t* c, int32_t seq, const ds
   a.table = table;
   a.max_blocks = c->max_blocks_per_seq;
   a.block_shift = shift;
+  a.num_blocks = c->num_blocks;
   a.per_row_table = 0;
   a.R = T;
   a.S = S;
@@ -356,7 +382,8 @@ dsa_status_t dsa_decode_paged(const dsa_paged_cache_t* c, int32_t B, int64_t max
   dsa_status_t s = check_dims(d);
   if (s != DSA_OK) return s;
   REQUIRE(B >= 0 && max_seq_len >= 0, DSA_ERR_INVALID_ARGUMENT, "negative B or max_seq_len");
-  REQUIRE(B <= 16384, DSA_ERR_UNSUPPORTED, "B=%d sequences above 16384 per decode call", B);
+  REQUIRE(B <= dsa::kDecodeMaxSeqs, DSA_ERR_UNSUPPORTED, "B=%d sequences above %d per decode call", B,
+          dsa::kDecodeMaxSeqs);
   if (B == 0) return ok();
   REQUIRE(max_seq_len >= 1, DSA_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 1");
   s = check_cache(c, max_seq_len, B);
@@ -382,9 +409,10 @@ dsa_status_t dsa_decode_paged(const dsa_paged_cache_t* c, int32_t B, int64_t max
   int32_t* idx = indices_out ? indices_out : reinterpret_cast<int32_t*>(ws + L.indices);
   const int shift = block_shift_of(c->block_size);
 
+  dsa::trace_call("dsa_decode_paged", workspace_bytes, L.total);
   hipError_t e = dsa::launch_indexer_decode(q8, q_scale, w, c->k8, c->k_scale, c->block_table,
-                                            c->max_blocks_per_seq, shift, c->seq_lens, B, max_seq_len, d->H_I,
-                                            d->D_I, logits, L.ld, stream);
+                                            c->max_blocks_per_seq, shift, c->num_blocks, c->seq_lens, B,
+                                            max_seq_len, d->H_I, d->D_I, logits, L.ld, stream);
   if (e != hipSuccess) return hip_status(e, "decode indexer launch");
   e = dsa::launch_topk(logits, L.ld, B, max_seq_len, 0, c->seq_lens, d->topk, idx, ws + L.topk, stream);
   if (e != hipSuccess) return hip_status(e, "top-k launch");
@@ -395,6 +423,7 @@ dsa_status_t dsa_decode_paged(const dsa_paged_cache_t* c, int32_t B, int64_t max
   a.table = c->block_table;
   a.max_blocks = c->max_blocks_per_seq;
   a.block_shift = shift;
+  a.num_blocks = c->num_blocks;
   a.per_row_table = 1;
   a.seq_lens = c->seq_lens;
   a.R = B;

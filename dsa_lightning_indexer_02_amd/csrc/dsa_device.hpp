@@ -79,14 +79,22 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Physical block of a block-table entry: ids outside [0, num_blocks) (a caller error: the
+// readers' precondition is that every entry covering a visible position lies in the pool) are
+// redirected to block 0, so a bad table gives unspecified scores instead of an out-of-bounds read.
+__device__ __forceinline__ int64_t safe_block(int32_t id, int64_t num_blocks) {
+  return (uint32_t)id < (uint64_t)num_blocks ? (int64_t)id : 0;
+}
+
 // Physical row of logical position s in one sequence's paged storage.  A null table is
 // the identity (contiguous storage).
 struct RowMap {
   const int32_t* table;
   int32_t block_shift;  // log2(block size)
+  int64_t num_blocks;   // pool size in blocks (table entries are clamped into it)
   __device__ __forceinline__ int64_t operator()(int64_t s) const {
     if (!table) return s;
-    int64_t blk = table[s >> block_shift];
+    const int64_t blk = safe_block(table[s >> block_shift], num_blocks);
     return (blk << block_shift) | (s & ((1 << block_shift) - 1));
   }
 };

@@ -8,6 +8,7 @@
 #include <algorithm>
 
 #include "dsa_device.hpp"
+#include "host_launch.hpp"
 
 namespace dsa {
 
@@ -18,13 +19,17 @@ size_t indexer_prefill_smem(int32_t H_I, bool e8);
 // dimension, which gfx950 caps at 65536 workgroups.
 int64_t indexer_prefill_max_rows();
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
-                                  const float* ks, const int32_t* table, int32_t block_shift, int64_t T,
+                                  const float* ks, const int32_t* table, int32_t block_shift,
+                                  int64_t num_blocks, int64_t T,
                                   int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, float* logits,
                                   int64_t ld, hipStream_t stream, const uint8_t* q_exp = nullptr,
                                   const uint8_t* k_exp = nullptr);
+// Sequences per decode call: the prefix table of per-sequence key groups sits in LDS.
+constexpr int32_t kDecodeMaxSeqs = 12288;
 hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
                                  const float* ks, const int32_t* table, int64_t max_blocks,
-                                 int32_t block_shift, const int32_t* seq_lens, int32_t B, int64_t max_len,
+                                 int32_t block_shift, int64_t num_blocks, const int32_t* seq_lens, int32_t B,
+                                 int64_t max_len,
                                  int32_t H_I, int32_t D_I, float* logits, int64_t ld, hipStream_t stream);
 
 // ---- FP8 quantization and paged append
@@ -70,6 +75,7 @@ struct MlaArgs {
   const int32_t* table;
   int64_t max_blocks;
   int32_t block_shift;
+  int64_t num_blocks;      // pool size in blocks (paged case)
   int32_t per_row_table;   // decode: row r uses table + r * max_blocks
   const int32_t* seq_lens; // decode: visible keys per row; null for prefill
   int64_t R;               // query rows

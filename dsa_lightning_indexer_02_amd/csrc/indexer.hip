@@ -196,7 +196,6 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
 // ---------------------------------------------------------------------------------------
 constexpr int IDX_DECODE_WAVES = 4;
 constexpr int IDX_DECODE_THREADS = IDX_DECODE_WAVES * WAVE;
-constexpr int IDX_DECODE_MAX_B = 16384;  // sequences per call (LDS prefix table)
 #ifndef IDX_DECODE_DEPTH
 #define IDX_DECODE_DEPTH 3                 // 64-key groups in flight per wave
 #endif
@@ -223,7 +222,7 @@ template <int NHT>
 __global__ __launch_bounds__(IDX_DECODE_THREADS, 2) void indexer_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int32_t* __restrict__ table,
-    int64_t max_blocks, int32_t block_shift, const int32_t* __restrict__ seq_lens, int32_t B,
+    int64_t max_blocks, int32_t block_shift, int64_t num_blocks, const int32_t* __restrict__ seq_lens, int32_t B,
     int32_t H_I, int32_t D_I, int64_t max_len, float* __restrict__ logits, int64_t ld) {
   extern __shared__ __align__(16) uint8_t smem[];
   int64_t* gstart = reinterpret_cast<int64_t*>(smem);                      // [B + 1] group prefix
@@ -300,7 +299,7 @@ __global__ __launch_bounds__(IDX_DECODE_THREADS, 2) void indexer_decode_kernel(
       wbase = (f - gstart[lo]) * 64;
       wrow = wbase;
       if (table && block_shift >= 6)
-        wrow = ((int64_t)table[(int64_t)lo * max_blocks + (wbase >> block_shift)] << block_shift) |
+        wrow = (safe_block(table[(int64_t)lo * max_blocks + (wbase >> block_shift)], num_blocks) << block_shift) |
                (wbase & ((1 << block_shift) - 1));
     }
   };
@@ -353,9 +352,9 @@ __global__ __launch_bounds__(IDX_DECODE_THREADS, 2) void indexer_decode_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t s = min(gr.base + q * 16 + j16, (int64_t)gr.n - 1);
-        row[q] = ((int64_t)tb[s >> block_shift] << block_shift) | (s & ((1 << block_shift) - 1));
+        row[q] = (safe_block(tb[s >> block_shift], num_blocks) << block_shift) | (s & ((1 << block_shift) - 1));
       }
-      rme = ((int64_t)tb[sme >> block_shift] << block_shift) | (sme & ((1 << block_shift) - 1));
+      rme = (safe_block(tb[sme >> block_shift], num_blocks) << block_shift) | (sme & ((1 << block_shift) - 1));
     }
     // Every lane loads, so no per-lane branch splits the group's loads: lanes whose k-range lies
     // past D_I re-read the row's last 32 bytes (finite codes of the same key), which meet zero
@@ -444,7 +443,7 @@ int64_t indexer_prefill_max_rows() { return (int64_t)IDX_ROWS * 65536; }
 
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
                                   const uint8_t* k8, const float* ks, const int32_t* table,
-                                  int32_t block_shift, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
+                                  int32_t block_shift, int64_t num_blocks, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
                                   int64_t q_start, float* logits, int64_t ld, hipStream_t stream,
                                   const uint8_t* q_exp, const uint8_t* k_exp) {
   if (T <= 0) return hipSuccess;
@@ -465,42 +464,46 @@ hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const floa
   const size_t smem = indexer_prefill_smem(H_I, e8);
   auto kernel = e8 ? (H_I == 64 ? indexer_prefill_kernel<NK, 64, true> : indexer_prefill_kernel<NK, 0, true>)
                    : (H_I == 64 ? indexer_prefill_kernel<NK, 64, false> : indexer_prefill_kernel<NK, 0, false>);
-  static bool attr_set[2][2] = {{false, false}, {false, false}};
-  if (!attr_set[e8][H_I == 64]) {
-    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set[e8][H_I == 64] = true;
-  }
-  hipLaunchKernelGGL(kernel, grid, dim3(IDX_PREFILL_WAVES * WAVE), smem, stream, q8, qs, w, k8, ks,
-                     RowMap{table, block_shift}, T, S, H_I, D_I, q_start, logits, ld, key_chunk, q_exp, k_exp);
-  return hipGetLastError();
+  hipError_t e = set_max_dynamic_lds((const void*)kernel);
+  if (e != hipSuccess) return e;
+  return launch(e8 ? "indexer_prefill_kernel<e8m0>" : "indexer_prefill_kernel", kernel, grid,
+                dim3(IDX_PREFILL_WAVES * WAVE), smem, stream, q8, qs, w, k8, ks, RowMap{table, block_shift, num_blocks},
+                T, S, H_I, D_I, q_start, logits, ld, key_chunk, q_exp, k_exp);
 }
+
+// Dynamic LDS of the decode indexer: the group prefix [B + 1] i64 and the visible lengths [B] i32.
+static size_t indexer_decode_smem(int32_t B) { return (size_t)(B + 1) * 8 + (size_t)B * 4; }
+static_assert((kDecodeMaxSeqs + 1) * 8 + kDecodeMaxSeqs * 4 + 64 <= 160 * 1024,
+              "the decode prefix table of the largest batch fits gfx950's LDS");
 
 hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float* w,
                                  const uint8_t* k8, const float* ks, const int32_t* table,
-                                 int64_t max_blocks, int32_t block_shift, const int32_t* seq_lens,
-                                 int32_t B, int64_t max_len, int32_t H_I, int32_t D_I, float* logits,
-                                 int64_t ld, hipStream_t stream) {
+                                 int64_t max_blocks, int32_t block_shift, int64_t num_blocks,
+                                 const int32_t* seq_lens, int32_t B, int64_t max_len, int32_t H_I, int32_t D_I,
+                                 float* logits, int64_t ld, hipStream_t stream) {
   if (B <= 0) return hipSuccess;
-  if (B > IDX_DECODE_MAX_B) return hipErrorInvalidValue;
+  if (B > kDecodeMaxSeqs) return hipErrorInvalidValue;
   const int nht = (H_I + 15) / 16;
   auto kernel = nht <= 1 ? indexer_decode_kernel<1> : nht <= 2 ? indexer_decode_kernel<2> : indexer_decode_kernel<4>;
-  const size_t smem = (size_t)(B + 1) * 8 + (size_t)B * 4;
-  // a grid of exactly the resident workgroups: the waves split the work evenly among themselves
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  const size_t smem = indexer_decode_smem(B);
+  hipError_t e = set_max_dynamic_lds((const void*)kernel);
   if (e != hipSuccess) return e;
-  int ncu = 0, per_cu = 0;
-  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  // a grid of exactly the resident workgroups: the waves split the work evenly among themselves.
+  // Residency = min(the register / static-LDS bound, LDS per CU / this call's dynamic LDS), from
+  // values cached once per device.
+  DeviceProps props;
+  e = device_props(&props);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, IDX_DECODE_THREADS, smem);
+  int per_cu = 0;
+  e = occupancy_without_lds((const void*)kernel, IDX_DECODE_THREADS, &per_cu);
   if (e != hipSuccess) return e;
+  per_cu = std::max(1, std::min<int>(per_cu, (int)(props.lds_per_cu / (smem + 64))));
   const int64_t groups_max = (int64_t)B * ((max_len + 63) / 64);
   const int64_t need = (groups_max + IDX_DECODE_WAVES - 1) / IDX_DECODE_WAVES;
-  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>((int64_t)std::max(per_cu, 1) * ncu, need));
-  hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(IDX_DECODE_THREADS), smem, stream, q8, qs, w, k8, ks,
-                     table, max_blocks, block_shift, seq_lens, B, H_I, D_I, max_len, logits, ld);
-  return hipGetLastError();
+  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>((int64_t)per_cu * props.cu_count, need));
+  return launch("indexer_decode_kernel", kernel, dim3((unsigned)nwg), dim3(IDX_DECODE_THREADS), smem, stream, q8,
+                qs, w, k8, ks, table, max_blocks, block_shift, num_blocks, seq_lens, B, H_I, D_I, max_len, logits,
+                ld);
 }
 
 }  // namespace dsa

@@ -907,17 +907,11 @@ static hipError_t launch_kl(const uint16_t* q, const uint16_t* kv, int64_t T, in
                             float sm_scale, int64_t q_start, const float* logits, int64_t ld, float* dlogits,
                             float* loss, hipStream_t stream) {
   using C = KlCfg<NKS>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&indexer_kl_kernel<NKS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::SMEM);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&indexer_kl_kernel<NKS>));
+  if (e != hipSuccess) return e;
   const int64_t grid = (T + KL_TOK - 1) / KL_TOK;
-  hipLaunchKernelGGL(indexer_kl_kernel<NKS>, dim3((unsigned)grid), dim3(KL_THREADS), C::SMEM, stream, q, kv, T, S,
-                     H, D, sm_scale * KL_LOG2E, q_start, logits, ld, dlogits, loss);
-  return hipGetLastError();
+  return launch("indexer_kl_kernel", indexer_kl_kernel<NKS>, dim3((unsigned)grid), dim3(KL_THREADS), C::SMEM, stream,
+                q, kv, T, S, H, D, sm_scale * KL_LOG2E, q_start, logits, ld, dlogits, loss);
 }
 
 hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t T, int64_t S, int32_t H, int32_t D,
@@ -946,16 +940,10 @@ static hipError_t launch_kl_sparse(const uint16_t* q, const uint16_t* kv, const 
                                    int64_t q_start, const float* logits, int64_t ld, float* dlogits, float* loss,
                                    hipStream_t stream) {
   constexpr size_t smem = kls_smem_bytes<NKS>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&indexer_kl_sparse_kernel<NKS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(indexer_kl_sparse_kernel<NKS>, dim3((unsigned)T), dim3(KLS_THREADS), smem, stream, q, kv, idx,
-                     k, lse, T, S, H, D, sm_scale * KL_LOG2E, q_start, logits, ld, dlogits, loss);
-  return hipGetLastError();
+  hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&indexer_kl_sparse_kernel<NKS>));
+  if (e != hipSuccess) return e;
+  return launch("indexer_kl_sparse_kernel", indexer_kl_sparse_kernel<NKS>, dim3((unsigned)T), dim3(KLS_THREADS), smem,
+                stream, q, kv, idx, k, lse, T, S, H, D, sm_scale * KL_LOG2E, q_start, logits, ld, dlogits, loss);
 }
 
 bool indexer_kl_sparse_supported(int32_t H, int32_t D, int32_t k) {
@@ -1005,37 +993,30 @@ static hipError_t launch_bwd(const uint8_t* q8, const float* qs, const float* w,
                              float* dq, float* dw, float* dk, void* workspace, const int32_t* idx, int32_t k,
                              hipStream_t stream) {
   using C = BwCfg<DI>;
+  hipError_t e;
   if (idx) {  // dq / dw over the listed keys only
     const int hgroups = (H_I + BL_WAVES * 16 - 1) / (BL_WAVES * 16);
-    hipLaunchKernelGGL(indexer_bwd_q_listed_kernel<DI>, dim3((unsigned)T, (unsigned)hgroups), dim3(BL_WAVES * WAVE), 0, stream, q8, qs,
-                       w, k8, ks, T, S, H_I, q_start, idx, k, dI, ld, dq, dw);
+    e = launch("indexer_bwd_q_listed_kernel", indexer_bwd_q_listed_kernel<DI>, dim3((unsigned)T, (unsigned)hgroups),
+               dim3(BL_WAVES * WAVE), 0, stream, q8, qs, w, k8, ks, T, S, H_I, q_start, idx, k, dI, ld, dq, dw);
   } else {
     const int64_t qtiles = (T + BW_ROWS - 1) / BW_ROWS;
     const int hgroups = (H_I + BQ_WAVES * BQ_HPW - 1) / (BQ_WAVES * BQ_HPW);
-    hipLaunchKernelGGL(indexer_bwd_q_kernel<DI>, dim3((unsigned)qtiles, (unsigned)hgroups), dim3(BQ_WAVES * WAVE), 0,
-                       stream, q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw);
+    e = launch("indexer_bwd_q_kernel", indexer_bwd_q_kernel<DI>, dim3((unsigned)qtiles, (unsigned)hgroups),
+               dim3(BQ_WAVES * WAVE), 0, stream, q8, qs, w, k8, ks, T, S, H_I, q_start, dI, ld, dq, dw);
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&indexer_bwd_k_kernel<DI>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BK_SMEM);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  e = set_max_dynamic_lds(reinterpret_cast<const void*>(&indexer_bwd_k_kernel<DI>));
+  if (e != hipSuccess) return e;
   const int64_t qchunk = indexer_bwd_qchunk(T);
   const int32_t nqc = (int32_t)((T + qchunk - 1) / qchunk);
   const int64_t kgroups = (S + BK_WAVES * BK_KPW - 1) / (BK_WAVES * BK_KPW);
   float* part = reinterpret_cast<float*>(workspace);
-  hipLaunchKernelGGL(indexer_bwd_k_kernel<DI>, dim3((unsigned)kgroups, (unsigned)nqc), dim3(BK_WAVES * WAVE),
-                     C::BK_SMEM, stream, q8, qs, w, k8, T, S, H_I, q_start, dI, ld, qchunk, part);
-  e = hipGetLastError();
+  e = launch("indexer_bwd_k_kernel", indexer_bwd_k_kernel<DI>, dim3((unsigned)kgroups, (unsigned)nqc),
+             dim3(BK_WAVES * WAVE), C::BK_SMEM, stream, q8, qs, w, k8, T, S, H_I, q_start, dI, ld, qchunk, part);
   if (e != hipSuccess) return e;
   const int64_t n4 = S * DI / 4;
-  hipLaunchKernelGGL(indexer_bwd_k_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, part, S,
-                     DI, T, q_start, qchunk, nqc, dk);
-  return hipGetLastError();
+  return launch("indexer_bwd_k_reduce_kernel", indexer_bwd_k_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)),
+                dim3(256), 0, stream, part, S, DI, T, q_start, qchunk, nqc, dk);
 }
 
 hipError_t launch_indexer_bwd(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,

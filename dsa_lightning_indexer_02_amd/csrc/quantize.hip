@@ -141,12 +141,10 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t rows, int32_t D, uint
   const int64_t pieces = rows * lanes;
   const int64_t grid = (pieces + QZ_THREADS * QZ_PIECES - 1) / (QZ_THREADS * QZ_PIECES);
   if (exps)
-    hipLaunchKernelGGL(quantize_rows_kernel<true>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, x, rows, D,
-                       lanes, codes, scales, exps);
-  else
-    hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, x, rows, D,
-                       lanes, codes, scales, exps);
-  return hipGetLastError();
+    return launch("quantize_rows_kernel<ue8m0>", quantize_rows_kernel<true>, dim3((unsigned)grid), dim3(QZ_THREADS),
+                  0, stream, x, rows, D, lanes, codes, scales, exps);
+  return launch("quantize_rows_kernel", quantize_rows_kernel<false>, dim3((unsigned)grid), dim3(QZ_THREADS), 0,
+                stream, x, rows, D, lanes, codes, scales, exps);
 }
 
 hipError_t launch_append_paged(uint8_t* k8_pool, float* ks_pool, uint16_t* kv_pool, int64_t num_blocks,
@@ -155,10 +153,9 @@ hipError_t launch_append_paged(uint8_t* k8_pool, float* ks_pool, uint16_t* kv_po
                                int32_t D_qk, const uint16_t* k, const uint16_t* kv, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t grid = (n + QZ_THREADS / WAVE - 1) / (QZ_THREADS / WAVE);
-  hipLaunchKernelGGL(append_paged_kernel, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream, k8_pool, ks_pool,
-                     kv_pool, num_blocks, block_shift, table, max_blocks, B, seq_ids, positions, n, D_I, D_qk,
-                     qz_lanes(D_I), k, kv);
-  return hipGetLastError();
+  return launch("append_paged_kernel", append_paged_kernel, dim3((unsigned)grid), dim3(QZ_THREADS), 0, stream,
+                k8_pool, ks_pool, kv_pool, num_blocks, block_shift, table, max_blocks, B, seq_ids, positions, n, D_I,
+                D_qk, qz_lanes(D_I), k, kv);
 }
 
 }  // namespace dsa

@@ -127,7 +127,7 @@ __device__ __forceinline__ void bf16x4_to_f16(const s16x4 raw, s16x8& dst, int h
 template <int DQK, int DV>
 __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ table, int64_t max_blocks, int32_t block_shift, int32_t per_row_table,
+    const int32_t* __restrict__ table, int64_t max_blocks, int32_t block_shift, int64_t num_blocks, int32_t per_row_table,
     const int32_t* __restrict__ seq_lens, int64_t S, int64_t q_start, int32_t H, int32_t k,
     float scale_log2, int32_t nsplit, int32_t keys_per_split, uint16_t* __restrict__ out,
     float* __restrict__ out_f32, float* __restrict__ lse, float* __restrict__ part_out,
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   const int i0 = sp * keys_per_split;
   const int i1 = min(k, i0 + keys_per_split);
   const int cnt = max(i1 - i0, 0);
-  const RowMap map{table ? (per_row_table ? table + r * max_blocks : table) : nullptr, block_shift};
+  const RowMap map{table ? (per_row_table ? table + r * max_blocks : table) : nullptr, block_shift, num_blocks};
 
   if (n <= 0) {  // nothing visible: out = 0, lse = -inf
     for (int p = tid; p < H * DV; p += MLA_THREADS) {
@@ -512,26 +512,17 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
   const int nsplit = a.nsplit;
   const int kps = (a.k + nsplit - 1) / nsplit;
   const size_t smem = mla_smem_bytes<DQK, DV>(kps);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<DQK, DV>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_max_dynamic_lds((const void*)sparse_mla_kernel<DQK, DV>);
+  if (e != hipSuccess) return e;
   const float scale_log2 = a.sm_scale * 1.4426950408889634f;
   dim3 grid((unsigned)a.R, (unsigned)nsplit);
-  hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), grid, dim3(MLA_THREADS), smem, stream, a.q, a.kv,
-                     a.idx, a.table, a.max_blocks, a.block_shift, a.per_row_table, a.seq_lens, a.S,
-                     a.q_start, a.H, a.k, scale_log2, nsplit, kps, a.out, a.out_f32, a.lse, a.part_out,
-                     a.part_lse);
-  hipError_t e = hipGetLastError();
+  e = launch("sparse_mla_kernel", sparse_mla_kernel<DQK, DV>, grid, dim3(MLA_THREADS), smem, stream, a.q, a.kv,
+             a.idx, a.table, a.max_blocks, a.block_shift, a.num_blocks, a.per_row_table, a.seq_lens, a.S, a.q_start,
+             a.H, a.k, scale_log2, nsplit, kps, a.out, a.out_f32, a.lse, a.part_out, a.part_lse);
   if (e != hipSuccess || nsplit == 1) return e;
   constexpr int HPB = COMBINE_THREADS / (DV / 4);
-  hipLaunchKernelGGL(mla_combine_kernel<DV>, dim3((unsigned)a.R, (unsigned)((a.H + HPB - 1) / HPB)),
-                     dim3(COMBINE_THREADS), 0, stream, a.part_out, a.part_lse, nsplit, a.H, a.out, a.out_f32,
-                     a.lse);
-  return hipGetLastError();
+  return launch("mla_combine_kernel", mla_combine_kernel<DV>, dim3((unsigned)a.R, (unsigned)((a.H + HPB - 1) / HPB)),
+                dim3(COMBINE_THREADS), 0, stream, a.part_out, a.part_lse, nsplit, a.H, a.out, a.out_f32, a.lse);
 }
 
 bool mla_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k) {

@@ -614,17 +614,16 @@ hipError_t launch_topk(const float* logits, int64_t ld, int64_t T, int64_t S, in
     ck = reinterpret_cast<uint32_t*>(workspace);
     ci = reinterpret_cast<int32_t*>(ck + (size_t)T * G * k);
   }
+  hipError_t e;
   if (G <= 1)
-    hipLaunchKernelGGL(topk_chunk_kernel<true>, dim3((unsigned)T, 1), dim3(TK_THREADS), 0, stream, logits, ld,
-                       T, S, q_start, seq_lens, k, indices, ck, ci, G);
+    e = launch("topk_chunk_kernel<whole row>", topk_chunk_kernel<true>, dim3((unsigned)T, 1), dim3(TK_THREADS), 0,
+               stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
   else
-    hipLaunchKernelGGL(topk_chunk_kernel<false>, dim3((unsigned)T, (unsigned)G), dim3(TK_THREADS), 0, stream,
-                       logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
-  hipError_t e = hipGetLastError();
+    e = launch("topk_chunk_kernel<chunk>", topk_chunk_kernel<false>, dim3((unsigned)T, (unsigned)G),
+               dim3(TK_THREADS), 0, stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
   if (e != hipSuccess || G <= 1) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, T, S, q_start,
-                     seq_lens, k, indices, ck, ci, G);
-  return hipGetLastError();
+  return launch("topk_merge_kernel", topk_merge_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, T, S,
+                q_start, seq_lens, k, indices, ck, ci, G);
 }
 
 }  // namespace dsa

@@ -25,6 +25,9 @@
  *    Launch failures return DSA_ERR_HIP.  Faults inside kernels surface at the caller's next
  *    synchronisation.  dsa_last_error() gives a thread-local message for the last failing call.
  *  - T == 0 (or B == 0) is a valid no-op.
+ *  - With the environment variable DSA_TRACE set (non-empty, not "0"), every kernel launch writes
+ *    one line to stderr (kernel, grid, block, dynamic LDS, stream), and the fused calls one line
+ *    with the workspace size given and used.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -51,6 +54,20 @@ const char *dsa_status_string(dsa_status_t s);
 /* Message of the last failing call on this host thread ("" if none). */
 const char *dsa_last_error(void);
 int dsa_abi_version(void);
+
+/*
+ * Stage timing, a profiling aid outside the method: after dsa_profile_begin(events, capacity),
+ * every kernel that a dsa_* call made on this host thread enqueues records events[i] (i = 0, 1,
+ * ... in launch order; caller-created hipEvent_t, timing enabled) on the call's stream right after
+ * the kernel, until capacity events are used or dsa_profile_end() is called, which stops the
+ * recording and returns the number recorded.  With an event recorded on the stream before the
+ * call, consecutive events bracket each kernel of a fused call.  dsa_profile_kernel_name(i)
+ * names the kernel behind events[i] of the last recording ("" out of range; the string is
+ * static).  begin returns DSA_ERR_INVALID_ARGUMENT for a NULL array or capacity < 1.
+ */
+dsa_status_t dsa_profile_begin(hipEvent_t *events, int32_t capacity);
+int32_t dsa_profile_end(void);
+const char *dsa_profile_kernel_name(int32_t i);
 
 /*
  * Lightning-indexer scores (summary page, "Method"; AMD article, "Lightning Indexer"):
@@ -110,6 +127,11 @@ dsa_status_t dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int
  *   kv [num_blocks][block_size][D_qk] bf16.
  * block_table [B][max_blocks_per_seq] i32; seq_lens [B] i32 (device; includes new tokens).
  * block_size must be a power of two (64 in the model deployment).
+ * Precondition of the readers (prefill, decode): every block_table entry that covers a visible
+ * position (s < q_start + T of the prefilled sequence; s < seq_lens[b] in decode) lies in
+ * [0, num_blocks); entries past them are never read.  The table lives in device memory, so the
+ * host cannot check it: an entry outside the pool is read as block 0 (no access leaves the
+ * pools) and the scores and outputs of the affected rows are then unspecified.
  */
 typedef struct {
   const uint8_t *k8;
@@ -133,7 +155,10 @@ typedef struct {
  * kernels as the three standalone calls.  q8/q_scale/w/q as in the standalone calls,
  * out [T][H][D_v] bf16, out_f32 (optional), lse [T][H] (optional), indices_out [T][topk]
  * (optional; written when non-NULL).  Workspace: dsa_prefill_workspace_size() bytes, 256-byte
- * aligned.  T <= 1,048,576 per call, as dsa_indexer_logits.
+ * aligned.  T <= 1,048,576 per call, as dsa_indexer_logits.  Once the call's stream work has
+ * completed, the first T * ld * 4 bytes of the workspace hold the index scores, fp32 [T][ld] with
+ * ld = (S + 3) / 4 * 4 and entries s < n_t written (the scores the top-k selected from); the rest
+ * of the workspace is private.
  */
 size_t dsa_prefill_workspace_size(const dsa_dims_t *d, int64_t T, int64_t S);
 dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t *c, int32_t seq, const dsa_dims_t *d, int64_t T,
@@ -147,7 +172,12 @@ dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t *c, int32_t seq, const ds
  * keys (max_seq_len >= every seq_lens[b], used for grid and workspace sizing).
  * q8 [B][H_I][D_I], q_scale [B][H_I], w [B][H_I], q [B][H][D_qk], out [B][H][D_v],
  * out_f32 / lse / indices_out optional as above.  Sparse MLA is split over index chunks and the
- * partial results are re-reduced in fp32.  B <= 16384 (DSA_ERR_UNSUPPORTED above).
+ * partial results are re-reduced in fp32.  B <= 12288 (the per-sequence key-group prefix table of
+ * the indexer sits in LDS; DSA_ERR_UNSUPPORTED above).
+ * Workspace layout visible to the caller: once the call's stream work has completed, the first
+ * B * ld * 4 bytes of the workspace hold the index scores, fp32 [B][ld] with
+ * ld = (max_seq_len + 3) / 4 * 4 and entries s < seq_lens[b] of row b written (the scores the
+ * top-k selected from; later entries are unspecified).  The rest of the workspace is private.
  */
 size_t dsa_decode_workspace_size(const dsa_dims_t *d, int32_t B, int64_t max_seq_len);
 dsa_status_t dsa_decode_paged(const dsa_paged_cache_t *c, int32_t B, int64_t max_seq_len,

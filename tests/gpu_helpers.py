@@ -88,6 +88,12 @@ class DecodeDev:
         self.max_len = int(inp.seq_lens.max())
 
     def run(self):
+        """(out, out_f32, lse, indices, scores): scores = the decode indexer's [B, ld] output, read from
+        the workspace prefix the decode call documents."""
         wl = self.inp.wl
-        return dsa.dsa_decode_paged(self.cache, self.max_len, dims_of(wl), self.q8, self.qs, self.w, self.q,
-                                    want_f32=True, want_indices=True)
+        B = self.q8.shape[0]
+        ws = torch.empty(dsa.decode_workspace_size(dims_of(wl), B, self.max_len), dtype=torch.uint8,
+                         device=self.q8.device)
+        res = dsa.dsa_decode_paged(self.cache, self.max_len, dims_of(wl), self.q8, self.qs, self.w, self.q,
+                                   want_f32=True, want_indices=True, workspace=ws)
+        return res + (dsa.decode_scores(ws, B, self.max_len),)

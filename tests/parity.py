@@ -1,10 +1,13 @@
 """Comparison rules between the HIP path and the oracle (the project's parity tolerances).
 
-Indexer: (i) |g - o| <= 1e-3 * A everywhere in the causal range, A = sum_j |w| qs ks sum_i |dec q8 * dec k8|
-         (the magnitude scale of the sum, A >= |o|); (ii) |g - o| / |o| <= 1e-3 where the relative error is
-         meaningful: |o| >= c * A with c = (oracle fp32 error bound + FP8 MFMA accumulation bound) / 1e-3,
-         i.e. ((D_I + H_I + 4) 2^-24 + 2^-14) / 1e-3.  Below that, the oracle's own rounding alone may exceed
-         1e-3 |o|.  The GPU error against the exact fp64 value is pinned separately to <= 2^-14 A.
+Indexer: on every causal entry, |g - o| <= 1e-3 |o| + beta A and |g - o| <= 1e-3 A, where
+         A = sum_j |w| qs ks sum_i |dec q8 * dec k8| (the magnitude scale of the sum, A >= |o|) and
+         beta(D_I, H_I) = c_mfma(D_I) + (D_I + H_I + 4) 2^-24: the oracle's first-order fp32 rounding bound
+         plus the gfx950 FP8 MFMA's accumulation allowance per dot product at that width (measured on
+         codes drawn like the workloads', re-checked by a GPU test every run; codes drawn otherwise use
+         the block-max form below).  The 1e-3 relative term dominates wherever |o| >= 1000 beta A; the
+         check reports that share.  The GPU error against the exact fp64 value is pinned separately to
+         <= (c_mfma(D_I) + (H_I + 3) 2^-24) A.
 Top-k:   the GPU selection run on the GPU's own logits must equal the oracle's selection on those
          same logits exactly (ties included); against the oracle's own logits the sets may differ
          only by swaps at the k-th boundary whose oracle scores lie within 1e-3 relative of the
@@ -46,31 +49,72 @@ def magnitude(q8, qs, w, k8, ks, rows_pos, S, chunk: int = 16) -> np.ndarray:
     return out
 
 
-MFMA_FP8_BOUND = 2.0 ** -14   # accumulation error allowance of the gfx950 FP8 MFMA, relative to A
+# Accumulation allowance of one gfx950 FP8 16x16x128 MFMA dot product at each indexer width D_I.
+# The MFMA does not accumulate in exact fp32, and its error follows the largest operands of each
+# 32-element block rather than the sum of |products| (test_gpu_parity.py::
+# test_fp8_mfma_accumulation_bound measures both on 3 x 1M dots and re-checks them every run):
+#  - MFMA_FP8_DOT: relative to the dot's sum of |products|, for codes drawn like the workloads'
+#    (per-row absmax-scaled N(0,1)); measured worst 2^-14.86, 2^-15.53, 2^-15.56, 2^-16.06 at
+#    D_I = 32, 64, 96, 128, allowance about 1.3-1.5x above;
+#  - MFMA_FP8_BLOCK: relative to sum over 32-element blocks of max|q| max|k|, for any codes (normal,
+#    cubed-normal and uniformly drawn codes); measured worst 2^-11.53, 2^-12.06, 2^-12.78, 2^-12.61,
+#    allowance about 1.4-1.7x above.
+MFMA_FP8_DOT = {32: 2.0 ** -14.5, 64: 2.0 ** -15, 96: 2.0 ** -15, 128: 2.0 ** -15.5}
+MFMA_FP8_BLOCK = {32: 2.0 ** -11, 64: 2.0 ** -11.5, 96: 2.0 ** -12, 128: 2.0 ** -12}
 
 
-def rel_threshold(D_I: int, H_I: int) -> float:
-    return ((D_I + H_I + 4) * 2.0 ** -24 + MFMA_FP8_BOUND) / IDX_REL
+def block_magnitude(q8, qs, w, k8, ks, rows_pos, S) -> np.ndarray:
+    """B[t, s] = sum_j |w| qs ks sum_b max_{i in b} |dec q8[t,j,i]| max_{i in b} |dec k8[s,i]| over the
+    32-element blocks b of the indexer width (the magnitude the MFMA's accumulation error follows);
+    NaN outside the causal range."""
+    tab = e4m3_abs_table()
+    D = k8.shape[1]
+    nb = D // 32
+    kb = (tab[k8] * np.abs(ks)[:, None]).reshape(-1, nb, 32).max(axis=2)             # [S, nb]
+    qb = (tab[q8] * np.abs(qs)[..., None]).reshape(q8.shape[0], q8.shape[1], nb, 32).max(axis=3)
+    out = np.einsum("th,thb,sb->ts", np.abs(w), qb, kb, optimize=True).astype(np.float32)
+    n = np.minimum(S, np.asarray(rows_pos) + 1)
+    out[np.arange(S)[None, :] >= n[:, None]] = np.nan
+    return out
 
 
-def check_indexer(g: np.ndarray, o: np.ndarray, A: np.ndarray, D_I: int, H_I: int, what: str = "indexer"):
+def indexer_beta(D_I: int, H_I: int) -> float:
+    """Absolute allowance of the indexer check relative to A (workload-like codes): MFMA accumulation
+    plus the oracle's first-order fp32 rounding bound."""
+    return MFMA_FP8_DOT[D_I] + (D_I + H_I + 4) * 2.0 ** -24
+
+
+def check_indexer(g: np.ndarray, o: np.ndarray, A: np.ndarray, D_I: int, H_I: int, what: str = "indexer",
+                  B: np.ndarray = None):
+    """Every causal entry within 1e-3 |o| + allowance, the allowance being indexer_beta A for
+    workload-like codes or, given the block magnitude B (any codes), MFMA_FP8_BLOCK B + the oracle's
+    rounding bound A.  Returns (worst |g - o| / bar, share of entries where 1e-3 |o| >= allowance)."""
     m = ~np.isnan(o)
     gm, om, Am = g[m].astype(np.float64), o[m].astype(np.float64), A[m].astype(np.float64)
     err = np.abs(gm - om)
     bad = err > IDX_ABS * Am
     assert not bad.any(), "%s: %d entries exceed 1e-3*A (worst %.3e of A)" % (
         what, bad.sum(), np.max(err / np.maximum(Am, 1e-30)))
-    big = np.abs(om) >= rel_threshold(D_I, H_I) * Am
-    rel = err[big] / np.abs(om[big])
-    assert rel.size == 0 or rel.max() <= IDX_REL, "%s: relative error %.3e" % (what, rel.max())
-    return float(np.max(err / np.maximum(Am, 1e-30))) if err.size else 0.0
+    if B is None:
+        allow = indexer_beta(D_I, H_I) * Am
+    else:
+        allow = MFMA_FP8_BLOCK[D_I] * B[m].astype(np.float64) + (D_I + H_I + 4) * 2.0 ** -24 * Am
+    tol = IDX_REL * np.abs(om) + allow
+    ratio = err / np.maximum(tol, 1e-300)
+    assert ratio.size == 0 or ratio.max() <= 1.0, \
+        "%s: %d entries exceed 1e-3|o| + allowance (worst %.3f of the bar)" % (what, (ratio > 1).sum(), ratio.max())
+    rel_share = float(np.mean(IDX_REL * np.abs(om) >= allow)) if om.size else 1.0
+    return (float(ratio.max()) if ratio.size else 0.0), rel_share
 
 
-def check_indexer_exact(g: np.ndarray, exact: np.ndarray, A: np.ndarray, what: str = "indexer vs exact"):
-    """GPU scores against the exact (fp64) value: within the FP8 MFMA accumulation bound plus fp32 epilogue."""
+def check_indexer_exact(g: np.ndarray, exact: np.ndarray, A: np.ndarray, D_I: int, H_I: int,
+                        what: str = "indexer vs exact"):
+    """GPU scores against the exact (fp64) value: within the FP8 MFMA accumulation allowance plus the
+    fp32 epilogue (H_I weighted additions, the weight and the key-scale products)."""
     m = ~np.isnan(exact)
     err = np.abs(g[m].astype(np.float64) - exact[m]) / np.maximum(A[m].astype(np.float64), 1e-30)
-    assert err.max() <= MFMA_FP8_BOUND + 2.0 ** -20, "%s: %.3e of A" % (what, err.max())
+    bound = MFMA_FP8_DOT[D_I] + (H_I + 3) * 2.0 ** -24
+    assert err.max() <= bound, "%s: %.3e of A (bound %.3e)" % (what, err.max(), bound)
     return float(err.max())
 
 

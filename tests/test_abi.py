@@ -118,9 +118,12 @@ def test_fused_argument_errors(lib):
              FAKE, need_d - 1, None) == WS_SMALL
     assert g(ctypes.byref(c2), 0, 131072, ctypes.byref(d), None, None, None, None, None, None, None, None,
              None, 0, None) == OK
-    assert g(ctypes.byref(c2), 16385, 131072, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+    # the decode batch cap follows the indexer's LDS prefix table (12288 sequences)
+    assert g(ctypes.byref(c2), 12289, 131072, ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
              FAKE, 1 << 40, None) == UNSUPPORTED
-    assert "16384" in _err(lib)
+    assert "12288" in _err(lib)
+    hdr = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    assert "B <= 12288" in hdr
 
 
 def test_quantize_and_append_argument_errors(lib):
@@ -200,3 +203,15 @@ def test_kl_sparse_argument_errors(lib):
     assert "lse" in _err(lib)
     assert f(FAKE, FAKE, None, 64, FAKE, 4, 8, 128, 576, sm, 0, FAKE, 8, FAKE, FAKE, None) == INVALID         # indices
     assert f(None, None, None, 64, None, 0, 8, 128, 576, sm, 0, None, 8, None, None, None) == OK              # T = 0
+
+
+def test_profile_events_host_side(lib):
+    # no recording active: end reports nothing; begin refuses a NULL array or an empty capacity
+    assert lib.dsa_profile_end() == 0
+    assert lib.dsa_profile_begin(None, 4) == INVALID
+    assert lib.dsa_profile_begin(FAKE, 0) == INVALID
+    assert lib.dsa_profile_kernel_name(0) == b"" and lib.dsa_profile_kernel_name(-1) == b""
+    # begin / end without a launch in between records nothing (no event is touched)
+    assert lib.dsa_profile_begin(FAKE, 4) == OK
+    assert lib.dsa_profile_end() == 0
+

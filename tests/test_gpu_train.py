@@ -171,7 +171,7 @@ def test_train_chain_prefill_4k_rows(dev):
     # the GPU's scores differ from the oracle's within the indexer bar; the loss moves by at most
     # sum |dI| |dlogit| <= 2 max |dlogit|, dI by at most (e - 1)-relative of pi
     A = parity.magnitude(inp.q8[rows], inp.qs[rows], inp.w[rows], inp.k8, inp.ks, pos, wl.S)
-    dmax = np.nanmax(A, axis=1) * (parity.MFMA_FP8_BOUND + 2.0 ** -20)
+    dmax = np.nanmax(A, axis=1) * (parity.indexer_beta(wl.D_I, wl.H_I) + (wl.H_I + 3) * 2.0 ** -24)
     g_loss, g_d = dget(loss)[rows], dget(d)[rows, :wl.S]
     for i, t in enumerate(rows):
         n = t + 1
