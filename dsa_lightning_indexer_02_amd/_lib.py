@@ -14,13 +14,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
 DSA_OK = 0
+TOPK_NOALLOC_SCRATCH_BYTES = 32 << 20   # DSA_TOPK_NOALLOC_SCRATCH_BYTES of include/dsa.h
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE_TOO_SMALL", 4: "DSA_ERR_HIP"}
 
 EXPORTS = [
     "dsa_status_string", "dsa_last_error", "dsa_abi_version", "dsa_profile_begin", "dsa_profile_end",
     "dsa_profile_kernel_name", "dsa_indexer_logits",
-    "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd",
+    "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_noalloc",
+    "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd",
     "dsa_prefill_workspace_size", "dsa_prefill_paged", "dsa_decode_workspace_size", "dsa_decode_paged",
     "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0", "dsa_indexer_logits_ue8m0",
     "dsa_indexer_kl_loss", "dsa_indexer_bwd_workspace_size", "dsa_indexer_bwd", "dsa_indexer_kl_loss_sparse",
@@ -78,6 +80,8 @@ def load(path: str = LIB_PATH):
     lib.dsa_topk_workspace_size.argtypes = [_i64, _i64, _i32]
     lib.dsa_topk_workspace_size.restype = _sz
     lib.dsa_topk.argtypes = [_p, _i64, _i64, _i64, _i64, _i32, _p, _p, _sz, _p]
+    lib.dsa_topk_noalloc.argtypes = [_p, _i64, _i64, _i64, _i64, _i32, _p, _p]
+    lib.dsa_topk_noalloc.restype = ctypes.c_int
     lib.dsa_sparse_mla_workspace_size.argtypes = [_i64, _i32, _i32, _i32]
     lib.dsa_sparse_mla_workspace_size.restype = _sz
     lib.dsa_sparse_mla_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _f32, _p, _p,

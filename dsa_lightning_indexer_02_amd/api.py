@@ -106,6 +106,19 @@ def dsa_topk(logits, k: int, S: int, q_start: int = 0, indices=None, workspace=N
     return indices
 
 
+def dsa_topk_noalloc(logits, k: int, S: int, q_start: int = 0, indices=None) -> torch.Tensor:
+    """dsa_topk without a workspace (the library's own per-GPU scratch array); ``indices`` given
+    makes the call allocate nothing at all."""
+    lib = load()
+    T = logits.shape[0]
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    status = lib.dsa_topk_noalloc(_dev(logits, "logits", 2, 4), logits.shape[1], T, S, q_start, k,
+                                  _dev(indices, "indices", 2, 4), _stream(logits))
+    check("dsa_topk_noalloc", status)
+    return indices
+
+
 def dsa_sparse_mla_fwd(q, kv, indices, sm_scale: float, D_v: int, q_start: int = 0, out=None,
                        out_f32=None, lse=None, want_f32: bool = False, want_lse: bool = True):
     """(out bf16 [T,H,D_v], out_f32 or None, lse or None) of MQA-mode sparse MLA."""

@@ -2,6 +2,8 @@
 // sequence.  Every check happens before the first launch, so a failing call enqueues nothing.
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "../../include/dsa.h"
@@ -146,6 +148,35 @@ dsa_status_t check_cache(const dsa_paged_cache_t* c, int64_t rows_needed_per_seq
   return DSA_OK;
 }
 
+// ---- scratch of the allocation-free top-k entry point
+// One file-scope device array per GPU the library runs on (held until the process ends).  Host
+// code never passes the array's name to a kernel or a copy: on the host that name is a stand-in,
+// not a device address.  The device address comes from hipGetSymbolAddress, once per device with
+// that device current, and is kept per device.
+constexpr size_t kNoallocScratchBytes = DSA_TOPK_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::map<int, void*> g_scratch_ptr;  // device id -> device address of that device's `scratch`
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return dsa::take_error(e);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return dsa::take_error(e);
+  g_scratch_ptr.emplace(dev, p);
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +288,33 @@ dsa_status_t dsa_topk(const float* logits, int64_t ld_logits, int64_t T, int64_t
           workspace_bytes, need);
   if (need) REQUIRE_PTR(workspace);
   return hip_status(dsa::launch_topk(logits, ld_logits, T, S, q_start, nullptr, k, indices, workspace, stream),
+                    "top-k launch");
+}
+
+dsa_status_t dsa_topk_noalloc(const float* logits, int64_t ld_logits, int64_t T, int64_t S, int64_t q_start, int32_t k,
+                              int32_t* indices, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  dsa_status_t s = check_topk(S, k);
+  if (s != DSA_OK) return s;
+  if (T == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1 when T > 0");
+  REQUIRE(k <= 2048 || S <= 32768, DSA_ERR_UNSUPPORTED, "k=%d above 2048 needs S <= 32768", k);
+  REQUIRE(ld_logits >= S && ld_logits % 4 == 0, DSA_ERR_INVALID_ARGUMENT,
+          "ld_logits=%lld must be >= S=%lld and a multiple of 4", (long long)ld_logits, (long long)S);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(indices);
+  const size_t need = dsa::topk_workspace_bytes(T, S, k);
+  REQUIRE(need <= kNoallocScratchBytes, DSA_ERR_UNSUPPORTED,
+          "dsa_topk_noalloc: %lld rows of %lld scores need %zu bytes of scratch, above its %zu-byte array "
+          "(use dsa_topk with a workspace, or fewer rows per call)",
+          (long long)T, (long long)S, need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if (need) {
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_status(e, "scratch symbol address");
+  }
+  dsa::trace_call("dsa_topk_noalloc", kNoallocScratchBytes, need);
+  return hip_status(dsa::launch_topk(logits, ld_logits, T, S, q_start, nullptr, k, indices, ws, stream),
                     "top-k launch");
 }
 

@@ -100,6 +100,22 @@ dsa_status_t dsa_topk(const float *logits, int64_t ld_logits, int64_t T, int64_t
                       hipStream_t stream);
 
 /*
+ * Allocation-free top-k, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same selection, order and
+ * arguments as dsa_topk, without a workspace.  Rows longer than 32768 keep their per-chunk
+ * candidates in a file-scope device array of the library, DSA_TOPK_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * per GPU, held until the process ends; a call whose dsa_topk_workspace_size(T, S, k) exceeds it
+ * (e.g. more than 512 rows of 131072 scores at k = 2048) returns DSA_ERR_UNSUPPORTED before
+ * anything is enqueued.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams or host threads) race and must be
+ * serialised by the caller.
+ */
+#define DSA_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dsa_status_t dsa_topk_noalloc(const float *logits, int64_t ld_logits, int64_t T, int64_t S, int64_t q_start,
+                              int32_t k, int32_t *indices, hipStream_t stream);
+
+/*
  * Sparse MLA forward, MQA mode (summary page, "Method"): for query row t, head h and the valid
  * entries i of indices[t] (0 <= idx < n_t; anything else, including -1, is skipped; duplicates
  * count with multiplicity):

@@ -215,3 +215,14 @@ def test_profile_events_host_side(lib):
     assert lib.dsa_profile_begin(FAKE, 4) == OK
     assert lib.dsa_profile_end() == 0
 
+
+def test_topk_noalloc_rejects_on_the_host(lib):
+    # 600 rows of 131072 scores need 600 * 4 chunks * 2048 * 8 bytes of candidates, above the
+    # 32 MiB array: refused before any device call (this runs without a GPU)
+    assert lib.dsa_topk_noalloc(FAKE, 131072, 600, 131072, 0, 2048, FAKE, None) == UNSUPPORTED
+    assert "scratch" in _err(lib)
+    assert lib.dsa_topk_noalloc(FAKE, 131072, 4, 131072, 0, 0, FAKE, None) == INVALID     # k
+    assert lib.dsa_topk_noalloc(None, 8, 0, 8, 0, 16, None, None) == OK                   # T = 0
+    assert dsa.TOPK_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert "DSA_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in open(HEADER).read()
+
