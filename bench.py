@@ -589,6 +589,73 @@ def run_indexer_train(name, args, dev):
     }
 
 
+def run_mla_bwd(name, args, dev):
+    """Sparse-MLA backward at a prefill shape: indexer -> top-2048 -> forward (for lse) once, then the
+    backward (dq, dkv) timed over the steps with a seeded dout; per-kernel times from stage events.
+    Algorithmic work per selected (row, head, entry): the score recompute 2 D_qk, dP 2 D_v, dq 2 D_qk,
+    dk 2 D_qk, dv 2 D_v flop (the second score pass that forms D and the pass split are this design's
+    own)."""
+    import torch
+    import dsa_lightning_indexer_02_amd as dsa
+    from dsa_inputs import get, prefill_inputs
+    wl = get(name.replace("sparse_mla_bwd_", "prefill_"))
+    print("generating %s inputs" % wl.name, file=sys.stderr, flush=True)
+    inp = prefill_inputs(wl)
+    q8, qs, w, k8, ks = (put(x, dev) for x in (inp.q8, inp.qs, inp.w, inp.k8, inp.ks))
+    q = put(inp.q, dev).view(torch.bfloat16)
+    kv = put(inp.kv, dev).view(torch.bfloat16)
+    del inp
+    T, S = wl.T, wl.S
+    lg = dsa.dsa_indexer_logits(q8, qs, w, k8, ks, wl.q_start)
+    idx = dsa.dsa_topk(lg, wl.topk, S, wl.q_start)
+    del lg
+    _, _, lse = dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v, wl.q_start)
+    g = torch.Generator(device=dev)
+    g.manual_seed(13)
+    dout = torch.randn((T, wl.H, wl.D_v), generator=g, device=dev).to(torch.bfloat16)
+    dq = torch.empty((T, wl.H, wl.D_qk), dtype=torch.float32, device=dev)
+    dkv = torch.empty((S, wl.D_qk), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, dsa.load().dsa_sparse_mla_bwd_workspace_size(T, wl.H)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        dsa.dsa_sparse_mla_bwd(q, kv, idx, lse, dout, wl.sm_scale, wl.q_start, dq, dkv, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    prof, names = [], []
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        dsa.dsa_profile_begin(ev[1:])
+        step()
+        names = dsa.dsa_profile_end()
+        prof.append(ev[:len(names) + 1])
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(names))] for e in prof])
+    step_ms = per.sum(axis=1)
+    kms = per.mean(axis=0)
+    wm = work_model(wl)
+    sel = wm["selected_rows"]
+    flop = 2.0 * wl.H * (3 * wl.D_qk + 2 * wl.D_v) * sel
+    kernels = [{"kernel": nm, "ms": float(t)} for nm, t in zip(names, kms)]
+    med = float(np.median(step_ms))
+    roof = {"kernel": "sparse_mla_bwd (dq kernel + dkv kernel)", "bound": "mfma", "achieved": flop / (med / 1e3) / 1e12,
+            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "traffic": None, "algorithmic_flop_per_launch": flop,
+            "avg_launch_ms": float(step_ms.mean())}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return {"metric": "query tokens/s (sparse MLA backward: dq, dkv, %s)" % name, "value": T / (med / 1e3),
+            "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": med,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16 scores, bf16 hi/lo dq, fp16 dkv contraction, fp32 accumulation and atomics",
+            "data": "synthetic (seeded PCG64 recipe; torch-seeded bf16 dout)", "config": {
+                "workload": name, "T": T, "S": S, "q_start": wl.q_start, "H": wl.H, "D_qk": wl.D_qk, "D_v": wl.D_v,
+                "topk": wl.topk, "parallelism": "single GPU"},
+            "roofline": roof, "kernels": kernels, "stages": None, "step_ms_events": percentiles(step_ms),
+            "fused_ms_per_step": None, "cpu_baseline": None}
+
+
 def run_one(name, args, dev, with_cpu: bool):
     from dsa_inputs import get
     if name in ("quantize_append_32k", "indexer_ue8m0_32k"):
@@ -604,6 +671,8 @@ def run_one(name, args, dev, with_cpu: bool):
                 "stages": res["stages"], "step_ms_events": res["step_ms_events"], "fused_ms_per_step": None,
                 "cpu_baseline": None}
         return line
+    if name.startswith("sparse_mla_bwd_"):
+        return run_mla_bwd(name, args, dev)
     if name.startswith("indexer_train_"):
         res = run_indexer_train(name, args, dev)
         what = ("scores + top-k + sparse attention + sparse-stage KL loss + backward"
@@ -688,7 +757,8 @@ def main():
     dsa.load()
     if args.all_configs:
         for name in ["tiny", "prefill_4k", "prefill_32k", "chunked_131k", "decode_64", "quantize_append_32k",
-                     "indexer_ue8m0_32k", "indexer_train_4k", "indexer_train_sparse_4k"]:
+                     "indexer_ue8m0_32k", "indexer_train_4k", "indexer_train_sparse_4k", "sparse_mla_bwd_4k",
+                     "sparse_mla_bwd_32k"]:
             print(json.dumps(run_one(name, args, dev, with_cpu=False)), flush=True)
             torch.cuda.empty_cache()
         return

@@ -10,6 +10,6 @@ from .api import (  # noqa: F401
     dsa_indexer_kl_loss, dsa_indexer_kl_loss_sparse,
     dsa_indexer_logits, dsa_indexer_logits_ue8m0, dsa_prefill_paged, dsa_profile_begin, dsa_profile_end,
     dsa_profile_kernel_name, dsa_quantize_fp8_rows,
-    dsa_quantize_fp8_rows_ue8m0, dsa_sparse_mla_fwd, dsa_topk, dsa_topk_noalloc, indexer_bwd_workspace_size, ld_for, make_dims,
+    dsa_quantize_fp8_rows_ue8m0, dsa_sparse_mla_bwd, dsa_sparse_mla_fwd, dsa_topk, dsa_topk_noalloc, indexer_bwd_workspace_size, ld_for, make_dims,
     prefill_workspace_size,
 )

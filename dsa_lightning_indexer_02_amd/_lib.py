@@ -22,7 +22,8 @@ EXPORTS = [
     "dsa_status_string", "dsa_last_error", "dsa_abi_version", "dsa_profile_begin", "dsa_profile_end",
     "dsa_profile_kernel_name", "dsa_indexer_logits",
     "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_noalloc",
-    "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd",
+    "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_fwd", "dsa_sparse_mla_bwd_workspace_size",
+    "dsa_sparse_mla_bwd",
     "dsa_prefill_workspace_size", "dsa_prefill_paged", "dsa_decode_workspace_size", "dsa_decode_paged",
     "dsa_quantize_fp8_rows", "dsa_append_paged", "dsa_quantize_fp8_rows_ue8m0", "dsa_indexer_logits_ue8m0",
     "dsa_indexer_kl_loss", "dsa_indexer_bwd_workspace_size", "dsa_indexer_bwd", "dsa_indexer_kl_loss_sparse",
@@ -86,6 +87,11 @@ def load(path: str = LIB_PATH):
     lib.dsa_sparse_mla_workspace_size.restype = _sz
     lib.dsa_sparse_mla_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _f32, _p, _p,
                                        _p, _p, _sz, _p]
+    lib.dsa_sparse_mla_bwd_workspace_size.argtypes = [_i64, _i32]
+    lib.dsa_sparse_mla_bwd_workspace_size.restype = _sz
+    lib.dsa_sparse_mla_bwd.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _f32, _p, _p, _p,
+                                       _sz, _p]
+    lib.dsa_sparse_mla_bwd.restype = ctypes.c_int
     lib.dsa_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), _i64, _i64]
     lib.dsa_prefill_workspace_size.restype = _sz
     lib.dsa_prefill_paged.argtypes = [ctypes.POINTER(PagedCache), _i32, ctypes.POINTER(Dims), _i64, _i64,

@@ -141,6 +141,29 @@ def dsa_sparse_mla_fwd(q, kv, indices, sm_scale: float, D_v: int, q_start: int =
     return out, out_f32, lse
 
 
+def dsa_sparse_mla_bwd(q, kv, indices, lse, dout, sm_scale: float, q_start: int = 0, dq=None, dkv=None,
+                       workspace=None):
+    """(dq f32 [T, H, D_qk], dkv f32 [S, D_qk]): gradients through dsa_sparse_mla_fwd on the same index
+    lists, given the forward's lse and dout = dL/dout (bf16 [T, H, D_v])."""
+    lib = load()
+    T, H, D_qk = q.shape
+    S = kv.shape[0]
+    k = indices.shape[1]
+    D_v = dout.shape[2]
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((T, H, D_qk), dtype=torch.float32, device=dev)
+    if dkv is None:
+        dkv = torch.empty((S, D_qk), dtype=torch.float32, device=dev)
+    workspace = _workspace(lib.dsa_sparse_mla_bwd_workspace_size(T, H), dev, workspace)
+    status = lib.dsa_sparse_mla_bwd(
+        _dev(q, "q", 3, 2), _dev(kv, "kv", 2, 2), _dev(indices, "indices", 2, 4), _dev(lse, "lse", 2, 4),
+        _dev(dout, "dout", 3, 2), T, S, H, D_qk, D_v, k, q_start, ctypes.c_float(sm_scale),
+        _dev(dq, "dq", 3, 4), _dev(dkv, "dkv", 2, 4), workspace.data_ptr(), workspace.numel(), _stream(q))
+    check("dsa_sparse_mla_bwd", status)
+    return dq, dkv
+
+
 # ------------------------------------------------------------------------------------------------
 @dataclass
 class PagedKV:

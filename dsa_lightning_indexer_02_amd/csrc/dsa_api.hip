@@ -358,6 +358,43 @@ dsa_status_t dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int
   return hip_status(dsa::launch_sparse_mla(a, stream), "sparse MLA launch");
 }
 
+size_t dsa_sparse_mla_bwd_workspace_size(int64_t T, int32_t H) {
+  if (T <= 0 || H <= 0) return 0;
+  return dsa::mla_bwd_workspace_bytes(T, H);
+}
+
+dsa_status_t dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, const float* lse,
+                                const uint16_t* dout, int64_t T, int64_t S, int32_t H,
+                                int32_t D_qk, int32_t D_v, int32_t k, int64_t q_start, float sm_scale, float* dq,
+                                float* dkv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
+  REQUIRE(k >= 1, DSA_ERR_INVALID_ARGUMENT, "k=%d must be >= 1", k);
+  REQUIRE(dsa::mla_bwd_supported(D_qk, D_v, H, k), DSA_ERR_UNSUPPORTED,
+          "sparse MLA backward with H=%d D_qk=%d D_v=%d k=%d not supported ((576, 512), 1 <= H <= 128, k <= 2048)",
+          H, D_qk, D_v, k);
+  REQUIRE(sm_scale > 0.f, DSA_ERR_INVALID_ARGUMENT, "sm_scale must be positive");
+  if (T == 0 && S == 0) return ok();
+  REQUIRE(S >= 1, DSA_ERR_INVALID_ARGUMENT, "S must be >= 1");
+  REQUIRE(S <= INT32_MAX, DSA_ERR_UNSUPPORTED, "S above 2^31");
+  REQUIRE_PTR(kv);
+  REQUIRE_PTR(dkv);
+  if (T > 0) {
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(indices);
+    REQUIRE_PTR(lse);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dq);
+  }
+  const size_t need = dsa::mla_bwd_workspace_bytes(T, H);
+  REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "sparse MLA backward workspace %zu < %zu bytes",
+          workspace_bytes, need);
+  if (need) REQUIRE_PTR(workspace);
+  dsa::trace_call("dsa_sparse_mla_bwd", workspace_bytes, need);
+  return hip_status(dsa::launch_sparse_mla_bwd(q, kv, indices, lse, dout, T, S, H, k, q_start, sm_scale, dq, dkv,
+                                               workspace, stream),
+                    "sparse MLA backward launch");
+}
+
 size_t dsa_prefill_workspace_size(const dsa_dims_t* d, int64_t T, int64_t S) {
   if (!d || T <= 0 || S <= 0 || d->topk <= 0) return 0;
   return prefill_layout(d, T, S).total;

@@ -136,6 +136,33 @@ dsa_status_t dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int
                                 hipStream_t stream);
 
 /*
+ * Sparse MLA backward (summary page, "Method": in the sparse training stage the main model trains
+ * with top-k selection on, its attention reading only the listed rows; AMD article, "Training
+ * Approach", sparse stage).  Gradients of a loss L through dsa_sparse_mla_fwd on the same lists,
+ * given dout = dL/dout.  For query row t, head h and the valid entries i of indices[t] (as in the
+ * forward: 0 <= idx_i < n_t, duplicates with multiplicity), p_i = exp(z_i - lse[t][h]):
+ *   dp_i = dout[t][h] . v_i,   D = sum_i p_i dp_i  (= dout[t][h] . out[t][h]),   ds_i = p_i (dp_i - D),
+ *   dq[t][h][:] = sm_scale sum_i ds_i k_i,
+ *   dkv[s][:]   = sum over (t, h, i) with idx_i = s of  sm_scale ds_i q[t][h][:]  (all D_qk columns)
+ *                 + p_i dout[t][h][:]  (the first D_v columns).
+ *   q, kv, indices, sm_scale, q_start as in the forward; lse [T][H] f32 is the forward's output on
+ *   the same inputs (D is summed from p and dp here, not taken from a rounded forward output);
+ *   dout [T][H][D_v] bf16; dq [T][H][D_qk] f32 and dkv [S][D_qk] f32 are outputs (every entry
+ *   written; keys no list selects get 0).  Workspace: dsa_sparse_mla_bwd_workspace_size(T, H)
+ *   bytes (the per-(t, h) D, passed between the two kernels).  dkv is accumulated with fp32
+ *   atomic adds across query rows and head halves, so its low bits depend on their order (dq is
+ *   deterministic).  ds and p enter the head contraction of dkv as fp16 (ds times sm_scale), dq's
+ *   contraction as a bf16 pair (16 significant bits); dout and q are converted bf16 -> fp16 for
+ *   dkv (exact for |x| in [2^-14, 65504]).  Supported: (D_qk, D_v) = (576, 512), 1 <= H <= 128,
+ *   1 <= k <= 2048; T = 0 with S > 0 zeroes dkv.
+ */
+size_t dsa_sparse_mla_bwd_workspace_size(int64_t T, int32_t H);
+dsa_status_t dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *indices, const float *lse,
+                                const uint16_t *dout, int64_t T, int64_t S, int32_t H,
+                                int32_t D_qk, int32_t D_v, int32_t k, int64_t q_start, float sm_scale, float *dq,
+                                float *dkv, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Paged cache (summary page, section "Key claims": the released indexer-logit kernels include paged
  * versions).  Logical key s
  * of sequence b lives in block block_table[b][s / block_size], slot s % block_size, of the pools

@@ -226,3 +226,31 @@ def test_topk_noalloc_rejects_on_the_host(lib):
     assert dsa.TOPK_NOALLOC_SCRATCH_BYTES == 32 << 20
     assert "DSA_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in open(HEADER).read()
 
+
+def test_sparse_mla_bwd_argument_errors(lib):
+    f = lib.dsa_sparse_mla_bwd
+    sm = ctypes.c_float(0.07)
+    need = lib.dsa_sparse_mla_bwd_workspace_size(8, 128)
+    assert need == 8 * 128 * 4 and lib.dsa_sparse_mla_bwd_workspace_size(0, 128) == 0
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 100, 128, 576, 512, 2048, 0, sm, FAKE, FAKE, FAKE, need, None]
+    bad = list(args)
+    bad[8] = 80                                                    # D_qk (only 576 / 512 is built)
+    assert f(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[7] = 129                                                   # H
+    assert f(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[16] = need - 1
+    assert f(*bad) == WS_SMALL
+    bad = list(args)
+    bad[3] = None                                                  # lse
+    assert f(*bad) == INVALID
+    assert "lse" in _err(lib)
+    bad = list(args)
+    bad[12] = ctypes.c_float(0.0)                                  # sm_scale
+    assert f(*bad) == INVALID
+    bad = list(args)
+    bad[10] = 0                                                    # k
+    assert f(*bad) == INVALID
+    assert f(None, None, None, None, None, 0, 0, 128, 576, 512, 16, 0, sm, None, None, None, 0, None) == OK
+
