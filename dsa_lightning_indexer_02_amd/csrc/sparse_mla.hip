@@ -327,7 +327,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         wait_vmcnt<0>();
       __syncthreads();  // stage blk complete; every wave is done with block blk - 1
 
-      // ---- fp16 V^T of this block
+      // ---- fp16 V^T of this block (VALU + LDS work) and the partial scores (MFMA work).  The two
+      // waves of a SIMD (waves w and w + 4) run them in opposite orders, so one's conversion runs
+      // beside the other's MFMAs instead of both waves doing the same kind of work at once.
+      auto vt_build = [&]() {
       if (converts) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {  // unit u = 2 m + lh: key quads 4 m + lh and 4 m + 2 + lh
@@ -339,12 +342,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         }
       }
 
+      };
       // row indices of the next gather, read now so that they are in registers after the barrier
       const int32_t next_rows = gather_rows(blk + 2);
       // ---- partial S^T[key][head] over this wave's contraction half; the K fragment of step
-      // ks + 1 is requested before the MFMA of step ks
+      // ks + 1 is requested before the MFMA of step ks.  MFMA runs raise the wave's issue priority
+      // so that the matrix pipe is fed first when both waves of the SIMD are ready.
       v16f sc = {};
+      auto qk = [&]() {
       if (active) {
+        __builtin_amdgcn_s_setprio(2);
         constexpr int LA = 3;  // K fragments in flight (order pinned by scheduling barriers)
         s16x8 Af[LA];
 #pragma unroll
@@ -356,10 +363,19 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
           sc = mfma_bf16_32x32x16(Af[ks % LA], Qf[ks], sc);
           __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         v4f* dst = reinterpret_cast<v4f*>(Sx) + wave * 4 * WAVE + lane;
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
           dst[qd * WAVE] = (v4f){sc[4 * qd], sc[4 * qd + 1], sc[4 * qd + 2], sc[4 * qd + 3]};
+      }
+      };
+      if (wave >= MLA_WAVES / 2) {
+        qk();
+        vt_build();
+      } else {
+        vt_build();
+        qk();
       }
       __syncthreads();  // partial scores of both halves posted; V^T complete; stage blk no longer read
       if (blk + 2 < nblk) gather_issue(blk + 2, next_rows);
@@ -403,6 +419,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       auto vfrag = [&](int st) {  // step st: key half m = st / NDT, value tile dt = st % NDT
         return *reinterpret_cast<const s16x8*>(vsrc + (st % C::NDT) * 32 * C::VT_STRIDE + 32 * (st / C::NDT));
       };
+      __builtin_amdgcn_s_setprio(2);
       constexpr int LV = 3;  // V^T fragments in flight (order pinned by scheduling barriers)
       s16x8 Vf[LV];
 #pragma unroll
@@ -414,6 +431,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         O[st % C::NDT] = mfma_f16_32x32x16(Vf[st % LV], Bp[st / C::NDT], O[st % C::NDT]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     // does any wave need the exact-maximum pass?
     if (pass == 0) {
