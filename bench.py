@@ -40,6 +40,16 @@ HEADLINE = "prefill_32k"
 METRIC = "query tokens/s (indexer+top-2048+sparse MLA) at L=32K"
 
 
+def copy_calibration(dev):
+    """One 1 GiB device-to-device copy: the reference a counter run scales FETCH_SIZE/WRITE_SIZE by."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def work_model(wl, n=None):
     """Algorithmic work of one pass (masked pairs and skipped dense work excluded).  ``n``: the
     visible key count of every query row (default: the prefill causal counts)."""
@@ -224,11 +234,7 @@ def run_prefill(wl, args, dev):
         fused_ms = (time.perf_counter() - f0) * 1e3 / args.steps
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
 
     wm = work_model(wl)
     stages = {
@@ -302,11 +308,14 @@ def run_decode(wl, args, dev, cpu_threads: int = 0):
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    # profiled pass: an event before the call and one after each of its kernels
+    # profiled pass: an event before the call and one after each of its kernels; an unprofiled call
+    # ahead of each keeps the GPU busy while the host enqueues, so the first interval holds no
+    # host-side launch latency
     nk = 8
     prof = []
     names = []
     for _ in range(args.steps):
+        step()
         if flush is not None:
             flush.zero_()
         evp = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
@@ -317,6 +326,8 @@ def run_decode(wl, args, dev, cpu_threads: int = 0):
         prof.append(evp[:len(names) + 1])
     torch.cuda.synchronize()
     kms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(names))] for e in prof]).mean(axis=0)
+    if args.copy_calibration:
+        copy_calibration(dev)
     n = lens
     sel = np.minimum(n, wl.topk)
     nsplit = max(1, min(-(-256 // B), wl.topk // 64))
