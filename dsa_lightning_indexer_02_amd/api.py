@@ -155,7 +155,7 @@ def dsa_sparse_mla_bwd(q, kv, indices, lse, dout, sm_scale: float, q_start: int 
         dq = torch.empty((T, H, D_qk), dtype=torch.float32, device=dev)
     if dkv is None:
         dkv = torch.empty((S, D_qk), dtype=torch.float32, device=dev)
-    workspace = _workspace(lib.dsa_sparse_mla_bwd_workspace_size(T, H), dev, workspace)
+    workspace = _workspace(lib.dsa_sparse_mla_bwd_workspace_size(T, S, H, k), dev, workspace)
     status = lib.dsa_sparse_mla_bwd(
         _dev(q, "q", 3, 2), _dev(kv, "kv", 2, 2), _dev(indices, "indices", 2, 4), _dev(lse, "lse", 2, 4),
         _dev(dout, "dout", 3, 2), T, S, H, D_qk, D_v, k, q_start, ctypes.c_float(sm_scale),

@@ -358,9 +358,9 @@ dsa_status_t dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int
   return hip_status(dsa::launch_sparse_mla(a, stream), "sparse MLA launch");
 }
 
-size_t dsa_sparse_mla_bwd_workspace_size(int64_t T, int32_t H) {
-  if (T <= 0 || H <= 0) return 0;
-  return dsa::mla_bwd_workspace_bytes(T, H);
+size_t dsa_sparse_mla_bwd_workspace_size(int64_t T, int64_t S, int32_t H, int32_t k) {
+  if (T <= 0 || S <= 0 || H <= 0 || k <= 0) return 0;
+  return dsa::mla_bwd_workspace_bytes(T, S, H, k);
 }
 
 dsa_status_t dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, const float* lse,
@@ -385,7 +385,7 @@ dsa_status_t dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int
     REQUIRE_PTR(dout);
     REQUIRE_PTR(dq);
   }
-  const size_t need = dsa::mla_bwd_workspace_bytes(T, H);
+  const size_t need = dsa::mla_bwd_workspace_bytes(T, S, H, k);
   REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "sparse MLA backward workspace %zu < %zu bytes",
           workspace_bytes, need);
   if (need) REQUIRE_PTR(workspace);

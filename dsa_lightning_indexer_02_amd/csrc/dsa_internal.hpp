@@ -95,7 +95,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
 
 // ---- sparse MLA backward
 bool mla_bwd_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k);
-size_t mla_bwd_workspace_bytes(int64_t T, int32_t H);
+size_t mla_bwd_workspace_bytes(int64_t T, int64_t S, int32_t H, int32_t k);
 hipError_t launch_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* lse,
                                  const uint16_t* dout, int64_t T, int64_t S, int32_t H, int32_t k, int64_t q_start,
                                  float sm_scale, float* dq, float* dkv, void* workspace, hipStream_t stream);

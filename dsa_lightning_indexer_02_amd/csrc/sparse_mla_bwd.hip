@@ -12,28 +12,36 @@
 // forward's rounded output: where one key dominates the softmax, ds is a small difference and a
 // rounded D would swamp it).
 //
-// Kernels (H heads in halves of 64 per workgroup, 4 waves, one per SIMD; wave (g, f) serves the 32
-// heads of group g and contraction half f, as in the forward):
-//  - sparse_mla_bwd_kernel<DKV = false>: per block of 32 gathered rows (DMA into LDS, XOR-swizzled as
-//    the forward), partial S^T = K Q^T and dP^T = V G^T over the wave's half (bf16 32x32x16 MFMA),
-//    summed with the partner's through LDS; p in fp32 on the accumulator layout (lane = head).  Pass
-//    0 sums p dp into D (written for the dKV kernel); pass 1 forms ds = p (dp - D) and
-//    dQ^T += K^T dS^T with K^T from transposing LDS reads of the gathered rows and ds split into a
-//    bf16 high part and a bf16 remainder (two MFMAs; 16 significant bits), accumulated over all
-//    blocks in registers, written once;
-//  - sparse_mla_bwd_kernel<DKV = true>: the same scores and D, then sm_scale ds and p as fp16 tiles
-//    [head][key] in LDS; each wave forms the dKV rows of the block for its share of the columns,
-//    contracting over the 64 heads (fp16 16x16x32 MFMA; Q^T and G^T fragments converted from bf16
-//    once per workgroup and kept in registers), and adds them to dkv with fp32 atomic adds (the two
-//    head halves and every query row selecting a key add into the same row).
+// Kernels, per chunk of up to 512 query rows (the chunk's buffers live in the caller's workspace):
+//  - sparse_mla_bwd_dq_kernel: H heads in halves of 64 per workgroup, 4 waves, one per SIMD; wave
+//    (g, f) serves the 32 heads of group g and contraction half f, as in the forward.  Per block of
+//    32 gathered rows (DMA into LDS, XOR-swizzled as the forward), partial S^T = K Q^T and
+//    dP^T = V G^T over the wave's half (bf16 32x32x16 MFMA), summed with the partner's through LDS;
+//    p in fp32 on the accumulator layout (lane = head).  Pass 0 sums p dp into D; pass 1 forms
+//    ds = p (dp - D) and dQ^T += K^T dS^T with K^T from transposing LDS reads of the gathered rows
+//    and ds split into a bf16 high part and a bf16 remainder (two MFMAs; 16 significant bits),
+//    accumulated over all blocks in registers and written once.  Pass 1 also writes sm_scale ds
+//    and p as fp16 [head][entry] tiles of the chunk (the dKV kernels' input).
+//  - mla_bwd_pos_kernel: per chunk, the first entry of each (key, row) pair (atomic minimum into
+//    a key-major map, so repeated keys of a list resolve to their first entry).
+//  - mla_bwd_dkv_contrib_kernel: one workgroup per row, all heads.  Q^T and G^T fragments (16
+//    columns x 32 heads, fp16) of the wave's 144 columns stay in registers; per block, the ds and p
+//    tiles are read from the chunk buffer into LDS and every entry's 576-wide dKV contribution
+//    sum_h sm_scale ds q_h + p g_h (fp16 16x16x32 MFMA, accumulator lane = four columns of one
+//    entry) is stored to its own slot with plain 16-byte stores.  Entries repeating an earlier key
+//    of the list are then added into that key's first slot, in entry order.
+//  - mla_bwd_dkv_reduce_kernel: one wave per key, adding the slots the map names in row order and
+//    the sum into dkv.  Every sum has a fixed order, so dkv is deterministic.
 #include "dsa_internal.hpp"
 
 namespace dsa {
 
 constexpr int BW_THREADS = 256;     // 4 waves
 constexpr int BWM_KB = 32;          // gathered rows per block
-constexpr int BWM_HEADS = 64;       // heads per workgroup
+constexpr int BWM_HEADS = 64;       // heads per dq workgroup
 constexpr int BWM_MAX_K = 2048;
+constexpr int BWM_CHUNK_ROWS = 512; // query rows per chunk of the dKV buffers
+constexpr int32_t BWM_NO_ENTRY = INT32_MAX;
 constexpr float BWM_LOG2E = 1.4426950408889634f;
 
 // Geometry of the 576 / 512 latent rows (the only width the backward is built for).
@@ -50,13 +58,14 @@ struct BwmCfg {
   static constexpr int DMA_INSTR = SLOTS / WAVE;          // 36 wave-wide transfers per block
   static constexpr int DMA_PW = DMA_INSTR / 4;            // 9 per wave
   static constexpr int SX_BYTES = 4 * 2 * WAVE * 16 * 4;  // partial S^T and dP^T of every wave
-  // dKV mode: columns per wave (dK over 576, dV over 512) in 16-wide MFMA tiles
-  static constexpr int KC = DQK / 4, VC = DV / 4;         // 144, 128
-  static constexpr int NKC = KC / 16, NVC = VC / 16;      // 9, 8
-  static constexpr int TILE_STRIDE = BWM_KB * 2 + 16;     // bytes per head row of an fp16 [head][key] tile
-  static constexpr int TILE_BYTES = BWM_HEADS * TILE_STRIDE;
+  // dKV contribution kernel: wave w owns columns [144 w, 144 w + 144): 9 tiles of 16 of dK, and the
+  // dV tiles among them (columns below 512: 9, 9, 9, 5)
+  static constexpr int CW = DQK / 4, NCT = CW / 16;       // 144, 9
+  static constexpr int TILE_STRIDE = BWM_KB * 2 + 16;     // bytes per head row of an fp16 [head][entry] tile
   static constexpr int STAGE_Q_STRIDE = DQK * 2 + 16;     // row stride of the staged Q / G (bf16)
+  static constexpr int STAGE_BYTES = 128 * STAGE_Q_STRIDE;
   static_assert(DMA_INSTR % 4 == 0 && 2 * DMA_PW <= WAVE, "gather transfers split evenly over 4 waves");
+  static_assert(2 * 128 * TILE_STRIDE <= STAGE_BYTES, "the tiles reuse the staging space");
   // chunk XOR of gathered row r (the forward's swizzle: conflict-free fragment and transposing reads)
   static __host__ __device__ __forceinline__ constexpr int swz(int r) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
@@ -64,18 +73,24 @@ struct BwmCfg {
   static __device__ __forceinline__ int slot(int r, int c) { return r * RC + (c ^ swz(r)); }
 };
 
-constexpr size_t bwm_smem_bytes(bool dkv) {
+constexpr size_t bwm_dq_smem_bytes() {
   using C = BwmCfg;
-  const size_t base = 2 * (size_t)C::K_BYTES + C::SX_BYTES + (size_t)(BWM_MAX_K + 4 + BWM_MAX_K / BWM_KB) * 4;
-  const size_t tiles = 2 * (size_t)C::TILE_BYTES;
-  const size_t stage = (size_t)BWM_HEADS * C::STAGE_Q_STRIDE;  // Q / G staging before the block loop
-  const size_t loop = base + (dkv ? tiles : 0);
-  return dkv && stage > loop ? stage : loop;
+  return 2 * (size_t)C::K_BYTES + C::SX_BYTES + (size_t)(BWM_MAX_K + 4 + BWM_MAX_K / BWM_KB) * 4;
 }
+constexpr size_t bwm_contrib_smem_bytes() {
+  return (size_t)BwmCfg::STAGE_BYTES + (BWM_MAX_K / BWM_KB) * 4 + (size_t)BWM_MAX_K * 4;
+}
+static_assert(bwm_dq_smem_bytes() <= kLdsPerWorkgroupMax && bwm_contrib_smem_bytes() <= kLdsPerWorkgroupMax,
+              "LDS budget");
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n4) reinterpret_cast<v4f*>(p)[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
 }
 
 __device__ __forceinline__ short f32_to_f16_bits(float x) { return __builtin_bit_cast(short, (_Float16)x); }
@@ -87,25 +102,44 @@ __device__ __forceinline__ short bf16_lo(float x) {
   return (short)f32_to_bf16(x - __uint_as_float((uint32_t)f32_to_bf16(x) << 16));
 }
 
-template <bool DKV>
-__global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_kernel(
+// Validity words of a list (bit e of word b: entry 32 b + e names a key in [0, n)), into LDS.
+__device__ __forceinline__ void list_validity(const int32_t* __restrict__ list, int32_t k, int64_t n,
+                                              uint32_t* vmask, int wave, int lane) {
+  for (int base = wave * WAVE; base < (k + 63) / 64 * 64; base += 4 * WAVE) {
+    const int i = base + lane;
+    bool v = false;
+    if (i < k) {
+      const int32_t li = list[i];
+      v = li >= 0 && li < n;
+    }
+    const uint64_t bits = __ballot(v);
+    if (lane == 0) {
+      vmask[base / 32] = (uint32_t)bits;
+      if (base + 32 < k) vmask[base / 32 + 1] = (uint32_t)(bits >> 32);
+    }
+  }
+}
+
+// dq of rows t0 .. t0 + R - 1 (latest first) and the chunk's fp16 ds / p tiles
+// dsp [R][2][Hp][kpad] (which 0: sm_scale ds, 1: p; heads past H and invalid entries hold 0).
+__global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-    const float* __restrict__ lse, float* __restrict__ delta, const uint16_t* __restrict__ dout, int64_t S,
-    int64_t q_start, int32_t H, int32_t k, float scale_log2, float sm_scale, float* __restrict__ dq,
-    float* __restrict__ dkv) {
+    const float* __restrict__ lse, const uint16_t* __restrict__ dout, int64_t S, int64_t q_start, int32_t H,
+    int32_t k, float scale_log2, float sm_scale, float* __restrict__ dq, int64_t t0, int32_t Hp, int32_t kpad,
+    uint16_t* __restrict__ dsp) {
   using C = BwmCfg;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* Kbuf = smem;                                            // [2][SLOTS] x 16 B
   v4f* Sx = reinterpret_cast<v4f*>(smem + 2 * C::K_BYTES);          // [wave][S, dP][4][64] x v4f
   int32_t* phys = reinterpret_cast<int32_t*>(smem + 2 * C::K_BYTES + C::SX_BYTES);
   uint32_t* vmask = reinterpret_cast<uint32_t*>(phys + BWM_MAX_K + 4);
-  uint8_t* tiles = reinterpret_cast<uint8_t*>(vmask + BWM_MAX_K / BWM_KB);  // DKV: fp16 [head][key] ds, p
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = wave >> 1, hf = wave & 1;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int64_t t = (int64_t)gridDim.x - 1 - blockIdx.x;  // latest rows first (longest lists)
+  const int r = (int)gridDim.x - 1 - (int)blockIdx.x;  // latest rows first (longest lists)
+  const int64_t t = t0 + r;
   const int h0 = blockIdx.y * BWM_HEADS;
   const int head = h0 + g * 32 + l32;
   const bool hv = head < H;
@@ -116,19 +150,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_kernel(
     const int32_t li = idx[t * k + i];
     phys[i] = (li >= 0 && li < n) ? li : -1;
   }
-  for (int base = wave * WAVE; base < (k + 63) / 64 * 64; base += 4 * WAVE) {
-    const int i = base + lane;
-    bool v = false;
-    if (i < k) {
-      const int32_t li = idx[t * k + i];
-      v = li >= 0 && li < n;
-    }
-    const uint64_t bits = __ballot(v);
-    if (lane == 0) {
-      vmask[base / 32] = (uint32_t)bits;
-      if (base + 32 < k) vmask[base / 32 + 1] = (uint32_t)(bits >> 32);
-    }
-  }
+  list_validity(idx + t * k, k, n, vmask, wave, lane);
 
   // ---- resident operands: queries and output gradients of this wave's heads and half, as the
   // B operands of S^T = K Q^T and dP^T = V G^T
@@ -149,54 +171,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_kernel(
   }
   // heads past H get p = 0 (exp2(-inf)) and ds = 0
   const float lse2 = hv ? lse[t * H + head] * BWM_LOG2E : INFINITY;
-  float dlt = 0.f;  // D of this lane's head: summed in pass 0 (dQ kernel) or read (dKV kernel)
-  if constexpr (DKV) dlt = hv ? delta[t * H + head] : 0.f;
-
-  // ---- DKV: B operands of the head contraction, Q^T and G^T fragments (lane = column, eight heads
-  // per lane group), staged through LDS once and converted bf16 -> fp16 (exact for |x| in
-  // [2^-14, 65504])
-  constexpr int NKC = DKV ? C::NKC : 1, NVC = DKV ? C::NVC : 1;
-  s16x8 QT[NKC][2], GT[NVC][2];
-  if constexpr (DKV) {
-    const int a = lane & 15, grp = lane >> 4;
-    auto stage_rows = [&](const uint16_t* src, int width) {
-      // rows h0 .. h0 + 63 of [t][h][width] into LDS, row stride STAGE_Q_STRIDE (zeros past H)
-      const int chunks = width / 8;
-      for (int p = tid; p < BWM_HEADS * chunks; p += BW_THREADS) {
-        const int r = p / chunks, c = p % chunks;
-        v4i v = {0, 0, 0, 0};
-        if (h0 + r < H) v = *reinterpret_cast<const v4i*>(src + (t * H + h0 + r) * (int64_t)width + c * 8);
-        *reinterpret_cast<v4i*>(smem + r * C::STAGE_Q_STRIDE + c * 16) = v;
-      }
-    };
-    // fragment (column tile col0, heads 32 kk .. 32 kk + 31): two transposing reads of rows
-    // 32 kk + 8 grp + {0..3}, {4..7}, columns col0 + 4 (a % 4)
-    auto frag = [&](int col0, int kk) {
-      s16x8 r;
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const int row = 32 * kk + 8 * grp + 4 * hlf + (a >> 2);
-        const s16x4 w = lds_transpose_read16(smem + row * C::STAGE_Q_STRIDE + (col0 + 4 * (a & 3)) * 2);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[4 * hlf + e] = f32_to_f16_bits(bf16_to_f32((uint16_t)w[e]));
-      }
-      return r;
-    };
-    stage_rows(q, C::DQK);
-    __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < NKC; ++ct)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) QT[ct][kk] = frag(wave * C::KC + ct * 16, kk);
-    __syncthreads();
-    stage_rows(dout, C::DV);
-    __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < NVC; ++ct)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) GT[ct][kk] = frag(wave * C::VC + ct * 16, kk);
-  }
-  __syncthreads();  // list, masks and staging done before the gathers overwrite the LDS
+  float dlt = 0.f;  // D of this lane's head, summed in pass 0
+  __syncthreads();  // list and masks done before the gathers overwrite the LDS
 
   const int32_t safe_row = 0;  // skipped entries gather row 0 (masked out)
   const uint32_t kbuf_lds = lds_offset(Kbuf);
@@ -244,27 +220,27 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_kernel(
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int odd = 0; odd < 2; ++odd) {
-        const int r = 4 * (grp >> 1) + (a >> 2) + 8 * j;
+        const int rr = 4 * (grp >> 1) + (a >> 2) + 8 * j;
         const int par = odd ^ hf;
-        const int c = 32 * hf + 8 * (hf & odd) + ((4 * par + low) ^ C::swz(r));
-        kt_base[j][odd] = (r * C::RC + c) * 16 + (a & 1) * 8;
+        const int c = 32 * hf + 8 * (hf & odd) + ((4 * par + low) ^ C::swz(rr));
+        kt_base[j][odd] = (rr * C::RC + c) * 16 + (a & 1) * 8;
       }
   }
 
-  v16f acc[DKV ? 1 : C::NQT];
-  if constexpr (!DKV) {
+  v16f acc[C::NQT];
 #pragma unroll
-    for (int dt = 0; dt < C::NQT; ++dt) acc[dt] = (v16f){};
-  }
+  for (int dt = 0; dt < C::NQT; ++dt) acc[dt] = (v16f){};
 
   const int nblk_all = (k + BWM_KB - 1) / BWM_KB;
   const uint64_t live = __ballot(lane < nblk_all && vmask[lane] != 0u);
   const int nblk = live ? 64 - __clzll(live) : 0;
   const v4f* Sx_peer = Sx + ((wave ^ 1) * 2) * 4 * WAVE + lane;
   v4f* Sx_mine = Sx + (wave * 2) * 4 * WAVE + lane;
+  // this wave's ds (f = 0) or p (f = 1) tile row of its lane's head
+  uint16_t* tile_row = dsp + ((int64_t)(r * 2 + hf) * Hp + head) * kpad;
 
-  // the dQ kernel walks the blocks twice (pass 0: D; pass 1: dQ), the dKV kernel once
-  for (int pass = DKV ? 1 : 0; pass < 2; ++pass) {
+  // the blocks are walked twice (pass 0: D; pass 1: dQ and the tiles)
+  for (int pass = 0; pass < 2; ++pass) {
   if (nblk > 0) gather(0);
   float dsum = 0.f;  // pass 0: this lane's part of sum_i p_i dp_i
   for (int blk = 0; blk < nblk; ++blk) {
@@ -313,100 +289,269 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_kernel(
     }
     if (pass == 0) continue;  // D only
 
-    if constexpr (!DKV) {
-      // dQ^T[d][head] += K^T[d][key] dS^T[key][head]: B = ds (hi, lo) for key steps m = 0, 1
-      s16x8 Bh[2], Bl[2];
+    // ---- the fp16 tiles: keys 8 qd + 4 lh + 0..3 of the block, four per 8-byte store
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        Bh[rr >> 3][rr & 7] = bf16_hi(ds[rr]);
-        Bl[rr >> 3][rr & 7] = bf16_lo(ds[rr]);
-      }
+    for (int qd = 0; qd < 4; ++qd) {
+      s16x4 v;
 #pragma unroll
-      for (int dt = 0; dt < C::NQT; ++dt)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int off = (dt >> 1) * 128 + m * 16 * C::RC * 16;
-          const s16x4 x0 = lds_transpose_read16(Kst + kt_base[0][dt & 1] + off);
-          const s16x4 x1 = lds_transpose_read16(Kst + kt_base[1][dt & 1] + off);
-          const s16x8 A = (s16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          acc[dt] = mfma_bf16_32x32x16(A, Bh[m], acc[dt]);
-          acc[dt] = mfma_bf16_32x32x16(A, Bl[m], acc[dt]);
-        }
-    } else {
-      // ---- ds (times sm_scale) and p as fp16 tiles [head][key]; wave f = 0 writes ds, f = 1 p
-      uint8_t* tile = tiles + hf * C::TILE_BYTES + (g * 32 + l32) * C::TILE_STRIDE;
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {  // keys 8 qd + 4 lh + 0..3
-        s16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = f32_to_f16_bits(hf == 0 ? ds[4 * qd + e] * sm_scale : pr[4 * qd + e]);
-        *reinterpret_cast<s16x4*>(tile + (8 * qd + 4 * lh) * 2) = v;
-      }
-      __syncthreads();  // both tiles complete
-      // A operands (16 keys x 32 heads): two transposing reads of head rows 32 kk + 8 grp + {0..3},
-      // {4..7}, key columns 16 kt + 4 (a % 4)
-      const int a = lane & 15, grp = lane >> 4;
-      auto afrag = [&](int which, int kt, int kk) {
-        s16x8 r;
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const int row = 32 * kk + 8 * grp + 4 * hlf + (a >> 2);
-          const s16x4 w = lds_transpose_read16(tiles + which * C::TILE_BYTES + row * C::TILE_STRIDE +
-                                                (16 * kt + 4 * (a & 3)) * 2);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[4 * hlf + e] = w[e];
-        }
-        return r;
-      };
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const s16x8 Ad0 = afrag(0, kt, 0), Ad1 = afrag(0, kt, 1);
-        const s16x8 Ap0 = afrag(1, kt, 0), Ap1 = afrag(1, kt, 1);
-        // accumulator lane l: column l % 16, keys 16 kt + 4 (l / 16) + r
-        int32_t pk[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pk[r] = phys[blk * BWM_KB + 16 * kt + 4 * grp + r];
-#pragma unroll
-        for (int ct = 0; ct < C::NKC; ++ct) {
-          v4f c = mfma_f16_16x16x32(Ad0, QT[ct][0], (v4f){0.f, 0.f, 0.f, 0.f});
-          c = mfma_f16_16x16x32(Ad1, QT[ct][1], c);
-          const int col = wave * C::KC + ct * 16 + a;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (pk[r] >= 0) atomicAdd(dkv + (int64_t)pk[r] * C::DQK + col, c[r]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < C::NVC; ++ct) {
-          v4f c = mfma_f16_16x16x32(Ap0, GT[ct][0], (v4f){0.f, 0.f, 0.f, 0.f});
-          c = mfma_f16_16x16x32(Ap1, GT[ct][1], c);
-          const int col = wave * C::VC + ct * 16 + a;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (pk[r] >= 0) atomicAdd(dkv + (int64_t)pk[r] * C::DQK + col, c[r]);
-        }
-      }
+      for (int e = 0; e < 4; ++e) v[e] = f32_to_f16_bits(hf == 0 ? ds[4 * qd + e] * sm_scale : pr[4 * qd + e]);
+      *reinterpret_cast<s16x4*>(tile_row + blk * BWM_KB + 8 * qd + 4 * lh) = v;
     }
+
+    // ---- dQ^T[d][head] += K^T[d][key] dS^T[key][head]: B = ds (hi, lo) for key steps m = 0, 1
+    s16x8 Bh[2], Bl[2];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      Bh[rr >> 3][rr & 7] = bf16_hi(ds[rr]);
+      Bl[rr >> 3][rr & 7] = bf16_lo(ds[rr]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::NQT; ++dt)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int off = (dt >> 1) * 128 + m * 16 * C::RC * 16;
+        const s16x4 x0 = lds_transpose_read16(Kst + kt_base[0][dt & 1] + off);
+        const s16x4 x1 = lds_transpose_read16(Kst + kt_base[1][dt & 1] + off);
+        const s16x8 A = (s16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        acc[dt] = mfma_bf16_32x32x16(A, Bh[m], acc[dt]);
+        acc[dt] = mfma_bf16_32x32x16(A, Bl[m], acc[dt]);
+      }
   }
   if (pass == 0) {
     // D of this lane's head: its 16 keys plus the other lane half's (both waves of a pair hold
     // the same sums)
     dlt = dsum + __shfl_xor(dsum, 32);
-    if (hv && hf == 0 && lh == 0) delta[t * H + head] = dlt;
   }
   }
   vm_wait<0>();
 
-  if constexpr (!DKV) {
-    if (!hv) return;
-    // accumulator element r of tile dt: column hf DH + 32 dt + 8 (r / 4) + 4 lh + r % 4 of the head
-    float* drow = dq + (t * H + head) * (int64_t)C::DQK + hf * C::DH;
+  if (!hv) return;
+  // accumulator element r of tile dt: column hf DH + 32 dt + 8 (r / 4) + 4 lh + r % 4 of the head
+  float* drow = dq + (t * H + head) * (int64_t)C::DQK + hf * C::DH;
 #pragma unroll
-    for (int dt = 0; dt < C::NQT; ++dt)
+  for (int dt = 0; dt < C::NQT; ++dt)
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<v4f*>(drow + dt * 32 + 8 * qd + 4 * lh) =
-            (v4f){acc[dt][4 * qd], acc[dt][4 * qd + 1], acc[dt][4 * qd + 2], acc[dt][4 * qd + 3]} * sm_scale;
+    for (int qd = 0; qd < 4; ++qd)
+      *reinterpret_cast<v4f*>(drow + dt * 32 + 8 * qd + 4 * lh) =
+          (v4f){acc[dt][4 * qd], acc[dt][4 * qd + 1], acc[dt][4 * qd + 2], acc[dt][4 * qd + 3]} * sm_scale;
+}
+
+// First entry of each (key, row) of the chunk: pos [keys][Rs] (BWM_NO_ENTRY where no entry).
+__global__ __launch_bounds__(256) void mla_bwd_pos_kernel(const int32_t* __restrict__ idx, int64_t t0, int32_t Rs,
+                                                          int64_t S, int64_t q_start, int32_t k,
+                                                          int32_t* __restrict__ pos) {
+  const int r = blockIdx.x;
+  const int64_t t = t0 + r;
+  const int64_t n = min(S, q_start + t + 1);
+  for (int i = threadIdx.x; i < k; i += 256) {
+    const int32_t s = idx[t * k + i];
+    if (s >= 0 && s < n) atomicMin(pos + (int64_t)s * Rs + r, i);
   }
+}
+
+// The dKV contribution of every entry of row t0 + blockIdx.x: contrib [Rs][kpad][576] f32.
+template <int NHS>  // 32-head steps of the contraction (Hp / 32)
+__global__ __launch_bounds__(BW_THREADS, 1) void mla_bwd_dkv_contrib_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ dsp, const int32_t* __restrict__ pos, int64_t t0, int32_t Rs, int64_t S,
+    int64_t q_start, int32_t H, int32_t k, int32_t kpad, float* __restrict__ contrib) {
+  using C = BwmCfg;
+  constexpr int HP = NHS * 32;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* stage = smem;  // Q / G staging, then the ds and p tiles [2][HP][TILE_STRIDE]
+  uint32_t* vmask = reinterpret_cast<uint32_t*>(smem + C::STAGE_BYTES);
+  int32_t* prim = reinterpret_cast<int32_t*>(vmask + BWM_MAX_K / BWM_KB);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int a = lane & 15, grp = lane >> 4;
+  const int r = blockIdx.x;
+  const int64_t t = t0 + r;
+  const int64_t n = min(S, q_start + t + 1);
+
+  // ---- each valid entry's first entry of its key (itself unless the key repeats), validity words
+  int dup = 0;
+  for (int i = tid; i < k; i += BW_THREADS) {
+    const int32_t s = idx[t * k + i];
+    int32_t first = -1;
+    if (s >= 0 && s < n) {
+      first = pos[(int64_t)s * Rs + r];
+      dup |= first != i;
+    }
+    prim[i] = first;
+  }
+  list_validity(idx + t * k, k, n, vmask, wave, lane);
+
+  // ---- A operands of the head contraction: Q^T and G^T fragments (16 columns x 32 heads; lane =
+  // column, eight heads per lane group), staged through LDS and converted bf16 -> fp16 (exact for
+  // |x| in [2^-14, 65504])
+  auto stage_rows = [&](const uint16_t* src, int width) {
+    // rows 0 .. HP - 1 of [t][h][width] into LDS, row stride STAGE_Q_STRIDE (zeros past H)
+    const int chunks = width / 8;
+    for (int p = tid; p < HP * chunks; p += BW_THREADS) {
+      const int h = p / chunks, c = p % chunks;
+      v4i v = {0, 0, 0, 0};
+      if (h < H) v = *reinterpret_cast<const v4i*>(src + (t * H + h) * (int64_t)width + c * 8);
+      *reinterpret_cast<v4i*>(stage + h * C::STAGE_Q_STRIDE + c * 16) = v;
+    }
+  };
+  // fragment (columns col0 .. col0 + 15, heads 32 kk .. 32 kk + 31): two transposing reads of rows
+  // 32 kk + 8 grp + {0..3}, {4..7}, columns col0 + 4 (a % 4)
+  auto frag = [&](int col0, int kk) {
+    s16x8 v;
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const int row = 32 * kk + 8 * grp + 4 * hlf + (a >> 2);
+      const s16x4 w = lds_transpose_read16(stage + row * C::STAGE_Q_STRIDE + (col0 + 4 * (a & 3)) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * hlf + e] = f32_to_f16_bits(bf16_to_f32((uint16_t)w[e]));
+    }
+    return v;
+  };
+  const int col_w = wave * C::CW;
+  const int nv = wave < 3 ? C::NCT : (C::DV - 3 * C::CW) / 16;  // dV tiles among the wave's columns
+  s16x8 QT[C::NCT][NHS], GT[C::NCT][NHS];
+  stage_rows(q, C::DQK);
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+    for (int kk = 0; kk < NHS; ++kk) QT[ct][kk] = frag(col_w + ct * 16, kk);
+  __syncthreads();
+  stage_rows(dout, C::DV);
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+    for (int kk = 0; kk < NHS; ++kk)
+      GT[ct][kk] = ct < nv ? frag(col_w + ct * 16, kk) : (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  const bool has_dup = __syncthreads_or(dup);  // also: staging reads done before the tiles overwrite it
+
+  // B operands: (entries 16 kt .. + 15) x (heads 32 kk .. + 31) of tile `which`, two transposing
+  // reads of head rows 32 kk + 8 grp + {0..3}, {4..7}, entry columns 16 kt + 4 (a % 4)
+  auto tfrag = [&](int which, int kt, int kk) {
+    s16x8 v;
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const int row = 32 * kk + 8 * grp + 4 * hlf + (a >> 2);
+      const s16x4 w = lds_transpose_read16(stage + (which * HP + row) * C::TILE_STRIDE + (16 * kt + 4 * (a & 3)) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * hlf + e] = w[e];
+    }
+    return v;
+  };
+  const int nblk = (k + BWM_KB - 1) / BWM_KB;
+  const uint16_t* tiles_g = dsp + (int64_t)r * 2 * HP * kpad;
+  for (int blk = 0; blk < nblk; ++blk) {
+    if (vmask[blk] == 0u) continue;  // no valid entry: nothing to contribute (workgroup-uniform)
+    // tiles of the block: 2 x HP head rows of 64 bytes, 16 bytes per thread and step
+    for (int p = tid; p < 2 * HP * 4; p += BW_THREADS) {
+      const int row = p >> 2, c = p & 3;  // row = which * HP + head
+      const v4i v = *reinterpret_cast<const v4i*>(tiles_g + (int64_t)row * kpad + blk * BWM_KB + c * 8);
+      *reinterpret_cast<v4i*>(stage + row * C::TILE_STRIDE + c * 16) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s16x8 Bd[NHS], Bp[NHS];
+#pragma unroll
+      for (int kk = 0; kk < NHS; ++kk) {
+        Bd[kk] = tfrag(0, kt, kk);
+        Bp[kk] = tfrag(1, kt, kk);
+      }
+      // accumulator lane l: columns 4 (l / 16) + 0..3 of the tile, entry 16 kt + l % 16
+      float* dst = contrib + ((int64_t)r * kpad + blk * BWM_KB + 16 * kt + a) * C::DQK + col_w + 4 * grp;
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct) {
+        v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NHS; ++kk) c = mfma_f16_16x16x32(QT[ct][kk], Bd[kk], c);
+        if (ct < nv) {
+#pragma unroll
+          for (int kk = 0; kk < NHS; ++kk) c = mfma_f16_16x16x32(GT[ct][kk], Bp[kk], c);
+        }
+        *reinterpret_cast<v4f*>(dst + ct * 16) = c;
+      }
+    }
+    __syncthreads();  // tiles read before the next block's overwrite them
+  }
+
+  if (has_dup) {
+    // entries repeating an earlier key of the list: added into the key's first slot in entry
+    // order (agent-scope accesses: the slots were stored by other waves)
+    __threadfence();
+    __syncthreads();
+    for (int i = 0; i < k; ++i) {
+      const int32_t j = prim[i];
+      if (j < 0 || j == i) continue;  // workgroup-uniform
+      if (tid < C::DQK / 4) {
+        float* dj = contrib + ((int64_t)r * kpad + j) * C::DQK + 4 * tid;
+        const float* di = contrib + ((int64_t)r * kpad + i) * C::DQK + 4 * tid;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = __hip_atomic_load(dj + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float y = __hip_atomic_load(di + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(dj + e, x + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+}
+
+// dkv[s] += the slots the map names for key s, in row order (one wave per key; lane c holds the
+// 16-byte column chunks c, c + 64 and, below 16, c + 128).
+__global__ __launch_bounds__(256) void mla_bwd_dkv_reduce_kernel(const int32_t* __restrict__ pos, int32_t Rs,
+                                                                 int32_t Rc, const float* __restrict__ contrib,
+                                                                 int32_t kpad, int64_t nkeys, float* __restrict__ dkv) {
+  constexpr int NC = BwmCfg::DQK / 4;  // 144 chunks per row
+  const int lane = threadIdx.x & 63;
+  const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= nkeys) return;
+  const bool third = lane + 128 < NC;
+  const int32_t* ps = pos + s * Rs;
+  const v4f* cv = reinterpret_cast<const v4f*>(contrib);
+  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+  for (int r0 = 0; r0 < Rc; r0 += WAVE) {
+    const int32_t v = r0 + lane < Rc ? ps[r0 + lane] : BWM_NO_ENTRY;
+    uint64_t m = __ballot(v != BWM_NO_ENTRY);
+    while (m) {
+      // up to four slots in flight, added in row order
+      int64_t off[4];
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        off[u] = 0;
+        if (m) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          const int32_t i = __shfl(v, b);
+          off[u] = ((int64_t)(r0 + b) * kpad + i) * NC;
+          cnt = u + 1;
+        }
+      }
+      v4f x0[4], x1[4], x2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < cnt) {
+          x0[u] = cv[off[u] + lane];
+          x1[u] = cv[off[u] + 64 + lane];
+          x2[u] = third ? cv[off[u] + 128 + lane] : a2;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < cnt) {
+          a0 += x0[u];
+          a1 += x1[u];
+          if (third) a2 += x2[u];
+        }
+      }
+    }
+  }
+  v4f* d = reinterpret_cast<v4f*>(dkv + s * BwmCfg::DQK);
+  d[lane] += a0;
+  d[lane + 64] += a1;
+  if (third) d[lane + 128] += a2;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -414,7 +559,29 @@ bool mla_bwd_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k) {
   return D_qk == BwmCfg::DQK && D_v == BwmCfg::DV && H >= 1 && H <= 128 && k >= 1 && k <= BWM_MAX_K;
 }
 
-size_t mla_bwd_workspace_bytes(int64_t T, int32_t H) { return (size_t)T * H * sizeof(float); }
+namespace {
+struct BwmLayout {
+  int32_t Rs, Hp, kpad;
+  size_t dsp, contrib, pos, total;  // byte offsets and size
+};
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+BwmLayout bwm_layout(int64_t T, int64_t S, int32_t H, int32_t k) {
+  BwmLayout L{};
+  L.Rs = (int32_t)std::min<int64_t>(T, BWM_CHUNK_ROWS);
+  L.Hp = H <= 64 ? 64 : 128;
+  L.kpad = (k + BWM_KB - 1) / BWM_KB * BWM_KB;
+  L.dsp = 0;
+  L.contrib = align256((size_t)L.Rs * 2 * L.Hp * L.kpad * sizeof(uint16_t));
+  L.pos = L.contrib + align256((size_t)L.Rs * L.kpad * BwmCfg::DQK * sizeof(float));
+  L.total = L.pos + align256((size_t)S * L.Rs * sizeof(int32_t));
+  return L;
+}
+}  // namespace
+
+size_t mla_bwd_workspace_bytes(int64_t T, int64_t S, int32_t H, int32_t k) {
+  if (T <= 0 || S <= 0 || H <= 0 || k <= 0) return 0;
+  return bwm_layout(T, S, H, k).total;
+}
 
 hipError_t launch_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* lse,
                                  const uint16_t* dout, int64_t T, int64_t S, int32_t H, int32_t k, int64_t q_start,
@@ -424,19 +591,44 @@ hipError_t launch_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const in
   hipError_t e = launch("fill_zero_kernel", fill_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
                         stream, dkv, n4);
   if (e != hipSuccess || T <= 0) return e;
-  float* delta = reinterpret_cast<float*>(workspace);
-  for (const void* kern : {(const void*)sparse_mla_bwd_kernel<false>, (const void*)sparse_mla_bwd_kernel<true>}) {
+  const BwmLayout L = bwm_layout(T, S, H, k);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  uint16_t* dsp = reinterpret_cast<uint16_t*>(ws + L.dsp);
+  float* contrib = reinterpret_cast<float*>(ws + L.contrib);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  const void* contrib_kernel =
+      L.Hp == 64 ? (const void*)mla_bwd_dkv_contrib_kernel<2> : (const void*)mla_bwd_dkv_contrib_kernel<4>;
+  for (const void* kern : {(const void*)sparse_mla_bwd_dq_kernel, contrib_kernel}) {
     e = set_max_dynamic_lds(kern);
     if (e != hipSuccess) return e;
   }
   const float scale_log2 = sm_scale * BWM_LOG2E;
-  const dim3 grid((unsigned)T, (unsigned)((H + BWM_HEADS - 1) / BWM_HEADS));
-  e = launch("sparse_mla_bwd_kernel<dq>", sparse_mla_bwd_kernel<false>, grid, dim3(BW_THREADS), bwm_smem_bytes(false),
-             stream, q, kv, idx, lse, delta, dout, S, q_start, H, k, scale_log2, sm_scale, dq, dkv);
-  if (e != hipSuccess) return e;
-  return launch("sparse_mla_bwd_kernel<dkv>", sparse_mla_bwd_kernel<true>, grid, dim3(BW_THREADS),
-                bwm_smem_bytes(true), stream, q, kv, idx, lse, delta, dout, S, q_start, H, k, scale_log2, sm_scale,
-                dq, dkv);
+  for (int64_t t0 = 0; t0 < T; t0 += L.Rs) {
+    const int32_t Rc = (int32_t)std::min<int64_t>(L.Rs, T - t0);
+    const int64_t nkeys = std::min<int64_t>(S, q_start + t0 + Rc);  // keys any row of the chunk can name
+    e = launch("sparse_mla_bwd_dq_kernel", sparse_mla_bwd_dq_kernel, dim3((unsigned)Rc, (unsigned)(L.Hp / BWM_HEADS)),
+               dim3(BW_THREADS), bwm_dq_smem_bytes(), stream, q, kv, idx, lse, dout, S, q_start, H, k, scale_log2,
+               sm_scale, dq, t0, L.Hp, L.kpad, dsp);
+    if (e != hipSuccess) return e;
+    const int64_t npos = nkeys * L.Rs;
+    e = launch("fill_i32_kernel", fill_i32_kernel, dim3((unsigned)((npos + 255) / 256)), dim3(256), 0, stream, pos,
+               npos, BWM_NO_ENTRY);
+    if (e != hipSuccess) return e;
+    e = launch("mla_bwd_pos_kernel", mla_bwd_pos_kernel, dim3((unsigned)Rc), dim3(256), 0, stream, idx, t0, L.Rs, S,
+               q_start, k, pos);
+    if (e != hipSuccess) return e;
+    if (L.Hp == 64)
+      e = launch("mla_bwd_dkv_contrib_kernel", mla_bwd_dkv_contrib_kernel<2>, dim3((unsigned)Rc), dim3(BW_THREADS),
+                 bwm_contrib_smem_bytes(), stream, q, dout, idx, dsp, pos, t0, L.Rs, S, q_start, H, k, L.kpad, contrib);
+    else
+      e = launch("mla_bwd_dkv_contrib_kernel", mla_bwd_dkv_contrib_kernel<4>, dim3((unsigned)Rc), dim3(BW_THREADS),
+                 bwm_contrib_smem_bytes(), stream, q, dout, idx, dsp, pos, t0, L.Rs, S, q_start, H, k, L.kpad, contrib);
+    if (e != hipSuccess) return e;
+    e = launch("mla_bwd_dkv_reduce_kernel", mla_bwd_dkv_reduce_kernel, dim3((unsigned)((nkeys + 3) / 4)), dim3(256),
+               0, stream, pos, L.Rs, Rc, contrib, L.kpad, nkeys, dkv);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace dsa

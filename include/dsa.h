@@ -148,15 +148,16 @@ dsa_status_t dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int
  *   q, kv, indices, sm_scale, q_start as in the forward; lse [T][H] f32 is the forward's output on
  *   the same inputs (D is summed from p and dp here, not taken from a rounded forward output);
  *   dout [T][H][D_v] bf16; dq [T][H][D_qk] f32 and dkv [S][D_qk] f32 are outputs (every entry
- *   written; keys no list selects get 0).  Workspace: dsa_sparse_mla_bwd_workspace_size(T, H)
- *   bytes (the per-(t, h) D, passed between the two kernels).  dkv is accumulated with fp32
- *   atomic adds across query rows and head halves, so its low bits depend on their order (dq is
- *   deterministic).  ds and p enter the head contraction of dkv as fp16 (ds times sm_scale), dq's
- *   contraction as a bf16 pair (16 significant bits); dout and q are converted bf16 -> fp16 for
- *   dkv (exact for |x| in [2^-14, 65504]).  Supported: (D_qk, D_v) = (576, 512), 1 <= H <= 128,
- *   1 <= k <= 2048; T = 0 with S > 0 zeroes dkv.
+ *   written; keys no list selects get 0).  Workspace: dsa_sparse_mla_bwd_workspace_size(T, S, H, k)
+ *   bytes, the buffers of one chunk of up to 512 query rows (fp16 ds and p per head and entry, one
+ *   fp32 576-wide dkv contribution per entry, a key-to-entry map over S keys: about 3 GB at 512 rows,
+ *   H = 128, k = 2048, S = 32768).  Both outputs are deterministic: each dkv row is the sum of its
+ *   contributions in (query row, entry) order, with no atomic adds.  ds and p enter the head
+ *   contraction of dkv as fp16 (ds times sm_scale), dq's contraction as a bf16 pair (16 significant
+ *   bits); dout and q are converted bf16 -> fp16 for dkv (exact for |x| in [2^-14, 65504]).
+ *   Supported: (D_qk, D_v) = (576, 512), 1 <= H <= 128, 1 <= k <= 2048; T = 0 with S > 0 zeroes dkv.
  */
-size_t dsa_sparse_mla_bwd_workspace_size(int64_t T, int32_t H);
+size_t dsa_sparse_mla_bwd_workspace_size(int64_t T, int64_t S, int32_t H, int32_t k);
 dsa_status_t dsa_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const int32_t *indices, const float *lse,
                                 const uint16_t *dout, int64_t T, int64_t S, int32_t H,
                                 int32_t D_qk, int32_t D_v, int32_t k, int64_t q_start, float sm_scale, float *dq,

@@ -230,8 +230,12 @@ def test_topk_noalloc_rejects_on_the_host(lib):
 def test_sparse_mla_bwd_argument_errors(lib):
     f = lib.dsa_sparse_mla_bwd
     sm = ctypes.c_float(0.07)
-    need = lib.dsa_sparse_mla_bwd_workspace_size(8, 128)
-    assert need == 8 * 128 * 4 and lib.dsa_sparse_mla_bwd_workspace_size(0, 128) == 0
+    need = lib.dsa_sparse_mla_bwd_workspace_size(8, 100, 128, 2048)
+    # chunk buffers: fp16 ds / p tiles, fp32 contributions, the key map
+    assert need == 8 * 2 * 128 * 2048 * 2 + 8 * 2048 * 576 * 4 + (100 * 8 * 4 + 255) // 256 * 256
+    assert lib.dsa_sparse_mla_bwd_workspace_size(0, 100, 128, 2048) == 0
+    big = lib.dsa_sparse_mla_bwd_workspace_size(100000, 131072, 64, 2047)   # 512-row chunks, heads to 64
+    assert big == 512 * 2 * 64 * 2048 * 2 + 512 * 2048 * 576 * 4 + 131072 * 512 * 4
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, 100, 128, 576, 512, 2048, 0, sm, FAKE, FAKE, FAKE, need, None]
     bad = list(args)
     bad[8] = 80                                                    # D_qk (only 576 / 512 is built)
