@@ -61,11 +61,9 @@ struct BwmCfg {
   // dKV contribution kernel: wave w owns columns [144 w, 144 w + 144): 9 tiles of 16 of dK, and the
   // dV tiles among them (columns below 512: 9, 9, 9, 5)
   static constexpr int CW = DQK / 4, NCT = CW / 16;       // 144, 9
-  static constexpr int TILE_STRIDE = BWM_KB * 2 + 16;     // bytes per head row of an fp16 [head][entry] tile
   static constexpr int STAGE_Q_STRIDE = DQK * 2 + 16;     // row stride of the staged Q / G (bf16)
   static constexpr int STAGE_BYTES = 128 * STAGE_Q_STRIDE;
   static_assert(DMA_INSTR % 4 == 0 && 2 * DMA_PW <= WAVE, "gather transfers split evenly over 4 waves");
-  static_assert(2 * 128 * TILE_STRIDE <= STAGE_BYTES, "the tiles reuse the staging space");
   // chunk XOR of gathered row r (the forward's swizzle: conflict-free fragment and transposing reads)
   static __host__ __device__ __forceinline__ constexpr int swz(int r) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
@@ -75,7 +73,8 @@ struct BwmCfg {
 
 constexpr size_t bwm_dq_smem_bytes() {
   using C = BwmCfg;
-  return 2 * (size_t)C::K_BYTES + C::SX_BYTES + (size_t)(BWM_MAX_K + 4 + BWM_MAX_K / BWM_KB) * 4;
+  return 2 * (size_t)C::K_BYTES + C::SX_BYTES + (size_t)(BWM_MAX_K + 4 + BWM_MAX_K / BWM_KB) * 4 +
+         4 * BWM_KB * 32 * 2;  // + the waves' transpose tiles
 }
 constexpr size_t bwm_contrib_smem_bytes() {
   return (size_t)BwmCfg::STAGE_BYTES + (BWM_MAX_K / BWM_KB) * 4 + (size_t)BWM_MAX_K * 4;
@@ -121,7 +120,7 @@ __device__ __forceinline__ void list_validity(const int32_t* __restrict__ list, 
 }
 
 // dq of rows t0 .. t0 + R - 1 (latest first) and the chunk's fp16 ds / p tiles
-// dsp [R][2][Hp][kpad] (which 0: sm_scale ds, 1: p; heads past H and invalid entries hold 0).
+// dsp [R][2][kpad][Hp] (which 0: sm_scale ds, 1: p; heads past H and invalid entries hold 0).
 __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const float* __restrict__ lse, const uint16_t* __restrict__ dout, int64_t S, int64_t q_start, int32_t H,
@@ -138,6 +137,8 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_dq_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = wave >> 1, hf = wave & 1;
   const int l32 = lane & 31, lh = lane >> 5;
+  // this wave's [32 entries][32 heads] fp16 transpose tile
+  uint16_t* ttile = reinterpret_cast<uint16_t*>(vmask + BWM_MAX_K / BWM_KB) + wave * BWM_KB * 32;
   const int r = (int)gridDim.x - 1 - (int)blockIdx.x;  // latest rows first (longest lists)
   const int64_t t = t0 + r;
   const int h0 = blockIdx.y * BWM_HEADS;
@@ -236,8 +237,9 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_dq_kernel(
   const int nblk = live ? 64 - __clzll(live) : 0;
   const v4f* Sx_peer = Sx + ((wave ^ 1) * 2) * 4 * WAVE + lane;
   v4f* Sx_mine = Sx + (wave * 2) * 4 * WAVE + lane;
-  // this wave's ds (f = 0) or p (f = 1) tile row of its lane's head
-  uint16_t* tile_row = dsp + ((int64_t)(r * 2 + hf) * Hp + head) * kpad;
+  // this wave's ds (f = 0) or p (f = 1) tile: lane L stores heads 16 (L % 2) .. + 15 of the wave's
+  // group, entry L / 2 of the block
+  uint16_t* tile_dst = dsp + ((int64_t)(r * 2 + hf) * kpad + (lane >> 1)) * Hp + h0 + g * 32 + 16 * (lane & 1);
 
   // the blocks are walked twice (pass 0: D; pass 1: dQ and the tiles)
   for (int pass = 0; pass < 2; ++pass) {
@@ -289,13 +291,18 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_dq_kernel(
     }
     if (pass == 0) continue;  // D only
 
-    // ---- the fp16 tiles: keys 8 qd + 4 lh + 0..3 of the block, four per 8-byte store
+    // ---- the fp16 tile of this wave (entry 8 (rr / 4) + 4 lh + rr % 4 of the block, head l32),
+    // transposed through LDS to head-contiguous rows and stored 16 bytes per lane twice
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      s16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = f32_to_f16_bits(hf == 0 ? ds[4 * qd + e] * sm_scale : pr[4 * qd + e]);
-      *reinterpret_cast<s16x4*>(tile_row + blk * BWM_KB + 8 * qd + 4 * lh) = v;
+    for (int rr = 0; rr < 16; ++rr)
+      ttile[(8 * (rr >> 2) + 4 * lh + (rr & 3)) * 32 + l32] =
+          (uint16_t)f32_to_f16_bits(hf == 0 ? ds[rr] * sm_scale : pr[rr]);
+    {
+      const v4i* src = reinterpret_cast<const v4i*>(ttile + (lane >> 1) * 32 + 16 * (lane & 1));
+      const v4i w0 = src[0], w1 = src[1];
+      v4i* dst = reinterpret_cast<v4i*>(tile_dst + (int64_t)blk * BWM_KB * Hp);
+      dst[0] = w0;
+      dst[1] = w1;
     }
 
     // ---- dQ^T[d][head] += K^T[d][key] dS^T[key][head]: B = ds (hi, lo) for key steps m = 0, 1
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void mla_bwd_dkv_contrib_kernel(
   using C = BwmCfg;
   constexpr int HP = NHS * 32;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* stage = smem;  // Q / G staging, then the ds and p tiles [2][HP][TILE_STRIDE]
+  uint8_t* stage = smem;  // Q / G staging
   uint32_t* vmask = reinterpret_cast<uint32_t*>(smem + C::STAGE_BYTES);
   int32_t* prim = reinterpret_cast<int32_t*>(vmask + BWM_MAX_K / BWM_KB);
 
@@ -425,55 +432,57 @@ __global__ __launch_bounds__(BW_THREADS, 1) void mla_bwd_dkv_contrib_kernel(
 #pragma unroll
     for (int kk = 0; kk < NHS; ++kk)
       GT[ct][kk] = ct < nv ? frag(col_w + ct * 16, kk) : (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-  const bool has_dup = __syncthreads_or(dup);  // also: staging reads done before the tiles overwrite it
+  const bool has_dup = __syncthreads_or(dup);
 
-  // B operands: (entries 16 kt .. + 15) x (heads 32 kk .. + 31) of tile `which`, two transposing
-  // reads of head rows 32 kk + 8 grp + {0..3}, {4..7}, entry columns 16 kt + 4 (a % 4)
-  auto tfrag = [&](int which, int kt, int kk) {
-    s16x8 v;
+  // B operands: (entries 16 kt .. + 15) x (heads 32 kk .. + 31) of tile `which`: lane l reads the
+  // eight heads 32 kk + 8 (l / 16) .. + 7 of entry 16 kt + l % 16, one 16-byte load
+  const uint16_t* tiles_g = dsp + (int64_t)r * 2 * kpad * HP + (int64_t)a * HP + 8 * grp;
+  auto load_frags = [&](int blk, s16x8 (&F)[2][2][NHS]) {
 #pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      const int row = 32 * kk + 8 * grp + 4 * hlf + (a >> 2);
-      const s16x4 w = lds_transpose_read16(stage + (which * HP + row) * C::TILE_STRIDE + (16 * kt + 4 * (a & 3)) * 2);
+    for (int which = 0; which < 2; ++which)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * hlf + e] = w[e];
-    }
-    return v;
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int kk = 0; kk < NHS; ++kk)
+          F[which][kt][kk] = *reinterpret_cast<const s16x8*>(
+              tiles_g + ((int64_t)which * kpad + blk * BWM_KB + 16 * kt) * HP + 32 * kk);
   };
   const int nblk = (k + BWM_KB - 1) / BWM_KB;
-  const uint16_t* tiles_g = dsp + (int64_t)r * 2 * HP * kpad;
-  for (int blk = 0; blk < nblk; ++blk) {
-    if (vmask[blk] == 0u) continue;  // no valid entry: nothing to contribute (workgroup-uniform)
-    // tiles of the block: 2 x HP head rows of 64 bytes, 16 bytes per thread and step
-    for (int p = tid; p < 2 * HP * 4; p += BW_THREADS) {
-      const int row = p >> 2, c = p & 3;  // row = which * HP + head
-      const v4i v = *reinterpret_cast<const v4i*>(tiles_g + (int64_t)row * kpad + blk * BWM_KB + c * 8);
-      *reinterpret_cast<v4i*>(stage + row * C::TILE_STRIDE + c * 16) = v;
-    }
-    __syncthreads();
+  // live blocks (at least one valid entry) in order; the rest contribute nothing
+  auto next_live = [&](int b) {
+    while (b < nblk && vmask[b] == 0u) ++b;
+    return b;
+  };
+  s16x8 F[2][2][NHS];
+  int blk = next_live(0);
+  if (blk < nblk) load_frags(blk, F);
+  while (blk < nblk) {
+    s16x8 cur[2][2][NHS];
+#pragma unroll
+    for (int which = 0; which < 2; ++which)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int kk = 0; kk < NHS; ++kk) cur[which][kt][kk] = F[which][kt][kk];
+    const int nxt = next_live(blk + 1);
+    if (nxt < nblk) load_frags(nxt, F);  // in flight during this block's MFMAs and stores
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      s16x8 Bd[NHS], Bp[NHS];
-#pragma unroll
-      for (int kk = 0; kk < NHS; ++kk) {
-        Bd[kk] = tfrag(0, kt, kk);
-        Bp[kk] = tfrag(1, kt, kk);
-      }
       // accumulator lane l: columns 4 (l / 16) + 0..3 of the tile, entry 16 kt + l % 16
       float* dst = contrib + ((int64_t)r * kpad + blk * BWM_KB + 16 * kt + a) * C::DQK + col_w + 4 * grp;
 #pragma unroll
       for (int ct = 0; ct < C::NCT; ++ct) {
         v4f c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < NHS; ++kk) c = mfma_f16_16x16x32(QT[ct][kk], Bd[kk], c);
+        for (int kk = 0; kk < NHS; ++kk) c = mfma_f16_16x16x32(QT[ct][kk], cur[0][kt][kk], c);
         if (ct < nv) {
 #pragma unroll
-          for (int kk = 0; kk < NHS; ++kk) c = mfma_f16_16x16x32(GT[ct][kk], Bp[kk], c);
+          for (int kk = 0; kk < NHS; ++kk) c = mfma_f16_16x16x32(GT[ct][kk], cur[1][kt][kk], c);
         }
         *reinterpret_cast<v4f*>(dst + ct * 16) = c;
       }
     }
-    __syncthreads();  // tiles read before the next block's overwrite them
+    blk = nxt;
   }
 
   if (has_dup) {
@@ -499,7 +508,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void mla_bwd_dkv_contrib_kernel(
 }
 
 // dkv[s] += the slots the map names for key s, in row order (one wave per key; lane c holds the
-// 16-byte column chunks c, c + 64 and, below 16, c + 128).
+// 16-byte column chunks c, c + 64 and, below 16, c + 128).  The slots are read once: streaming loads.
 __global__ __launch_bounds__(256) void mla_bwd_dkv_reduce_kernel(const int32_t* __restrict__ pos, int32_t Rs,
                                                                  int32_t Rc, const float* __restrict__ contrib,
                                                                  int32_t kpad, int64_t nkeys, float* __restrict__ dkv) {
@@ -511,9 +520,14 @@ __global__ __launch_bounds__(256) void mla_bwd_dkv_reduce_kernel(const int32_t* 
   const int32_t* ps = pos + s * Rs;
   const v4f* cv = reinterpret_cast<const v4f*>(contrib);
   v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-  for (int r0 = 0; r0 < Rc; r0 += WAVE) {
-    const int32_t v = r0 + lane < Rc ? ps[r0 + lane] : BWM_NO_ENTRY;
-    uint64_t m = __ballot(v != BWM_NO_ENTRY);
+  // the key's map entries of every row of the chunk, all requested at once
+  constexpr int NJ = BWM_CHUNK_ROWS / WAVE;
+  int32_t v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) v[j] = j * WAVE + lane < Rc ? ps[j * WAVE + lane] : BWM_NO_ENTRY;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    uint64_t m = __ballot(v[j] != BWM_NO_ENTRY);
     while (m) {
       // up to four slots in flight, added in row order
       int64_t off[4];
@@ -524,8 +538,8 @@ __global__ __launch_bounds__(256) void mla_bwd_dkv_reduce_kernel(const int32_t* 
         if (m) {
           const int b = __builtin_ctzll(m);
           m &= m - 1;
-          const int32_t i = __shfl(v, b);
-          off[u] = ((int64_t)(r0 + b) * kpad + i) * NC;
+          const int32_t i = __shfl(v[j], b);
+          off[u] = ((int64_t)(j * WAVE + b) * kpad + i) * NC;
           cnt = u + 1;
         }
       }
@@ -533,9 +547,9 @@ __global__ __launch_bounds__(256) void mla_bwd_dkv_reduce_kernel(const int32_t* 
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (u < cnt) {
-          x0[u] = cv[off[u] + lane];
-          x1[u] = cv[off[u] + 64 + lane];
-          x2[u] = third ? cv[off[u] + 128 + lane] : a2;
+          x0[u] = __builtin_nontemporal_load(cv + off[u] + lane);
+          x1[u] = __builtin_nontemporal_load(cv + off[u] + 64 + lane);
+          x2[u] = third ? __builtin_nontemporal_load(cv + off[u] + 128 + lane) : a2;
         }
       }
 #pragma unroll
