@@ -308,23 +308,27 @@ def run_decode(wl, args, dev, cpu_threads: int = 0):
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    # profiled pass: an event before the call and one after each of its kernels; an unprofiled call
-    # ahead of each keeps the GPU busy while the host enqueues, so the first interval holds no
-    # host-side launch latency
+    # profiled pass: an event before the call and one after each of its kernels.  The events are
+    # created (and their HIP events materialised) up front, and two unprofiled calls ahead of each
+    # profiled one keep the GPU busy while the host enqueues, so no interval holds host latency.
     nk = 8
-    prof = []
+    prof = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    for evp in prof:
+        for ev in evp:
+            ev.record(stream)
+    torch.cuda.synchronize()
     names = []
-    for _ in range(args.steps):
+    for evp in prof:
+        step()
         step()
         if flush is not None:
             flush.zero_()
-        evp = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
         evp[0].record(stream)
         dsa.dsa_profile_begin(evp[1:])
         step()
         names = dsa.dsa_profile_end()
-        prof.append(evp[:len(names) + 1])
     torch.cuda.synchronize()
+    prof = [evp[:len(names) + 1] for evp in prof]
     kms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(names))] for e in prof]).mean(axis=0)
     if args.copy_calibration:
         copy_calibration(dev)
@@ -639,16 +643,20 @@ def run_mla_bwd(name, args, dev):
     # stage events after every launch (a zero fill, then five kernels per chunk of 512 rows); an
     # unprofiled call ahead of each keeps the GPU busy while the host enqueues
     nev = 2 + 5 * (-(-T // 512))
-    prof, names = [], []
-    for _ in range(args.steps):
+    prof = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for ev in prof:
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    names = []
+    for ev in prof:
         step()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
         ev[0].record(stream)
         dsa.dsa_profile_begin(ev[1:])
         step()
         names = dsa.dsa_profile_end()
-        prof.append(ev[:len(names) + 1])
     torch.cuda.synchronize()
+    prof = [ev[:len(names) + 1] for ev in prof]
     per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(names))] for e in prof])
     step_ms = per.sum(axis=1)
     # per kernel: its launches summed within a call, averaged over the calls
