@@ -2,19 +2,30 @@
 // Selection"; DeepSeek-V3.2-Exp summary page, section "Method": top-k = 2048): for query row t,
 // the k highest scores among its n_t visible keys; equal scores go to the lower key index.
 //
-// A workgroup of 512 threads holds up to 32768 scores of one row in registers as
-// order-preserving uint32 keys and runs an exact radix select over them: the first digit
-// window starts at the highest bit where the row's minimum and maximum keys differ, each
-// pass builds an LDS histogram of an 11-bit digit among the keys that still match the
-// threshold's known prefix, and at most three passes pin the k-th largest key exactly.
-// Emission is an ordered compaction: per group of 256 positions, wave ballots give every
-// selected element its rank (mbcnt), the slots are staged in LDS and the index list leaves in
-// coalesced 16-byte stores.  The output is deterministic: every key above the threshold in index
-// order, then the lowest-index ties.
+// A row is processed in chunks of up to 32768 scores, one workgroup of 256 threads per chunk and
+// about 33 KB of LDS, so four chunks are in flight per CU.  The chunk is streamed from memory
+// instead of held in registers (a second read of a chunk just read comes from the caches):
+//   1. one pass over a quarter of the chunk samples one score per 16-byte unit (2048 samples);
+//      an exact radix select over the samples puts a pivot a safe margin below the expected
+//      position of the k-th largest score;
+//   2. one pass over the whole chunk appends every score at or above the pivot (as an
+//      order-preserving uint32 key and its position) to an LDS candidate list, one LDS atomic
+//      per wave and batch;
+//   3. an exact radix select over the candidates (11-bit digits, the first window starting at
+//      the highest bit where their maximum and minimum differ) gives the threshold key tau and
+//      the number of its copies to take; every element >= tau is a candidate, so this is exact;
+//   4. ordered emission: candidates set their position's bit in one of two LDS bitmaps (above
+//      tau / equal to tau), a block scan of the bit counts gives every selected position its
+//      output slot, and the index list is staged in LDS and stored with 16-byte stores.
+// When the candidates cannot hold the selection (fewer than k, or more than 4096: an unlucky
+// sample, heavy ties, or k itself large), the radix select and the bitmaps run over the whole
+// chunk by streaming passes instead.  The output is deterministic: every key above the threshold
+// in index order, then the lowest-index ties.
 //
 // Rows longer than 32768 are cut into chunks; each chunk emits its own top-k candidates
-// (key, index) and a merge pass runs the same select over the concatenated candidates.  This
-// is exact: an element in the row's top-k is in its chunk's top-k under the same order.
+// (key, index) and a merge pass (one 512-thread workgroup per row, candidates in registers)
+// runs the same select over the concatenated candidates.  This is exact: an element in the row's
+// top-k is in its chunk's top-k under the same order.
 #include "dsa_internal.hpp"
 
 namespace dsa {
@@ -28,18 +39,10 @@ constexpr int64_t TK_CHUNK = (int64_t)TK_THREADS * TK_CHUNK_EPT;
 constexpr int TK_MERGE_EPT = 16;  // 8192 candidates per merge
 constexpr int TK_STAGE = 2048;    // index lists up to this length are staged in LDS
 
-constexpr int TK_CAND = 4096;     // candidate keys of the sampled threshold search
-constexpr int TK_CAND_EPT = TK_CAND / TK_THREADS;
-
-constexpr int TK_MAP_WORDS = TK_CHUNK_EPT * TK_THREADS / 32;  // one bit per position of a chunk
-
+// merge kernel state
 struct TopkShared {
   uint32_t hist[TK_BINS];
   int32_t stage[TK_STAGE];
-  uint32_t cand[TK_CAND];
-  uint32_t cpos[TK_CAND];           // position of each candidate in the chunk
-  uint32_t gtmap[TK_MAP_WORDS];     // selected positions above tau
-  uint32_t eqmap[TK_MAP_WORDS];     // positions equal to tau
   uint32_t wsum[TK_WAVES][2];
   uint32_t red[TK_WAVES][2];
   uint32_t sel_bin, sel_above, sel_cnt;
@@ -76,10 +79,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 __device__ __forceinline__ void hist_clear(TopkShared& sh) {
   for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
   if (threadIdx.x == 0) sh.small_n = 0;
-  for (int i = threadIdx.x; i < TK_MAP_WORDS; i += TK_THREADS) {
-    sh.gtmap[i] = 0;
-    sh.eqmap[i] = 0;
-  }
 }
 
 // Maximum and minimum of the valid keys (0 = no element) of the workgroup.
@@ -233,140 +232,6 @@ __device__ void radix_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx
   k_rem = need;
 }
 
-// Exact threshold search over a chunk of cn > k valid elements (maximum mx, minimum mn) that
-// touches most keys once (returns the number of candidates left in sh.cand / sh.cpos, or 0 when
-// the select ran over all keys instead): the radix select over a 1-in-16 sample of the keys puts a pivot (a
-// sample order statistic) a safe margin below the expected position of the k-th largest key;
-// the keys at or above the pivot are counted, and when there
-// are between k and TK_CAND of them they are compacted into LDS, where the radix select finds
-// tau and the tie count among them (every key >= tau is a candidate, so both are exact).
-// Outside that window (an unlucky or adversarial sample) the radix select runs over all keys.
-// Chunks of at most TK_CAND elements skip the sample.  The histogram is zero on entry and exit.
-template <int EPT>
-__device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32_t k, uint32_t mx, uint32_t mn,
-                                      TopkShared& sh, uint32_t& tau, uint32_t& k_rem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (mx == mn) {
-    tau = mx;
-    k_rem = k;
-    return 0;
-  }
-  uint32_t pivot = mn;  // every valid key
-  if (cn > TK_CAND) {
-    // sample element 17 i (i < EPT / 16) of every thread; lane l's copy sits at the lane-0 position + 4 l
-    // (elem_pos), so the number of valid samples follows from cn without a reduction
-    constexpr int NS = EPT / 16;  // sampled elements per thread, 17 apart
-    static_assert(NS >= 1 && 17 * (NS - 1) < EPT, "sample positions");
-    uint32_t smp[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) smp[i] = key[17 * i];
-    uint32_t m = 0;
-    for (int w = 0; w < TK_WAVES; ++w)
-      for (int i = 0; i < NS; ++i) {
-        const int64_t rest = cn - elem_pos<EPT>(w, 0, 17 * i);  // valid lanes: 4 l < rest
-        m += (uint32_t)min<int64_t>(WAVE, max<int64_t>(0, (rest + 3) / 4));
-      }
-    // rank sought among the m sampled keys: the expected rank of the k-th largest key plus four
-    // binomial standard deviations; none (the pivot stays mn) when the sample is too small
-    const float er = (float)k * (float)m / (float)cn;
-    const float w = er + 4.0f * sqrtf(er) + 16.0f;
-    if (w <= (float)m) {
-      // Digit passes over the samples toward the one of rank w, stopped as soon as the lower edge
-      // of the bin holding it leaves few enough samples at or above it: the pivot only has to keep
-      // between k and TK_CAND keys, not be that sample exactly.
-      const int hb = 31 - __clz(mx ^ mn);  // mx > mn here
-      int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
-      int bits = hb - shift + 1;
-      uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));
-      const uint32_t w0 = (uint32_t)w;
-      uint32_t need = w0;
-      const float per_sample = (float)cn / (float)m;
-      while (true) {
-        uint32_t bin, above, cnt;
-        hist_pass<NS>(smp, shift, bits, prefix, sh, [&](uint32_t) { return need; }, bin, above, &cnt);
-        need -= above;
-        prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
-        if (shift == 0 || (float)(w0 - need + cnt) * per_sample <= 0.75f * (float)TK_CAND) break;
-        bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
-        shift -= bits;
-      }
-      pivot = max(prefix << shift, mn);  // lower edge of the bin (prefix holds every bit above shift)
-    }
-  }
-  uint32_t c = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) c += key[e] >= pivot;  // pivot >= mn >= 1: valid keys only
-  // exclusive offsets of this thread's candidates
-  const uint32_t incl = wave_incl_scan(c, lane);
-  if (lane == 63) sh.wsum[wave][1] = incl;
-  __syncthreads();
-  uint32_t off = incl - c, total = 0;
-  for (int i = 0; i < TK_WAVES; ++i) {
-    const uint32_t w = sh.wsum[i][1];
-    if (i < wave) off += w;
-    total += w;
-  }
-  if (total < k || total > (uint32_t)TK_CAND) {  // workgroup-uniform
-    radix_select<EPT>(key, k, mx, mn, sh, tau, k_rem);
-    return 0;
-  }
-  // an opaque copy of the pivot: the counting loop's 64 compare masks are recomputed here rather
-  // than kept (in scalar registers) across the scan
-  uint32_t pv = __builtin_amdgcn_readfirstlane(pivot);
-  asm volatile("" : "+s"(pv));
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (key[e] >= pv) {
-      sh.cand[off] = key[e];
-      sh.cpos[off] = (uint32_t)elem_pos<EPT>(wave, lane, e);
-      ++off;
-    }
-  __syncthreads();
-  uint32_t ck[TK_CAND_EPT];
-#pragma unroll
-  for (int j = 0; j < TK_CAND_EPT; ++j) {
-    const uint32_t i = (uint32_t)(tid + j * TK_THREADS);
-    ck[j] = i < total ? sh.cand[i] : 0u;
-  }
-  radix_select<TK_CAND_EPT>(ck, k, mx, pivot, sh, tau, k_rem);
-  return total;
-}
-
-// Ordered emission from the candidate list (every selected element is a candidate): each
-// candidate above tau sets its position's bit in one LDS bitmap, each equal to tau in another;
-// thread t then owns positions 64 t .. 64 t + 63 (two words of each map), and one block scan of
-// its two bit counts (packed in one word) gives its output offsets: every position above tau in
-// ascending order, then the first k_rem positions equal to tau.  The maps are zero on entry.
-template <typename Emit>
-__device__ void emit_candidates(TopkShared& sh, uint32_t total, uint32_t tau, uint32_t k, uint32_t k_rem,
-                                Emit emit) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (uint32_t i = (uint32_t)tid; i < total; i += TK_THREADS) {
-    const uint32_t kk = sh.cand[i], p = sh.cpos[i];
-    if (kk > tau)
-      atomicOr(&sh.gtmap[p >> 5], 1u << (p & 31));
-    else if (kk == tau)
-      atomicOr(&sh.eqmap[p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
-  static_assert(TK_MAP_WORDS == 2 * TK_THREADS, "two map words per thread");
-  uint32_t g0 = sh.gtmap[2 * tid], g1 = sh.gtmap[2 * tid + 1];
-  uint32_t e0 = sh.eqmap[2 * tid], e1 = sh.eqmap[2 * tid + 1];
-  const uint32_t cnt = (uint32_t)(__popc(g0) + __popc(g1)) | ((uint32_t)(__popc(e0) + __popc(e1)) << 16);
-  const uint32_t incl = wave_incl_scan(cnt, lane);
-  if (lane == 63) sh.wsum[wave][0] = incl;
-  __syncthreads();
-  uint32_t off = incl - cnt;
-  for (int i = 0; i < wave; ++i) off += sh.wsum[i][0];
-  uint32_t go = off & 0xFFFFu, eo = off >> 16;
-  const int base = 64 * tid;
-  for (; g0; g0 &= g0 - 1) emit(base + __builtin_ctz(g0), go++);
-  for (; g1; g1 &= g1 - 1) emit(base + 32 + __builtin_ctz(g1), go++);
-  const uint32_t n_gt = k - k_rem;
-  for (; e0 && eo < k_rem; e0 &= e0 - 1) emit(base + __builtin_ctz(e0), n_gt + eo++);
-  for (; e1 && eo < k_rem; e1 &= e1 - 1) emit(base + 32 + __builtin_ctz(e1), n_gt + eo++);
-}
-
 // Number of set bits of a wave mask held by lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m, uint32_t acc) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, acc));
@@ -457,73 +322,418 @@ __device__ __forceinline__ void store_staged(const TopkShared& sh, int32_t* __re
   }
 }
 
-// Load this thread's elements of scores[0 .. n) (1 <= n <= 512 * EPT) as keys (0 past n).  The
-// loads are unconditional so that all of them are in flight before the first one is waited for:
-// a group of four past the end re-reads the row's last aligned group, which is in bounds because
-// rows start 16-byte aligned and their stride is a multiple of four floats.
-template <int EPT>
-__device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t n, uint32_t (&key)[EPT]) {
+// ---------------------------------------------------------------------------------------------
+// Chunk selection (256 threads; the chunk streamed, see the header).
+constexpr int TS_THREADS = 256;
+constexpr int TS_WAVES = TS_THREADS / WAVE;
+constexpr int TS_BPT = TK_BINS / TS_THREADS;          // histogram bins per thread in the suffix scan
+constexpr int TS_UNITS = (int)(TK_CHUNK / 4);          // 16-byte units of a full chunk
+constexpr int TS_UPT = TS_UNITS / TS_THREADS;          // units per thread (32)
+constexpr int TS_BATCH = 8;                            // units in flight per thread
+constexpr int TS_SPT = TS_UPT / 4;                     // sampled units per thread (8)
+constexpr int TS_SAMPLES = TS_THREADS * TS_SPT;        // 2048
+constexpr int TS_CAND = 4096;                          // candidate capacity
+constexpr int TS_CPT = TS_CAND / TS_THREADS;           // candidate slots per thread (16)
+constexpr int TS_MAP_WORDS = (int)(TK_CHUNK / 32);     // one bit per position of a chunk
+constexpr int TS_MPT = TS_MAP_WORDS / TS_THREADS;      // map words per thread (4)
+static_assert(TS_UPT % TS_BATCH == 0 && TS_MPT == 4, "chunk geometry");
+
+struct TsShared {
+  union {                                        // the histogram is zero whenever a select ends,
+    uint32_t hist[TK_BINS];                      // so the bitmaps that reuse it start cleared
+    struct {
+      uint32_t gt[TS_MAP_WORDS];                 // positions above tau
+      uint32_t eq[TS_MAP_WORDS];                 // positions equal to tau
+    } map;
+  } h;
+  union {
+    uint32_t samples[TS_SAMPLES];                // sample keys (0: none)
+    uint16_t cand[TS_CAND];                      // candidate positions in the chunk
+    int32_t stage[TK_STAGE];                     // the staged index list
+  } u;
+  uint32_t wsum[TS_WAVES][2];
+  uint32_t red[TS_WAVES][3];
+  uint32_t sel_bin, sel_above, sel_cnt;
+  uint32_t small[WAVE];
+  uint32_t small_n;
+  uint32_t ccount;                               // candidates appended
+};
+static_assert(2 * TS_MAP_WORDS <= TK_BINS, "the bitmaps fit the histogram");
+
+// Inverse of score_key on the keys of non-NaN scores (key 0x7FFFFFFF, never produced, reads -0.0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Block-wide (max, min - 1, sum) of per-thread values (max 0 / min - 1 0xFFFFFFFF: nothing).
+__device__ __forceinline__ void ts_block_reduce(uint32_t& mx, uint32_t& mnm1, uint32_t& sum, TsShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int last = (int)(((n + 3) & ~(int64_t)3) - 4);
-  v4f v[EPT / 4];
-#pragma unroll
-  for (int q = 0; q < EPT / 4; ++q)
-    v[q] = *reinterpret_cast<const v4f*>(row + min(elem_pos<EPT>(wave, lane, 4 * q), last));
-#pragma unroll
-  for (int q = 0; q < EPT / 4; ++q) {
-    const int p = elem_pos<EPT>(wave, lane, 4 * q);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) key[4 * q + c] = p + c < n ? score_key(v[q][c]) : 0u;
+  mx = wave_max_u32(mx);
+  mnm1 = wave_min_u32(mnm1);
+  for (int o = 32; o > 0; o >>= 1) sum += (uint32_t)__shfl_xor((int)sum, o);
+  if (lane == 0) {
+    sh.red[wave][0] = mx;
+    sh.red[wave][1] = mnm1;
+    sh.red[wave][2] = sum;
+  }
+  __syncthreads();
+  mx = 0;
+  mnm1 = 0xFFFFFFFFu;
+  sum = 0;
+  for (int i = 0; i < TS_WAVES; ++i) {
+    mx = max(mx, sh.red[i][0]);
+    mnm1 = min(mnm1, sh.red[i][1]);
+    sum += sh.red[i][2];
   }
 }
 
-// The selection of one chunk of cn (k < cn <= 512 EPT) elements with EPT elements per thread.
-template <int EPT>
-__device__ __forceinline__ void chunk_select(const float* __restrict__ logits, int64_t ld, int64_t t, int chunk,
-                                             int64_t c0, int64_t cn, bool single, int32_t k,
-                                             int32_t* __restrict__ out_idx, uint32_t* __restrict__ cand_key,
-                                             int32_t* __restrict__ cand_idx, int32_t G, TopkShared& sh) {
-  uint32_t key[EPT];
-  hist_clear(sh);
-  load_keys<EPT>(logits + t * ld + c0, cn, key);
-  uint32_t mx, mn, tau, k_rem;
-  block_minmax<EPT>(key, sh, mx, mn);
-  const uint32_t ncand = sampled_threshold<EPT>(key, cn, (uint32_t)k, mx, mn, sh, tau, k_rem);
-  // emission from the candidates when they hold the selection, else from the registers
-  auto emit = [&](auto&& f) {
-    if (ncand)
-      emit_candidates(sh, ncand, tau, (uint32_t)k, k_rem, f);
-    else
-      emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh, f);
+// One histogram pass over the keys visit() produces (0 = none): as hist_pass, for 256 threads.
+// The histogram is zero on entry and on exit; need must lie in 1 .. (matching keys).
+template <typename Visit>
+__device__ void ts_hist_pass(Visit visit, int shift, int bits, uint32_t prefix, TsShared& sh, uint32_t need,
+                             uint32_t& bin, uint32_t& above_out, uint32_t& cnt_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi_shift = shift + bits;
+  const uint32_t dmask = (1u << bits) - 1u;
+  visit([&](uint32_t kk) {
+    const bool match = kk != 0 && (hi_shift >= 32 ? true : ((kk >> hi_shift) == prefix));
+    if (match) atomicAdd(&sh.h.hist[(kk >> shift) & dmask], 1u);
+  });
+  __syncthreads();
+  // suffix counts: thread t owns the bins TS_BPT (255 - t) .. + TS_BPT - 1 (highest bins first)
+  const int b0 = TS_BPT * (TS_THREADS - 1 - tid);
+  uint32_t h[TS_BPT];
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < TS_BPT; ++i) {
+    h[i] = sh.h.hist[b0 + i];
+    sh.h.hist[b0 + i] = 0;
+    own += h[i];
+  }
+  const uint32_t incl = wave_incl_scan(own, lane);
+  if (lane == 63) sh.wsum[wave][0] = incl;
+  __syncthreads();
+  uint32_t above = incl - own;
+  for (int i = 0; i < wave; ++i) above += sh.wsum[i][0];
+  if (above < need && need <= above + own) {
+    uint32_t a = above;
+    for (int i = TS_BPT - 1; i >= 0; --i) {
+      if (need <= a + h[i]) {
+        sh.sel_bin = (uint32_t)(b0 + i);
+        sh.sel_above = a;
+        sh.sel_cnt = h[i];
+        break;
+      }
+      a += h[i];
+    }
+  }
+  __syncthreads();
+  bin = sh.sel_bin;
+  above_out = sh.sel_above;
+  cnt_out = sh.sel_cnt;
+}
+
+// The end of an exact select once the bin holding the sought rank has cnt <= 64 keys: as
+// small_finish.  sh.small_n is zero on entry and on exit.
+template <typename Visit>
+__device__ void ts_small_finish(Visit visit, int shift, uint32_t prefix, uint32_t cnt, uint32_t need, TsShared& sh,
+                                uint32_t& tau, uint32_t& k_rem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  visit([&](uint32_t kk) {
+    if (kk != 0 && (kk >> shift) == prefix) sh.small[atomicAdd(&sh.small_n, 1u)] = kk;
+  });
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t x = (uint32_t)lane < cnt ? sh.small[lane] : 0u;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t m = 0; m < cnt; ++m) {
+      const uint32_t y = sh.small[m];
+      gt += y > x;
+      eq += y == x;
+    }
+    if ((uint32_t)lane < cnt && gt < need && need <= gt + eq) {  // every copy of tau writes the same
+      sh.sel_bin = x;
+      sh.sel_above = need - gt;
+    }
+    if (lane == 0) sh.small_n = 0;
+  }
+  __syncthreads();
+  tau = sh.sel_bin;
+  k_rem = sh.sel_above;
+}
+
+// Exact select over the keys visit() produces: tau (the k-th largest) and k_rem (how many keys
+// equal to tau are taken).  mx, mn: maximum and a lower bound >= 1 of the valid keys.  Requires at
+// least k valid keys and a zero histogram.
+template <typename Visit>
+__device__ void ts_radix_select(Visit visit, uint32_t k, uint32_t mx, uint32_t mn, TsShared& sh, uint32_t& tau,
+                                uint32_t& k_rem) {
+  if (mx == mn) {
+    tau = mx;
+    k_rem = k;
+    return;
+  }
+  const int hb = 31 - __clz(mx ^ mn);
+  int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
+  int bits = hb - shift + 1;
+  uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));
+  uint32_t need = k;
+  while (true) {
+    uint32_t bin, above, cnt;
+    ts_hist_pass(visit, shift, bits, prefix, sh, need, bin, above, cnt);
+    need -= above;
+    prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
+    if (shift == 0) break;
+    if (cnt <= (uint32_t)WAVE) {  // workgroup-uniform
+      ts_small_finish(visit, shift, prefix, cnt, need, sh, tau, k_rem);
+      return;
+    }
+    bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
+    shift -= bits;
+  }
+  tau = prefix;
+  k_rem = need;
+}
+
+// Ordered emission from the bitmaps: thread t owns positions 128 t .. 128 t + 127 (four words of
+// each map); one block scan of its two bit counts (packed in one word) gives the output slots:
+// every position above tau in ascending order, then the first k_rem positions equal to tau.
+template <typename Emit>
+__device__ void ts_emit_maps(TsShared& sh, uint32_t k, uint32_t k_rem, Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t g[TS_MPT], e[TS_MPT];
+  uint32_t ng = 0, ne = 0;
+#pragma unroll
+  for (int i = 0; i < TS_MPT; ++i) {
+    g[i] = sh.h.map.gt[TS_MPT * tid + i];
+    e[i] = sh.h.map.eq[TS_MPT * tid + i];
+    ng += (uint32_t)__popc(g[i]);
+    ne += (uint32_t)__popc(e[i]);
+  }
+  const uint32_t cnt = ng | (ne << 16);
+  const uint32_t incl = wave_incl_scan(cnt, lane);
+  if (lane == 63) sh.wsum[wave][0] = incl;
+  __syncthreads();  // also: every bitmap word read before the staged list may overwrite LDS
+  uint32_t off = incl - cnt;
+  for (int i = 0; i < wave; ++i) off += sh.wsum[i][0];
+  uint32_t go = off & 0xFFFFu, eo = off >> 16;
+  const uint32_t n_gt = k - k_rem;
+  const int base = 128 * tid;
+#pragma unroll
+  for (int i = 0; i < TS_MPT; ++i)
+    for (uint32_t m = g[i]; m; m &= m - 1) emit(base + 32 * i + __builtin_ctz(m), go++);
+#pragma unroll
+  for (int i = 0; i < TS_MPT; ++i)
+    for (uint32_t m = e[i]; m && eo < k_rem; m &= m - 1) emit(base + 32 * i + __builtin_ctz(m), n_gt + eo++);
+}
+
+// The selection of one chunk of cn (k < cn <= 32768) scores at row (row + 16-byte aligned).
+template <typename Emit>
+__device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t k, TsShared& sh, Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const v4f* row4 = reinterpret_cast<const v4f*>(row);
+  const int nunits = (cn + 3) >> 2;
+  const int last = nunits - 1;
+  // every key of the chunk (0 past cn), streamed in batches of TS_BATCH units per thread; a unit
+  // past the end re-reads the last one (in bounds: rows are 16-byte aligned, their stride a
+  // multiple of four floats)
+  auto stream_keys = [&](auto&& f) {
+    for (int j0 = 0; j0 * TS_THREADS < nunits; j0 += TS_BATCH) {  // workgroup-uniform
+      v4f v[TS_BATCH];
+#pragma unroll
+      for (int b = 0; b < TS_BATCH; ++b) v[b] = row4[min(tid + TS_THREADS * (j0 + b), last)];
+#pragma unroll
+      for (int b = 0; b < TS_BATCH; ++b) {
+        const int p0 = 4 * (tid + TS_THREADS * (j0 + b));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) f(p0 + c < cn ? score_key(v[b][c]) : 0u);
+      }
+    }
   };
-  if (single) {
-    if (k <= TK_STAGE) {
-      emit([&](int pos, uint32_t slot) { sh.stage[slot] = (int32_t)(c0 + pos); });
-      store_staged(sh, out_idx, k);
+
+  // ---- 1. the pivot: every element when the chunk is small, else a radix select over samples
+  float pf = -__builtin_inff();
+  if (cn > TS_CAND) {
+    // sampled units: thread t of wave w reads units t + 256 j for j = w, w + 4, ... (a quarter of
+    // the chunk), sample = the unit's first score
+    uint32_t smx = 0, smnm1 = 0xFFFFFFFFu, m = 0;
+    {
+      v4f v[TS_SPT];
+#pragma unroll
+      for (int i = 0; i < TS_SPT; ++i) v[i] = row4[min(tid + TS_THREADS * (wave + 4 * i), last)];
+#pragma unroll
+      for (int i = 0; i < TS_SPT; ++i) {
+        const int p = 4 * (tid + TS_THREADS * (wave + 4 * i));
+        const uint32_t kk = p < cn ? score_key(v[i][0]) : 0u;
+        sh.u.samples[tid + TS_THREADS * i] = kk;
+        smx = max(smx, kk);
+        smnm1 = min(smnm1, kk - 1u);
+        m += kk != 0;
+      }
+    }
+    ts_block_reduce(smx, smnm1, m, sh);  // its barrier also publishes the samples
+    // rank sought among the m samples: the expected rank of the k-th largest score plus four
+    // binomial standard deviations; none (the pivot stays -inf) when the sample is too small
+    const float er = (float)k * (float)m / (float)cn;
+    const float w = er + 4.0f * sqrtf(er) + 16.0f;
+    if (w <= (float)m && smx != smnm1 + 1u) {
+      auto visit_samples = [&](auto&& f) {
+#pragma unroll
+        for (int i = 0; i < TS_SPT; ++i) f(sh.u.samples[tid + TS_THREADS * i]);
+      };
+      const uint32_t smn = smnm1 + 1u;
+      const int hb = 31 - __clz(smx ^ smn);
+      int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
+      int bits = hb - shift + 1;
+      uint32_t prefix = (hb == 31) ? 0u : (smx >> (hb + 1));
+      const uint32_t w0 = (uint32_t)w;
+      uint32_t need = w0;
+      const float per_sample = (float)cn / (float)m;
+      // digit passes toward the sample of rank w, stopped once the lower edge of the bin holding
+      // it leaves few enough samples at or above it: the pivot only has to keep between k and
+      // TS_CAND scores, not be that sample exactly
+      while (true) {
+        uint32_t bin, above, cnt;
+        ts_hist_pass(visit_samples, shift, bits, prefix, sh, need, bin, above, cnt);
+        need -= above;
+        prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
+        if (shift == 0 || (float)(w0 - need + cnt) * per_sample <= 0.75f * (float)TS_CAND) break;
+        bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
+        shift -= bits;
+      }
+      pf = key_score(max(prefix << shift, smn));  // lower edge of the bin, at least the sample minimum
+    }
+  }
+  // ---- 2. the candidates: the positions of every score >= pf (NaN-free comparison of floats;
+  // the key order is the float order with -0 == +0), appended in batches with one LDS atomic per
+  // wave; a lane visits only its selected bits, so the append costs follow the candidates, not
+  // the chunk
+  const float pv = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(pf)));
+  if (tid == 0) sh.ccount = 0;
+  __syncthreads();  // also: every sample read before the candidate list overwrites them
+  for (int j0 = 0; j0 * TS_THREADS < nunits; j0 += TS_BATCH) {  // workgroup-uniform
+    v4f v[TS_BATCH];
+#pragma unroll
+    for (int b = 0; b < TS_BATCH; ++b) v[b] = row4[min(tid + TS_THREADS * (j0 + b), last)];
+    uint32_t selm = 0;  // bit 4 b + c: unit b, score c selected
+    if (4 * TS_THREADS * (j0 + TS_BATCH) <= cn) {  // every position of the batch visible
+#pragma unroll
+      for (int b = 0; b < TS_BATCH; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) selm |= (uint32_t)(v[b][c] >= pv) << (4 * b + c);
     } else {
-      emit([&](int pos, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
+#pragma unroll
+      for (int b = 0; b < TS_BATCH; ++b) {
+        const int p0 = 4 * (tid + TS_THREADS * (j0 + b));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) selm |= (uint32_t)(p0 + c < cn && v[b][c] >= pv) << (4 * b + c);
+      }
+    }
+    const uint32_t nsel = (uint32_t)__popc(selm);
+    const uint32_t incl = wave_incl_scan(nsel, lane);
+    uint32_t base = 0;
+    if (lane == 63 && incl) base = atomicAdd(&sh.ccount, incl);
+    base = (uint32_t)__shfl((int)base, 63) + incl - nsel;
+    const int pbase = 4 * (tid + TS_THREADS * j0);
+    for (uint32_t m = selm; m; m &= m - 1) {
+      const int e = __builtin_ctz(m);
+      if (base < (uint32_t)TS_CAND) sh.u.cand[base] = (uint16_t)(pbase + 4 * TS_THREADS * (e >> 2) + (e & 3));
+      ++base;
+    }
+  }
+  __syncthreads();
+  const uint32_t total = sh.ccount;
+  uint32_t tau, k_rem;
+  if (total >= k && total <= (uint32_t)TS_CAND) {  // workgroup-uniform
+    // ---- 3. exact select over the candidates (slot tid + 256 j of this thread)
+    uint32_t ck[TS_CPT], cp[TS_CPT];
+    uint32_t cmx = 0, cmnm1 = 0xFFFFFFFFu, dummy = 0;
+#pragma unroll
+    for (int j = 0; j < TS_CPT; ++j) {
+      const uint32_t i = (uint32_t)(tid + TS_THREADS * j);
+      cp[j] = i < total ? sh.u.cand[i] : 0u;
+    }
+    float cv[TS_CPT];
+#pragma unroll
+    for (int j = 0; j < TS_CPT; ++j) cv[j] = row[cp[j]];  // scores re-read (cache), all in flight
+#pragma unroll
+    for (int j = 0; j < TS_CPT; ++j) {
+      const uint32_t i = (uint32_t)(tid + TS_THREADS * j);
+      ck[j] = i < total ? score_key(cv[j]) : 0u;
+      cmx = max(cmx, ck[j]);
+      cmnm1 = min(cmnm1, ck[j] - 1u);
+    }
+    ts_block_reduce(cmx, cmnm1, dummy, sh);
+    auto visit_cand = [&](auto&& f) {
+#pragma unroll
+      for (int j = 0; j < TS_CPT; ++j) f(ck[j]);
+    };
+    ts_radix_select(visit_cand, k, cmx, cmnm1 + 1u, sh, tau, k_rem);
+    // ---- 4. the bitmaps from the candidates (the histogram is zero after the select)
+#pragma unroll
+    for (int j = 0; j < TS_CPT; ++j) {
+      const uint32_t kk = ck[j], p = cp[j];
+      if (kk > tau)
+        atomicOr(&sh.h.map.gt[p >> 5], 1u << (p & 31));
+      else if (kk == tau && kk != 0)
+        atomicOr(&sh.h.map.eq[p >> 5], 1u << (p & 31));
     }
   } else {
-    uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
-    int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
-    const float* row = logits + t * ld + c0;
-    emit([&](int pos, uint32_t slot) {
-      ck[slot] = score_key(row[pos]);  // re-read (L2): keeps the key array out of the loop
-      ci[slot] = (int32_t)(c0 + pos);
+    // the candidates do not hold the selection: select and bitmaps over the whole chunk
+    uint32_t mx = 0, mnm1 = 0xFFFFFFFFu, dummy = 0;
+    stream_keys([&](uint32_t kk) {
+      mx = max(mx, kk);
+      mnm1 = min(mnm1, kk - 1u);
     });
+    ts_block_reduce(mx, mnm1, dummy, sh);
+    ts_radix_select(stream_keys, k, mx, mnm1 + 1u, sh, tau, k_rem);
+    for (int j0 = 0; j0 * TS_THREADS < nunits; j0 += TS_BATCH) {
+      v4f v[TS_BATCH];
+#pragma unroll
+      for (int b = 0; b < TS_BATCH; ++b) v[b] = row4[min(tid + TS_THREADS * (j0 + b), last)];
+#pragma unroll
+      for (int b = 0; b < TS_BATCH; ++b) {
+        const int p0 = 4 * (tid + TS_THREADS * (j0 + b));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t pp = (uint32_t)(p0 + c);
+          const uint32_t kk = p0 + c < cn ? score_key(v[b][c]) : 0u;
+          if (kk > tau)
+            atomicOr(&sh.h.map.gt[pp >> 5], 1u << (pp & 31));
+          else if (kk == tau && kk != 0)
+            atomicOr(&sh.h.map.eq[pp >> 5], 1u << (pp & 31));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  ts_emit_maps(sh, k, k_rem, emit);
+}
+
+// Copy the staged index list (k <= TK_STAGE entries) to dst (256 threads).
+__device__ __forceinline__ void ts_store_staged(const TsShared& sh, int32_t* __restrict__ dst, int32_t k) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (((uintptr_t)dst & 15) == 0) {
+    const int k4 = k & ~3;
+    for (int i = 4 * tid; i < k4; i += 4 * TS_THREADS)
+      *reinterpret_cast<v4i*>(dst + i) = *reinterpret_cast<const v4i*>(sh.u.stage + i);
+    for (int i = k4 + tid; i < k; i += TS_THREADS) dst[i] = sh.u.stage[i];
+  } else {
+    for (int i = tid; i < k; i += TS_THREADS) dst[i] = sh.u.stage[i];
   }
 }
 
 // One chunk of one row.  SINGLE (every row fits one chunk): the final index list; otherwise
 // the chunk's candidates go to cand_key / cand_idx [rows][G][k] (key 0 = empty slot) and rows of
 // one chunk still write their final list.
-// mode 0: prefill rows (n_t = min(S, q_start + t + 1)); mode 1: decode rows (n = seq_lens[t]).
+// Prefill rows: n_t = min(S, q_start + t + 1); decode rows (seq_lens given): n = seq_lens[t].
 template <bool SINGLE>
-__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_chunk_kernel(
+__global__ __launch_bounds__(TS_THREADS) void topk_chunk_kernel(
     const float* __restrict__ logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
     const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, int32_t G) {
-  __shared__ TopkShared sh;
+  __shared__ TsShared sh;
   const int64_t t = blockIdx.x;  // rows on x: up to 2^31 - 1 of them in one launch
   const int chunk = blockIdx.y;
   const int64_t n = seq_lens ? min((int64_t)max(seq_lens[t], 0), S) : min(S, q_start + t + 1);
@@ -535,7 +745,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4
   int32_t* out_idx = indices + t * k;
 
   if (cn <= k) {  // everything in the chunk is selected
-    for (int64_t i = tid; i < k; i += TK_THREADS) {
+    for (int64_t i = tid; i < k; i += TS_THREADS) {
       if (single) {
         out_idx[i] = i < cn ? (int32_t)(c0 + i) : -1;
       } else {
@@ -545,13 +755,24 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4
     }
     return;
   }
-  // the narrowest register layout that holds the chunk: the work per row follows its length
-  if (cn <= TK_CHUNK / 4)
-    chunk_select<TK_CHUNK_EPT / 4>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
-  else if (cn <= TK_CHUNK / 2)
-    chunk_select<TK_CHUNK_EPT / 2>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
-  else
-    chunk_select<TK_CHUNK_EPT>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
+  for (int i = tid; i < TK_BINS; i += TS_THREADS) sh.h.hist[i] = 0;
+  if (tid == 0) sh.small_n = 0;
+  // one emission target per workgroup: the staged list, the output list, or the chunk's candidates
+  const int mode = single ? (k <= TK_STAGE ? 0 : 1) : 2;
+  uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
+  int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
+  const float* row = logits + t * ld + c0;
+  ts_chunk_select(row, (int)cn, (uint32_t)k, sh, [&](int pos, uint32_t slot) {
+    if (mode == 0) {
+      sh.u.stage[slot] = (int32_t)(c0 + pos);
+    } else if (mode == 1) {
+      out_idx[slot] = (int32_t)(c0 + pos);
+    } else {
+      ck[slot] = score_key(row[pos]);  // re-read (cache): keeps the keys out of the emission
+      ci[slot] = (int32_t)(c0 + pos);
+    }
+  });
+  if (mode == 0) ts_store_staged(sh, out_idx, k);
 }
 
 // Merge the chunk candidates of rows with more than one chunk.
@@ -616,11 +837,11 @@ hipError_t launch_topk(const float* logits, int64_t ld, int64_t T, int64_t S, in
   }
   hipError_t e;
   if (G <= 1)
-    e = launch("topk_chunk_kernel<whole row>", topk_chunk_kernel<true>, dim3((unsigned)T, 1), dim3(TK_THREADS), 0,
+    e = launch("topk_chunk_kernel<whole row>", topk_chunk_kernel<true>, dim3((unsigned)T, 1), dim3(TS_THREADS), 0,
                stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
   else
     e = launch("topk_chunk_kernel<chunk>", topk_chunk_kernel<false>, dim3((unsigned)T, (unsigned)G),
-               dim3(TK_THREADS), 0, stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
+               dim3(TS_THREADS), 0, stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
   if (e != hipSuccess || G <= 1) return e;
   return launch("topk_merge_kernel", topk_merge_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, T, S,
                 q_start, seq_lens, k, indices, ck, ci, G);
