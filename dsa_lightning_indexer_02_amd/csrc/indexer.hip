@@ -14,13 +14,13 @@ namespace dsa {
 // ---------------------------------------------------------------------------------------
 // Prefill: a workgroup owns 16 consecutive query rows (the MFMA M dimension) and a range of
 // keys.  The 16 rows' FP8 queries for every head sit in LDS ([head][row][128 B + pad]); the
-// twelve waves take disjoint 16-key tiles, keep NK tiles of keys in registers (MFMA B operand)
+// eight waves take disjoint 16-key tiles, keep NK tiles of keys in registers (MFMA B operand)
 // and loop over the heads, so the head reduction happens inside each lane's accumulators
 // without any cross-lane traffic.
 // ---------------------------------------------------------------------------------------
 constexpr int IDX_ROWS = 16;
 constexpr int IDX_QROW_BYTES = 144;  // 128 B of codes + 16 B pad (bank spread)
-constexpr int IDX_PREFILL_WAVES = 12;  // three waves per SIMD: VALU of one beside MFMAs of another
+constexpr int IDX_PREFILL_WAVES = 8;  // two waves per SIMD: VALU of one beside MFMAs of the other
 
 // HI > 0: the head count is a compile-time constant and the head loop is fully unrolled;
 // HI == 0: any head count (plain loop).
@@ -167,13 +167,25 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
       }
     }
     // lane (j16, g) holds rows t0 + 4g + r for key base + 16 kt + j16
-#pragma unroll
-    for (int kt = 0; kt < NK; ++kt) {
-      const int64_t s = base + kt * 16 + j16;
+    if (base + NK * 16 <= c1 && base + NK * 16 <= q_start + t0 + 1 && t0 + IDX_ROWS <= T) {
+      // every (row, key) of the pass is visible (wave-uniform): no per-element test, one row
+      // pointer per r and the key tile as an immediate offset
+      float* lrow = logits + (t0 + 4 * g) * ld + base + j16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + 4 * g + r;
-        if (t < T && s < c1 && s < q_start + t + 1) logits[t * ld + s] = E8 ? acc[kt][r] : acc[kt][r] * ksv[kt];
+#pragma unroll
+        for (int kt = 0; kt < NK; ++kt) lrow[kt * 16] = E8 ? acc[kt][r] : acc[kt][r] * ksv[kt];
+        lrow += ld;
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < NK; ++kt) {
+        const int64_t s = base + kt * 16 + j16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = t0 + 4 * g + r;
+          if (t < T && s < c1 && s < q_start + t + 1) logits[t * ld + s] = E8 ? acc[kt][r] : acc[kt][r] * ksv[kt];
+        }
       }
     }
   }
@@ -447,7 +459,7 @@ hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const floa
                                   int64_t q_start, float* logits, int64_t ld, hipStream_t stream,
                                   const uint8_t* q_exp, const uint8_t* k_exp) {
   if (T <= 0) return hipSuccess;
-  constexpr int NK = 4;
+  constexpr int NK = 8;  // 16-key tiles per wave and pass (MFMA B operands in registers)
   const int64_t tiles = (T + IDX_ROWS - 1) / IDX_ROWS;
   const int64_t n_last = std::min<int64_t>(S, q_start + T);
   // split keys only when the tiles alone cannot fill the chip
