@@ -257,7 +257,7 @@ def run_prefill(wl, args, dev):
                 "achieved": wm["indexer_flop"] / (stage_ms[0] / 1e3) / 1e12, "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s",
                 "traffic": None, "algorithmic_flop_per_launch": wm["indexer_flop"]}
     else:
-        roof = {"kernel": "topk_chunk_kernel", "bound": "hbm",
+        roof = {"kernel": "topk_row_kernel", "bound": "hbm",
                 "achieved": wm["topk_bytes"] / (stage_ms[1] / 1e3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "traffic": None, "algorithmic_bytes_per_launch": wm["topk_bytes"]}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -341,9 +341,9 @@ def run_decode(wl, args, dev, cpu_threads: int = 0):
     kbytes = {
         "indexer_decode_kernel": float(n.sum() * (wl.D_I + 4) + B * wl.H_I * (wl.D_I + 8)
                                        + ((n + 63) // 64).sum() * 4 + 4 * n.sum()),
-        "topk_chunk_kernel<whole row>": float(4 * n.sum() + 4 * B * wl.topk),
+        "topk_row_kernel": float(4 * n.sum() + 4 * B * wl.topk),
         # rows over 32768 keys: per-chunk candidates (key + index) written, then merged
-        "topk_chunk_kernel<chunk>": float(4 * n.sum() + B * G * wl.topk * 8),
+        "topk_chunk_kernel": float(4 * n.sum() + B * G * wl.topk * 8),
         "topk_merge_kernel": float(B * G * wl.topk * 8 + 4 * B * wl.topk),
         "sparse_mla_kernel": float(sel.sum() * wl.D_qk * 2 + B * wl.H * wl.D_qk * 2 + B * wl.topk * 4
                                    + B * nsplit * wl.H * (wl.D_v + 1) * 4),

@@ -2,30 +2,33 @@
 // Selection"; DeepSeek-V3.2-Exp summary page, section "Method": top-k = 2048): for query row t,
 // the k highest scores among its n_t visible keys; equal scores go to the lower key index.
 //
-// A row is processed in chunks of up to 32768 scores, one workgroup of 256 threads per chunk and
-// about 33 KB of LDS, so four chunks are in flight per CU.  The chunk is streamed from memory
-// instead of held in registers (a second read of a chunk just read comes from the caches):
-//   1. one pass over a quarter of the chunk samples one score per 16-byte unit (2048 samples);
+// When every row fits 32768 scores, each row is one workgroup of 256 threads and about 17 KB of
+// LDS (six per CU), and the row is streamed from memory instead of held in registers (a second
+// read of a row just read comes from the caches):
+//   1. one pass over a quarter of the row samples one score per 16-byte unit (2048 samples);
 //      an exact radix select over the samples puts a pivot a safe margin below the expected
 //      position of the k-th largest score;
-//   2. one pass over the whole chunk appends every score at or above the pivot (as an
-//      order-preserving uint32 key and its position) to an LDS candidate list, one LDS atomic
-//      per wave and batch;
-//   3. an exact radix select over the candidates (11-bit digits, the first window starting at
-//      the highest bit where their maximum and minimum differ) gives the threshold key tau and
-//      the number of its copies to take; every element >= tau is a candidate, so this is exact;
+//   2. one pass over the whole row counts the scores at or above the pivot and appends their
+//      positions to an LDS candidate list (each thread walks the set bits of its compare mask);
+//   3. an exact radix select over the candidates' keys (re-read, 11-bit digits, the first window
+//      starting at the highest bit where their maximum and minimum differ) gives the threshold
+//      key tau and the number of its copies to take; every element >= tau is a candidate, so
+//      this is exact;
 //   4. ordered emission: candidates set their position's bit in one of two LDS bitmaps (above
 //      tau / equal to tau), a block scan of the bit counts gives every selected position its
 //      output slot, and the index list is staged in LDS and stored with 16-byte stores.
 // When the candidates cannot hold the selection (fewer than k, or more than 4096: an unlucky
 // sample, heavy ties, or k itself large), the radix select and the bitmaps run over the whole
-// chunk by streaming passes instead.  The output is deterministic: every key above the threshold
+// row by streaming passes instead.  The output is deterministic: every key above the threshold
 // in index order, then the lowest-index ties.
 //
-// Rows longer than 32768 are cut into chunks; each chunk emits its own top-k candidates
-// (key, index) and a merge pass (one 512-thread workgroup per row, candidates in registers)
-// runs the same select over the concatenated candidates.  This is exact: an element in the row's
-// top-k is in its chunk's top-k under the same order.
+// Longer rows are cut into chunks of 32768, one workgroup of 512 threads per chunk with the
+// chunk in registers (64 scores per thread: every chunk but a row's last is full, and the
+// register form reads it once); the same sampled pivot, candidate select and bitmap emission
+// give the chunk's own top-k candidates (key, index), and a merge pass (one 512-thread
+// workgroup per row, candidates in registers) runs the select over the concatenated
+// candidates.  This is exact: an element in the row's top-k is in its chunk's top-k under the
+// same order.
 #include "dsa_internal.hpp"
 
 namespace dsa {
@@ -323,7 +326,256 @@ __device__ __forceinline__ void store_staged(const TopkShared& sh, int32_t* __re
 }
 
 // ---------------------------------------------------------------------------------------------
-// Chunk selection (256 threads; the chunk streamed, see the header).
+// Chunks of rows that span several chunks (512 threads, the chunk held in registers, 64 scores
+// per thread): one read of the chunk, the sampled pivot and the candidate compaction run on the
+// registers, and the candidates are written for the merge.
+
+constexpr int TK_CAND = 4096;     // candidate keys of the sampled threshold search
+constexpr int TK_CAND_EPT = TK_CAND / TK_THREADS;
+constexpr int TK_MAP_WORDS = TK_CHUNK_EPT * TK_THREADS / 32;  // one bit per position of a chunk
+
+struct TopkChunkShared : TopkShared {
+  uint32_t cand[TK_CAND];
+  uint32_t cpos[TK_CAND];           // position of each candidate in the chunk
+  uint32_t gtmap[TK_MAP_WORDS];     // selected positions above tau
+  uint32_t eqmap[TK_MAP_WORDS];     // positions equal to tau
+};
+
+// Exact threshold search over a chunk of cn > k valid elements (maximum mx, minimum mn) that
+// touches most keys once (returns the number of candidates left in sh.cand / sh.cpos, or 0 when
+// the select ran over all keys instead): the radix select over a 1-in-16 sample of the keys puts a pivot (a
+// sample order statistic) a safe margin below the expected position of the k-th largest key;
+// the keys at or above the pivot are counted, and when there
+// are between k and TK_CAND of them they are compacted into LDS, where the radix select finds
+// tau and the tie count among them (every key >= tau is a candidate, so both are exact).
+// Outside that window (an unlucky or adversarial sample) the radix select runs over all keys.
+// Chunks of at most TK_CAND elements skip the sample.  The histogram is zero on entry and exit.
+template <int EPT>
+__device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32_t k, uint32_t mx, uint32_t mn,
+                                      TopkChunkShared& sh, uint32_t& tau, uint32_t& k_rem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (mx == mn) {
+    tau = mx;
+    k_rem = k;
+    return 0;
+  }
+  uint32_t pivot = mn;  // every valid key
+  if (cn > TK_CAND) {
+    // sample element 17 i (i < EPT / 16) of every thread; lane l's copy sits at the lane-0 position + 4 l
+    // (elem_pos), so the number of valid samples follows from cn without a reduction
+    constexpr int NS = EPT / 16;  // sampled elements per thread, 17 apart
+    static_assert(NS >= 1 && 17 * (NS - 1) < EPT, "sample positions");
+    uint32_t smp[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) smp[i] = key[17 * i];
+    uint32_t m = 0;
+    for (int w = 0; w < TK_WAVES; ++w)
+      for (int i = 0; i < NS; ++i) {
+        const int64_t rest = cn - elem_pos<EPT>(w, 0, 17 * i);  // valid lanes: 4 l < rest
+        m += (uint32_t)min<int64_t>(WAVE, max<int64_t>(0, (rest + 3) / 4));
+      }
+    // rank sought among the m sampled keys: the expected rank of the k-th largest key plus four
+    // binomial standard deviations; none (the pivot stays mn) when the sample is too small
+    const float er = (float)k * (float)m / (float)cn;
+    const float w = er + 4.0f * sqrtf(er) + 16.0f;
+    if (w <= (float)m) {
+      // Digit passes over the samples toward the one of rank w, stopped as soon as the lower edge
+      // of the bin holding it leaves few enough samples at or above it: the pivot only has to keep
+      // between k and TK_CAND keys, not be that sample exactly.
+      const int hb = 31 - __clz(mx ^ mn);  // mx > mn here
+      int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
+      int bits = hb - shift + 1;
+      uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));
+      const uint32_t w0 = (uint32_t)w;
+      uint32_t need = w0;
+      const float per_sample = (float)cn / (float)m;
+      while (true) {
+        uint32_t bin, above, cnt;
+        hist_pass<NS>(smp, shift, bits, prefix, sh, [&](uint32_t) { return need; }, bin, above, &cnt);
+        need -= above;
+        prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
+        if (shift == 0 || (float)(w0 - need + cnt) * per_sample <= 0.75f * (float)TK_CAND) break;
+        bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
+        shift -= bits;
+      }
+      pivot = max(prefix << shift, mn);  // lower edge of the bin (prefix holds every bit above shift)
+    }
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) c += key[e] >= pivot;  // pivot >= mn >= 1: valid keys only
+  // exclusive offsets of this thread's candidates
+  const uint32_t incl = wave_incl_scan(c, lane);
+  if (lane == 63) sh.wsum[wave][1] = incl;
+  __syncthreads();
+  uint32_t off = incl - c, total = 0;
+  for (int i = 0; i < TK_WAVES; ++i) {
+    const uint32_t w = sh.wsum[i][1];
+    if (i < wave) off += w;
+    total += w;
+  }
+  if (total < k || total > (uint32_t)TK_CAND) {  // workgroup-uniform
+    radix_select<EPT>(key, k, mx, mn, sh, tau, k_rem);
+    return 0;
+  }
+  // an opaque copy of the pivot: the counting loop's 64 compare masks are recomputed here rather
+  // than kept (in scalar registers) across the scan
+  uint32_t pv = __builtin_amdgcn_readfirstlane(pivot);
+  asm volatile("" : "+s"(pv));
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (key[e] >= pv) {
+      sh.cand[off] = key[e];
+      sh.cpos[off] = (uint32_t)elem_pos<EPT>(wave, lane, e);
+      ++off;
+    }
+  __syncthreads();
+  uint32_t ck[TK_CAND_EPT];
+#pragma unroll
+  for (int j = 0; j < TK_CAND_EPT; ++j) {
+    const uint32_t i = (uint32_t)(tid + j * TK_THREADS);
+    ck[j] = i < total ? sh.cand[i] : 0u;
+  }
+  radix_select<TK_CAND_EPT>(ck, k, mx, pivot, sh, tau, k_rem);
+  return total;
+}
+
+// Ordered emission from the candidate list (every selected element is a candidate): each
+// candidate above tau sets its position's bit in one LDS bitmap, each equal to tau in another;
+// thread t then owns positions 64 t .. 64 t + 63 (two words of each map), and one block scan of
+// its two bit counts (packed in one word) gives its output offsets: every position above tau in
+// ascending order, then the first k_rem positions equal to tau.  The maps are zero on entry.
+template <typename Emit>
+__device__ void emit_candidates(TopkChunkShared& sh, uint32_t total, uint32_t tau, uint32_t k, uint32_t k_rem,
+                                Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (uint32_t i = (uint32_t)tid; i < total; i += TK_THREADS) {
+    const uint32_t kk = sh.cand[i], p = sh.cpos[i];
+    if (kk > tau)
+      atomicOr(&sh.gtmap[p >> 5], 1u << (p & 31));
+    else if (kk == tau)
+      atomicOr(&sh.eqmap[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  static_assert(TK_MAP_WORDS == 2 * TK_THREADS, "two map words per thread");
+  uint32_t g0 = sh.gtmap[2 * tid], g1 = sh.gtmap[2 * tid + 1];
+  uint32_t e0 = sh.eqmap[2 * tid], e1 = sh.eqmap[2 * tid + 1];
+  const uint32_t cnt = (uint32_t)(__popc(g0) + __popc(g1)) | ((uint32_t)(__popc(e0) + __popc(e1)) << 16);
+  const uint32_t incl = wave_incl_scan(cnt, lane);
+  if (lane == 63) sh.wsum[wave][0] = incl;
+  __syncthreads();
+  uint32_t off = incl - cnt;
+  for (int i = 0; i < wave; ++i) off += sh.wsum[i][0];
+  uint32_t go = off & 0xFFFFu, eo = off >> 16;
+  const int base = 64 * tid;
+  for (; g0; g0 &= g0 - 1) emit(base + __builtin_ctz(g0), go++);
+  for (; g1; g1 &= g1 - 1) emit(base + 32 + __builtin_ctz(g1), go++);
+  const uint32_t n_gt = k - k_rem;
+  for (; e0 && eo < k_rem; e0 &= e0 - 1) emit(base + __builtin_ctz(e0), n_gt + eo++);
+  for (; e1 && eo < k_rem; e1 &= e1 - 1) emit(base + 32 + __builtin_ctz(e1), n_gt + eo++);
+}
+
+// Load this thread's elements of scores[0 .. n) (1 <= n <= 512 * EPT) as keys (0 past n).  The
+// loads are unconditional so that all of them are in flight before the first one is waited for:
+// a group of four past the end re-reads the row's last aligned group, which is in bounds because
+// rows start 16-byte aligned and their stride is a multiple of four floats.
+template <int EPT>
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t n, uint32_t (&key)[EPT]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int last = (int)(((n + 3) & ~(int64_t)3) - 4);
+  v4f v[EPT / 4];
+#pragma unroll
+  for (int q = 0; q < EPT / 4; ++q)
+    v[q] = *reinterpret_cast<const v4f*>(row + min(elem_pos<EPT>(wave, lane, 4 * q), last));
+#pragma unroll
+  for (int q = 0; q < EPT / 4; ++q) {
+    const int p = elem_pos<EPT>(wave, lane, 4 * q);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[4 * q + c] = p + c < n ? score_key(v[q][c]) : 0u;
+  }
+}
+
+// The selection of one chunk of cn (k < cn <= 512 EPT) elements with EPT elements per thread.
+template <int EPT>
+__device__ __forceinline__ void chunk_select(const float* __restrict__ logits, int64_t ld, int64_t t, int chunk,
+                                             int64_t c0, int64_t cn, bool single, int32_t k,
+                                             int32_t* __restrict__ out_idx, uint32_t* __restrict__ cand_key,
+                                             int32_t* __restrict__ cand_idx, int32_t G, TopkChunkShared& sh) {
+  uint32_t key[EPT];
+  hist_clear(sh);
+  for (int i = threadIdx.x; i < TK_MAP_WORDS; i += TK_THREADS) {
+    sh.gtmap[i] = 0;
+    sh.eqmap[i] = 0;
+  }
+  load_keys<EPT>(logits + t * ld + c0, cn, key);
+  uint32_t mx, mn, tau, k_rem;
+  block_minmax<EPT>(key, sh, mx, mn);
+  const uint32_t ncand = sampled_threshold<EPT>(key, cn, (uint32_t)k, mx, mn, sh, tau, k_rem);
+  // emission from the candidates when they hold the selection, else from the registers
+  auto emit = [&](auto&& f) {
+    if (ncand)
+      emit_candidates(sh, ncand, tau, (uint32_t)k, k_rem, f);
+    else
+      emit_selected<EPT>(key, tau, (uint32_t)k, k_rem, sh, f);
+  };
+  if (single) {
+    if (k <= TK_STAGE) {
+      emit([&](int pos, uint32_t slot) { sh.stage[slot] = (int32_t)(c0 + pos); });
+      store_staged(sh, out_idx, k);
+    } else {
+      emit([&](int pos, uint32_t slot) { out_idx[slot] = (int32_t)(c0 + pos); });
+    }
+  } else {
+    uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
+    int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
+    const float* row = logits + t * ld + c0;
+    emit([&](int pos, uint32_t slot) {
+      ck[slot] = score_key(row[pos]);  // re-read (L2): keeps the key array out of the loop
+      ci[slot] = (int32_t)(c0 + pos);
+    });
+  }
+}
+
+// One chunk of a row when rows may span several chunks: the chunk's candidates go to cand_key /
+// cand_idx [rows][G][k] (key 0 = empty slot); rows of one chunk write their final list.
+// Prefill rows: n_t = min(S, q_start + t + 1); decode rows (seq_lens given): n = seq_lens[t].
+__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_chunk_kernel(
+    const float* __restrict__ logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
+    const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices,
+    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, int32_t G) {
+  __shared__ TopkChunkShared sh;
+  const int64_t t = blockIdx.x;  // rows on x: up to 2^31 - 1 of them in one launch
+  const int chunk = blockIdx.y;
+  const int64_t n = seq_lens ? min((int64_t)max(seq_lens[t], 0), S) : min(S, q_start + t + 1);
+  const int64_t c0 = (int64_t)chunk * TK_CHUNK;
+  if (c0 >= n && chunk > 0) return;
+  const int64_t cn = min(n - c0, TK_CHUNK);  // elements of this chunk
+  const bool single = n <= TK_CHUNK;
+  const int tid = threadIdx.x;
+  int32_t* out_idx = indices + t * k;
+
+  if (cn <= k) {  // everything in the chunk is selected
+    for (int64_t i = tid; i < k; i += TK_THREADS) {
+      if (single) {
+        out_idx[i] = i < cn ? (int32_t)(c0 + i) : -1;
+      } else {
+        cand_key[(t * G + chunk) * (int64_t)k + i] = i < cn ? score_key(logits[t * ld + c0 + i]) : 0u;
+        cand_idx[(t * G + chunk) * (int64_t)k + i] = i < cn ? (int32_t)(c0 + i) : -1;
+      }
+    }
+    return;
+  }
+  // the narrowest register layout that holds the chunk: the work per row follows its length
+  if (cn <= TK_CHUNK / 4)
+    chunk_select<TK_CHUNK_EPT / 4>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
+  else if (cn <= TK_CHUNK / 2)
+    chunk_select<TK_CHUNK_EPT / 2>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
+  else
+    chunk_select<TK_CHUNK_EPT>(logits, ld, t, chunk, c0, cn, single, k, out_idx, cand_key, cand_idx, G, sh);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Whole rows of at most one chunk (256 threads; the row streamed, see the header).
 constexpr int TS_THREADS = 256;
 constexpr int TS_WAVES = TS_THREADS / WAVE;
 constexpr int TS_BPT = TK_BINS / TS_THREADS;          // histogram bins per thread in the suffix scan
@@ -724,55 +976,31 @@ __device__ __forceinline__ void ts_store_staged(const TsShared& sh, int32_t* __r
   }
 }
 
-// One chunk of one row.  SINGLE (every row fits one chunk): the final index list; otherwise
-// the chunk's candidates go to cand_key / cand_idx [rows][G][k] (key 0 = empty slot) and rows of
-// one chunk still write their final list.
+// One whole row (every row fits one chunk): its final index list.
 // Prefill rows: n_t = min(S, q_start + t + 1); decode rows (seq_lens given): n = seq_lens[t].
-template <bool SINGLE>
-__global__ __launch_bounds__(TS_THREADS) void topk_chunk_kernel(
-    const float* __restrict__ logits, int64_t ld, int64_t T, int64_t S, int64_t q_start,
-    const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices,
-    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx, int32_t G) {
+__global__ __launch_bounds__(TS_THREADS) void topk_row_kernel(
+    const float* __restrict__ logits, int64_t ld, int64_t S, int64_t q_start,
+    const int32_t* __restrict__ seq_lens, int32_t k, int32_t* __restrict__ indices) {
   __shared__ TsShared sh;
   const int64_t t = blockIdx.x;  // rows on x: up to 2^31 - 1 of them in one launch
-  const int chunk = blockIdx.y;
   const int64_t n = seq_lens ? min((int64_t)max(seq_lens[t], 0), S) : min(S, q_start + t + 1);
-  const int64_t c0 = (int64_t)chunk * TK_CHUNK;
-  if (c0 >= n && chunk > 0) return;
-  const int64_t cn = min(n - c0, TK_CHUNK);  // elements of this chunk
-  const bool single = SINGLE || n <= TK_CHUNK;
   const int tid = threadIdx.x;
   int32_t* out_idx = indices + t * k;
-
-  if (cn <= k) {  // everything in the chunk is selected
-    for (int64_t i = tid; i < k; i += TS_THREADS) {
-      if (single) {
-        out_idx[i] = i < cn ? (int32_t)(c0 + i) : -1;
-      } else {
-        cand_key[(t * G + chunk) * (int64_t)k + i] = i < cn ? score_key(logits[t * ld + c0 + i]) : 0u;
-        cand_idx[(t * G + chunk) * (int64_t)k + i] = i < cn ? (int32_t)(c0 + i) : -1;
-      }
-    }
+  if (n <= k) {  // everything visible is selected
+    for (int64_t i = tid; i < k; i += TS_THREADS) out_idx[i] = i < n ? (int32_t)i : -1;
     return;
   }
   for (int i = tid; i < TK_BINS; i += TS_THREADS) sh.h.hist[i] = 0;
   if (tid == 0) sh.small_n = 0;
-  // one emission target per workgroup: the staged list, the output list, or the chunk's candidates
-  const int mode = single ? (k <= TK_STAGE ? 0 : 1) : 2;
-  uint32_t* ck = cand_key + (t * G + chunk) * (int64_t)k;
-  int32_t* ci = cand_idx + (t * G + chunk) * (int64_t)k;
-  const float* row = logits + t * ld + c0;
-  ts_chunk_select(row, (int)cn, (uint32_t)k, sh, [&](int pos, uint32_t slot) {
-    if (mode == 0) {
-      sh.u.stage[slot] = (int32_t)(c0 + pos);
-    } else if (mode == 1) {
-      out_idx[slot] = (int32_t)(c0 + pos);
-    } else {
-      ck[slot] = score_key(row[pos]);  // re-read (cache): keeps the keys out of the emission
-      ci[slot] = (int32_t)(c0 + pos);
-    }
+  const float* row = logits + t * ld;
+  const bool staged = k <= TK_STAGE;  // the list staged in LDS, else written straight out
+  ts_chunk_select(row, (int)n, (uint32_t)k, sh, [&](int pos, uint32_t slot) {
+    if (staged)
+      sh.u.stage[slot] = pos;
+    else
+      out_idx[slot] = pos;
   });
-  if (mode == 0) ts_store_staged(sh, out_idx, k);
+  if (staged) ts_store_staged(sh, out_idx, k);
 }
 
 // Merge the chunk candidates of rows with more than one chunk.
@@ -835,14 +1063,12 @@ hipError_t launch_topk(const float* logits, int64_t ld, int64_t T, int64_t S, in
     ck = reinterpret_cast<uint32_t*>(workspace);
     ci = reinterpret_cast<int32_t*>(ck + (size_t)T * G * k);
   }
-  hipError_t e;
   if (G <= 1)
-    e = launch("topk_chunk_kernel<whole row>", topk_chunk_kernel<true>, dim3((unsigned)T, 1), dim3(TS_THREADS), 0,
-               stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
-  else
-    e = launch("topk_chunk_kernel<chunk>", topk_chunk_kernel<false>, dim3((unsigned)T, (unsigned)G),
-               dim3(TS_THREADS), 0, stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
-  if (e != hipSuccess || G <= 1) return e;
+    return launch("topk_row_kernel", topk_row_kernel, dim3((unsigned)T), dim3(TS_THREADS), 0, stream, logits, ld,
+                  S, q_start, seq_lens, k, indices);
+  const hipError_t e = launch("topk_chunk_kernel", topk_chunk_kernel, dim3((unsigned)T, (unsigned)G),
+                              dim3(TK_THREADS), 0, stream, logits, ld, T, S, q_start, seq_lens, k, indices, ck, ci, G);
+  if (e != hipSuccess) return e;
   return launch("topk_merge_kernel", topk_merge_kernel, dim3((unsigned)T), dim3(TK_THREADS), 0, stream, T, S,
                 q_start, seq_lens, k, indices, ck, ci, G);
 }
