@@ -296,7 +296,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   auto gather = [&](int blk) { gather_issue(blk, gather_rows(blk)); };
 
   v16f O[C::NDT];
-  float mref, mlane = -INFINITY, lsum;  // mlane: this lane's running maximum (its head, its keys)
+  float mref, mlane = -INFINITY, lsum;  // mlane: this lane's running raw maximum (its head, its keys)
   // blocks up to the last one holding a valid entry (all later entries are masked: a row with fewer
   // visible keys than list entries skips its padding); one validity word per lane, the same answer
   // in every wave
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     for (int dt = 0; dt < C::NDT; ++dt) O[dt] = (v16f){};
     lsum = 0.f;
     // pass 1: the exact row maximum of pass 0; pass 0: unset, probabilities are 0 until a valid entry
-    mref = pass ? fmaxf(mlane, __shfl_xor(mlane, 32)) : INFINITY;
+    mref = pass ? fmaxf(mlane, __shfl_xor(mlane, 32)) * scale_log2 : INFINITY;
     bool have_ref = pass != 0;  // wave-uniform: all heads of a wave get their reference together
     bool overflow = false;
 
@@ -381,34 +381,38 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       if (blk + 2 < nblk) gather_issue(blk + 2, next_rows);
       if (!active) continue;
 
-      // ---- full scores (own + partner partial) in log2 units, masked entries at -inf
-      const uint32_t vm = vmask_lds[blk];
-      const uint32_t vt = vm >> (4 * lh);
-      const uint32_t vbits = (vt & 0xFu) | ((vt >> 4) & 0xF0u) | ((vt >> 8) & 0xF00u) | ((vt >> 12) & 0xF000u);
+      // ---- full raw scores (own + partner partial), masked entries at -inf.  Element 4 qd + e
+      // of a lane is key 8 qd + 4 lh + e: its validity is one bit of the block mask for each half
+      // of the wave, so the lane mask of every element is built by two scalar bit-field extracts.
+      const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask_lds[blk]);
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const v4f pv = Sx_peer[qd * WAVE];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = 4 * qd + e;
-          const bool valid = (vbits >> rr) & 1u;
-          const float v = valid ? (sc[rr] + pv[e]) * scale_log2 : -INFINITY;
+          const int bl = 8 * qd + e;
+          const uint32_t lo = (uint32_t)((int32_t)(vm << (31 - bl)) >> 31);
+          const uint32_t hi = (uint32_t)((int32_t)(vm << (27 - bl)) >> 31);
+          const bool valid = __builtin_amdgcn_inverse_ballot_w64(((uint64_t)hi << 32) | lo);
+          const float v = valid ? sc[rr] + pv[e] : -INFINITY;
           sc[rr] = v;
           mlane = fmaxf(mlane, v);
         }
       }
       (void)Sx_mine;
       if (!have_ref && vm != 0u) {  // wave-uniform: the block mask is shared by all lanes
-        // first block with a valid entry: its maximum becomes the reference
-        mref = fmaxf(mlane, __shfl_xor(mlane, 32));
+        // first block with a valid entry: its maximum becomes the reference (log2 units; the
+        // scale is positive, so the maximum commutes with it)
+        mref = fmaxf(mlane, __shfl_xor(mlane, 32)) * scale_log2;
         have_ref = true;
       }
-      overflow |= mlane > mref + MLA_HEADROOM;
+      overflow |= mlane * scale_log2 > mref + MLA_HEADROOM;
       // ---- probabilities (fp16) packed as the B operands of out^T = V^T P^T (keys 0-15, 16-31)
       s16x8 Bp[2];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float p = __builtin_amdgcn_exp2f(sc[rr] - mref);  // exp2(-inf) = 0
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[rr], scale_log2, -mref));  // exp2(-inf) = 0
         lsum += p;
         Bp[rr >> 3][rr & 7] = __builtin_bit_cast(short, (_Float16)p);
       }
