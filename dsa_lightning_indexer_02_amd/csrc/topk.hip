@@ -185,8 +185,9 @@ __device__ void small_finish(const uint32_t (&key)[EPT], int shift, uint32_t pre
   if (wave == 0) {
     const uint32_t x = (uint32_t)lane < cnt ? sh.small[lane] : 0u;
     uint32_t gt = 0, eq = 0;
-    for (uint32_t m = 0; m < cnt; ++m) {
-      const uint32_t y = sh.small[m];
+    const uint32_t cu = (uint32_t)__builtin_amdgcn_readfirstlane((int)cnt);  // workgroup-uniform
+    for (uint32_t m = 0; m < cu; ++m) {
+      const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)m);  // lane m holds small[m]
       gt += y > x;
       eq += y == x;
     }
@@ -687,19 +688,20 @@ __device__ void ts_hist_pass(Visit visit, int shift, int bits, uint32_t prefix, 
 
 // The end of an exact select once the bin holding the sought rank has cnt <= 64 keys: as
 // small_finish.  sh.small_n is zero on entry and on exit.
-template <typename Visit>
-__device__ void ts_small_finish(Visit visit, int shift, uint32_t prefix, uint32_t cnt, uint32_t need, TsShared& sh,
-                                uint32_t& tau, uint32_t& k_rem) {
+template <typename Visit, typename Match>
+__device__ void ts_small_finish_if(Visit visit, Match match, uint32_t cnt, uint32_t need, TsShared& sh,
+                                   uint32_t& tau, uint32_t& k_rem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   visit([&](uint32_t kk) {
-    if (kk != 0 && (kk >> shift) == prefix) sh.small[atomicAdd(&sh.small_n, 1u)] = kk;
+    if (kk != 0 && match(kk)) sh.small[atomicAdd(&sh.small_n, 1u)] = kk;
   });
   __syncthreads();
   if (wave == 0) {
     const uint32_t x = (uint32_t)lane < cnt ? sh.small[lane] : 0u;
     uint32_t gt = 0, eq = 0;
-    for (uint32_t m = 0; m < cnt; ++m) {
-      const uint32_t y = sh.small[m];
+    const uint32_t cu = (uint32_t)__builtin_amdgcn_readfirstlane((int)cnt);  // workgroup-uniform
+    for (uint32_t m = 0; m < cu; ++m) {
+      const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)m);  // lane m holds small[m]
       gt += y > x;
       eq += y == x;
     }
@@ -712,6 +714,66 @@ __device__ void ts_small_finish(Visit visit, int shift, uint32_t prefix, uint32_
   __syncthreads();
   tau = sh.sel_bin;
   k_rem = sh.sel_above;
+}
+
+template <typename Visit>
+__device__ void ts_small_finish(Visit visit, int shift, uint32_t prefix, uint32_t cnt, uint32_t need, TsShared& sh,
+                                uint32_t& tau, uint32_t& k_rem) {
+  ts_small_finish_if(visit, [&](uint32_t kk) { return (kk >> shift) == prefix; }, cnt, need, sh, tau, k_rem);
+}
+
+// Bin of score v among TS_LIN bins of equal width 1 / scale from lo (clamped to the first and the
+// last bin): monotonic in v, so a higher bin holds only larger scores and a bin's rank window is
+// exact whatever the rounding of the arithmetic.
+constexpr int TS_LIN = 1024;
+constexpr int TS_LPT = TS_LIN / TS_THREADS;  // bins per thread in the suffix scan
+__device__ __forceinline__ int ts_lin_bin(float v, float lo, float scale) {
+  return min(TS_LIN - 1, max(0, (int)((v - lo) * scale)));
+}
+
+// One histogram pass over the scores of the keys visit() produces (0 = none) that match(), in
+// TS_LIN bins of width 1 / scale from lo (lo and scale finite): the bin holding the need-th
+// largest of them (1 <= need <= their count), the matching keys above it and in it.  The
+// histogram is zero on entry and on exit.
+template <typename Visit, typename Match>
+__device__ void ts_lin_pass(Visit visit, Match match, float lo, float scale, uint32_t need, TsShared& sh, int& bin,
+                            uint32_t& above_out, uint32_t& cnt_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  visit([&](uint32_t kk) {
+    if (kk != 0 && match(kk)) atomicAdd(&sh.h.hist[ts_lin_bin(key_score(kk), lo, scale)], 1u);
+  });
+  __syncthreads();
+  // thread t owns bins TS_LPT (255 - t) .. + TS_LPT - 1: the highest bins first
+  const int b0 = TS_LPT * (TS_THREADS - 1 - tid);
+  uint32_t h[TS_LPT];
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < TS_LPT; ++i) {
+    h[i] = sh.h.hist[b0 + i];
+    sh.h.hist[b0 + i] = 0;
+    own += h[i];
+  }
+  const uint32_t incl = wave_incl_scan(own, lane);
+  if (lane == 63) sh.wsum[wave][0] = incl;
+  __syncthreads();
+  uint32_t above = incl - own;
+  for (int i = 0; i < wave; ++i) above += sh.wsum[i][0];
+  if (above < need && need <= above + own) {
+    uint32_t a = above;
+    for (int i = TS_LPT - 1; i >= 0; --i) {
+      if (need <= a + h[i]) {
+        sh.sel_bin = (uint32_t)(b0 + i);
+        sh.sel_above = a;
+        sh.sel_cnt = h[i];
+        break;
+      }
+      a += h[i];
+    }
+  }
+  __syncthreads();
+  bin = (int)sh.sel_bin;
+  above_out = sh.sel_above;
+  cnt_out = sh.sel_cnt;
 }
 
 // Exact select over the keys visit() produces: tau (the k-th largest) and k_rem (how many keys
@@ -833,27 +895,18 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
 #pragma unroll
         for (int i = 0; i < TS_SPT; ++i) f(sh.u.samples[tid + TS_THREADS * i]);
       };
-      const uint32_t smn = smnm1 + 1u;
-      const int hb = 31 - __clz(smx ^ smn);
-      int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
-      int bits = hb - shift + 1;
-      uint32_t prefix = (hb == 31) ? 0u : (smx >> (hb + 1));
-      const uint32_t w0 = (uint32_t)w;
-      uint32_t need = w0;
-      const float per_sample = (float)cn / (float)m;
-      // digit passes toward the sample of rank w, stopped once the lower edge of the bin holding
-      // it leaves few enough samples at or above it: the pivot only has to keep between k and
-      // TS_CAND scores, not be that sample exactly
-      while (true) {
-        uint32_t bin, above, cnt;
-        ts_hist_pass(visit_samples, shift, bits, prefix, sh, need, bin, above, cnt);
-        need -= above;
-        prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
-        if (shift == 0 || (float)(w0 - need + cnt) * per_sample <= 0.75f * (float)TS_CAND) break;
-        bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
-        shift -= bits;
+      // one histogram pass over the samples in TS_LIN bins of equal width over their value
+      // range: the pivot is the lower edge of the bin holding the sample of rank w, moved down by
+      // more than the rounding of the bin arithmetic (a lower pivot only adds candidates)
+      const float lo = key_score(smnm1 + 1u), hi = key_score(smx);
+      const float range = hi - lo;
+      if (range < __builtin_inff()) {  // workgroup-uniform; lo < hi since the keys differ
+        const float scale = (float)TS_LIN / range;
+        int b;
+        uint32_t above, cnt;
+        ts_lin_pass(visit_samples, [](uint32_t) { return true; }, lo, scale, (uint32_t)w, sh, b, above, cnt);
+        pf = (lo + (float)b / scale) - (fabsf(lo) + fabsf(hi)) * 0x1p-20f;
       }
-      pf = key_score(max(prefix << shift, smn));  // lower edge of the bin, at least the sample minimum
     }
   }
   // ---- 2. the candidates: the positions of every score >= pf (NaN-free comparison of floats;
@@ -920,7 +973,36 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
 #pragma unroll
       for (int j = 0; j < TS_CPT; ++j) f(ck[j]);
     };
-    ts_radix_select(visit_cand, k, cmx, cmnm1 + 1u, sh, tau, k_rem);
+    // TS_LIN bins of equal width over the candidates' value range, and when the bin holding the
+    // k-th largest has more than 64 candidates, TS_LIN sub-bins of that bin; one wave then ranks
+    // the (at most 64) candidates of the final bin exactly.  Heavier ties: the radix select over
+    // the keys.
+    const uint32_t cmn = cmnm1 + 1u;
+    const float lo = key_score(cmn), hi = key_score(cmx);
+    bool done = false;
+    if (cmx != cmn && hi - lo < __builtin_inff()) {  // workgroup-uniform
+      const float scale = (float)TS_LIN / (hi - lo);
+      int b;
+      uint32_t above, cnt;
+      ts_lin_pass(visit_cand, [](uint32_t) { return true; }, lo, scale, k, sh, b, above, cnt);
+      auto in_b = [&](uint32_t kk) { return ts_lin_bin(key_score(kk), lo, scale) == b; };
+      if (cnt <= (uint32_t)WAVE) {
+        ts_small_finish_if(visit_cand, in_b, cnt, k - above, sh, tau, k_rem);
+        done = true;
+      } else {
+        const float lo2 = lo + (float)b / scale, scale2 = scale * (float)TS_LIN;
+        int b2;
+        uint32_t above2, cnt2;
+        ts_lin_pass(visit_cand, in_b, lo2, scale2, k - above, sh, b2, above2, cnt2);
+        if (cnt2 <= (uint32_t)WAVE) {
+          ts_small_finish_if(
+              visit_cand, [&](uint32_t kk) { return in_b(kk) && ts_lin_bin(key_score(kk), lo2, scale2) == b2; }, cnt2,
+              k - above - above2, sh, tau, k_rem);
+          done = true;
+        }
+      }
+    }
+    if (!done) ts_radix_select(visit_cand, k, cmx, cmn, sh, tau, k_rem);
     // ---- 4. the bitmaps from the candidates (the histogram is zero after the select)
 #pragma unroll
     for (int j = 0; j < TS_CPT; ++j) {
