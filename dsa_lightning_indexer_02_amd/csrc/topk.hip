@@ -54,6 +54,19 @@ struct TopkShared {
   uint32_t kmax, kmin;
 };
 
+// Inverse of score_key on the keys of non-NaN scores (key 0x7FFFFFFF, never produced, reads -0.0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Bin of score v among LIN_BINS bins of equal width 1 / scale from lo (clamped to the first and
+// the last bin): monotonic in v, so a higher bin holds only larger scores and a bin's rank window
+// is exact whatever the rounding of the arithmetic.
+constexpr int LIN_BINS = 1024;
+__device__ __forceinline__ int lin_bin(float v, float lo, float scale) {
+  return min(LIN_BINS - 1, max(0, (int)((v - lo) * scale)));
+}
+
 // Position of element e of this thread inside the workgroup's range.
 template <int EPT>
 __device__ __forceinline__ int elem_pos(int wave, int lane, int e) {
@@ -172,14 +185,14 @@ __device__ void hist_pass(const uint32_t (&key)[EPT], int shift, int bits, uint3
 // valid keys whose bits from shift up equal prefix) are collected in LDS and one wave ranks them:
 // tau is the key with fewer than `need` keys above it and at least `need` at or above it, k_rem
 // the count of its copies to take.  sh.small_n is zero on entry and on exit.
-template <int EPT>
-__device__ void small_finish(const uint32_t (&key)[EPT], int shift, uint32_t prefix, uint32_t cnt, uint32_t need,
-                             TopkShared& sh, uint32_t& tau, uint32_t& k_rem) {
+template <int EPT, typename Match>
+__device__ void small_finish_if(const uint32_t (&key)[EPT], Match match, uint32_t cnt, uint32_t need, TopkShared& sh,
+                                uint32_t& tau, uint32_t& k_rem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const uint32_t kk = key[e];
-    if (kk != 0 && (kk >> shift) == prefix) sh.small[atomicAdd(&sh.small_n, 1u)] = kk;
+    if (kk != 0 && match(kk)) sh.small[atomicAdd(&sh.small_n, 1u)] = kk;
   }
   __syncthreads();
   if (wave == 0) {
@@ -200,6 +213,12 @@ __device__ void small_finish(const uint32_t (&key)[EPT], int shift, uint32_t pre
   __syncthreads();
   tau = sh.sel_bin;
   k_rem = sh.sel_above;
+}
+
+template <int EPT>
+__device__ void small_finish(const uint32_t (&key)[EPT], int shift, uint32_t prefix, uint32_t cnt, uint32_t need,
+                             TopkShared& sh, uint32_t& tau, uint32_t& k_rem) {
+  small_finish_if<EPT>(key, [&](uint32_t kk) { return (kk >> shift) == prefix; }, cnt, need, sh, tau, k_rem);
 }
 
 // Exact threshold search given the maximum mx and a lower bound mn (>= 1) of the valid keys
@@ -234,6 +253,84 @@ __device__ void radix_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx
   }
   tau = prefix;
   k_rem = need;
+}
+
+// One histogram pass over the scores of the valid keys that match(), in LIN_BINS bins of width
+// 1 / scale from lo (lo and scale finite): the bin holding the need-th largest of them (1 <= need
+// <= their count), the matching keys above it and in it.  The histogram is zero on entry and on
+// exit.
+constexpr int TK_LPT = LIN_BINS / TK_THREADS;  // bins per thread in the suffix scan
+template <int EPT, typename Match>
+__device__ void lin_pass(const uint32_t (&key)[EPT], Match match, float lo, float scale, uint32_t need,
+                         TopkShared& sh, int& bin, uint32_t& above_out, uint32_t& cnt_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t kk = key[e];
+    if (kk != 0 && match(kk)) atomicAdd(&sh.hist[lin_bin(key_score(kk), lo, scale)], 1u);
+  }
+  __syncthreads();
+  const int b0 = TK_LPT * (TK_THREADS - 1 - tid);  // the highest bins first
+  uint32_t h[TK_LPT];
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < TK_LPT; ++i) {
+    h[i] = sh.hist[b0 + i];
+    sh.hist[b0 + i] = 0;
+    own += h[i];
+  }
+  const uint32_t incl = wave_incl_scan(own, lane);
+  if (lane == 63) sh.wsum[wave][0] = incl;
+  __syncthreads();
+  uint32_t above = incl - own;
+  for (int i = 0; i < wave; ++i) above += sh.wsum[i][0];
+  if (above < need && need <= above + own) {
+    uint32_t a = above;
+    for (int i = TK_LPT - 1; i >= 0; --i) {
+      if (need <= a + h[i]) {
+        sh.sel_bin = (uint32_t)(b0 + i);
+        sh.sel_above = a;
+        sh.sel_cnt = h[i];
+        break;
+      }
+      a += h[i];
+    }
+  }
+  __syncthreads();
+  bin = (int)sh.sel_bin;
+  above_out = sh.sel_above;
+  cnt_out = sh.sel_cnt;
+}
+
+// Exact select as radix_select, starting with LIN_BINS equal-width bins over the value range
+// [key_score(mn), key_score(mx)] and one refinement of the bin holding the k-th largest; once that
+// bin has at most 64 keys one wave ranks them.  Heavier ties fall back to the radix select.
+template <int EPT>
+__device__ void lin_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx, uint32_t mn, TopkShared& sh,
+                           uint32_t& tau, uint32_t& k_rem) {
+  const float lo = key_score(mn), hi = key_score(mx);
+  if (mx != mn && hi - lo < __builtin_inff()) {  // workgroup-uniform
+    const float scale = (float)LIN_BINS / (hi - lo);
+    int b;
+    uint32_t above, cnt;
+    lin_pass<EPT>(key, [](uint32_t) { return true; }, lo, scale, k, sh, b, above, cnt);
+    auto in_b = [&](uint32_t kk) { return lin_bin(key_score(kk), lo, scale) == b; };
+    if (cnt <= (uint32_t)WAVE) {
+      small_finish_if<EPT>(key, in_b, cnt, k - above, sh, tau, k_rem);
+      return;
+    }
+    const float lo2 = lo + (float)b / scale, scale2 = scale * (float)LIN_BINS;
+    int b2;
+    uint32_t above2, cnt2;
+    lin_pass<EPT>(key, in_b, lo2, scale2, k - above, sh, b2, above2, cnt2);
+    if (cnt2 <= (uint32_t)WAVE) {
+      small_finish_if<EPT>(
+          key, [&](uint32_t kk) { return in_b(kk) && lin_bin(key_score(kk), lo2, scale2) == b2; }, cnt2,
+          k - above - above2, sh, tau, k_rem);
+      return;
+    }
+  }
+  radix_select<EPT>(key, k, mx, mn, sh, tau, k_rem);
 }
 
 // Number of set bits of a wave mask held by lanes below this one.
@@ -379,27 +476,17 @@ __device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, ui
     // binomial standard deviations; none (the pivot stays mn) when the sample is too small
     const float er = (float)k * (float)m / (float)cn;
     const float w = er + 4.0f * sqrtf(er) + 16.0f;
-    if (w <= (float)m) {
-      // Digit passes over the samples toward the one of rank w, stopped as soon as the lower edge
-      // of the bin holding it leaves few enough samples at or above it: the pivot only has to keep
-      // between k and TK_CAND keys, not be that sample exactly.
-      const int hb = 31 - __clz(mx ^ mn);  // mx > mn here
-      int shift = hb >= TK_DIGIT - 1 ? hb - (TK_DIGIT - 1) : 0;
-      int bits = hb - shift + 1;
-      uint32_t prefix = (hb == 31) ? 0u : (mx >> (hb + 1));
-      const uint32_t w0 = (uint32_t)w;
-      uint32_t need = w0;
-      const float per_sample = (float)cn / (float)m;
-      while (true) {
-        uint32_t bin, above, cnt;
-        hist_pass<NS>(smp, shift, bits, prefix, sh, [&](uint32_t) { return need; }, bin, above, &cnt);
-        need -= above;
-        prefix = (shift + bits >= 32 ? 0u : (prefix << bits)) | bin;
-        if (shift == 0 || (float)(w0 - need + cnt) * per_sample <= 0.75f * (float)TK_CAND) break;
-        bits = shift >= TK_DIGIT ? TK_DIGIT : shift;
-        shift -= bits;
-      }
-      pivot = max(prefix << shift, mn);  // lower edge of the bin (prefix holds every bit above shift)
+    const float lo = key_score(mn), hi = key_score(mx);
+    if (w <= (float)m && hi - lo < __builtin_inff()) {  // workgroup-uniform; mx > mn here
+      // one histogram pass over the samples in LIN_BINS equal-width bins over the chunk's value
+      // range: the pivot is the lower edge of the bin holding the sample of rank w, moved down by
+      // more than the rounding of the bin arithmetic (a lower pivot only adds candidates)
+      const float scale = (float)LIN_BINS / (hi - lo);
+      int b;
+      uint32_t above, cnt;
+      lin_pass<NS>(smp, [](uint32_t) { return true; }, lo, scale, (uint32_t)w, sh, b, above, cnt);
+      const float pf = (lo + (float)b / scale) - (fabsf(lo) + fabsf(hi)) * 0x1p-20f;
+      pivot = max(score_key(pf), mn);
     }
   }
   uint32_t c = 0;
@@ -437,7 +524,7 @@ __device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, ui
     const uint32_t i = (uint32_t)(tid + j * TK_THREADS);
     ck[j] = i < total ? sh.cand[i] : 0u;
   }
-  radix_select<TK_CAND_EPT>(ck, k, mx, pivot, sh, tau, k_rem);
+  lin_select<TK_CAND_EPT>(ck, k, mx, pivot, sh, tau, k_rem);
   return total;
 }
 
@@ -613,10 +700,6 @@ struct TsShared {
 };
 static_assert(2 * TS_MAP_WORDS <= TK_BINS, "the bitmaps fit the histogram");
 
-// Inverse of score_key on the keys of non-NaN scores (key 0x7FFFFFFF, never produced, reads -0.0).
-__device__ __forceinline__ float key_score(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 // Block-wide (max, min - 1, sum) of per-thread values (max 0 / min - 1 0xFFFFFFFF: nothing).
 __device__ __forceinline__ void ts_block_reduce(uint32_t& mx, uint32_t& mnm1, uint32_t& sum, TsShared& sh) {
@@ -722,17 +805,10 @@ __device__ void ts_small_finish(Visit visit, int shift, uint32_t prefix, uint32_
   ts_small_finish_if(visit, [&](uint32_t kk) { return (kk >> shift) == prefix; }, cnt, need, sh, tau, k_rem);
 }
 
-// Bin of score v among TS_LIN bins of equal width 1 / scale from lo (clamped to the first and the
-// last bin): monotonic in v, so a higher bin holds only larger scores and a bin's rank window is
-// exact whatever the rounding of the arithmetic.
-constexpr int TS_LIN = 1024;
-constexpr int TS_LPT = TS_LIN / TS_THREADS;  // bins per thread in the suffix scan
-__device__ __forceinline__ int ts_lin_bin(float v, float lo, float scale) {
-  return min(TS_LIN - 1, max(0, (int)((v - lo) * scale)));
-}
+constexpr int TS_LPT = LIN_BINS / TS_THREADS;  // bins per thread in the suffix scan
 
 // One histogram pass over the scores of the keys visit() produces (0 = none) that match(), in
-// TS_LIN bins of width 1 / scale from lo (lo and scale finite): the bin holding the need-th
+// LIN_BINS bins of width 1 / scale from lo (lo and scale finite): the bin holding the need-th
 // largest of them (1 <= need <= their count), the matching keys above it and in it.  The
 // histogram is zero on entry and on exit.
 template <typename Visit, typename Match>
@@ -740,7 +816,7 @@ __device__ void ts_lin_pass(Visit visit, Match match, float lo, float scale, uin
                             uint32_t& above_out, uint32_t& cnt_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   visit([&](uint32_t kk) {
-    if (kk != 0 && match(kk)) atomicAdd(&sh.h.hist[ts_lin_bin(key_score(kk), lo, scale)], 1u);
+    if (kk != 0 && match(kk)) atomicAdd(&sh.h.hist[lin_bin(key_score(kk), lo, scale)], 1u);
   });
   __syncthreads();
   // thread t owns bins TS_LPT (255 - t) .. + TS_LPT - 1: the highest bins first
@@ -895,13 +971,13 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
 #pragma unroll
         for (int i = 0; i < TS_SPT; ++i) f(sh.u.samples[tid + TS_THREADS * i]);
       };
-      // one histogram pass over the samples in TS_LIN bins of equal width over their value
+      // one histogram pass over the samples in LIN_BINS bins of equal width over their value
       // range: the pivot is the lower edge of the bin holding the sample of rank w, moved down by
       // more than the rounding of the bin arithmetic (a lower pivot only adds candidates)
       const float lo = key_score(smnm1 + 1u), hi = key_score(smx);
       const float range = hi - lo;
       if (range < __builtin_inff()) {  // workgroup-uniform; lo < hi since the keys differ
-        const float scale = (float)TS_LIN / range;
+        const float scale = (float)LIN_BINS / range;
         int b;
         uint32_t above, cnt;
         ts_lin_pass(visit_samples, [](uint32_t) { return true; }, lo, scale, (uint32_t)w, sh, b, above, cnt);
@@ -973,30 +1049,30 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
 #pragma unroll
       for (int j = 0; j < TS_CPT; ++j) f(ck[j]);
     };
-    // TS_LIN bins of equal width over the candidates' value range, and when the bin holding the
-    // k-th largest has more than 64 candidates, TS_LIN sub-bins of that bin; one wave then ranks
+    // LIN_BINS bins of equal width over the candidates' value range, and when the bin holding the
+    // k-th largest has more than 64 candidates, LIN_BINS sub-bins of that bin; one wave then ranks
     // the (at most 64) candidates of the final bin exactly.  Heavier ties: the radix select over
     // the keys.
     const uint32_t cmn = cmnm1 + 1u;
     const float lo = key_score(cmn), hi = key_score(cmx);
     bool done = false;
     if (cmx != cmn && hi - lo < __builtin_inff()) {  // workgroup-uniform
-      const float scale = (float)TS_LIN / (hi - lo);
+      const float scale = (float)LIN_BINS / (hi - lo);
       int b;
       uint32_t above, cnt;
       ts_lin_pass(visit_cand, [](uint32_t) { return true; }, lo, scale, k, sh, b, above, cnt);
-      auto in_b = [&](uint32_t kk) { return ts_lin_bin(key_score(kk), lo, scale) == b; };
+      auto in_b = [&](uint32_t kk) { return lin_bin(key_score(kk), lo, scale) == b; };
       if (cnt <= (uint32_t)WAVE) {
         ts_small_finish_if(visit_cand, in_b, cnt, k - above, sh, tau, k_rem);
         done = true;
       } else {
-        const float lo2 = lo + (float)b / scale, scale2 = scale * (float)TS_LIN;
+        const float lo2 = lo + (float)b / scale, scale2 = scale * (float)LIN_BINS;
         int b2;
         uint32_t above2, cnt2;
         ts_lin_pass(visit_cand, in_b, lo2, scale2, k - above, sh, b2, above2, cnt2);
         if (cnt2 <= (uint32_t)WAVE) {
           ts_small_finish_if(
-              visit_cand, [&](uint32_t kk) { return in_b(kk) && ts_lin_bin(key_score(kk), lo2, scale2) == b2; }, cnt2,
+              visit_cand, [&](uint32_t kk) { return in_b(kk) && lin_bin(key_score(kk), lo2, scale2) == b2; }, cnt2,
               k - above - above2, sh, tau, k_rem);
           done = true;
         }
@@ -1109,7 +1185,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   for (int e = 0; e < TK_MERGE_EPT; ++e) key[e] = elem_pos<TK_MERGE_EPT>(wave, lane, e) < total ? raw[e] : 0u;
   uint32_t mx, mn, tau, k_rem;
   block_minmax<TK_MERGE_EPT>(key, sh, mx, mn);
-  radix_select<TK_MERGE_EPT>(key, (uint32_t)k, mx, mn, sh, tau, k_rem);
+  lin_select<TK_MERGE_EPT>(key, (uint32_t)k, mx, mn, sh, tau, k_rem);
   int32_t* out_idx = indices + t * k;
   if (k <= TK_STAGE) {
     emit_selected<TK_MERGE_EPT>(key, tau, (uint32_t)k, k_rem, sh,
