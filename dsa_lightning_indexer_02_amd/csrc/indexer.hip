@@ -14,13 +14,12 @@ namespace dsa {
 // ---------------------------------------------------------------------------------------
 // Prefill: a workgroup owns 16 consecutive query rows (the MFMA M dimension) and a range of
 // keys.  The 16 rows' FP8 queries for every head sit in LDS ([head][row][128 B + pad]); the
-// eight waves take disjoint 16-key tiles, keep NK tiles of keys in registers (MFMA B operand)
+// NW waves take disjoint 16-key tiles, keep NK tiles of keys in registers (MFMA B operand)
 // and loop over the heads, so the head reduction happens inside each lane's accumulators
 // without any cross-lane traffic.
 // ---------------------------------------------------------------------------------------
 constexpr int IDX_ROWS = 16;
 constexpr int IDX_QROW_BYTES = 144;  // 128 B of codes + 16 B pad (bank spread)
-constexpr int IDX_PREFILL_WAVES = 8;  // two waves per SIMD: VALU of one beside MFMAs of the other
 
 // HI > 0: the head count is a compile-time constant and the head loop is fully unrolled;
 // HI == 0: any head count (plain loop).
@@ -28,8 +27,8 @@ constexpr int IDX_PREFILL_WAVES = 8;  // two waves per SIMD: VALU of one beside 
 // 2^(e - 127)) applied inside the MFMA as its operand scales (lane l's byte scales the row or
 // column l % 16 it supplies), so the epilogue weighs by w alone and applies no key scale; qs and
 // ks are not read.  Otherwise the fp32 scales qs, ks are applied in the epilogue.
-template <int NK, int HI, bool E8>
-__global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kernel(
+template <int NW, int NK, int HI, bool E8>
+__global__ __launch_bounds__(NW * WAVE) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, RowMap keymap, int64_t T,
     int64_t S, int32_t H_I, int32_t D_I, int64_t q_start, float* __restrict__ logits, int64_t ld,
@@ -73,7 +72,7 @@ __global__ __launch_bounds__(IDX_PREFILL_WAVES * WAVE) void indexer_prefill_kern
   __syncthreads();
 
   const bool klane_has_bytes = (g * 32) < D_I;
-  const int64_t pass_keys = (int64_t)IDX_PREFILL_WAVES * NK * 16;
+  const int64_t pass_keys = (int64_t)NW * NK * 16;
   // key tiles of one pass (MFMA B operands) and their scales (E8: exponent bytes)
   auto load_keys = [&](int64_t base, v8i (&B)[NK], float (&ksv)[NK], int (&kb)[NK]) {
 #pragma unroll
@@ -453,18 +452,17 @@ size_t indexer_prefill_smem(int32_t H_I, bool e8) {
 
 int64_t indexer_prefill_max_rows() { return (int64_t)IDX_ROWS * 65536; }
 
-hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
+template <int NW, int NK>
+static hipError_t launch_indexer_prefill_cfg(const uint8_t* q8, const float* qs, const float* w,
                                   const uint8_t* k8, const float* ks, const int32_t* table,
                                   int32_t block_shift, int64_t num_blocks, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
                                   int64_t q_start, float* logits, int64_t ld, hipStream_t stream,
                                   const uint8_t* q_exp, const uint8_t* k_exp) {
-  if (T <= 0) return hipSuccess;
-  constexpr int NK = 8;  // 16-key tiles per wave and pass (MFMA B operands in registers)
   const int64_t tiles = (T + IDX_ROWS - 1) / IDX_ROWS;
   const int64_t n_last = std::min<int64_t>(S, q_start + T);
   // split keys only when the tiles alone cannot fill the chip
   int64_t key_chunk = n_last;
-  const int64_t unit = (int64_t)IDX_PREFILL_WAVES * NK * 16;
+  const int64_t unit = (int64_t)NW * NK * 16;
   if (tiles < 1024) {
     int64_t want = (1024 + tiles - 1) / tiles;
     key_chunk = std::max<int64_t>(unit, ((n_last + want - 1) / want + unit - 1) / unit * unit);
@@ -474,13 +472,29 @@ hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const floa
   dim3 grid((unsigned)chunks, (unsigned)tiles);
   const bool e8 = q_exp != nullptr;
   const size_t smem = indexer_prefill_smem(H_I, e8);
-  auto kernel = e8 ? (H_I == 64 ? indexer_prefill_kernel<NK, 64, true> : indexer_prefill_kernel<NK, 0, true>)
-                   : (H_I == 64 ? indexer_prefill_kernel<NK, 64, false> : indexer_prefill_kernel<NK, 0, false>);
+  auto kernel = e8 ? (H_I == 64 ? indexer_prefill_kernel<NW, NK, 64, true> : indexer_prefill_kernel<NW, NK, 0, true>)
+                   : (H_I == 64 ? indexer_prefill_kernel<NW, NK, 64, false> : indexer_prefill_kernel<NW, NK, 0, false>);
   hipError_t e = set_max_dynamic_lds((const void*)kernel);
   if (e != hipSuccess) return e;
   return launch(e8 ? "indexer_prefill_kernel<e8m0>" : "indexer_prefill_kernel", kernel, grid,
-                dim3(IDX_PREFILL_WAVES * WAVE), smem, stream, q8, qs, w, k8, ks, RowMap{table, block_shift, num_blocks},
+                dim3(NW * WAVE), smem, stream, q8, qs, w, k8, ks, RowMap{table, block_shift, num_blocks},
                 T, S, H_I, D_I, q_start, logits, ld, key_chunk, q_exp, k_exp);
+}
+
+hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
+                                  const uint8_t* k8, const float* ks, const int32_t* table,
+                                  int32_t block_shift, int64_t num_blocks, int64_t T, int64_t S, int32_t H_I, int32_t D_I,
+                                  int64_t q_start, float* logits, int64_t ld, hipStream_t stream,
+                                  const uint8_t* q_exp, const uint8_t* k_exp) {
+  if (T <= 0) return hipSuccess;
+  // Long key ranges (16384 keys or more): eight waves (two per SIMD) of eight 16-key tiles, each
+  // wave's VALU beside the other's MFMAs; shorter ones: twelve waves of four tiles, whose smaller
+  // passes split the causal triangle into more, better balanced workgroups.
+  const int64_t n_last = std::min<int64_t>(S, q_start + T);
+  return n_last >= 16384 ? launch_indexer_prefill_cfg<8, 8>(q8, qs, w, k8, ks, table, block_shift, num_blocks, T, S,
+                                                           H_I, D_I, q_start, logits, ld, stream, q_exp, k_exp)
+                         : launch_indexer_prefill_cfg<12, 4>(q8, qs, w, k8, ks, table, block_shift, num_blocks, T, S,
+                                                            H_I, D_I, q_start, logits, ld, stream, q_exp, k_exp);
 }
 
 // Dynamic LDS of the decode indexer: the group prefix [B + 1] i64 and the visible lengths [B] i32.

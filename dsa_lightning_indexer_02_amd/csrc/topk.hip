@@ -5,15 +5,16 @@
 // When every row fits 32768 scores, each row is one workgroup of 256 threads and about 17 KB of
 // LDS (six per CU), and the row is streamed from memory instead of held in registers (a second
 // read of a row just read comes from the caches):
-//   1. one pass over a quarter of the row samples one score per 16-byte unit (2048 samples);
-//      an exact radix select over the samples puts a pivot a safe margin below the expected
-//      position of the k-th largest score;
+//   1. one pass over an eighth of the row samples two scores per 16-byte unit (2048 samples);
+//      one histogram pass in equal-width value bins over the samples puts a pivot a safe margin
+//      below the expected position of the k-th largest score;
 //   2. one pass over the whole row counts the scores at or above the pivot and appends their
 //      positions to an LDS candidate list (each thread walks the set bits of its compare mask);
-//   3. an exact radix select over the candidates' keys (re-read, 11-bit digits, the first window
-//      starting at the highest bit where their maximum and minimum differ) gives the threshold
-//      key tau and the number of its copies to take; every element >= tau is a candidate, so
-//      this is exact;
+//   3. an exact select over the candidates' scores (re-read): a histogram pass in equal-width
+//      value bins (a second one inside a crowded bin) narrows the k-th largest to at most 64
+//      candidates, which one wave ranks; that gives the threshold key tau and the number of its
+//      copies to take (heavy ties fall back to a radix select over the keys); every element
+//      >= tau is a candidate, so this is exact;
 //   4. ordered emission: candidates set their position's bit in one of two LDS bitmaps (above
 //      tau / equal to tau), a block scan of the bit counts gives every selected position its
 //      output slot, and the index list is staged in LDS and stored with 16-byte stores.
@@ -670,7 +671,7 @@ constexpr int TS_BPT = TK_BINS / TS_THREADS;          // histogram bins per thre
 constexpr int TS_UNITS = (int)(TK_CHUNK / 4);          // 16-byte units of a full chunk
 constexpr int TS_UPT = TS_UNITS / TS_THREADS;          // units per thread (32)
 constexpr int TS_BATCH = 8;                            // units in flight per thread
-constexpr int TS_SPT = TS_UPT / 4;                     // sampled units per thread (8)
+constexpr int TS_SPT = TS_UPT / 4;                     // samples per thread (8: two from each of four units)
 constexpr int TS_SAMPLES = TS_THREADS * TS_SPT;        // 2048
 constexpr int TS_CAND = 4096;                          // candidate capacity
 constexpr int TS_CPT = TS_CAND / TS_THREADS;           // candidate slots per thread (16)
@@ -944,17 +945,17 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
   // ---- 1. the pivot: every element when the chunk is small, else a radix select over samples
   float pf = -__builtin_inff();
   if (cn > TS_CAND) {
-    // sampled units: thread t of wave w reads units t + 256 j for j = w, w + 4, ... (a quarter of
-    // the chunk), sample = the unit's first score
+    // sampled units: thread t of wave w reads units t + 256 j for j = w, w + 8, ... (an eighth of
+    // the chunk, in 1 KB blocks), samples = the unit's first two scores
     uint32_t smx = 0, smnm1 = 0xFFFFFFFFu, m = 0;
     {
-      v4f v[TS_SPT];
+      v4f v[TS_SPT / 2];
 #pragma unroll
-      for (int i = 0; i < TS_SPT; ++i) v[i] = row4[min(tid + TS_THREADS * (wave + 4 * i), last)];
+      for (int i = 0; i < TS_SPT / 2; ++i) v[i] = row4[min(tid + TS_THREADS * (wave + 8 * i), last)];
 #pragma unroll
       for (int i = 0; i < TS_SPT; ++i) {
-        const int p = 4 * (tid + TS_THREADS * (wave + 4 * i));
-        const uint32_t kk = p < cn ? score_key(v[i][0]) : 0u;
+        const int p = 4 * (tid + TS_THREADS * (wave + 8 * (i >> 1))) + (i & 1);
+        const uint32_t kk = p < cn ? score_key(v[i >> 1][i & 1]) : 0u;
         sh.u.samples[tid + TS_THREADS * i] = kk;
         smx = max(smx, kk);
         smnm1 = min(smnm1, kk - 1u);
