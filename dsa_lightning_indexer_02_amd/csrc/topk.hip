@@ -65,8 +65,13 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // is exact whatever the rounding of the arithmetic.
 constexpr int LIN_BINS = 1024;
 __device__ __forceinline__ int lin_bin(float v, float lo, float scale) {
-  return min(LIN_BINS - 1, max(0, (int)((v - lo) * scale)));
+  // clamped as a float, so the conversion is defined for every input: a scale that overflowed
+  // (a range of a few ulps) gives 0 * inf = NaN -> bin 0 for v = lo and inf -> the last bin above
+  return (int)fminf(fmaxf((v - lo) * scale, 0.0f), (float)(LIN_BINS - 1));
 }
+
+// Whether value bins over [lo, hi] are usable: their width must be a finite float.
+__device__ __forceinline__ bool lin_range_ok(float lo, float hi) { return hi - lo < __builtin_inff(); }
 
 // Position of element e of this thread inside the workgroup's range.
 template <int EPT>
@@ -310,7 +315,7 @@ template <int EPT>
 __device__ void lin_select(const uint32_t (&key)[EPT], uint32_t k, uint32_t mx, uint32_t mn, TopkShared& sh,
                            uint32_t& tau, uint32_t& k_rem) {
   const float lo = key_score(mn), hi = key_score(mx);
-  if (mx != mn && hi - lo < __builtin_inff()) {  // workgroup-uniform
+  if (mx != mn && lin_range_ok(lo, hi)) {  // workgroup-uniform
     const float scale = (float)LIN_BINS / (hi - lo);
     int b;
     uint32_t above, cnt;
@@ -478,7 +483,7 @@ __device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, ui
     const float er = (float)k * (float)m / (float)cn;
     const float w = er + 4.0f * sqrtf(er) + 16.0f;
     const float lo = key_score(mn), hi = key_score(mx);
-    if (w <= (float)m && hi - lo < __builtin_inff()) {  // workgroup-uniform; mx > mn here
+    if (w <= (float)m && lin_range_ok(lo, hi)) {  // workgroup-uniform; mx > mn here
       // one histogram pass over the samples in LIN_BINS equal-width bins over the chunk's value
       // range: the pivot is the lower edge of the bin holding the sample of rank w, moved down by
       // more than the rounding of the bin arithmetic (a lower pivot only adds candidates)
@@ -486,7 +491,7 @@ __device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, ui
       int b;
       uint32_t above, cnt;
       lin_pass<NS>(smp, [](uint32_t) { return true; }, lo, scale, (uint32_t)w, sh, b, above, cnt);
-      const float pf = (lo + (float)b / scale) - (fabsf(lo) + fabsf(hi)) * 0x1p-20f;
+      const float pf = (lo + (float)b / scale) - (fabsf(lo) * 0x1p-20f + fabsf(hi) * 0x1p-20f);
       pivot = max(score_key(pf), mn);
     }
   }
@@ -977,12 +982,12 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
       // more than the rounding of the bin arithmetic (a lower pivot only adds candidates)
       const float lo = key_score(smnm1 + 1u), hi = key_score(smx);
       const float range = hi - lo;
-      if (range < __builtin_inff()) {  // workgroup-uniform; lo < hi since the keys differ
+      if (lin_range_ok(lo, hi)) {  // workgroup-uniform
         const float scale = (float)LIN_BINS / range;
         int b;
         uint32_t above, cnt;
         ts_lin_pass(visit_samples, [](uint32_t) { return true; }, lo, scale, (uint32_t)w, sh, b, above, cnt);
-        pf = (lo + (float)b / scale) - (fabsf(lo) + fabsf(hi)) * 0x1p-20f;
+        pf = (lo + (float)b / scale) - (fabsf(lo) * 0x1p-20f + fabsf(hi) * 0x1p-20f);
       }
     }
   }
@@ -1057,7 +1062,7 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
     const uint32_t cmn = cmnm1 + 1u;
     const float lo = key_score(cmn), hi = key_score(cmx);
     bool done = false;
-    if (cmx != cmn && hi - lo < __builtin_inff()) {  // workgroup-uniform
+    if (cmx != cmn && lin_range_ok(lo, hi)) {  // workgroup-uniform
       const float scale = (float)LIN_BINS / (hi - lo);
       int b;
       uint32_t above, cnt;

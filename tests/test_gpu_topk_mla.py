@@ -86,6 +86,25 @@ def test_topk_heavy_tail(dev):
     _topk_case(dev, s, 39990, 2048, "heavy tail")
 
 
+@pytest.mark.parametrize("S", [32768, 131072])
+def test_topk_value_range_extremes(dev, S):
+    """The pivot and the exact selects bin scores by value over their range: a lone outlier crowds
+    every other score into one bin (refinement, then the key radix), a range beyond the float range
+    skips the value bins altogether; rows of 32768 take the whole-row kernel, 131072 the chunks and
+    the merge."""
+    g = block_rng(38, 0, S)
+    s = g.standard_normal((6, S)).astype(np.float32)
+    s[0, g.integers(0, S)] = 1.0e4                       # crowded bins, refined
+    s[1, g.integers(0, S)] = 1.0e6                       # crowded beyond the refinement
+    s[2, ::2] = 3.0e38                                   # max - min overflows the float range
+    s[2, 1::2] = -3.0e38 * g.random(S // 2).astype(np.float32)
+    s[3, g.choice(S, S // 50, replace=False)] *= 1000.0  # a heavy upper tail
+    s[4] = np.float32(1.0) + np.float32(2.0 ** -23) * g.integers(0, 4, S).astype(np.float32)  # four values
+    s[5, : S // 2] = -0.0
+    s[5, S // 2:] = 0.0                                  # signed zeros only
+    _topk_case(dev, s, S - 6, 2048, "value-range extremes, rows of %d" % S)
+
+
 @pytest.mark.parametrize("S", [8192, 16384, 32768])
 def test_topk_sample_adversarial(dev, S):
     # A row of n <= 32768 scores is held as EPT = 16, 32 or 64 elements per thread (the narrowest
