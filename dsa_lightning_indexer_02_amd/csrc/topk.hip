@@ -447,13 +447,13 @@ struct TopkChunkShared : TopkShared {
 
 // Exact threshold search over a chunk of cn > k valid elements (maximum mx, minimum mn) that
 // touches most keys once (returns the number of candidates left in sh.cand / sh.cpos, or 0 when
-// the select ran over all keys instead): the radix select over a 1-in-16 sample of the keys puts a pivot (a
-// sample order statistic) a safe margin below the expected position of the k-th largest key;
-// the keys at or above the pivot are counted, and when there
-// are between k and TK_CAND of them they are compacted into LDS, where the radix select finds
-// tau and the tie count among them (every key >= tau is a candidate, so both are exact).
-// Outside that window (an unlucky or adversarial sample) the radix select runs over all keys.
-// Chunks of at most TK_CAND elements skip the sample.  The histogram is zero on entry and exit.
+// the select ran over all keys instead): a histogram of a 1-in-16 sample of the keys in
+// equal-width value bins puts a pivot a safe margin below the expected position of the k-th
+// largest key; the keys at or above the pivot are counted, and when there are between k and
+// TK_CAND of them they are compacted into LDS, where the exact select finds tau and the tie
+// count among them (every key >= tau is a candidate, so both are exact).  Outside that window
+// (an unlucky or adversarial sample) the radix select runs over all keys.  Chunks of at most
+// TK_CAND elements skip the sample.  The histogram is zero on entry and exit.
 template <int EPT>
 __device__ uint32_t sampled_threshold(const uint32_t (&key)[EPT], int64_t cn, uint32_t k, uint32_t mx, uint32_t mn,
                                       TopkChunkShared& sh, uint32_t& tau, uint32_t& k_rem) {
@@ -947,7 +947,7 @@ __device__ void ts_chunk_select(const float* __restrict__ row, int cn, uint32_t 
     }
   };
 
-  // ---- 1. the pivot: every element when the chunk is small, else a radix select over samples
+  // ---- 1. the pivot: every element when the row is small, else a value histogram of samples
   float pf = -__builtin_inff();
   if (cn > TS_CAND) {
     // sampled units: thread t of wave w reads units t + 256 j for j = w, w + 8, ... (an eighth of
