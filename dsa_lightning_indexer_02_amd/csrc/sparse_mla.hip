@@ -282,7 +282,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int j = 0; j < DMA_PW; ++j) {
       const int i = wave + j * MLA_WAVES;
-      if (i < C::DMA_INSTR) {  // wave-uniform
+      // transfers whose index stays below DMA_INSTR for every wave need no test
+      if (j * MLA_WAVES + MLA_WAVES - 1 < C::DMA_INSTR || i < C::DMA_INSTR) {  // wave-uniform
         const int s = i * WAVE + ln;
         const int rr = s / C::RC;
         const int c = (s % C::RC) ^ C::swz(rr);
@@ -385,19 +386,32 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       // of a lane is key 8 qd + 4 lh + e: its validity is one bit of the block mask for each half
       // of the wave, so the lane mask of every element is built by two scalar bit-field extracts.
       const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask_lds[blk]);
+      if (vm == 0xFFFFFFFFu) {  // wave-uniform: every entry of the block is valid (no masks)
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const v4f pv = Sx_peer[qd * WAVE];
+        for (int qd = 0; qd < 4; ++qd) {
+          const v4f pv = Sx_peer[qd * WAVE];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = 4 * qd + e;
-          const int bl = 8 * qd + e;
-          const uint32_t lo = (uint32_t)((int32_t)(vm << (31 - bl)) >> 31);
-          const uint32_t hi = (uint32_t)((int32_t)(vm << (27 - bl)) >> 31);
-          const bool valid = __builtin_amdgcn_inverse_ballot_w64(((uint64_t)hi << 32) | lo);
-          const float v = valid ? sc[rr] + pv[e] : -INFINITY;
-          sc[rr] = v;
-          mlane = fmaxf(mlane, v);
+          for (int e = 0; e < 4; ++e) {
+            const float v = sc[4 * qd + e] + pv[e];
+            sc[4 * qd + e] = v;
+            mlane = fmaxf(mlane, v);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const v4f pv = Sx_peer[qd * WAVE];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rr = 4 * qd + e;
+            const int bl = 8 * qd + e;
+            const uint32_t lo = (uint32_t)((int32_t)(vm << (31 - bl)) >> 31);
+            const uint32_t hi = (uint32_t)((int32_t)(vm << (27 - bl)) >> 31);
+            const bool valid = __builtin_amdgcn_inverse_ballot_w64(((uint64_t)hi << 32) | lo);
+            const float v = valid ? sc[rr] + pv[e] : -INFINITY;
+            sc[rr] = v;
+            mlane = fmaxf(mlane, v);
+          }
         }
       }
       (void)Sx_mine;
