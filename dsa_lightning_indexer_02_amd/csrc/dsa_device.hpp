@@ -110,6 +110,11 @@ __device__ __forceinline__ void lds_dma_16B(const void* gaddr, uint32_t lds_base
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gaddr) : "memory");
 }
 
+// The same transfer from a scalar base address: lane l's 16 bytes at base + voff (32-bit per lane).
+__device__ __forceinline__ void lds_dma_16B_sbase(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(base) : "memory");
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding): at most N operations pending.
 template <int N>
 __device__ __forceinline__ void vm_wait() {

@@ -144,6 +144,20 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
   auto issue = [&](int blk) {
     if (grp == 0) return;
     const uint32_t base = kbuf_lds + (uint32_t)((blk % KL_STAGES) * C::K_BYTES);
+    if (C::RC >= WAVE && D == C::DP && (int64_t)(blk + 1) * KL_KB <= S) {  // workgroup-uniform
+      // a whole block of unpadded rows is one contiguous range of the cache: slot sl (row
+      // sl / RC) takes source chunk (sl % RC) ^ swz(row), and as RC is a multiple of SWZ the XOR
+      // only flips bits 4-6 of the byte offset: offset = 16 sl ^ 16 swz(row).  A transfer of 64
+      // slots spans at most two rows when RC >= 64.
+      const uint16_t* src = kv + (int64_t)blk * KL_KB * D;
+      for (int i = issuer; i < C::DMA_INSTR; i += KL_ISSUERS) {
+        const int first = (i * WAVE) / C::RC;                       // uniform: the transfer's first row
+        const int r = first + (lane >= (first + 1) * C::RC - i * WAVE ? 1 : 0);
+        const uint32_t off = ((uint32_t)(i * WAVE + lane) << 4) ^ ((uint32_t)C::swz(r) << 4);
+        lds_dma_16B_sbase(src, off, base + (uint32_t)(i * WAVE * 16));
+      }
+      return;
+    }
     for (int i = issuer; i < C::DMA_INSTR; i += KL_ISSUERS) {
       const int sl = i * WAVE + lane;
       const int r = sl / C::RC, c = (sl % C::RC) ^ C::swz(r);
