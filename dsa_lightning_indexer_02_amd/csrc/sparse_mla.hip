@@ -90,22 +90,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait until at most n of this wave's vector-memory operations are pending (n wave-uniform, small).
-__device__ __forceinline__ void wait_vmcnt_pending(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    default: wait_vmcnt<9>(); break;
-  }
-}
-
 // Transposing LDS read (gfx950): within each group of 16 lanes, lane i receives element i % 4 of
 // the 4 x 16-bit words addressed by lanes 4 j + i / 4 of its group, j = 0..3.
 __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
@@ -322,10 +306,15 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     for (int blk = 0; blk < nblk; ++blk) {
       const uint8_t* Kst = Kbuf + (blk % MLA_STAGES) * C::K_BYTES;
       // this wave's transfers of block blk are done once at most those of blk + 1 are pending
-      if (blk + 1 < nblk)
-        wait_vmcnt_pending(my_dma);
-      else
+      if (blk + 1 < nblk) {
+        // every wave issues DMA_PW or DMA_PW - 1 transfers per block: two immediate waits
+        if (my_dma == DMA_PW)
+          wait_vmcnt<DMA_PW>();
+        else
+          wait_vmcnt<DMA_PW - 1>();
+      } else {
         wait_vmcnt<0>();
+      }
       __syncthreads();  // stage blk complete; every wave is done with block blk - 1
 
       // ---- fp16 V^T of this block (VALU + LDS work) and the partial scores (MFMA work).  The two
