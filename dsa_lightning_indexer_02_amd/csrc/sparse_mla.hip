@@ -46,6 +46,10 @@ struct MlaCfg {
   static constexpr int SLOTS = MLA_KB * RC;                  // 16-byte slots per stage
   static constexpr int K_BYTES = SLOTS * 16;
   static constexpr int DMA_INSTR = SLOTS / WAVE;             // wave-wide 1 KiB transfers per block
+  static constexpr int DMA_PW = (DMA_INSTR + MLA_WAVES - 1) / MLA_WAVES;  // transfers per wave (max)
+  // wide rows: per wave, the 16-bit source descriptor of each of its transfers per lane (chunk
+  // byte offset in the row | 0x8000 for the transfer's second row) and the row each lane pair reads
+  static constexpr int GTAB_BYTES = RC >= WAVE ? MLA_WAVES * (DMA_PW + 1) * WAVE * 2 : 0;
   static constexpr int SX_BYTES = MLA_WAVES * WAVE * 16 * 4; // partial S^T of every wave (fp32)
   static constexpr int VT_STRIDE = 2 * MLA_KB + 16;          // bytes per fp16 V^T row (one value column)
   static constexpr int VT_BYTES = DV * VT_STRIDE;
@@ -69,7 +73,7 @@ size_t mla_smem_bytes(int32_t keys_per_wg) {
   using C = MlaCfg<DQK, DV>;
   (void)keys_per_wg;
   return (size_t)MLA_STAGES * C::K_BYTES + C::SX_BYTES + C::VT_BYTES +
-         (size_t)(MLA_MAX_K + 4 + MLA_MAX_K / MLA_KB) * sizeof(int32_t);
+         (size_t)(MLA_MAX_K + 4 + MLA_MAX_K / MLA_KB) * sizeof(int32_t) + C::GTAB_BYTES;
 }
 
 // One wave-wide global -> LDS transfer: lane l's 16 bytes at gaddr land at lds_base + 16 l.
@@ -108,7 +112,9 @@ __device__ __forceinline__ void bf16x4_to_f16(const s16x4 raw, s16x8& dst, int h
   }
 }
 
-template <int DQK, int DV>
+// OFF32: every row of the latent cache lies within 4 GiB of its base, so a gathered chunk's address
+// is the base plus a 32-bit offset (row * row bytes + chunk offset: one 24-bit multiply-add).
+template <int DQK, int DV, bool OFF32>
 __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ table, int64_t max_blocks, int32_t block_shift, int64_t num_blocks, int32_t per_row_table,
@@ -171,6 +177,27 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       vmask_lds[base / 32] = (uint32_t)bits;
       if (base + 32 < cnt) vmask_lds[base / 32 + 1] = (uint32_t)(bits >> 32);
     }
+  }
+  // The gather's per-lane slot arithmetic (row = slot / RC, swizzled chunk) is the same for every
+  // block: each wave tabulates it once for its own transfers.
+  uint16_t* gtab = reinterpret_cast<uint16_t*>(vmask_lds + MLA_MAX_K / MLA_KB);  // [WAVES][DMA_PW][64]
+  uint16_t* rtab = gtab + MLA_WAVES * C::DMA_PW * WAVE;                            // [WAVES][64]
+  if constexpr (C::RC >= WAVE) {
+#pragma unroll
+    for (int j = 0; j < C::DMA_PW; ++j) {
+      const int i = wave + j * MLA_WAVES;
+      if (i < C::DMA_INSTR) {
+        const int sl = i * WAVE + lane;
+        const int rr = sl / C::RC;
+        const int c = (sl % C::RC) ^ C::swz(rr);
+        gtab[(wave * C::DMA_PW + j) * WAVE + lane] =
+            (uint16_t)((c * 16) | (rr != (i * WAVE) / C::RC ? 0x8000 : 0));
+      }
+    }
+    // lane 2 j / 2 j + 1: the row of the first / last slot of transfer j (0xFFFF: no transfer)
+    const int j = lane >> 1, i = wave + j * MLA_WAVES;
+    rtab[wave * WAVE + lane] =
+        (j < C::DMA_PW && i < C::DMA_INSTR) ? (uint16_t)((i * WAVE + (lane & 1) * (WAVE - 1)) / C::RC) : (uint16_t)0xFFFF;
   }
   // Skipped entries are gathered from a row that certainly holds finite data (the sequence's
   // first key) and masked out of the softmax.
@@ -236,15 +263,19 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   // reads the physical rows of all this wave's transfers with one LDS read (lane 2 j / 2 j + 1:
   // first / last row of its j-th transfer), early enough for the value to be there when
   // gather_issue takes them by readlane.  Narrower rows look their row up per lane.
-  constexpr int DMA_PW = (C::DMA_INSTR + MLA_WAVES - 1) / MLA_WAVES;  // transfers per wave (max)
+  constexpr int DMA_PW = C::DMA_PW;
   static_assert(2 * DMA_PW <= WAVE, "one lane pair per transfer");
   auto gather_rows = [&](int blk) {
-    const int j = lane >> 1, i = wave + j * MLA_WAVES;
-    const int rr = (i * WAVE + (lane & 1) * (WAVE - 1)) / C::RC;
-    const int e = blk * MLA_KB + rr;
-    int32_t pr = -1;
-    if (j < DMA_PW && i < C::DMA_INSTR && e < cnt) pr = phys[e];
-    return pr >= 0 ? pr : safe_row;
+    if constexpr (C::RC < WAVE) {  // narrow rows: each lane looks its row up in gather_issue
+      (void)blk;
+      return safe_row;
+    } else {
+      const int rr = rtab[wave * WAVE + lane];
+      const int e = blk * MLA_KB + rr;
+      int32_t pr = -1;
+      if (rr != 0xFFFF && e < cnt) pr = phys[e];
+      return pr >= 0 ? pr : safe_row;
+    }
   };
   auto gather_issue = [&](int blk, int32_t prow) {
     const uint32_t base = kbuf_lds + (uint32_t)((blk % MLA_STAGES) * C::K_BYTES);
@@ -259,23 +290,23 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         const uint16_t* src = kv + (int64_t)(pr >= 0 ? pr : safe_row) * DQK + c * 8;
         if (C::DQK_PAD == DQK || c * 8 < DQK) dma_16B(src, base + (uint32_t)(i * WAVE * 16));
       }
-      return;
-    }
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the per-lane slot math here rather than keep it live
+    } else {
+    static_assert(C::DQK_PAD == DQK, "every chunk of a wide row is gathered");
 #pragma unroll
     for (int j = 0; j < DMA_PW; ++j) {
       const int i = wave + j * MLA_WAVES;
       // transfers whose index stays below DMA_INSTR for every wave need no test
       if (j * MLA_WAVES + MLA_WAVES - 1 < C::DMA_INSTR || i < C::DMA_INSTR) {  // wave-uniform
-        const int s = i * WAVE + ln;
-        const int rr = s / C::RC;
-        const int c = (s % C::RC) ^ C::swz(rr);
-        const int first = (i * WAVE) / C::RC;
+        const uint32_t t = gtab[(wave * DMA_PW + j) * WAVE + lane];
         const int32_t pa = __builtin_amdgcn_readlane(prow, 2 * j), pb = __builtin_amdgcn_readlane(prow, 2 * j + 1);
-        const uint16_t* src = kv + (int64_t)(rr == first ? pa : pb) * DQK + c * 8;
-        if (C::DQK_PAD == DQK || c * 8 < DQK) dma_16B(src, base + (uint32_t)(i * WAVE * 16));
+        const uint32_t row = (t & 0x8000u) ? (uint32_t)pb : (uint32_t)pa;
+        const uint32_t lds = base + (uint32_t)(i * WAVE * 16);
+        if constexpr (OFF32)
+          lds_dma_16B_sbase(kv, __umul24(row, (uint32_t)(DQK * 2)) + (t & 0x7FFFu), lds);
+        else
+          dma_16B(reinterpret_cast<const uint8_t*>(kv) + (uint64_t)row * (DQK * 2) + (t & 0x7FFFu), lds);
       }
+    }
     }
   };
   auto gather = [&](int blk) { gather_issue(blk, gather_rows(blk)); };
@@ -537,11 +568,15 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
   const int nsplit = a.nsplit;
   const int kps = (a.k + nsplit - 1) / nsplit;
   const size_t smem = mla_smem_bytes<DQK, DV>(kps);
-  hipError_t e = set_max_dynamic_lds((const void*)sparse_mla_kernel<DQK, DV>);
+  // rows of the latent cache the gather may name: the paged pool, or the S contiguous keys
+  const int64_t kv_rows = a.table ? (a.num_blocks << a.block_shift) : a.S;
+  const bool off32 = (uint64_t)kv_rows * DQK * 2 <= 0xFFFFFFFFull;
+  auto kernel = off32 ? sparse_mla_kernel<DQK, DV, true> : sparse_mla_kernel<DQK, DV, false>;
+  hipError_t e = set_max_dynamic_lds((const void*)kernel);
   if (e != hipSuccess) return e;
   const float scale_log2 = a.sm_scale * 1.4426950408889634f;
   dim3 grid((unsigned)a.R, (unsigned)nsplit);
-  e = launch("sparse_mla_kernel", sparse_mla_kernel<DQK, DV>, grid, dim3(MLA_THREADS), smem, stream, a.q, a.kv,
+  e = launch("sparse_mla_kernel", kernel, grid, dim3(MLA_THREADS), smem, stream, a.q, a.kv,
              a.idx, a.table, a.max_blocks, a.block_shift, a.num_blocks, a.per_row_table, a.seq_lens, a.S, a.q_start,
              a.H, a.k, scale_log2, nsplit, kps, a.out, a.out_f32, a.lse, a.part_out, a.part_lse);
   if (e != hipSuccess || nsplit == 1) return e;
