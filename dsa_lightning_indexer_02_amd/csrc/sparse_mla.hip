@@ -369,9 +369,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       // ---- partial S^T[key][head] over this wave's contraction half; the K fragment of step
       // ks + 1 is requested before the MFMA of step ks.  MFMA runs raise the wave's issue priority
       // so that the matrix pipe is fed first when both waves of the SIMD are ready.
-      v16f sc = {};
+      v16f sc;
       auto qk = [&]() {
-      if (active) {
+      if (!active) {
+        asm volatile("" : "=v"(sc));  // an inactive wave never reads its scores: no zeroing
+      } else {
         __builtin_amdgcn_s_setprio(2);
         constexpr int LA = 3;  // K fragments in flight (order pinned by scheduling barriers)
         s16x8 Af[LA];
@@ -381,7 +383,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         for (int ks = 0; ks < C::NKS; ++ks) {
           if (ks + LA - 1 < C::NKS) Af[(ks + LA - 1) % LA] = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(ks + LA - 1));
           __builtin_amdgcn_sched_barrier(0);
-          sc = mfma_bf16_32x32x16(Af[ks % LA], Qf[ks], sc);
+          // the first product takes a zero accumulator operand (no register zeroing)
+          sc = mfma_bf16_32x32x16(Af[ks % LA], Qf[ks], ks == 0 ? (v16f){} : sc);
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
