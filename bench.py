@@ -182,6 +182,8 @@ def run_prefill(wl, args, dev):
     out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
     tk_ws = torch.empty(max(1, dsa.load().dsa_topk_workspace_size(T, S, wl.topk)), dtype=torch.uint8, device=dev)
+    mla_ws = torch.empty(max(1, dsa.load().dsa_sparse_mla_workspace_size(T, S, wl.H, wl.D_qk, wl.D_v, wl.topk)),
+                         dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -193,7 +195,7 @@ def run_prefill(wl, args, dev):
         dsa.dsa_topk(logits, wl.topk, S, wl.q_start, idx, tk_ws)
         if ev:
             ev[2].record(stream)
-        dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v, wl.q_start, out=out, lse=lse)
+        dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v, wl.q_start, out=out, lse=lse, workspace=mla_ws)
         if ev:
             ev[3].record(stream)
 
@@ -534,6 +536,8 @@ def run_indexer_train(name, args, dev):
         out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
         tk_ws = torch.empty(max(1, dsa.load().dsa_topk_workspace_size(T, S, wl.topk)), dtype=torch.uint8, device=dev)
+        mla_ws = torch.empty(max(1, dsa.load().dsa_sparse_mla_workspace_size(T, S, wl.H, wl.D_qk, wl.D_v, wl.topk)),
+                             dtype=torch.uint8, device=dev)
     nstage = 5 if sparse else 3
 
     def step(ev=None):
@@ -546,7 +550,7 @@ def run_indexer_train(name, args, dev):
         if sparse:
             dsa.dsa_topk(logits, wl.topk, S, wl.q_start, idx, tk_ws)
             mark(2)
-            dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v, wl.q_start, out=out, lse=lse)
+            dsa.dsa_sparse_mla_fwd(q, kv, idx, wl.sm_scale, wl.D_v, wl.q_start, out=out, lse=lse, workspace=mla_ws)
             mark(3)
             dsa.dsa_indexer_kl_loss_sparse(q, kv, idx, lse, logits, wl.sm_scale, wl.q_start, dlogits=logits,
                                            loss=loss)

@@ -83,7 +83,7 @@ def load(path: str = LIB_PATH):
     lib.dsa_topk.argtypes = [_p, _i64, _i64, _i64, _i64, _i32, _p, _p, _sz, _p]
     lib.dsa_topk_noalloc.argtypes = [_p, _i64, _i64, _i64, _i64, _i32, _p, _p]
     lib.dsa_topk_noalloc.restype = ctypes.c_int
-    lib.dsa_sparse_mla_workspace_size.argtypes = [_i64, _i32, _i32, _i32]
+    lib.dsa_sparse_mla_workspace_size.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32]
     lib.dsa_sparse_mla_workspace_size.restype = _sz
     lib.dsa_sparse_mla_fwd.argtypes = [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _i64, _f32, _p, _p,
                                        _p, _p, _sz, _p]

@@ -120,13 +120,23 @@ def dsa_topk_noalloc(logits, k: int, S: int, q_start: int = 0, indices=None) -> 
 
 
 def dsa_sparse_mla_fwd(q, kv, indices, sm_scale: float, D_v: int, q_start: int = 0, out=None,
-                       out_f32=None, lse=None, want_f32: bool = False, want_lse: bool = True):
-    """(out bf16 [T,H,D_v], out_f32 or None, lse or None) of MQA-mode sparse MLA."""
+                       out_f32=None, lse=None, want_f32: bool = False, want_lse: bool = True,
+                       staging: str = "fp16", workspace=None):
+    """(out bf16 [T,H,D_v], out_f32 or None, lse or None) of MQA-mode sparse MLA.  ``staging``
+    "fp16" passes a workspace (the library's fp16 staging where the dims have it), "bf16" none."""
     lib = load()
     T, H, D_qk = q.shape
     S = kv.shape[0]
     k = indices.shape[1]
     dev = q.device
+    if staging not in ("fp16", "bf16"):
+        raise ValueError("staging must be 'fp16' or 'bf16'")
+    ws_ptr, ws_bytes = None, 0
+    if staging == "fp16":
+        need = lib.dsa_sparse_mla_workspace_size(T, S, H, D_qk, D_v, k)
+        if need > 0:
+            workspace = _workspace(need, dev, workspace)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty((T, H, D_v), dtype=torch.bfloat16, device=dev)
     if out_f32 is None and want_f32:
@@ -135,7 +145,7 @@ def dsa_sparse_mla_fwd(q, kv, indices, sm_scale: float, D_v: int, q_start: int =
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     status = lib.dsa_sparse_mla_fwd(
         _dev(q, "q", 3, 2), _dev(kv, "kv", 2, 2), _dev(indices, "indices", 2, 4), T, S, H, D_qk, D_v, k,
-        q_start, ctypes.c_float(sm_scale), _dev(out, "out", 3, 2), _opt(out_f32), _opt(lse), None, 0,
+        q_start, ctypes.c_float(sm_scale), _dev(out, "out", 3, 2), _opt(out_f32), _opt(lse), ws_ptr, ws_bytes,
         _stream(q))
     check("dsa_sparse_mla_fwd", status)
     return out, out_f32, lse

@@ -87,7 +87,7 @@ int32_t decode_splits(int32_t B, int32_t k) {
 }
 
 struct PrefillLayout {
-  size_t logits, indices, topk, total;
+  size_t logits, indices, topk, kv16, total;
   int64_t ld;
 };
 PrefillLayout prefill_layout(const dsa_dims_t* d, int64_t T, int64_t S) {
@@ -96,7 +96,8 @@ PrefillLayout prefill_layout(const dsa_dims_t* d, int64_t T, int64_t S) {
   L.logits = 0;
   L.indices = round_up((size_t)T * L.ld * sizeof(float), kAlign);
   L.topk = L.indices + round_up((size_t)T * d->topk * sizeof(int32_t), kAlign);
-  L.total = L.topk + round_up(dsa::topk_workspace_bytes(T, S, d->topk), kAlign);
+  L.kv16 = L.topk + round_up(dsa::topk_workspace_bytes(T, S, d->topk), kAlign);
+  L.total = L.kv16 + round_up(dsa::mla_kv16_bytes(S, d->D_qk, d->D_v), kAlign);
   return L;
 }
 
@@ -318,14 +319,15 @@ dsa_status_t dsa_topk_noalloc(const float* logits, int64_t ld_logits, int64_t T,
                     "top-k launch");
 }
 
-size_t dsa_sparse_mla_workspace_size(int64_t, int32_t, int32_t, int32_t) { return 0; }
+size_t dsa_sparse_mla_workspace_size(int64_t T, int64_t S, int32_t H, int32_t D_qk, int32_t D_v, int32_t k) {
+  if (T <= 0 || S <= 0 || H <= 0 || k <= 0) return 0;
+  return round_up(dsa::mla_kv16_bytes(S, D_qk, D_v), kAlign);
+}
 
 dsa_status_t dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* indices, int64_t T,
                                 int64_t S, int32_t H, int32_t D_qk, int32_t D_v, int32_t k, int64_t q_start,
                                 float sm_scale, uint16_t* out, float* out_f32, float* lse, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   REQUIRE(T >= 0 && S >= 0 && q_start >= 0, DSA_ERR_INVALID_ARGUMENT, "negative T, S or q_start");
   dsa_status_t s = check_mla_dims(H, D_qk, D_v, k);
   if (s != DSA_OK) return s;
@@ -339,10 +341,19 @@ dsa_status_t dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int
   REQUIRE_PTR(out);
   OPTIONAL_PTR(out_f32);
   OPTIONAL_PTR(lse);
+  // a workspace selects fp16 staging where the dims have it (it must then hold the fp16 copy)
+  const size_t kv16 = round_up(dsa::mla_kv16_bytes(S, D_qk, D_v), kAlign);
+  if (workspace != nullptr && kv16 > 0) {
+    REQUIRE(workspace_bytes >= kv16, DSA_ERR_WORKSPACE_TOO_SMALL, "sparse MLA workspace %zu < %zu bytes",
+            workspace_bytes, kv16);
+    REQUIRE((reinterpret_cast<uintptr_t>(workspace) % kAlign) == 0, DSA_ERR_INVALID_ARGUMENT,
+            "workspace must be 256-byte aligned");
+  }
   dsa::MlaArgs a{};
   a.q = q;
   a.kv = kv;
   a.idx = indices;
+  a.kv_f16 = (workspace != nullptr && kv16 > 0) ? static_cast<uint16_t*>(workspace) : nullptr;
   a.R = T;
   a.S = S;
   a.q_start = q_start;
@@ -462,6 +473,7 @@ dsa_status_t dsa_prefill_paged(const dsa_paged_cache_t* c, int32_t seq, const ds
   a.out = out;
   a.out_f32 = out_f32;
   a.lse = lse;
+  a.kv_f16 = dsa::mla_kv16_bytes(S, d->D_qk, d->D_v) > 0 ? reinterpret_cast<uint16_t*>(ws + L.kv16) : nullptr;
   return hip_status(dsa::launch_sparse_mla(a, stream), "sparse MLA launch");
 }
 

@@ -89,8 +89,13 @@ struct MlaArgs {
   float* lse;
   float* part_out;
   float* part_lse;
+  // fp16 staging (576/512, one sequence): S x D_qk fp16 of workspace for the converted rows; null
+  // selects bf16 staging
+  uint16_t* kv_f16;
 };
 bool mla_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k);
+// workspace bytes of the fp16 copy for fp16 staging (0: that staging is not available for the dims)
+size_t mla_kv16_bytes(int64_t S, int32_t D_qk, int32_t D_v);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
 
 // ---- sparse MLA backward

@@ -30,12 +30,14 @@ constexpr int MLA_THREADS = MLA_WAVES * WAVE;
 constexpr int MLA_KB = 32;             // selected rows per block
 constexpr int MLA_GROUP_HEADS = 32;    // heads per group (one 32x32 tile), served by a wave pair
 constexpr int MLA_GROUPS = MLA_WAVES / 2;
-constexpr int MLA_STAGES = 2;          // gathered-row buffers in flight
+constexpr int MLA_STAGES = 2;          // gathered-row buffers in flight (bf16 staging)
+constexpr int MLA_STAGES_F16 = 3;      // the same, fp16 staging (the value phase reads the stage)
 constexpr int MLA_MAX_K = 2048;        // index entries per workgroup (LDS row list)
 constexpr float MLA_HEADROOM = 15.0f;  // log2 headroom of fp16 probabilities above the reference
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool F16 = false>
 struct MlaCfg {
+  static constexpr int STAGES = F16 ? MLA_STAGES_F16 : MLA_STAGES;
   static constexpr int DH = ((DQK + 1) / 2 + 15) / 16 * 16;  // q.k columns per wave of a pair
   static constexpr int DQK_PAD = 2 * DH;
   static constexpr int NKS = DH / 16;                        // 32x32x16 steps of the partial S^T
@@ -52,7 +54,7 @@ struct MlaCfg {
   static constexpr int GTAB_BYTES = RC >= WAVE ? MLA_WAVES * (DMA_PW + 1) * WAVE * 2 : 0;
   static constexpr int SX_BYTES = MLA_WAVES * WAVE * 16 * 4; // partial S^T of every wave (fp32)
   static constexpr int VT_STRIDE = 2 * MLA_KB + 16;          // bytes per fp16 V^T row (one value column)
-  static constexpr int VT_BYTES = DV * VT_STRIDE;
+  static constexpr int VT_BYTES = F16 ? 0 : DV * VT_STRIDE;  // fp16 staging reads V from the stage
   static_assert(DQK % 8 == 0 && DV % 64 == 0 && DV <= DQK && DV <= 64 * MLA_WAVES, "unsupported MLA dims");
   static_assert(SLOTS % WAVE == 0, "gather slots must fill whole waves");
   // Chunk XOR of gathered row r.  gfx950's LDS serves a 16-byte-per-lane read 16 lanes at a time
@@ -68,11 +70,11 @@ struct MlaCfg {
   static __device__ __forceinline__ int slot(int r, int c) { return r * RC + (c ^ swz(r)); }
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool F16 = false>
 size_t mla_smem_bytes(int32_t keys_per_wg) {
-  using C = MlaCfg<DQK, DV>;
+  using C = MlaCfg<DQK, DV, F16>;
   (void)keys_per_wg;
-  return (size_t)MLA_STAGES * C::K_BYTES + C::SX_BYTES + C::VT_BYTES +
+  return (size_t)C::STAGES * C::K_BYTES + C::SX_BYTES + C::VT_BYTES +
          (size_t)(MLA_MAX_K + 4 + MLA_MAX_K / MLA_KB) * sizeof(int32_t) + C::GTAB_BYTES;
 }
 
@@ -114,7 +116,12 @@ __device__ __forceinline__ void bf16x4_to_f16(const s16x4 raw, s16x8& dst, int h
 
 // OFF32: every row of the latent cache lies within 4 GiB of its base, so a gathered chunk's address
 // is the base plus a 32-bit offset (row * row bytes + chunk offset: one 24-bit multiply-add).
-template <int DQK, int DV, bool OFF32>
+// F16: kv holds the latent rows in fp16 (mla_kv_to_f16_kernel) and the queries are converted to fp16
+// as they are loaded: S^T is an fp16 MFMA (the same products: bf16 -> fp16 is exact in fp16's normal
+// range), and the value phase takes its V^T operands straight from the gathered rows by transposing
+// LDS reads, so no V^T buffer is built; with the stage read until the end of a block, three stages
+// keep the gather two blocks ahead.
+template <int DQK, int DV, bool OFF32, bool F16>
 __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ table, int64_t max_blocks, int32_t block_shift, int64_t num_blocks, int32_t per_row_table,
@@ -122,11 +129,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     float scale_log2, int32_t nsplit, int32_t keys_per_split, uint16_t* __restrict__ out,
     float* __restrict__ out_f32, float* __restrict__ lse, float* __restrict__ part_out,
     float* __restrict__ part_lse) {
-  using C = MlaCfg<DQK, DV>;
+  using C = MlaCfg<DQK, DV, F16>;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* Kbuf = smem;                                                  // [STAGES][SLOTS] x 16 B
-  float* Sx = reinterpret_cast<float*>(smem + MLA_STAGES * C::K_BYTES);  // [WAVES][4][64] x v4f
-  uint8_t* Vt = smem + MLA_STAGES * C::K_BYTES + C::SX_BYTES;            // [DV][VT_STRIDE] fp16
+  float* Sx = reinterpret_cast<float*>(smem + C::STAGES * C::K_BYTES);   // [WAVES][4][64] x v4f
+  uint8_t* Vt = smem + C::STAGES * C::K_BYTES + C::SX_BYTES;             // [DV][VT_STRIDE] fp16 (bf16 staging)
   int32_t* phys = reinterpret_cast<int32_t*>(Vt + C::VT_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   const int32_t safe_row = (int32_t)map(0);
   // zero the padding chunks of every stage once; the gather never writes them
   if (C::DQK_PAD > DQK) {
-    for (int p = tid; p < MLA_STAGES * MLA_KB * C::RC; p += MLA_THREADS) {
+    for (int p = tid; p < C::STAGES * MLA_KB * C::RC; p += MLA_THREADS) {
       const int st = p / (MLA_KB * C::RC), rr = (p / C::RC) % MLA_KB, c = p % C::RC;
       if (c * 8 >= DQK)
         *reinterpret_cast<v4i*>(Kbuf + st * C::K_BYTES + C::slot(rr, c) * 16) = (v4i){0, 0, 0, 0};
@@ -221,6 +228,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     const bool ok = head < H && col < DQK;
     s16x8 v = *reinterpret_cast<const s16x8*>(q + (r * H + (ok ? head : 0)) * (int64_t)DQK + (ok ? col : 0));
     if (!ok) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (F16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = __builtin_bit_cast(short, (_Float16)__uint_as_float((uint32_t)(uint16_t)v[e] << 16));
+    }
     asm volatile("" : "+v"(v));  // keep the queries resident: no re-load from memory per block
     Qf[ks] = v;
   }
@@ -277,8 +289,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       return pr >= 0 ? pr : safe_row;
     }
   };
-  auto gather_issue = [&](int blk, int32_t prow) {
-    const uint32_t base = kbuf_lds + (uint32_t)((blk % MLA_STAGES) * C::K_BYTES);
+  auto gather_issue = [&](int blk, int stage, int32_t prow) {
+    const uint32_t base = kbuf_lds + (uint32_t)(stage * C::K_BYTES);
     if constexpr (C::RC < WAVE) {
       (void)prow;
       for (int i = wave; i < C::DMA_INSTR; i += MLA_WAVES) {
@@ -309,8 +321,27 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     }
     }
   };
-  auto gather = [&](int blk) { gather_issue(blk, gather_rows(blk)); };
+  auto gather = [&](int blk) { gather_issue(blk, blk, gather_rows(blk)); };  // blocks 0 and 1: stages 0 and 1
 
+  // fp16 staging: the V^T operand of value step (m, dt) by transposing reads of the gathered rows.
+  // The 16-lane group g of the wave reads key quad 4 m + lh (k-elements 0-3; + 2 for k-elements 4-7),
+  // value columns f DV/2 + 32 dt + 16 (g & 1) + 0..15: its lane a addresses row 4 quad + a / 4,
+  // columns + 4 (a % 4) .. + 3, so that lane i of the group receives column + i at the quad's four
+  // keys.  Per lane: one base for each (quad parity rd, dt parity); m and dt / 2 add constants.
+  int vb[2][2];
+  static_assert(!F16 || C::STAGES == 3, "fp16 staging rotates three stages");
+  if constexpr (F16) {
+    const int g = lane >> 4, a = lane & 15, t = a >> 2;
+    const int y = 2 * (g & 1) + ((a & 3) >> 1);  // chunk within the 32-column tile pair half
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int rowq = 4 * (lh + 2 * rd) + t;     // row within the 16-key half (its swizzle is the row's)
+      const int z = (y ^ C::swz(rowq)) & (C::SWZ - 1);
+#pragma unroll
+      for (int od = 0; od < 2; ++od)  // odd dt: chunk bit 2 set before the XOR
+        vb[rd][od] = (rowq * C::RC + hf * (C::DVH / 8) + (z ^ (4 * od))) * 16 + 8 * (a & 1);
+    }
+  }
   v16f O[C::NDT];
   float mref, mlane = -INFINITY, lsum;  // mlane: this lane's running raw maximum (its head, its keys)
   // blocks up to the last one holding a valid entry (all later entries are masked: a row with fewer
@@ -334,8 +365,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
 
     if (nblk > 0) gather(0);
     if (nblk > 1) gather(1);
+    int32_t next_rows = 0;  // fp16 staging: rows of the gather issued in the next block
+    if constexpr (F16) next_rows = gather_rows(2);
+    int cur = 0;            // fp16 staging: stage of block blk
     for (int blk = 0; blk < nblk; ++blk) {
-      const uint8_t* Kst = Kbuf + (blk % MLA_STAGES) * C::K_BYTES;
+      const uint8_t* Kst = Kbuf + (F16 ? cur : blk % MLA_STAGES) * C::K_BYTES;
       // this wave's transfers of block blk are done once at most those of blk + 1 are pending
       if (blk + 1 < nblk) {
         // every wave issues DMA_PW or DMA_PW - 1 transfers per block: two immediate waits
@@ -347,12 +381,16 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         wait_vmcnt<0>();
       }
       __syncthreads();  // stage blk complete; every wave is done with block blk - 1
+      if constexpr (F16) {  // the stage of block blk - 1 is free: gather block blk + 2 into it
+        if (blk + 2 < nblk) gather_issue(blk + 2, cur == 0 ? 2 : cur - 1, next_rows);
+        next_rows = gather_rows(blk + 3);
+      }
 
       // ---- fp16 V^T of this block (VALU + LDS work) and the partial scores (MFMA work).  The two
       // waves of a SIMD (waves w and w + 4) run them in opposite orders, so one's conversion runs
       // beside the other's MFMAs instead of both waves doing the same kind of work at once.
       auto vt_build = [&]() {
-      if (converts) {
+      if (!F16 && converts) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {  // unit u = 2 m + lh: key quads 4 m + lh and 4 m + 2 + lh
           const int m = u >> 1, hh = u & 1;
@@ -364,8 +402,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       }
 
       };
-      // row indices of the next gather, read now so that they are in registers after the barrier
-      const int32_t next_rows = gather_rows(blk + 2);
+      // bf16 staging: row indices of the next gather, read now so that they are in registers after
+      // the barrier
+      if constexpr (!F16) next_rows = gather_rows(blk + 2);
       // ---- partial S^T[key][head] over this wave's contraction half; the K fragment of step
       // ks + 1 is requested before the MFMA of step ks.  MFMA runs raise the wave's issue priority
       // so that the matrix pipe is fed first when both waves of the SIMD are ready.
@@ -384,7 +423,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
           if (ks + LA - 1 < C::NKS) Af[(ks + LA - 1) % LA] = *reinterpret_cast<const s16x8*>(Kst + kfrag_off(ks + LA - 1));
           __builtin_amdgcn_sched_barrier(0);
           // the first product takes a zero accumulator operand (no register zeroing)
-          sc = mfma_bf16_32x32x16(Af[ks % LA], Qf[ks], ks == 0 ? (v16f){} : sc);
+          if constexpr (F16)
+            sc = mfma_f16_32x32x16(Af[ks % LA], Qf[ks], ks == 0 ? (v16f){} : sc);
+          else
+            sc = mfma_bf16_32x32x16(Af[ks % LA], Qf[ks], ks == 0 ? (v16f){} : sc);
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
@@ -394,15 +436,21 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
           dst[qd * WAVE] = (v4f){sc[4 * qd], sc[4 * qd + 1], sc[4 * qd + 2], sc[4 * qd + 3]};
       }
       };
-      if (wave >= MLA_WAVES / 2) {
+      if constexpr (F16) {
         qk();
-        vt_build();
+        __syncthreads();  // partial scores of both halves posted
+        cur = cur == C::STAGES - 1 ? 0 : cur + 1;
       } else {
-        vt_build();
-        qk();
+        if (wave >= MLA_WAVES / 2) {
+          qk();
+          vt_build();
+        } else {
+          vt_build();
+          qk();
+        }
+        __syncthreads();  // partial scores of both halves posted; V^T complete; stage blk no longer read
+        if (blk + 2 < nblk) gather_issue(blk + 2, blk % MLA_STAGES, next_rows);
       }
-      __syncthreads();  // partial scores of both halves posted; V^T complete; stage blk no longer read
-      if (blk + 2 < nblk) gather_issue(blk + 2, next_rows);
       if (!active) continue;
 
       // ---- full raw scores (own + partner partial), masked entries at -inf.  Element 4 qd + e
@@ -458,7 +506,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       constexpr int NSTEP = C::NDT * 2;
       const uint8_t* vsrc = Vt + (hf * C::DVH + l32) * C::VT_STRIDE + 16 * lh;
       auto vfrag = [&](int st) {  // step st: key half m = st / NDT, value tile dt = st % NDT
-        return *reinterpret_cast<const s16x8*>(vsrc + (st % C::NDT) * 32 * C::VT_STRIDE + 32 * (st / C::NDT));
+        const int m = st / C::NDT, dt = st % C::NDT;
+        if constexpr (F16) {
+          const uint8_t* p = Kst + m * 16 * C::RC * 16 + (dt >> 1) * 128;
+          const s16x4 lo = lds_read_tr16(p + vb[0][dt & 1]), hi = lds_read_tr16(p + vb[1][dt & 1]);
+          return (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          return *reinterpret_cast<const s16x8*>(vsrc + dt * 32 * C::VT_STRIDE + 32 * m);
+        }
       };
       __builtin_amdgcn_s_setprio(2);
       constexpr int LV = 3;  // V^T fragments in flight (order pinned by scheduling barriers)
@@ -565,23 +620,75 @@ __global__ __launch_bounds__(COMBINE_THREADS) void mla_combine_kernel(const floa
   if (d == 0 && lse) lse[r * H + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
+// fp16 copy of the latent rows for the fp16-staged attention: logical rows [0, rows) of one sequence
+// (through its block table, or contiguous) -> dst [rows][D] fp16, round to nearest even (exact for
+// |v| in [2^-17, 65504]; smaller magnitudes land on fp16's 2^-24 grid, larger ones overflow).
+// Each thread converts 16-byte chunks (8 values), grid-stride.
+constexpr int KV16_THREADS = 256;
+__global__ __launch_bounds__(KV16_THREADS) void mla_kv_to_f16_kernel(const uint16_t* __restrict__ kv, RowMap map,
+                                                                   int64_t rows, int32_t D,
+                                                                   uint16_t* __restrict__ dst) {
+  const int cpr = D / 8;  // chunks per row
+  const int64_t n = rows * cpr;
+  for (int64_t c = (int64_t)blockIdx.x * KV16_THREADS + threadIdx.x; c < n; c += (int64_t)gridDim.x * KV16_THREADS) {
+    const int64_t row = c / cpr;
+    const int ch = (int)(c - row * cpr);
+    const v4i w = *reinterpret_cast<const v4i*>(kv + map(row) * D + ch * 8);
+    v4i o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = (uint32_t)w[e];
+      const _Float16 lo = (_Float16)__uint_as_float(u << 16), hi = (_Float16)__uint_as_float(u & 0xFFFF0000u);
+      o[e] = (int)((uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16));
+    }
+    *reinterpret_cast<v4i*>(dst + row * D + ch * 8) = o;
+  }
+}
+
+size_t mla_kv16_bytes(int64_t S, int32_t D_qk, int32_t D_v) {
+  return (D_qk == 576 && D_v == 512 && S > 0) ? (size_t)S * D_qk * sizeof(uint16_t) : 0;
+}
+
 // ---------------------------------------------------------------------------------------------
-template <int DQK, int DV>
-static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
-  const int nsplit = a.nsplit;
-  const int kps = (a.k + nsplit - 1) / nsplit;
-  const size_t smem = mla_smem_bytes<DQK, DV>(kps);
-  // rows of the latent cache the gather may name: the paged pool, or the S contiguous keys
-  const int64_t kv_rows = a.table ? (a.num_blocks << a.block_shift) : a.S;
+template <int DQK, int DV, bool F16>
+static hipError_t launch_mla_kernel(const MlaArgs& a, const uint16_t* kv, const int32_t* table, int64_t kv_rows,
+                                    int nsplit, int kps, hipStream_t stream) {
+  const size_t smem = mla_smem_bytes<DQK, DV, F16>(kps);
+  // rows of the latent cache the gather may name: the paged pool, or the contiguous keys
   const bool off32 = (uint64_t)kv_rows * DQK * 2 <= 0xFFFFFFFFull;
-  auto kernel = off32 ? sparse_mla_kernel<DQK, DV, true> : sparse_mla_kernel<DQK, DV, false>;
+  auto kernel = off32 ? sparse_mla_kernel<DQK, DV, true, F16> : sparse_mla_kernel<DQK, DV, false, F16>;
   hipError_t e = set_max_dynamic_lds((const void*)kernel);
   if (e != hipSuccess) return e;
   const float scale_log2 = a.sm_scale * 1.4426950408889634f;
   dim3 grid((unsigned)a.R, (unsigned)nsplit);
-  e = launch("sparse_mla_kernel", kernel, grid, dim3(MLA_THREADS), smem, stream, a.q, a.kv,
-             a.idx, a.table, a.max_blocks, a.block_shift, a.num_blocks, a.per_row_table, a.seq_lens, a.S, a.q_start,
-             a.H, a.k, scale_log2, nsplit, kps, a.out, a.out_f32, a.lse, a.part_out, a.part_lse);
+  return launch("sparse_mla_kernel", kernel, grid, dim3(MLA_THREADS), smem, stream, a.q, kv, a.idx, table,
+                a.max_blocks, a.block_shift, a.num_blocks, a.per_row_table, a.seq_lens, a.S, a.q_start, a.H, a.k,
+                scale_log2, nsplit, kps, a.out, a.out_f32, a.lse, a.part_out, a.part_lse);
+}
+
+template <int DQK, int DV>
+static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
+  const int nsplit = a.nsplit;
+  const int kps = (a.k + nsplit - 1) / nsplit;
+  hipError_t e;
+  if constexpr (DQK == 576 && DV == 512) {
+    if (a.kv_f16 && !a.per_row_table) {
+      // one sequence's S rows -> contiguous fp16, then the fp16-staged kernel over them
+      const int64_t chunks = a.S * (DQK / 8);
+      const int64_t want = (chunks + KV16_THREADS - 1) / KV16_THREADS;
+      const unsigned g = (unsigned)std::max<int64_t>(std::min<int64_t>(want, 8192), 1);  // grid-stride beyond
+      e = launch("mla_kv_to_f16_kernel", mla_kv_to_f16_kernel, dim3(g), dim3(KV16_THREADS), 0,
+                 stream, a.kv, RowMap{a.table, a.block_shift, a.num_blocks}, a.S, (int32_t)DQK, a.kv_f16);
+      if (e != hipSuccess) return e;
+      e = launch_mla_kernel<DQK, DV, true>(a, a.kv_f16, nullptr, a.S, nsplit, kps, stream);
+    } else {
+      e = launch_mla_kernel<DQK, DV, false>(a, a.kv, a.table, a.table ? (a.num_blocks << a.block_shift) : a.S,
+                                            nsplit, kps, stream);
+    }
+  } else {
+    e = launch_mla_kernel<DQK, DV, false>(a, a.kv, a.table, a.table ? (a.num_blocks << a.block_shift) : a.S,
+                                          nsplit, kps, stream);
+  }
   if (e != hipSuccess || nsplit == 1) return e;
   constexpr int HPB = COMBINE_THREADS / (DV / 4);
   return launch("mla_combine_kernel", mla_combine_kernel<DV>, dim3((unsigned)a.R, (unsigned)((a.H + HPB - 1) / HPB)),

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -124,11 +124,18 @@ dsa_status_t dsa_topk_noalloc(const float *logits, int64_t ld_logits, int64_t T,
  *   q [T][H][D_qk] bf16, kv [S][D_qk] bf16 (K = all D_qk columns, V = the first D_v),
  *   indices [T][k] i32, out [T][H][D_v] bf16, out_f32 [T][H][D_v] f32 (optional, NULL to skip),
  *   lse [T][H] f32 (optional).  Probabilities are rounded to fp16 for the P.V product and V is
- *   converted bf16 -> fp16, exact for |v| in [2^-14, 65504] (precondition |v| <= 65504).
+ *   converted bf16 -> fp16, exact for |v| in [2^-17, 65504] (precondition |v| <= 65504).
  *   Supported: (D_qk, D_v) in {(576, 512), (80, 64)}, 1 <= H <= 128, 1 <= k <= 2048.
- *   The workspace is unused (size 0) and may be NULL.
+ *   Workspace (device, 256-byte aligned): NULL runs the bf16-staged kernel.  Non-NULL, with
+ *   dsa_sparse_mla_workspace_size() bytes (DSA_ERR_WORKSPACE_TOO_SMALL below that), selects fp16
+ *   staging where the dims have it ((576, 512); the size is 0 and the workspace unused otherwise):
+ *   the S latent rows are first converted to fp16 in the workspace (round to nearest even), q is
+ *   converted as it is loaded, and the scores come from fp16 products — the same products while
+ *   every q and kv value has |x| in [2^-17, 65504] (precondition |q|, |kv| <= 65504; smaller
+ *   magnitudes round to fp16's 2^-24 grid).  The two stagings agree to the tolerance of the fp32
+ *   accumulation, not bit for bit.  The workspace holds nothing the caller reads.
  */
-size_t dsa_sparse_mla_workspace_size(int64_t T, int32_t H, int32_t D_v, int32_t k);
+size_t dsa_sparse_mla_workspace_size(int64_t T, int64_t S, int32_t H, int32_t D_qk, int32_t D_v, int32_t k);
 dsa_status_t dsa_sparse_mla_fwd(const uint16_t *q, const uint16_t *kv, const int32_t *indices,
                                 int64_t T, int64_t S, int32_t H, int32_t D_qk, int32_t D_v, int32_t k,
                                 int64_t q_start, float sm_scale, uint16_t *out, float *out_f32,
@@ -199,7 +206,9 @@ typedef struct {
  * kernels as the three standalone calls.  q8/q_scale/w/q as in the standalone calls,
  * out [T][H][D_v] bf16, out_f32 (optional), lse [T][H] (optional), indices_out [T][topk]
  * (optional; written when non-NULL).  Workspace: dsa_prefill_workspace_size() bytes, 256-byte
- * aligned.  T <= 1,048,576 per call, as dsa_indexer_logits.  Once the call's stream work has
+ * aligned; at (D_qk, D_v) = (576, 512) it includes the fp16 copy of the sequence's S latent rows
+ * and the sparse MLA runs with fp16 staging (see dsa_sparse_mla_fwd; precondition |q|, |kv| <=
+ * 65504).  T <= 1,048,576 per call, as dsa_indexer_logits.  Once the call's stream work has
  * completed, the first T * ld * 4 bytes of the workspace hold the index scores, fp32 [T][ld] with
  * ld = (S + 3) / 4 * 4 and entries s < n_t written (the scores the top-k selected from); the rest
  * of the workspace is private.

@@ -36,13 +36,13 @@ class PrefillDev:
         self.kv = dput(inp.kv, dev).view(torch.bfloat16)
 
 
-def run_chain(d: PrefillDev):
+def run_chain(d: PrefillDev, staging: str = "fp16"):
     wl = d.inp.wl
     S = d.k8.shape[0]
     logits = dsa.dsa_indexer_logits(d.q8, d.qs, d.w, d.k8, d.ks, q_start=wl.q_start)
     idx = dsa.dsa_topk(logits, wl.topk, S, q_start=wl.q_start)
     out, out_f32, lse = dsa.dsa_sparse_mla_fwd(d.q, d.kv, idx, wl.sm_scale, wl.D_v, q_start=wl.q_start,
-                                               want_f32=True)
+                                               want_f32=True, staging=staging)
     return logits, idx, out, out_f32, lse
 
 

@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     assert lib.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
 
 
@@ -89,6 +89,15 @@ def test_mla_argument_errors(lib):
              None) == INVALID
     assert f(FAKE, FAKE, None, 4, 8, 128, 576, 512, 64, 0, sm, FAKE, None, None, None, 0, None) == INVALID
     assert f(FAKE, FAKE, FAKE, 4, 8, 128, 576, 512, 64, 0, sm, FAKE, FAKE + 8, None, None, 0, None) == INVALID
+    # fp16 staging: the workspace holds the fp16 copy of the S latent rows (576/512 only)
+    ws = lib.dsa_sparse_mla_workspace_size
+    assert ws(4, 8, 128, 576, 512, 64) == 8 * 576 * 2
+    assert ws(4, 9, 128, 576, 512, 64) == (9 * 576 * 2 + 255) // 256 * 256
+    assert ws(4, 8, 128, 80, 64, 64) == 0 and ws(0, 8, 128, 576, 512, 64) == 0
+    need = ws(4, 8, 128, 576, 512, 64)
+    assert f(FAKE, FAKE, FAKE, 4, 8, 128, 576, 512, 64, 0, sm, FAKE, None, None, FAKE, need - 1, None) == WS_SMALL
+    assert f(FAKE, FAKE, FAKE, 4, 8, 128, 576, 512, 64, 0, sm, FAKE, None, None, FAKE + 8, need, None) == INVALID
+    assert "aligned" in _err(lib)
 
 
 def test_fused_argument_errors(lib):

@@ -27,12 +27,12 @@ def _log(*a):
     print(*a, flush=True)
 
 
-def _full_check(wl, dev, mla_rows=None, idx_rows=None):
+def _full_check(wl, dev, mla_rows=None, idx_rows=None, staging="fp16"):
     """Whole-path parity for a prefill workload; oracle on all rows or on the given subsets."""
-    _log("case", wl.name, "T", wl.T, "S", wl.S)
+    _log("case", wl.name, "T", wl.T, "S", wl.S, "staging", staging)
     inp = prefill_inputs(wl)
     d = PrefillDev(inp, dev)
-    logits, idx, out, out_f32, lse = run_chain(d)
+    logits, idx, out, out_f32, lse = run_chain(d, staging)
     torch.cuda.synchronize()
     S = wl.S
     rows = np.arange(wl.T) if idx_rows is None else np.asarray(idx_rows)
@@ -71,11 +71,13 @@ def test_tiny_full(dev):
     _full_check(get("tiny"), dev)
 
 
-def test_prefill_4k(dev):
+@pytest.mark.parametrize("staging", ["fp16", "bf16"])
+def test_prefill_4k(dev, staging):
+    """fp16 staging (latent rows converted in the workspace) and bf16 staging (no workspace)."""
     wl = get("prefill_4k")
     rows = np.unique(np.concatenate([np.arange(0, 4096, 61), [0, 1, 2047, 2048, 2049, 4094, 4095]]))
     mla_rows = np.array([0, 1, 17, 1000, 2046, 2047, 2048, 2049, 3001, 4095])
-    _full_check(wl, dev, mla_rows=mla_rows, idx_rows=rows)
+    _full_check(wl, dev, mla_rows=mla_rows, idx_rows=rows, staging=staging)
 
 
 def test_ragged_small_prefill(dev):

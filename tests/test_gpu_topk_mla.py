@@ -136,27 +136,31 @@ def test_topk_row_lengths_across_layouts(dev):
 
 
 # ------------------------------------------------------------------------------------- MLA
-def _mla_case(dev, T, S, H, D_qk, D_v, k, idx, q_start, sm, name, seed=40):
+def _mla_case(dev, T, S, H, D_qk, D_v, k, idx, q_start, sm, name, seed=40, staging="fp16", q=None, kv=None):
     import dsa_lightning_indexer_02_amd as dsa
-    print("case", name, flush=True)
+    print("case", name, "staging", staging, flush=True)
     g = block_rng(seed, 0, 0)
-    q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
-    kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
+    if q is None:
+        q = to_bf16_bits(g.standard_normal((T, H, D_qk)).astype(np.float32))
+    if kv is None:
+        kv = to_bf16_bits(g.standard_normal((S, D_qk)).astype(np.float32))
     out, f32, lse = dsa.dsa_sparse_mla_fwd(dput(q, dev).view(torch.bfloat16), dput(kv, dev).view(torch.bfloat16),
-                                           dput(idx.astype(np.int32), dev), sm, D_v, q_start=q_start, want_f32=True)
+                                           dput(idx.astype(np.int32), dev), sm, D_v, q_start=q_start, want_f32=True,
+                                           staging=staging)
     o, _, ol = oracle.sparse_mla(q, idx.astype(np.int32), q_start + np.arange(T), kv, D_v, sm)
     parity.check_mla(bf16_vals(out), dget(f32), dget(lse), o, ol, name)
     return dget(f32), dget(lse)
 
 
-def test_mla_invalid_duplicate_entries(dev):
+@pytest.mark.parametrize("staging", ["fp16", "bf16"])
+def test_mla_invalid_duplicate_entries(dev, staging):
     g = block_rng(41, 0, 0)
     T, S, k = 24, 3000, 2048
     idx = g.integers(-5, S + 50, size=(T, k))
     idx[:, 10:20] = idx[:, 0:10]          # duplicates
     idx[5] = -1                           # nothing valid in row 5
     idx[6, 1:] = -1                       # a single entry
-    _mla_case(dev, T, S, 128, 576, 512, k, idx, 2000, 1 / np.sqrt(192), "invalid/duplicate")
+    _mla_case(dev, T, S, 128, 576, 512, k, idx, 2000, 1 / np.sqrt(192), "invalid/duplicate", staging=staging)
 
 
 def test_mla_small_dims_and_heads(dev):
@@ -167,13 +171,28 @@ def test_mla_small_dims_and_heads(dev):
     _mla_case(dev, T, S, 100, 576, 512, k, idx, 200, 0.07, "H=100 (partial head tile)")
 
 
-def test_mla_k1_and_large_logits(dev):
+@pytest.mark.parametrize("staging", ["fp16", "bf16"])
+def test_mla_k1_and_large_logits(dev, staging):
     g = block_rng(43, 0, 0)
     T, S = 16, 500
     idx1 = g.integers(0, S, size=(T, 1))
-    f32, lse = _mla_case(dev, T, S, 128, 576, 512, 1, idx1, S, 1 / np.sqrt(192), "k=1")
+    f32, lse = _mla_case(dev, T, S, 128, 576, 512, 1, idx1, S, 1 / np.sqrt(192), "k=1", staging=staging)
     idx = np.stack([g.permutation(S)[:256] for _ in range(T)])
-    _mla_case(dev, T, S, 128, 576, 512, 256, idx, S, 2.0, "sharp softmax (rescale path)")
+    _mla_case(dev, T, S, 128, 576, 512, 256, idx, S, 2.0, "sharp softmax (rescale path)", staging=staging)
+
+
+@pytest.mark.parametrize("staging", ["fp16", "bf16"])
+def test_mla_value_magnitude_spread(dev, staging):
+    """q and kv with magnitudes from 2^-24 up to a few units (every element N(0,1) times 2^e, e
+    uniform in [-24, 0]): fp16 staging meets fp16's subnormal range and rounds the values below
+    2^-17 to its 2^-24 grid; the results still meet the attention bar against the exact oracle."""
+    g = block_rng(46, 0, 0)
+    T, S, k = 20, 1500, 512
+    q = g.standard_normal((T, 128, 576)) * np.exp2(g.integers(-24, 1, size=(T, 128, 576)))
+    kv = g.standard_normal((S, 576)) * np.exp2(g.integers(-24, 1, size=(S, 576)))
+    idx = np.stack([g.permutation(S)[:k] for _ in range(T)])
+    _mla_case(dev, T, S, 128, 576, 512, k, idx, S, 1 / np.sqrt(192), "magnitude spread", staging=staging,
+              q=to_bf16_bits(q.astype(np.float32)), kv=to_bf16_bits(kv.astype(np.float32)))
 
 
 def test_many_rows_one_launch(dev):
