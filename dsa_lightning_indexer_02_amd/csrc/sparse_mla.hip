@@ -165,22 +165,42 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     }
     return;
   }
-  // physical rows of this workgroup's index entries (-1: skipped entry)
-  for (int i = tid; i < cnt; i += MLA_THREADS) {
-    const int32_t li = idx[r * k + i0 + i];
-    phys[i] = (li >= 0 && li < n) ? (int32_t)map(li) : -1;
+  // The prologue overlaps its memory latencies: the index entries (four per thread) are loaded
+  // first, then the block-table lookups they need, then the queries; the tables below are built
+  // while the queries are in flight, and the first gathers are issued before the queries are
+  // awaited.
+  static_assert(MLA_MAX_K == 4 * MLA_THREADS, "four index entries per thread");
+  int32_t prow4[4];
+  bool valid4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + j * MLA_THREADS;
+    const int32_t li = i < cnt ? idx[r * k + i0 + i] : -1;
+    valid4[j] = li >= 0 && li < n;
+    prow4[j] = li;
   }
-  // validity bit mask of every 32-entry block (bit i: entry 32 b + i is gathered and attended)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) prow4[j] = valid4[j] ? (int32_t)map(prow4[j]) : -1;  // -1: skipped entry
+  // queries of this wave's head group and contraction half, as B operands of S^T = K Q^T (loads
+  // only: converted and pinned to registers before the block loop)
+  const bool active = hg * MLA_GROUP_HEADS < H;
+  const int head = hg * MLA_GROUP_HEADS + l32;
+  s16x8 Qf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    const int col = hf * C::DH + ks * 16 + lh * 8;
+    const bool ok = head < H && col < DQK;
+    Qf[ks] = *reinterpret_cast<const s16x8*>(q + (r * H + (ok ? head : 0)) * (int64_t)DQK + (ok ? col : 0));
+  }
+  // physical rows of the index entries, and the validity bit mask of every 32-entry block (bit i:
+  // entry 32 b + i is gathered and attended)
   uint32_t* vmask_lds = reinterpret_cast<uint32_t*>(phys + MLA_MAX_K + 4);
-  for (int base = wave * WAVE; base < (cnt + 63) / 64 * 64; base += MLA_WAVES * WAVE) {
-    const int i = base + lane;
-    bool v = false;
-    if (i < cnt) {
-      const int32_t li = idx[r * k + i0 + i];
-      v = li >= 0 && li < n;
-    }
-    const uint64_t bits = __ballot(v);
-    if (lane == 0) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + j * MLA_THREADS, base = wave * WAVE + j * MLA_THREADS;
+    if (i < cnt) phys[i] = prow4[j];
+    const uint64_t bits = __ballot(valid4[j]);
+    if (lane == 0 && base < cnt) {
       vmask_lds[base / 32] = (uint32_t)bits;
       if (base + 32 < cnt) vmask_lds[base / 32 + 1] = (uint32_t)(bits >> 32);
     }
@@ -218,24 +238,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     }
   }
 
-  // queries of this wave's head group and contraction half, as B operands of S^T = K Q^T
-  const bool active = hg * MLA_GROUP_HEADS < H;
-  const int head = hg * MLA_GROUP_HEADS + l32;
-  s16x8 Qf[C::NKS];
-#pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-    const int col = hf * C::DH + ks * 16 + lh * 8;
-    const bool ok = head < H && col < DQK;
-    s16x8 v = *reinterpret_cast<const s16x8*>(q + (r * H + (ok ? head : 0)) * (int64_t)DQK + (ok ? col : 0));
-    if (!ok) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (F16) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = __builtin_bit_cast(short, (_Float16)__uint_as_float((uint32_t)(uint16_t)v[e] << 16));
-    }
-    asm volatile("" : "+v"(v));  // keep the queries resident: no re-load from memory per block
-    Qf[ks] = v;
-  }
   __syncthreads();
 
   const uint32_t kbuf_lds = lds_addr(Kbuf);
@@ -354,6 +356,23 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   int32_t* overflow_flag = phys + MLA_MAX_K;  // one int after the row list
   const v4f* Sx_mine = reinterpret_cast<const v4f*>(Sx) + wave * 4 * WAVE + lane;
   const v4f* Sx_peer = reinterpret_cast<const v4f*>(Sx) + (wave ^ 1) * 4 * WAVE + lane;
+  // first two gathers of the first pass, then the queries (zero outside the heads and columns,
+  // fp16 for fp16 staging), pinned to registers: no re-load from memory per block
+  if (nblk > 0) gather(0);
+  if (nblk > 1) gather(1);
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    const int col = hf * C::DH + ks * 16 + lh * 8;
+    s16x8 v = Qf[ks];
+    if (!(head < H && col < DQK)) v = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (F16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = __builtin_bit_cast(short, (_Float16)__uint_as_float((uint32_t)(uint16_t)v[e] << 16));
+    }
+    asm volatile("" : "+v"(v));
+    Qf[ks] = v;
+  }
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) O[dt] = (v16f){};
@@ -363,8 +382,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
     bool have_ref = pass != 0;  // wave-uniform: all heads of a wave get their reference together
     bool overflow = false;
 
-    if (nblk > 0) gather(0);
-    if (nblk > 1) gather(1);
+    if (pass > 0) {  // the first pass issued its first gathers before the queries were awaited
+      if (nblk > 0) gather(0);
+      if (nblk > 1) gather(1);
+    }
     int32_t next_rows = 0;  // fp16 staging: rows of the gather issued in the next block
     if constexpr (F16) next_rows = gather_rows(2);
     int cur = 0;            // fp16 staging: stage of block blk
@@ -555,10 +576,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
       for (int qd = 0; qd < 4; ++qd) {
         const int d = hf * C::DVH + dt * 32 + 8 * qd + 4 * lh;
         const v4f o = (v4f){O[dt][4 * qd], O[dt][4 * qd + 1], O[dt][4 * qd + 2], O[dt][4 * qd + 3]} * inv;
-        s16x4 ob;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ob[e] = (short)f32_to_bf16(o[e]);
-        *reinterpret_cast<s16x4*>(orow + d) = ob;
+        *reinterpret_cast<v2i*>(orow + d) = (v2i){(int)f32x2_to_bf16x2(o[0], o[1]), (int)f32x2_to_bf16x2(o[2], o[3])};
         if (out_f32) *reinterpret_cast<v4f*>(out_f32 + (r * H + head) * (int64_t)DV + d) = o;
       }
     if (hf == 0 && lh == 0 && lse) lse[r * H + head] = lse_v;
@@ -612,10 +630,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void mla_combine_kernel(const floa
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   const v4f o = acc * inv;
-  s16x4 ob;
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) ob[rr] = (short)f32_to_bf16(o[rr]);
-  *reinterpret_cast<s16x4*>(out + (r * H + h) * (int64_t)DV + d) = ob;
+  *reinterpret_cast<v2i*>(out + (r * H + h) * (int64_t)DV + d) =
+      (v2i){(int)f32x2_to_bf16x2(o[0], o[1]), (int)f32x2_to_bf16x2(o[2], o[3])};
   if (out_f32) *reinterpret_cast<v4f*>(out_f32 + (r * H + h) * (int64_t)DV + d) = o;
   if (d == 0 && lse) lse[r * H + h] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
