@@ -10,14 +10,20 @@
 // groups of 32, one 32x32 MFMA tile each; every group is served by a pair of waves that split
 // the contraction: wave half f holds the queries of columns [f D_qk/2, (f+1) D_qk/2) and the
 // fp32 output accumulators of value columns [f D_v/2, (f+1) D_v/2).  Per block of 32 selected
-// rows (gathered HBM/L2 -> LDS by DMA, bf16, row-major):
-//   1. each wave forms its partial S^T = K_f Q_f^T (bf16 32x32x16 MFMA) and posts it in LDS;
+// rows (gathered HBM/L2 -> LDS by DMA, row-major):
+//   1. each wave forms its partial S^T = K_f Q_f^T (32x32x16 MFMA) and posts it in LDS;
 //   2. each wave adds its partner's partial (addition commutes, so both hold the same S^T),
 //      and computes the probabilities of its 16 entries per lane in fp16;
 //   3. out^T = V^T P^T (fp16 32x32x16 MFMA): the S^T accumulator layout is the B-operand layout
-//      of P^T, so probabilities never leave registers.  V^T is built once per block by all waves
-//      (transposing LDS reads of the gathered rows, bf16 -> fp16 in registers, exact for |v| in
-//      [2^-14, 65504]) into an fp16 buffer whose key order matches that B-operand layout.
+//      of P^T, so probabilities never leave registers.
+// Two stagings of the gathered rows.  fp16 staging (the prefill path, given a workspace): the
+// rows were converted to fp16 beforehand (mla_kv_to_f16_kernel), the queries are converted as
+// they are loaded, S^T is an fp16 MFMA of the same values, and step 3 takes its V^T operands
+// straight from the gathered rows by transposing LDS reads; three stages rotate.  bf16 staging
+// (decode, and calls without a workspace): S^T is a bf16 MFMA, and V^T is built once per block
+// by all waves (transposing LDS reads, bf16 -> fp16 in registers) into an fp16 buffer whose key
+// order matches the B-operand layout of P^T; two stages rotate.  Either way bf16 -> fp16 is exact
+// for |x| in [2^-17, 65504].
 // P is rounded to fp16 (11-bit significand) rather than bf16.  The softmax reference maximum is
 // fixed at the first block holding a valid entry; a second pass with the exact row maximum runs
 // only if a later block exceeds it by more than 2^15 (the fp16 headroom).
