@@ -360,7 +360,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
   const uint64_t live = __ballot(lane < nblk_all && vmask_lds[lane] != 0u);
   const int nblk = live ? 64 - __clzll(live) : 0;
   int32_t* overflow_flag = phys + MLA_MAX_K;  // one int after the row list
-  const v4f* Sx_mine = reinterpret_cast<const v4f*>(Sx) + wave * 4 * WAVE + lane;
   const v4f* Sx_peer = reinterpret_cast<const v4f*>(Sx) + (wave ^ 1) * 4 * WAVE + lane;
   // first two gathers of the first pass, then the queries (zero outside the heads and columns,
   // fp16 for fp16 staging), pinned to registers: no re-load from memory per block
@@ -413,9 +412,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
         next_rows = gather_rows(blk + 3);
       }
 
-      // ---- fp16 V^T of this block (VALU + LDS work) and the partial scores (MFMA work).  The two
-      // waves of a SIMD (waves w and w + 4) run them in opposite orders, so one's conversion runs
-      // beside the other's MFMAs instead of both waves doing the same kind of work at once.
+      // ---- bf16 staging: fp16 V^T of this block (VALU + LDS work) and the partial scores (MFMA
+      // work).  The two waves of a SIMD (waves w and w + 4) run them in opposite orders, so one's
+      // conversion runs beside the other's MFMAs instead of both waves doing the same kind of work
+      // at once.  fp16 staging has no V^T to build.
       auto vt_build = [&]() {
       if (!F16 && converts) {
 #pragma unroll
@@ -512,7 +512,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void sparse_mla_kernel(
           }
         }
       }
-      (void)Sx_mine;
       if (!have_ref && vm != 0u) {  // wave-uniform: the block mask is shared by all lanes
         // first block with a valid entry: its maximum becomes the reference (log2 units; the
         // scale is positive, so the maximum commutes with it)
@@ -720,11 +719,6 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t stream) {
 bool mla_supported(int32_t D_qk, int32_t D_v, int32_t H, int32_t k) {
   const bool dims = (D_qk == 576 && D_v == 512) || (D_qk == 80 && D_v == 64);
   return dims && H >= 1 && H <= MLA_GROUPS * MLA_GROUP_HEADS && k >= 1 && k <= MLA_MAX_K;
-}
-
-size_t mla_smem_for(int32_t D_qk, int32_t D_v, int32_t keys_per_wg) {
-  if (D_qk == 576) return mla_smem_bytes<576, 512>(keys_per_wg);
-  return mla_smem_bytes<80, 64>(keys_per_wg);
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
