@@ -44,6 +44,11 @@ constexpr int KL_KB = 32;
 constexpr int KL_STAGES = 4;
 constexpr int KL_ISSUERS = KL_WAVES - KL_TOK;  // waves with grp != 0
 
+template <int P>  // a compile-time pass number
+struct PassTag {
+  static constexpr int value = P;
+};
+
 template <int NKS>  // NKS 16-column contraction steps: the latent row padded to 16 NKS columns
 struct KlCfg {
   static constexpr int DP = 16 * NKS;
@@ -174,12 +179,11 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
   for (int u = 0; u < KP; ++u) kbase[u] = (l32 * C::RC + ((2 * u + lh) ^ kx)) * 16;
   auto koff = [&](int ks) { return kbase[ks % KP] + (ks / KP) * (2 * KP * 16); };
 
-  float st_m[16], st_l[16], lse2[16];
+  float st_m[16], st_l[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     st_m[r] = KL_NEG;
     st_l[r] = 0.f;
-    lse2[r] = INFINITY;
   }
   const float inv_h = 1.0f / (float)H;
   float lacc = 0.f;  // loss of the row (log2 units), lanes 0..31 of the row's first wave
@@ -198,7 +202,13 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
     }
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
+  // The two passes are separate straight-line phases: the running maxima and sums of the first and
+  // the normalisers of the second are never live together, which leaves the registers for the
+  // fragment look-ahead (with all three sets live the compiler serialised every LDS read with its
+  // MFMA).
+  float lse2[16];
+  auto block_loop = [&](auto pass_tag) {
+    constexpr int pass = decltype(pass_tag)::value;
     for (int b = 0; b < KL_STAGES - 1 && b < nblk; ++b) issue(b);
     for (int blk = 0; blk < nblk; ++blk) {
       // this wave's copies of block blk are done once at most those of the blocks after it are
@@ -206,7 +216,9 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
       const int later = min(KL_STAGES - 2, nblk - 1 - blk);
       vm_wait_pending(later * my_dma);
       __syncthreads();  // block blk is in LDS; every wave is done with block blk - 1
-      if (pass == 1 && blk > 0 && row_ok) finalize(blk - 1);
+      if constexpr (pass == 1) {
+        if (blk > 0 && row_ok) finalize(blk - 1);
+      }
       if (blk + KL_STAGES - 1 < nblk) issue(blk + KL_STAGES - 1);
       if (!active) continue;
       const uint8_t* Kst = Kbuf + (blk % KL_STAGES) * C::K_BYTES;
@@ -218,11 +230,13 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (ks + LA - 1 < NKS) Bf[(ks + LA - 1) % LA] = *reinterpret_cast<const s16x8*>(Kst + koff(ks + LA - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the look-ahead: each product waits for its own fragment only
         acc = mfma_bf16_32x32x16(Qf[ks], Bf[ks % LA], acc);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // lane: key blk * KB + l32; element r: head 32 grp + 8 (r / 4) + 4 lh + r % 4
       const bool valid = (int64_t)blk * KL_KB + l32 < n;
-      if (pass == 0) {
+      if constexpr (pass == 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) lse_push(st_m[r], st_l[r], valid ? acc[r] * scale_log2 : -INFINITY);
       } else {
@@ -234,22 +248,21 @@ __global__ __launch_bounds__(KL_THREADS, 1) void indexer_kl_kernel(
         if (lh == 0) red[((blk & 1) * KL_TOK + tok) * KL_GROUPS * KL_KB + grp * KL_KB + l32] = ps;
       }
     }
-    if (pass == 0) {
-      // each head's normaliser: merge the 32 lanes that hold it (one key column each)
+  };
+  block_loop(PassTag<0>{});
+  // each head's normaliser: merge the 32 lanes that hold it (one key column each)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float m = st_m[r], l = st_l[r];
-        for (int o = 1; o < 32; o <<= 1) lse_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
-        const int hh = grp * 32 + 8 * (r / 4) + 4 * lh + r % 4;
-        lse2[r] = (hh < H && l > 0.f) ? m + __builtin_amdgcn_logf(l) : INFINITY;
-      }
-      __syncthreads();  // both stages free before pass 2 refills them
-    } else {
-      vm_wait<0>();
-      __syncthreads();
-      if (row_ok && nblk > 0) finalize(nblk - 1);
-    }
+  for (int r = 0; r < 16; ++r) {
+    float m = st_m[r], l = st_l[r];
+    for (int o = 1; o < 32; o <<= 1) lse_merge(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
+    const int hh = grp * 32 + 8 * (r / 4) + 4 * lh + r % 4;
+    lse2[r] = (hh < H && l > 0.f) ? m + __builtin_amdgcn_logf(l) : INFINITY;
   }
+  __syncthreads();  // every stage free before the second pass refills them
+  block_loop(PassTag<1>{});
+  vm_wait<0>();
+  __syncthreads();
+  if (row_ok && nblk > 0) finalize(nblk - 1);
   if (grp == 0 && row_ok) {
     float v = lh == 0 ? lacc : 0.f;
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
