@@ -312,17 +312,28 @@ __global__ __launch_bounds__(BW_THREADS, 1) void sparse_mla_bwd_dq_kernel(
       Bh[rr >> 3][rr & 7] = bf16_hi(ds[rr]);
       Bl[rr >> 3][rr & 7] = bf16_lo(ds[rr]);
     }
+    // A fragment of step i = (tile dt, key step m) = (i / 2, i % 2), read LA - 1 steps ahead so that
+    // each pair of products waits for its own fragment only
+    auto afrag = [&](int i) {
+      const int dt = i >> 1, m = i & 1;
+      const int off = (dt >> 1) * 128 + m * 16 * C::RC * 16;
+      const s16x4 x0 = lds_transpose_read16(Kst + kt_base[0][dt & 1] + off);
+      const s16x4 x1 = lds_transpose_read16(Kst + kt_base[1][dt & 1] + off);
+      return (s16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    };
+    constexpr int NSTEP = 2 * C::NQT, LA = 3;
+    s16x8 Af[LA];
 #pragma unroll
-    for (int dt = 0; dt < C::NQT; ++dt)
+    for (int i = 0; i < LA - 1; ++i) Af[i] = afrag(i);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int off = (dt >> 1) * 128 + m * 16 * C::RC * 16;
-        const s16x4 x0 = lds_transpose_read16(Kst + kt_base[0][dt & 1] + off);
-        const s16x4 x1 = lds_transpose_read16(Kst + kt_base[1][dt & 1] + off);
-        const s16x8 A = (s16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        acc[dt] = mfma_bf16_32x32x16(A, Bh[m], acc[dt]);
-        acc[dt] = mfma_bf16_32x32x16(A, Bl[m], acc[dt]);
-      }
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + LA - 1 < NSTEP) Af[(i + LA - 1) % LA] = afrag(i + LA - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int dt = i >> 1, m = i & 1;
+      acc[dt] = mfma_bf16_32x32x16(Af[i % LA], Bh[m], acc[dt]);
+      acc[dt] = mfma_bf16_32x32x16(Af[i % LA], Bl[m], acc[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if (pass == 0) {
     // D of this lane's head: its 16 keys plus the other lane half's (both waves of a pair hold
